@@ -1,0 +1,222 @@
+"""Thin ctypes binding over libcsa_attn.so (include/csa_attn.h).
+
+Argument marshalling only: every step of the CSA / HCA path runs in the HIP
+kernels behind the C ABI.  torch provides device memory (tensors passed by
+data_ptr()) and the current HIP stream.  There is no fallback: if the shared
+library is missing or fails to load, every call raises.
+"""
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa_attn.so")
+
+F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
+STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_CAPACITY",
+          4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_HIP"}
+EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
+           "csa_attn_workspace_size", "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "attn_out_proj_grouped",
+           "csa_last_error"]
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class KVCacheT(C.Structure):
+    _fields_ = [("rec", C.c_void_p), ("fmt", C.c_int32), ("d", C.c_int32), ("d_rope", C.c_int32),
+                ("ring", C.c_int32), ("cap", C.c_int64)]
+
+
+class IdxCacheT(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("fmt", C.c_int32), ("di", C.c_int32),
+                ("cap", C.c_int64)]
+
+
+class AttnParamsT(C.Structure):
+    _fields_ = [("head_dim", C.c_int32), ("rope_dim", C.c_int32), ("window", C.c_int32), ("m", C.c_int32),
+                ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("rms_eps", C.c_float)]
+
+
+_lib = None
+_V, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python long_context_attention_23_amd/build.py")
+        L = C.CDLL(LIB_PATH)
+        L.csa_kv_record_bytes.restype = _SZ
+        L.csa_kv_record_bytes.argtypes = [_I32, _I32, _I32]
+        L.csa_last_error.restype = C.c_char_p
+        L.csa_last_error.argtypes = []
+        L.csa_compress_kv.restype = C.c_int
+        L.csa_compress_kv.argtypes = [_V, _I32, _I32, _I64, _I32, _V, _I32, _V, _V, _V, _F, _I32, _F,
+                                      C.POINTER(KVCacheT), C.POINTER(IdxCacheT), _V]
+        L.csa_indexer_topk_workspace_size.restype = _SZ
+        L.csa_indexer_topk_workspace_size.argtypes = [_I32, _I32, _I64, _I32]
+        L.csa_indexer_topk.restype = C.c_int
+        L.csa_indexer_topk.argtypes = [_V, _V, _I32, _V, C.POINTER(IdxCacheT), _V, _I32, _I32, _I32, _I32,
+                                       _I32, _V, _V, _SZ, _V]
+        L.csa_attn_workspace_size.restype = _SZ
+        L.csa_attn_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I64, _I32, _I32, _I32]
+        L.csa_sparse_mqa_attn.restype = C.c_int
+        L.csa_sparse_mqa_attn.argtypes = [_V, _I32, _V, _V, _I32, C.POINTER(KVCacheT), C.POINTER(KVCacheT), _V,
+                                          _V, C.POINTER(AttnParamsT), _I32, _I32, _I32, _V, _I32, _V, _SZ, _V]
+        L.hca_dense_mqa_attn.restype = C.c_int
+        L.hca_dense_mqa_attn.argtypes = [_V, _I32, _V, C.POINTER(KVCacheT), C.POINTER(KVCacheT), _V, _V,
+                                         C.POINTER(AttnParamsT), _I32, _I32, _I32, _V, _I32, _V, _SZ, _V]
+        L.attn_out_proj_grouped.restype = C.c_int
+        L.attn_out_proj_grouped.argtypes = [_V, _I32, _V, _I32, _I64, _I32, _I32, _I32, _V, _I32, _V]
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise CsaError(status, lib().csa_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return C.c_void_p(stream)
+    if torch.cuda.is_available():
+        return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return None
+
+
+def torch_dtype_code(t):
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def kv_record_bytes(fmt, d, d_rope):
+    return int(lib().csa_kv_record_bytes(fmt, d, d_rope))
+
+
+class KVCache:
+    """[B][cap] records of one KV format (see csa_kv_cache)."""
+
+    def __init__(self, B, cap, d, d_rope, fmt, ring=False, device="cuda", rec=None):
+        self.B, self.cap, self.d, self.d_rope, self.fmt, self.ring = B, cap, d, d_rope, fmt, bool(ring)
+        self.rec_bytes = kv_record_bytes(fmt, d, d_rope)
+        self.rec = rec if rec is not None else torch.zeros((B, cap, self.rec_bytes), dtype=torch.uint8, device=device)
+
+    def struct(self):
+        return KVCacheT(self.rec.data_ptr(), self.fmt, self.d, self.d_rope, 1 if self.ring else 0, self.cap)
+
+
+class IdxCache:
+    """[B][cap] indexer key rows (see csa_idx_cache)."""
+
+    def __init__(self, B, cap, di, fmt, device="cuda", codes=None, scales=None):
+        self.B, self.cap, self.di, self.fmt = B, cap, di, fmt
+        rb = {F32: 4 * di, BF16: 2 * di, FP4_E2M1: di // 2}[fmt]
+        self.codes = codes if codes is not None else torch.zeros((B, cap, rb), dtype=torch.uint8, device=device)
+        if fmt == FP4_E2M1:
+            self.scales = scales if scales is not None else torch.zeros((B, cap, di // 32), dtype=torch.uint8, device=device)
+        else:
+            self.scales = None
+
+    def struct(self):
+        return IdxCacheT(self.codes.data_ptr(), None if self.scales is None else self.scales.data_ptr(),
+                         self.fmt, self.di, self.cap)
+
+
+def compress_kv(x, tok_start, m, score_bias, *, score_proj=None, gamma=None, eps=1e-6, rope_dim=0,
+                rope_base=10000.0, kv_out=None, idx_out=None, stream=None):
+    """csa_compress_kv.  x: [B, T, d] float32 / bfloat16; tok_start: int32 [B]."""
+    B, T, d = x.shape
+    kvs = C.byref(kv_out.struct()) if kv_out is not None else None
+    ixs = C.byref(idx_out.struct()) if idx_out is not None else None
+    _check(lib().csa_compress_kv(_ptr(x), torch_dtype_code(x), B, T, d, _ptr(tok_start), m, _ptr(score_bias),
+                                 _ptr(score_proj), _ptr(gamma), eps, rope_dim, rope_base, kvs, ixs, _stream(stream)))
+
+
+def indexer_workspace_bytes(B, Tq, key_cap, topk):
+    return int(lib().csa_indexer_topk_workspace_size(B, Tq, key_cap, topk))
+
+
+def indexer_topk(q_idx, q_dtype, w_idx, keys, q_pos, m, topk, *, q_scales=None, out=None, workspace=None,
+                 stream=None):
+    """csa_indexer_topk.  q_idx: [B, Tq, Hi, row bytes] uint8 codes (or f32 / bf16 [B, Tq, Hi, di]);
+    w_idx: f32 [B, Tq, Hi]; q_pos: int32 [B, Tq].  Returns int32 [B, Tq, topk]."""
+    B, Tq, Hi = w_idx.shape
+    if out is None:
+        out = torch.empty((B, Tq, topk), dtype=torch.int32, device=w_idx.device)
+    need = indexer_workspace_bytes(B, Tq, keys.cap, topk)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w_idx.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().csa_indexer_topk(_ptr(q_idx), _ptr(q_scales), q_dtype, _ptr(w_idx), C.byref(keys.struct()),
+                                  _ptr(q_pos), B, Tq, Hi, m, topk, _ptr(out), _ptr(workspace), wsb, _stream(stream)))
+    return out
+
+
+def attn_workspace_bytes(B, Tq, H, d, max_comp_entries, window, q_dtype, comp_fmt):
+    return int(lib().csa_attn_workspace_size(B, Tq, H, d, max_comp_entries, window, q_dtype, comp_fmt))
+
+
+def attn_params(d, dr, window, m, base=10000.0, scale=None, eps=1e-6):
+    return AttnParamsT(d, dr, window, m, base, (d ** -0.5) if scale is None else scale, eps)
+
+
+def _attn(sparse, q, q_pos, comp, win, sink, params, *, topk_idx=None, gamma_q=None, out=None,
+          out_dtype=None, workspace=None, stream=None):
+    B, Tq, H, d = q.shape
+    qd = torch_dtype_code(q)
+    if out is None:
+        out = torch.empty((B, Tq, H, d), dtype=out_dtype or q.dtype, device=q.device)
+    od = torch_dtype_code(out)
+    k = topk_idx.shape[-1] if sparse else 0
+    need = attn_workspace_bytes(B, Tq, H, d, k if sparse else comp.cap, params.window, qd, comp.fmt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_ = None if win is None else C.byref(win.struct())
+    if sparse:
+        st = lib().csa_sparse_mqa_attn(_ptr(q), qd, _ptr(q_pos), _ptr(topk_idx), k, C.byref(comp.struct()), ws_,
+                                       _ptr(gamma_q), _ptr(sink), C.byref(params), B, Tq, H, _ptr(out), od,
+                                       _ptr(workspace), wsb, _stream(stream))
+    else:
+        st = lib().hca_dense_mqa_attn(_ptr(q), qd, _ptr(q_pos), C.byref(comp.struct()), ws_, _ptr(gamma_q),
+                                      _ptr(sink), C.byref(params), B, Tq, H, _ptr(out), od, _ptr(workspace), wsb,
+                                      _stream(stream))
+    _check(st)
+    return out
+
+
+def sparse_mqa_attn(q, q_pos, topk_idx, comp, win, sink, params, **kw):
+    """csa_sparse_mqa_attn.  q: [B, Tq, H, d]; topk_idx: int32 [B, Tq, k]."""
+    return _attn(True, q, q_pos, comp, win, sink, params, topk_idx=topk_idx, **kw)
+
+
+def hca_dense_mqa_attn(q, q_pos, comp, win, sink, params, **kw):
+    """hca_dense_mqa_attn.  q: [B, Tq, H, d]."""
+    return _attn(False, q, q_pos, comp, win, sink, params, **kw)
+
+
+def out_proj_grouped(o, W, *, y=None, y_dtype=None, stream=None):
+    """attn_out_proj_grouped.  o: [M, Hd]; W: [G, D/G, Hd/G]; returns y [M, D]."""
+    M, Hd = o.shape
+    G, dg, _ = W.shape
+    D = G * dg
+    if y is None:
+        y = torch.empty((M, D), dtype=y_dtype or o.dtype, device=o.device)
+    _check(lib().attn_out_proj_grouped(_ptr(o), torch_dtype_code(o), _ptr(W), torch_dtype_code(W), M, Hd, D, G,
+                                       _ptr(y), torch_dtype_code(y), _stream(stream)))
+    return y

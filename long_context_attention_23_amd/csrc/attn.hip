@@ -1,0 +1,310 @@
+// attn.hip -- csa_sparse_mqa_attn / hca_dense_mqa_attn.
+//
+// Method: "DeepSeek-V4 ... open-source declaration" (peacm.com) section 3.2:
+// CSA step 3 (multi-query attention over the top-k compressed blocks), the
+// HCA paragraph (dense attention over every compressed entry) and the four
+// tricks (query RMSNorm, partial RoPE with a RoPE at -i on the output, the
+// raw 128-token window visible to every query, a learnable sink logit in the
+// softmax denominator); "DeepSeek V4 (Flash & Pro)" wiki article: HCA is a
+// dense MQA stream plus a 128-token window.
+//
+// Decomposition (flash-decoding): a query row's entry list -- its compressed
+// entries (top-k slots, or every visible block) followed by its W window
+// positions -- is cut into fixed splits of kAttnSplit entries; one workgroup
+// per (split, row, head group) keeps a running max / sum / output per head,
+// and a combine kernel merges the splits in split order, adds the sink and
+// applies the output RoPE.  A row whose list fits in one split is finished
+// in place.  Split sizes depend only on the row's own entry count, so the
+// result of a row does not depend on the batch it is in.
+//
+// This file holds the generic kernel (fp32 VALU, any cache format); the MFMA
+// kernel for bf16 queries lives in attn_mfma.hip.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnTile = 8;
+constexpr int kAttnSplit = 256;
+constexpr int kAttnMaxD = 1024;
+constexpr int kAttnQFloats = 4096;
+
+__device__ __forceinline__ int64_t comp_slots(const AttnArgs& a, int64_t t) {
+    if (a.topk) return a.k;
+    int64_t n = t < 0 ? 0 : (t + 1) / a.m;
+    return n < a.ccap ? n : a.ccap;
+}
+
+// record of entry e of a row (nullptr if masked)
+__device__ __forceinline__ const uint8_t* entry_rec(const AttnArgs& a, int64_t row, int64_t b, int64_t t,
+                                                    int64_t nc, int64_t e, int& fmt) {
+    if (e < nc) {
+        int64_t j = e;
+        if (a.topk) {
+            j = a.topk[row * a.k + e];
+            int64_t vis = t < 0 ? 0 : (t + 1) / a.m;
+            if (vis > a.ccap) vis = a.ccap;
+            if (j < 0 || j >= vis) return nullptr;
+        }
+        fmt = a.comp_fmt;
+        return a.comp + (b * a.ccap + j) * a.comp_rec;
+    }
+    int64_t s = t - a.W + 1 + (e - nc);
+    if (s < 0) return nullptr;
+    fmt = a.win_fmt;
+    return a.win + (b * a.wcap + s % a.wcap) * a.win_rec;
+}
+
+__device__ __forceinline__ float rec_value(const uint8_t* rec, int fmt, int d, int dr, int k) {
+    if (fmt == CSA_F32) return reinterpret_cast<const float*>(rec)[k];
+    if (fmt == CSA_BF16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(rec)[k]);
+    const int dn = d - dr;
+    if (k < dn) return e4m3_to_f32(rec[k]) * *reinterpret_cast<const float*>(rec + dn + 2 * dr);
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(rec + dn)[k - dn]);
+}
+
+// q^ = RoPE_t(RMSNorm(q)) for heads [h0, h0+hg) into qs[hh*d + k]; one wave per head
+template <typename QT>
+__device__ void query_prologue(const AttnArgs& a, int64_t row, int h0, int hg, int64_t t, float* qs) {
+    const int d = a.d, lane = threadIdx.x & (kWave - 1), nw = blockDim.x / kWave;
+    const QT* q = reinterpret_cast<const QT*>(a.q) + (row * a.H + h0) * d;
+    for (int hh = threadIdx.x / kWave; hh < hg; hh += nw) {
+        float ss = 0.0f;
+        for (int k = lane; k < d; k += kWave) {
+            float v = ld_scalar<QT>(q, (size_t)hh * d + k);
+            ss += v * v;
+        }
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
+        for (int k = lane; k < d; k += kWave) {
+            float v = ld_scalar<QT>(q, (size_t)hh * d + k) * inv;
+            qs[hh * d + k] = a.gamma_q ? v * a.gamma_q[k] : v;
+        }
+        // RoPE_t on the last dr dims (each lane rotates its own pairs)
+        const int off = d - a.dr;
+        for (int p = lane; p < a.dr / 2; p += kWave) {
+            float sn, cs;
+            rope_sincos((double)t, p, a.dr, a.base, sn, cs);
+            float x0 = qs[hh * d + off + 2 * p], x1 = qs[hh * d + off + 2 * p + 1];
+            qs[hh * d + off + 2 * p] = x0 * cs - x1 * sn;
+            qs[hh * d + off + 2 * p + 1] = x0 * sn + x1 * cs;
+        }
+    }
+}
+
+// output RoPE_{-t} on the last dr dims of one head's vector v[0..d), by
+// nthreads threads starting at lane0
+__device__ __forceinline__ void rotate_out(const AttnArgs& a, int64_t t, float* v, int lane0, int nthreads) {
+    const int d = a.d, off = d - a.dr;
+    for (int p = lane0; p < a.dr / 2; p += nthreads) {
+        float sn, cs;
+        rope_sincos(-(double)t, p, a.dr, a.base, sn, cs);
+        float x0 = v[off + 2 * p], x1 = v[off + 2 * p + 1];
+        v[off + 2 * p] = x0 * cs - x1 * sn;
+        v[off + 2 * p + 1] = x0 * sn + x1 * cs;
+    }
+}
+
+template <typename QT, typename OT>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, int nsplit_max) {
+    __shared__ float qs[kAttnQFloats];
+    __shared__ float kv[kAttnTile * (kAttnMaxD + 1)];
+    __shared__ float pz[kAttnQFloats / 64 * kAttnTile];   // [hg][tile]
+    __shared__ float mrun[kAttnQFloats / 64], lrun[kAttnQFloats / 64], alph[kAttnQFloats / 64];
+    __shared__ int valid[kAttnTile];
+
+    const int64_t row = blockIdx.y, b = row / a.Tq;
+    const int64_t t = a.q_pos[row];
+    const int64_t nc = comp_slots(a, t);
+    const int64_t ne = nc + a.W;
+    const int64_t nsplit = (ne + kAttnSplit - 1) / kAttnSplit;
+    const int64_t s = blockIdx.x;
+    if (s >= nsplit && !(s == 0 && ne == 0)) return;
+    const int64_t e0 = s * kAttnSplit, e1 = min(e0 + (int64_t)kAttnSplit, ne);
+    const int h0 = blockIdx.z * HG, hg = min(HG, a.H - h0);
+    const int d = a.d, ld = d + 1;
+    const int tid = threadIdx.x;
+
+    query_prologue<QT>(a, row, h0, hg, t, qs);
+    for (int hh = tid; hh < hg; hh += blockDim.x) { mrun[hh] = -INFINITY; lrun[hh] = 0.0f; }
+    constexpr int kMaxOwn = kAttnQFloats / kAttnThreads;
+    float o[kMaxOwn];
+#pragma unroll
+    for (int q = 0; q < kMaxOwn; q++) o[q] = 0.0f;
+    __syncthreads();
+
+    for (int64_t et = e0; et < e1; et += kAttnTile) {
+        const int nt = (int)min((int64_t)kAttnTile, e1 - et);
+        if (tid < kAttnTile) {
+            int fmt;
+            valid[tid] = tid < nt && entry_rec(a, row, b, t, nc, et + tid, fmt) != nullptr;
+        }
+        for (int idx = tid; idx < kAttnTile * d; idx += blockDim.x) {
+            const int ee = idx / d, k = idx % d;
+            float v = 0.0f;
+            if (ee < nt) {
+                int fmt = 0;
+                const uint8_t* rec = entry_rec(a, row, b, t, nc, et + ee, fmt);
+                if (rec) v = rec_value(rec, fmt, d, a.dr, k);
+            }
+            kv[ee * ld + k] = v;
+        }
+        __syncthreads();
+        for (int idx = tid; idx < hg * kAttnTile; idx += blockDim.x) {
+            const int hh = idx / kAttnTile, ee = idx % kAttnTile;
+            float z = -INFINITY;
+            if (ee < nt && valid[ee]) {
+                float acc = 0.0f;
+                for (int k = 0; k < d; k++) acc = fmaf(qs[hh * d + k], kv[ee * ld + k], acc);
+                z = acc * a.scale;
+            }
+            pz[hh * kAttnTile + ee] = z;
+        }
+        __syncthreads();
+        for (int hh = tid; hh < hg; hh += blockDim.x) {
+            float mt = -INFINITY;
+            for (int ee = 0; ee < kAttnTile; ee++) mt = fmaxf(mt, pz[hh * kAttnTile + ee]);
+            const float mo = mrun[hh], mn = fmaxf(mo, mt);
+            float al = 1.0f, sum = 0.0f;
+            if (mn != -INFINITY) {
+                al = expf(mo - mn);
+                for (int ee = 0; ee < kAttnTile; ee++) {
+                    float p = expf(pz[hh * kAttnTile + ee] - mn);
+                    pz[hh * kAttnTile + ee] = p;
+                    sum += p;
+                }
+            } else {
+                for (int ee = 0; ee < kAttnTile; ee++) pz[hh * kAttnTile + ee] = 0.0f;
+            }
+            lrun[hh] = lrun[hh] * al + sum;
+            mrun[hh] = mn;
+            alph[hh] = al;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kMaxOwn; q++) {
+            const int idx = tid + q * kAttnThreads;
+            if (idx < hg * d) {
+                const int hh = idx / d, k = idx % d;
+                float acc = o[q] * alph[hh];
+                for (int ee = 0; ee < kAttnTile; ee++) acc = fmaf(pz[hh * kAttnTile + ee], kv[ee * ld + k], acc);
+                o[q] = acc;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (nsplit <= 1) {
+        // whole list in this split: normalise with the sink, rotate, store
+#pragma unroll
+        for (int q = 0; q < kMaxOwn; q++) {
+            const int idx = tid + q * kAttnThreads;
+            if (idx < hg * d) {
+                const int hh = idx / d;
+                const float sk = a.sink[h0 + hh], mr = mrun[hh];
+                const float M = fmaxf(mr, sk);
+                float v = 0.0f;
+                if (M != -INFINITY) {
+                    const float den = lrun[hh] * expf(mr - M) + expf(sk - M);
+                    v = (mr == -INFINITY) ? 0.0f : o[q] * expf(mr - M) / den;
+                }
+                qs[idx] = v;
+            }
+        }
+        __syncthreads();
+        const int lane = tid & (kWave - 1), nw = blockDim.x / kWave;
+        for (int hh = tid / kWave; hh < hg; hh += nw) rotate_out(a, t, qs + hh * d, lane, kWave);
+        __syncthreads();
+        OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h0) * d;
+        for (int idx = tid; idx < hg * d; idx += blockDim.x) st_scalar<OT>(out, idx, qs[idx]);
+        return;
+    }
+    // partials: o (relative to mrun), m, l
+    float* wo = reinterpret_cast<float*>(a.ws);
+    float* wml = wo + (size_t)a.rows * nsplit_max * a.H * d;
+    const size_t base = ((size_t)row * nsplit_max + s) * a.H + h0;
+#pragma unroll
+    for (int q = 0; q < kMaxOwn; q++) {
+        const int idx = tid + q * kAttnThreads;
+        if (idx < hg * d) wo[base * d + idx] = o[q];
+    }
+    for (int hh = tid; hh < hg; hh += blockDim.x) {
+        wml[(base + hh) * 2] = mrun[hh];
+        wml[(base + hh) * 2 + 1] = lrun[hh];
+    }
+}
+
+// merge the splits of (row, head) in split order
+template <typename OT>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int nsplit_max, int split) {
+    __shared__ float v[kAttnMaxD];
+    __shared__ float wsc[1024];
+    __shared__ float sden;
+    const int h = blockIdx.x;
+    const int64_t row = blockIdx.y;
+    const int64_t t = a.q_pos[row];
+    const int64_t nc = comp_slots(a, t);
+    const int64_t ne = nc + a.W;
+    const int64_t nsplit = (ne + split - 1) / split;
+    if (nsplit <= 1) return;
+    const float* wo = reinterpret_cast<const float*>(a.ws);
+    const float* wml = wo + (size_t)a.rows * nsplit_max * a.H * a.d;
+    const int d = a.d;
+    const float sk = a.sink[h];
+    if (threadIdx.x == 0) {
+        float M = sk;
+        for (int64_t s = 0; s < nsplit; s++) M = fmaxf(M, wml[(((size_t)row * nsplit_max + s) * a.H + h) * 2]);
+        float den = (M == -INFINITY) ? 0.0f : expf(sk - M);
+        for (int64_t s = 0; s < nsplit; s++) {
+            const size_t i = (((size_t)row * nsplit_max + s) * a.H + h) * 2;
+            const float ms = wml[i], ls = wml[i + 1];
+            const float w = (ms == -INFINITY) ? 0.0f : expf(ms - M);
+            wsc[s] = w;
+            den += ls * w;
+        }
+        sden = den;
+    }
+    __syncthreads();
+    const float den = sden;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) {
+        float acc = 0.0f;
+        for (int64_t s = 0; s < nsplit; s++)
+            acc = fmaf(wsc[s], wo[(((size_t)row * nsplit_max + s) * a.H + h) * d + k], acc);
+        v[k] = den > 0.0f ? acc / den : 0.0f;
+    }
+    __syncthreads();
+    rotate_out(a, t, v, threadIdx.x, blockDim.x);
+    __syncthreads();
+    OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
+}
+
+int64_t attn_ws_bytes(int64_t rows, int32_t H, int32_t d, int64_t max_entries, int32_t q_fmt, int32_t comp_fmt) {
+    (void)q_fmt;
+    (void)comp_fmt;
+    const int64_t nsplit = (max_entries + kAttnSplit - 1) / kAttnSplit;
+    if (nsplit <= 1) return 0;
+    return rows * nsplit * H * ((int64_t)d + 2) * 4;
+}
+
+hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st) {
+    if (a.rows == 0) return hipSuccess;
+    const int64_t nsplit = max((int64_t)1, (max_entries + kAttnSplit - 1) / kAttnSplit);
+    const int HG = min(min(a.H, kAttnQFloats / 64), kAttnQFloats / a.d);
+    const int ngroups = (a.H + HG - 1) / HG;
+    dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)ngroups);
+    const bool qb = a.q_fmt == CSA_BF16, ob = a.out_fmt == CSA_BF16;
+    if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+    if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+    if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+    if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+    if (nsplit > 1) {
+        dim3 g2((unsigned)a.H, (unsigned)a.rows);
+        if (ob) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, kAttnSplit);
+        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, kAttnSplit);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace csa

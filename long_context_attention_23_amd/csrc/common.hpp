@@ -1,0 +1,144 @@
+// common.hpp -- device helpers shared by the CSA / HCA kernels (gfx950, wave64).
+//
+// Number formats are handled with bit operations (the CPU checker encodes the
+// same byte layouts independently, by searching the value grids).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa_attn.h"
+
+namespace csa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round to nearest even; NaN -> canonical quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- E4M3FN
+// value = (-1)^s * (e ? (1 + m/8) 2^(e-7) : m 2^-9); 0x7F / 0xFF are NaN
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t s = (c & 0x80u) << 24, e = (c >> 3) & 15u, m = c & 7u;
+    float v;
+    if (e == 0) v = (float)m * 0.001953125f;                      // m * 2^-9
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+    if (e == 15 && m == 7) v = __uint_as_float(0x7FC00000u);
+    return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// bf16 bit pattern of an E4M3 value (exact: bf16 holds every E4M3 value)
+__device__ __forceinline__ uint16_t e4m3_to_bf16(uint32_t c) {
+    return (uint16_t)(__float_as_uint(e4m3_to_f32(c)) >> 16);
+}
+
+// round to nearest even on the E4M3 grid, saturating to +-448; NaN -> 0x7F
+__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t s = (u >> 24) & 0x80u;
+    float a = fabsf(x);
+    if (a != a) return 0x7F;
+    if (a >= 448.0f) return (uint8_t)(s | 0x7Eu);
+    if (a < 0.015625f) {                                           // below 2^-6: quantum 2^-9
+        uint32_t q = (uint32_t)rintf(a * 512.0f);                  // 0..8; 8 is the first normal
+        return (uint8_t)(s | q);
+    }
+    uint32_t ua = __float_as_uint(a);
+    ua += 0x7FFFFu + ((ua >> 20) & 1u);                            // RNE to 3 mantissa bits
+    uint32_t e = (ua >> 23) - 120u, m = (ua >> 20) & 7u;
+    return (uint8_t)(s | (e << 3) | m);
+}
+
+// ---------------------------------------------------------------- E2M1 / E8M0
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+    uint32_t mag = c & 7u;
+    float v = (mag < 2) ? 0.5f * (float)mag : __uint_as_float(((mag >> 1) + 126u) << 23 | (mag & 1u) << 22);
+    return (c & 8u) ? -v : v;
+}
+
+// nearest E2M1 code, ties to even, saturating at +-6 (x already divided by the scale)
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+    float a = fabsf(x);
+    if (a != a) return 0;
+    uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+    return c | ((__float_as_uint(x) >> 28) & 8u);
+}
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+    // 2^(s-127); s = 0 is 2^-127 (subnormal float); 255 is NaN
+    if (s == 255u) return __uint_as_float(0x7FC00000u);
+    return s == 0 ? 5.877471754111438e-39f : __uint_as_float(s << 23);
+}
+
+// ---------------------------------------------------------------- RoPE
+// angle of pair i at position pos, formed in fp64 (positions reach 2^20 and
+// more, where an fp32 product would be off by tens of milliradians)
+__device__ __forceinline__ void rope_sincos(double pos, int i, int dr, float base, float& s, float& c) {
+    double theta = pos * pow((double)base, -2.0 * (double)i / (double)dr);
+    double sd, cd;
+    sincos(theta, &sd, &cd);
+    s = (float)sd;
+    c = (float)cd;
+}
+
+// ---------------------------------------------------------------- score keys
+// order-preserving map float -> uint32 (larger float, larger key); NaN -> 0; -0 == +0
+__device__ __forceinline__ uint32_t score_key(float s) {
+    if (s != s) return 0u;
+    s = s + 0.0f;
+    uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// block-wide reductions; `red` is LDS scratch of >= blockDim/64 floats
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = wave_sum(v);
+    int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.0f;
+    for (int i = 0; i < nw; i++) t += red[i];
+    return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+    v = wave_max(v);
+    int w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+    __syncthreads();
+    if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+    __syncthreads();
+    float t = red[0];
+    for (int i = 1; i < nw; i++) t = fmaxf(t, red[i]);
+    return t;
+}
+
+// load one scalar of an f32 / bf16 array as float
+template <typename T> __device__ __forceinline__ float ld_scalar(const T* p, size_t i);
+template <> __device__ __forceinline__ float ld_scalar<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld_scalar<uint16_t>(const uint16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T> __device__ __forceinline__ void st_scalar(T* p, size_t i, float v);
+template <> __device__ __forceinline__ void st_scalar<float>(float* p, size_t i, float v) { p[i] = v; }
+template <> __device__ __forceinline__ void st_scalar<uint16_t>(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+
+}  // namespace csa

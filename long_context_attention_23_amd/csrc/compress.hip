@@ -1,0 +1,162 @@
+// compress.hip -- csa_compress_kv: block pooling, RMSNorm, partial RoPE and the
+// cache quantisers.
+//
+// Method: "DeepSeek-V4 ... open-source declaration" (peacm.com) section 3.2,
+// CSA step 1 (every m tokens become one compressed KV entry through an
+// attention-like mechanism; HCA uses 128:1) and the four tricks (KV RMSNorm,
+// RoPE on the last 64 dims); "technical report digest" section 2.1.4 (FP8
+// non-RoPE dims + BF16 RoPE dims) and section 3.2 (FP4 indexer keys with 1x32
+// scales).  Reading of "attention-like": softmax weights over a learned
+// m-position score vector (plus an optional content score), summed over the
+// block's tokens.
+//
+// One workgroup of 256 threads per output block.  The work is streaming and
+// memory-bound (m tokens of d values in, one record out); the block's pooled
+// vector lives in LDS between the pooling, normalisation, rotation and
+// quantisation phases.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+constexpr int kCompThreads = 256;
+constexpr int kMaxD = 1024;
+constexpr int kMaxM = 1024;
+
+
+template <typename XT>
+__global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
+    __shared__ float sv[kMaxD];
+    __shared__ float sz[kMaxM];
+    __shared__ float red[kCompThreads / kWave];
+    __shared__ int se[kMaxD / 32];
+
+    const int tid = threadIdx.x;
+    const int b = blockIdx.y;
+    const int64_t i = blockIdx.x;
+    const int d = a.d, m = a.m;
+    const int64_t j = (int64_t)a.tok_start[b] / m + i;
+    if (!a.ring && j >= a.cap) return;
+    const int64_t slot = a.ring ? j % a.cap : j;
+    const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + i * m) * d;
+
+    // ---- pooling weights: z_r = bias_r + <u, x_r>, softmax over r
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
+    for (int r = 0; r < m; r += kCompThreads / kWave) {
+        int rr = r + wv;
+        float z = 0.0f;
+        if (a.sproj && rr < m) {
+            for (int k = lane; k < d; k += kWave) z += a.sproj[k] * ld_scalar<XT>(xb, (size_t)rr * d + k);
+            z = wave_sum(z);
+        }
+        if (rr < m && lane == 0) sz[rr] = a.sbias[rr] + z;
+    }
+    __syncthreads();
+    float zmax = -INFINITY;
+    for (int r = tid; r < m; r += kCompThreads) zmax = fmaxf(zmax, sz[r]);
+    zmax = block_max(zmax, red);
+    float zsum = 0.0f;
+    for (int r = tid; r < m; r += kCompThreads) zsum += expf(sz[r] - zmax);
+    zsum = block_sum(zsum, red);
+    for (int r = tid; r < m; r += kCompThreads) sz[r] = expf(sz[r] - zmax) / zsum;
+    __syncthreads();
+
+    // ---- pooled vector c = sum_r pi_r x_r (token order), then RMSNorm
+    float c[kMaxD / kCompThreads];
+    float ss = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kMaxD / kCompThreads; q++) {
+        int k = tid + q * kCompThreads;
+        float acc = 0.0f;
+        if (k < d)
+            for (int r = 0; r < m; r++) acc += sz[r] * ld_scalar<XT>(xb, (size_t)r * d + k);
+        c[q] = acc;
+        ss += acc * acc;
+    }
+    float inv = 1.0f;
+    if (a.gamma) {
+        ss = block_sum(ss, red);
+        inv = 1.0f / sqrtf(ss / (float)d + a.eps);
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxD / kCompThreads; q++) {
+        int k = tid + q * kCompThreads;
+        if (k < d) sv[k] = a.gamma ? c[q] * inv * a.gamma[k] : c[q];
+    }
+    __syncthreads();
+
+    // ---- RoPE at the block's start position j*m on the last dr dims
+    const int off = d - a.dr;
+    for (int p = tid; p < a.dr / 2; p += kCompThreads) {
+        float sn, cs;
+        rope_sincos((double)(j * m), p, a.dr, a.base, sn, cs);
+        float x0 = sv[off + 2 * p], x1 = sv[off + 2 * p + 1];
+        sv[off + 2 * p] = x0 * cs - x1 * sn;
+        sv[off + 2 * p + 1] = x0 * sn + x1 * cs;
+    }
+    __syncthreads();
+
+    // ---- quantise into the output record
+    const size_t r = (size_t)b * a.cap + slot;
+    uint8_t* rec = a.out + r * a.rec_bytes;
+    if (a.fmt == CSA_F32) {
+        for (int k = tid; k < d; k += kCompThreads) reinterpret_cast<float*>(rec)[k] = sv[k];
+    } else if (a.fmt == CSA_BF16) {
+        for (int k = tid; k < d; k += kCompThreads) reinterpret_cast<uint16_t*>(rec)[k] = f32_to_bf16(sv[k]);
+    } else if (a.fmt == CSA_FP8_E4M3) {
+        const int dn = d - a.dr;
+        float amax = 0.0f;
+        for (int k = tid; k < dn; k += kCompThreads) amax = fmaxf(amax, fabsf(sv[k]));
+        amax = block_max(amax, red);
+        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+        for (int k = tid; k < dn; k += kCompThreads) rec[k] = f32_to_e4m3(sv[k] / scale);
+        for (int k = tid; k < a.dr; k += kCompThreads)
+            reinterpret_cast<uint16_t*>(rec + dn)[k] = f32_to_bf16(sv[dn + k]);
+        const int tail = dn + 2 * a.dr;
+        for (int k = tail + tid; k < a.rec_bytes; k += kCompThreads) rec[k] = 0;
+        if (tid == 0) *reinterpret_cast<float*>(rec + tail) = scale;
+    } else {  // FP4 E2M1 indexer row with one E8M0 scale per 32 values
+        const int nb = d / 32;
+        if (tid < nb) {
+            float amax = 0.0f;
+            for (int k = 0; k < 32; k++) amax = fmaxf(amax, fabsf(sv[tid * 32 + k]));
+            int e = INT32_MIN;
+            if (amax > 0.0f) {
+                int ex;
+                frexpf(amax, &ex);          // amax in [2^(ex-1), 2^ex)
+                e = ex - 1 - 2;
+            }
+            se[tid] = e;
+        }
+        __syncthreads();
+        int emax = INT32_MIN;
+        for (int q = 0; q < nb; q++) emax = max(emax, se[q]);
+        __syncthreads();
+        if (tid < nb) {
+            int e = se[tid];
+            if (emax == INT32_MIN) e = 0;             // all-zero row
+            else e = max(e, emax - 14);               // keep FP4 -> FP8 lossless
+            e = min(max(e, -127), 127);
+            se[tid] = e;
+            a.out_scales[r * nb + tid] = (uint8_t)(e + 127);
+        }
+        __syncthreads();
+        for (int k = tid; k < d / 2; k += kCompThreads) {
+            int e = se[(2 * k) / 32];
+            uint32_t c0 = f32_to_e2m1(ldexpf(sv[2 * k], -e));
+            uint32_t c1 = f32_to_e2m1(ldexpf(sv[2 * k + 1], -e));
+            rec[k] = (uint8_t)(c0 | (c1 << 4));
+        }
+    }
+}
+
+hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st) {
+    int64_t nblk = a.T / a.m;
+    if (nblk == 0 || a.B == 0) return hipSuccess;
+    dim3 grid((unsigned)nblk, (unsigned)a.B);
+    if (x_dtype == CSA_F32) hipLaunchKernelGGL(k_compress<float>, grid, dim3(kCompThreads), 0, st, a);
+    else hipLaunchKernelGGL(k_compress<uint16_t>, grid, dim3(kCompThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,452 @@
+// indexer.hip -- csa_indexer_topk: lightning-indexer scores and exact top-k.
+//
+// Method: "DeepSeek-V4 ... open-source declaration" (peacm.com) section 3.2,
+// CSA step 2 (a lightweight indexer scores every query against the compressed
+// blocks and the top-k blocks are kept); "technical report digest" section
+// 3.2 (the indexer QK path in FP4 E2M1 with 1x32 scales).  Reading of the
+// score: S_j = sum_h w_h * ReLU(<q_h, k_j>); of the selection: largest S,
+// ties to the smaller block index, output in ascending block order.
+//
+// Exactness.  Scores are fp32; selection compares the 64-bit composite
+// (order-preserving score key, inverted block index), which is unique per
+// block, so "the k largest composites" is exactly the specified set.
+//
+// Small path (<= 4096 visible keys, e.g. prefill of a short context): one
+//   workgroup per query row keeps every score in LDS, radix-selects in LDS and
+//   emits the set by a j-ordered compaction.
+// Large path (decode against 10^5..10^6 keys): three kernels over key chunks
+//   and rows --
+//   A  score + 4096-bin LDS histogram of the top 12 key bits, merged into a
+//      per-row global histogram with integer atomics;
+//   C  every chunk finds the threshold bin from that histogram and appends
+//      keys above it to the row's "selected" list and keys in it to the
+//      "candidate" list (wave-aggregated appends);
+//   D  one workgroup per row radix-selects the remaining count among the
+//      candidates (8-bit digits over the composite), then bitonic-sorts the k
+//      block indices.  The append order of A/C does not matter: D's result
+//      depends only on the sets.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace csa {
+
+constexpr int kIdxThreads = 256;
+constexpr int kIdxFinalThreads = 1024;
+constexpr int kMaxHi = 16;
+constexpr int kMaxDi = 256;
+
+// ------------------------------------------------------------------ scoring
+// decode 8 consecutive values [k0, k0+8) of an indexer row
+template <int FMT>
+__device__ __forceinline__ void load8(const uint8_t* row, const uint8_t* scales, int k0, float* v) {
+    if constexpr (FMT == CSA_F32) {
+        const float4* p = reinterpret_cast<const float4*>(row + 4 * k0);
+        float4 a = p[0], b = p[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else if constexpr (FMT == CSA_BF16) {
+        uint4 a = *reinterpret_cast<const uint4*>(row + 2 * k0);
+        uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    } else {  // FP4: 8 codes in 4 bytes, one scale per 32 values
+        uint32_t c = *reinterpret_cast<const uint32_t*>(row + k0 / 2);
+        float s = e8m0_to_f32(scales[k0 / 32]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = e2m1_to_f32((c >> (4 * i)) & 15u) * s;
+    }
+}
+
+__host__ __device__ constexpr int row_bytes(int fmt, int di) {
+    return fmt == CSA_F32 ? 4 * di : fmt == CSA_BF16 ? 2 * di : di / 2;
+}
+
+// decode the query's Hi indexer rows into LDS as qs[k][h] (Hi contiguous per dim)
+template <int QF>
+__device__ void stage_query(const IndexerArgs& a, int64_t row, float* qs, float* ws) {
+    const int di = a.di, Hi = a.Hi;
+    const int rb = row_bytes(QF, di);
+    for (int idx = threadIdx.x; idx < Hi * (di / 8); idx += blockDim.x) {
+        int h = idx / (di / 8), k0 = (idx % (di / 8)) * 8;
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + (row * Hi + h) * rb;
+        const uint8_t* qsc = a.q_scales ? a.q_scales + (row * Hi + h) * (di / 32) : nullptr;
+        float v[8];
+        load8<QF>(qrow, qsc, k0, v);
+#pragma unroll
+        for (int u = 0; u < 8; u++) qs[(k0 + u) * kMaxHi + h] = v[u];
+    }
+    for (int h = threadIdx.x; h < Hi; h += blockDim.x) ws[h] = a.w[row * Hi + h];
+}
+
+// S_j for one key row, fp32, dims in order then heads in order
+template <int KF>
+__device__ __forceinline__ float score_one(const IndexerArgs& a, const uint8_t* krow, const uint8_t* ksc,
+                                           const float* qs, const float* ws) {
+    float acc[kMaxHi];
+#pragma unroll
+    for (int h = 0; h < kMaxHi; h++) acc[h] = 0.0f;
+    for (int k0 = 0; k0 < a.di; k0 += 8) {
+        float v[8];
+        load8<KF>(krow, ksc, k0, v);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const float* qk = qs + (k0 + u) * kMaxHi;
+#pragma unroll
+            for (int h = 0; h < kMaxHi; h++)
+                if (h < a.Hi) acc[h] = fmaf(qk[h], v[u], acc[h]);
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kMaxHi; h++)
+        if (h < a.Hi) s = fmaf(ws[h], fmaxf(acc[h], 0.0f), s);
+    return s;
+}
+
+__device__ __forceinline__ int64_t visible_blocks(const IndexerArgs& a, int64_t row) {
+    int64_t t = a.q_pos[row];
+    int64_t n = t < 0 ? 0 : (t + 1) / a.m;
+    return n < a.cap ? n : a.cap;
+}
+
+// ------------------------------------------------------------------ radix helpers
+// Find, in a 256-bin histogram (descending digit order), the digit whose
+// cumulative count from the top first reaches `need`.  Executed by one full
+// wave; returns (digit, count strictly above it) in every lane.
+__device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, uint32_t need, uint32_t& digit,
+                                                uint32_t& above) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint32_t h4[4], s = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) { h4[q] = hist[255 - 4 * lane - q]; s += h4[q]; }
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    uint64_t bal = __ballot(incl >= need);
+    int L = bal ? __builtin_ctzll(bal) : kWave - 1;
+    uint32_t cum = __shfl(incl - s, L, kWave);
+    uint32_t d = 0, ab = cum;
+    if (lane == L) {
+        uint32_t c = cum;
+        d = 255 - 4 * L - 3;
+        ab = c;
+        for (int q = 0; q < 4; q++) {
+            if (c + h4[q] >= need) { d = 255 - 4 * L - q; ab = c; break; }
+            c += h4[q];
+        }
+    }
+    digit = __shfl(d, L, kWave);
+    above = __shfl(ab, L, kWave);
+}
+
+// Radix select over n composites get(i) (nbits significant bits): returns the
+// composite of the need-th largest.  Block-wide; hist is LDS [256], sh LDS [4].
+template <typename Get>
+__device__ uint64_t radix_select(Get get, int64_t n, int nbits, uint32_t need, uint32_t* hist, uint32_t* sh) {
+    uint64_t prefix = 0, pmask = 0;
+    for (int shift = ((nbits + 7) / 8) * 8 - 8; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            uint64_t c = get(i);
+            if ((c & pmask) == prefix) atomicAdd(&hist[(c >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            uint32_t dg, ab;
+            wave_pick_digit(hist, need, dg, ab);
+            if (threadIdx.x == 0) { sh[0] = dg; sh[1] = ab; }
+        }
+        __syncthreads();
+        prefix |= (uint64_t)sh[0] << shift;
+        pmask |= (uint64_t)255u << shift;
+        need -= sh[1];
+        __syncthreads();
+    }
+    return prefix;
+}
+
+__device__ __forceinline__ int bits_for(int64_t n) {   // bits to hold values 0..n-1 (>= 1)
+    int b = 1;
+    while (b < 62 && ((int64_t)1 << b) < n) b++;
+    return b;
+}
+
+// ------------------------------------------------------------------ small path
+template <int QF, int KF>
+__global__ __launch_bounds__(kIdxThreads) void k_idx_small(IndexerArgs a) {
+    __shared__ float qs[kMaxDi * kMaxHi];
+    __shared__ float ws[kMaxHi];
+    __shared__ uint32_t keys[kIdxSmallMaxKeys];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t wcount[kIdxThreads / kWave];
+
+    const int64_t row = blockIdx.x;
+    const int64_t b = row / a.Tq;
+    const int64_t n = visible_blocks(a, row);
+    int32_t* out = a.out + row * a.topk;
+    stage_query<QF>(a, row, qs, ws);
+    __syncthreads();
+    const int rb = row_bytes(KF, a.di);
+    for (int64_t j = threadIdx.x; j < n; j += blockDim.x) {
+        const uint8_t* krow = a.keys + (b * a.cap + j) * rb;
+        const uint8_t* ksc = a.key_scales ? a.key_scales + (b * a.cap + j) * (a.di / 32) : nullptr;
+        keys[j] = score_key(score_one<KF>(a, krow, ksc, qs, ws));
+    }
+    __syncthreads();
+
+    uint64_t thr = 0;                 // every composite >= thr is selected
+    const int jb = bits_for(n);
+    const uint64_t jmask = ((uint64_t)1 << jb) - 1;
+    if (n > a.topk) {
+        auto get = [&](int64_t i) -> uint64_t { return ((uint64_t)keys[i] << jb) | (jmask - (uint64_t)i); };
+        thr = radix_select(get, n, 32 + jb, (uint32_t)a.topk, hist, sh);
+    }
+    // j-ordered compaction of the selected set
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    int base = 0;
+    for (int64_t j0 = 0; j0 < n; j0 += blockDim.x) {
+        int64_t j = j0 + threadIdx.x;
+        bool sel = false;
+        if (j < n) sel = ((((uint64_t)keys[j]) << jb) | (jmask - (uint64_t)j)) >= thr;
+        uint64_t bal = __ballot(sel);
+        if (lane == 0) wcount[wv] = __popcll(bal);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wv; w++) off += wcount[w];
+        int tot = 0;
+        for (int w = 0; w < (int)(blockDim.x / kWave); w++) tot += wcount[w];
+        if (sel) out[off + __popcll(bal & ((1ull << lane) - 1))] = (int32_t)j;
+        base += tot;
+        __syncthreads();
+    }
+    for (int i = base + threadIdx.x; i < a.topk; i += blockDim.x) out[i] = -1;
+}
+
+// ------------------------------------------------------------------ large path
+struct RowWs {
+    uint32_t* hist;     // [4096]
+    uint32_t* counts;   // [0] selected, [1] candidates
+    uint32_t* scores;   // [cap]
+    int32_t* sel;       // [topk]
+    uint2* cand;        // [cap] (key, j)
+};
+
+__device__ __forceinline__ RowWs row_ws(const IndexerArgs& a, int64_t r) {
+    uint8_t* base = a.ws + r * a.ws_row_bytes;
+    RowWs w;
+    w.hist = reinterpret_cast<uint32_t*>(base);
+    w.counts = w.hist + kIdxHistBins;
+    w.scores = w.counts + 4;
+    w.sel = reinterpret_cast<int32_t*>(w.scores + a.cap);
+    size_t off = (size_t)(kIdxHistBins + 4) * 4 + (size_t)a.cap * 4 + (size_t)a.topk * 4;
+    off = (off + 15) & ~(size_t)15;
+    w.cand = reinterpret_cast<uint2*>(base + off);
+    return w;
+}
+
+int64_t idx_ws_row_bytes(int64_t cap, int32_t topk) {
+    int64_t off = (int64_t)(kIdxHistBins + 4) * 4 + cap * 4 + (int64_t)topk * 4;
+    off = (off + 15) & ~(int64_t)15;
+    off += cap * 8;
+    return (off + 255) & ~(int64_t)255;
+}
+
+__global__ void k_idx_zero(IndexerArgs a) {
+    const int64_t r = blockIdx.x;
+    uint32_t* p = reinterpret_cast<uint32_t*>(a.ws + r * a.ws_row_bytes);
+    for (int i = threadIdx.x; i < kIdxHistBins + 4; i += blockDim.x) p[i] = 0;
+}
+
+template <int QF, int KF>
+__global__ __launch_bounds__(kIdxThreads) void k_idx_score(IndexerArgs a) {
+    __shared__ float qs[kMaxDi * kMaxHi];
+    __shared__ float ws[kMaxHi];
+    __shared__ uint32_t lh[kIdxHistBins];
+    const int64_t r = blockIdx.y, row = a.row0 + r;
+    const int64_t b = row / a.Tq;
+    const int64_t n = visible_blocks(a, row);
+    const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
+    if (n <= a.topk || c0 >= n) return;
+    RowWs w = row_ws(a, r);
+    stage_query<QF>(a, row, qs, ws);
+    for (int i = threadIdx.x; i < kIdxHistBins; i += blockDim.x) lh[i] = 0;
+    __syncthreads();
+    const int rb = row_bytes(KF, a.di);
+    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
+    for (int64_t j = c0 + threadIdx.x; j < c1; j += blockDim.x) {
+        const uint8_t* krow = a.keys + (b * a.cap + j) * rb;
+        const uint8_t* ksc = a.key_scales ? a.key_scales + (b * a.cap + j) * (a.di / 32) : nullptr;
+        uint32_t key = score_key(score_one<KF>(a, krow, ksc, qs, ws));
+        w.scores[j] = key;
+        atomicAdd(&lh[key >> 20], 1u);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kIdxHistBins; i += blockDim.x)
+        if (lh[i]) atomicAdd(&w.hist[i], lh[i]);
+}
+
+// threshold bin of the 4096-bin histogram, computed by one wave
+__device__ __forceinline__ void wave_pick_bin(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int per = kIdxHistBins / kWave;   // 64 bins per lane, descending
+    uint32_t s = 0;
+    for (int q = 0; q < per; q++) s += hist[kIdxHistBins - 1 - per * lane - q];
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    uint64_t bal = __ballot(incl >= need);
+    int L = bal ? __builtin_ctzll(bal) : kWave - 1;
+    uint32_t cum = __shfl(incl - s, L, kWave);
+    uint32_t bb = 0, ab = cum;
+    if (lane == L) {
+        uint32_t c = cum;
+        for (int q = 0; q < per; q++) {
+            uint32_t hb = hist[kIdxHistBins - 1 - per * L - q];
+            if (c + hb >= need) { bb = kIdxHistBins - 1 - per * L - q; ab = c; break; }
+            c += hb;
+        }
+    }
+    bin = __shfl(bb, L, kWave);
+    above = __shfl(ab, L, kWave);
+}
+
+__global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
+    __shared__ uint32_t sh[2];
+    const int64_t r = blockIdx.y, row = a.row0 + r;
+    const int64_t n = visible_blocks(a, row);
+    const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
+    if (n <= a.topk || c0 >= n) return;
+    RowWs w = row_ws(a, r);
+    if (threadIdx.x < kWave) {
+        uint32_t bin, above;
+        wave_pick_bin(w.hist, (uint32_t)a.topk, bin, above);
+        if (threadIdx.x == 0) { sh[0] = bin; sh[1] = above; }
+    }
+    __syncthreads();
+    const uint32_t tbin = sh[0];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
+    for (int64_t j0 = c0; j0 < c1; j0 += blockDim.x) {
+        int64_t j = j0 + threadIdx.x;
+        uint32_t key = j < c1 ? w.scores[j] : 0u;
+        uint32_t bin = key >> 20;
+        bool sure = j < c1 && bin > tbin;
+        bool cand = j < c1 && bin == tbin;
+        uint64_t bs = __ballot(sure), bc = __ballot(cand);
+        uint32_t os = 0, oc = 0;
+        if (lane == 0) {
+            if (bs) os = atomicAdd(&w.counts[0], (uint32_t)__popcll(bs));
+            if (bc) oc = atomicAdd(&w.counts[1], (uint32_t)__popcll(bc));
+        }
+        os = __shfl(os, 0, kWave);
+        oc = __shfl(oc, 0, kWave);
+        uint64_t below = (1ull << lane) - 1;
+        if (sure) w.sel[os + __popcll(bs & below)] = (int32_t)j;
+        if (cand) w.cand[oc + __popcll(bc & below)] = make_uint2(key, (uint32_t)j);
+    }
+}
+
+__global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
+    __shared__ int32_t arr[kIdxMaxTopk];
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sh[4];
+    const int64_t r = blockIdx.x, row = a.row0 + r;
+    const int64_t n = visible_blocks(a, row);
+    int32_t* out = a.out + row * a.topk;
+    if (n <= a.topk) {
+        for (int64_t i = threadIdx.x; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
+        return;
+    }
+    RowWs w = row_ws(a, r);
+    const uint32_t nsel = w.counts[0], ncand = w.counts[1];
+    const uint32_t need = (uint32_t)a.topk - nsel;     // 1 <= need <= ncand by construction
+    const int jb = bits_for(a.cap);
+    const uint64_t jmask = ((uint64_t)1 << jb) - 1;
+    const uint2* cand = w.cand;
+    auto get = [&](int64_t i) -> uint64_t {
+        uint2 c = cand[i];
+        return ((uint64_t)(c.x & 0xFFFFFu) << jb) | (jmask - (uint64_t)c.y);
+    };
+    const uint64_t thr = radix_select(get, (int64_t)ncand, 20 + jb, need, hist, sh);
+    // gather the k indices: every "sure" block plus candidates at or above thr
+    for (uint32_t i = threadIdx.x; i < nsel && i < (uint32_t)a.topk; i += blockDim.x) arr[i] = w.sel[i];
+    if (threadIdx.x == 0) sh[2] = nsel;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x)
+        if (get(i) >= thr) {
+            const uint32_t pos = atomicAdd(&sh[2], 1u);
+            if (pos < (uint32_t)a.topk) arr[pos] = (int32_t)cand[i].y;
+        }
+    int P = 1;
+    while (P < a.topk) P <<= 1;
+    for (int i = a.topk + threadIdx.x; i < P; i += blockDim.x) arr[i] = INT32_MAX;
+    __syncthreads();
+    // bitonic sort ascending of P entries
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < P / 2; i += blockDim.x) {
+                int lo = 2 * i - (i & (stride - 1));
+                int hi = lo + stride;
+                bool up = (lo & size) == 0;
+                int x = arr[lo], y = arr[hi];
+                if ((x > y) == up) { arr[lo] = y; arr[hi] = x; }
+            }
+            __syncthreads();
+        }
+    }
+    for (int i = threadIdx.x; i < a.topk; i += blockDim.x) out[i] = arr[i];
+}
+
+// ------------------------------------------------------------------ launcher
+template <int QF, int KF>
+static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st) {
+    if (total_rows == 0) return hipSuccess;
+    if (a.cap <= kIdxSmallMaxKeys) {
+        a.row0 = 0;
+        a.rows = (int32_t)total_rows;
+        hipLaunchKernelGGL((k_idx_small<QF, KF>), dim3((unsigned)total_rows), dim3(kIdxThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    const int64_t per_batch = ws_bytes / a.ws_row_bytes;
+    const unsigned nchunk = (unsigned)((a.cap + kIdxChunk - 1) / kIdxChunk);
+    for (int64_t r0 = 0; r0 < total_rows; r0 += per_batch) {
+        const int64_t nr = min(per_batch, total_rows - r0);
+        a.row0 = (int32_t)r0;
+        a.rows = (int32_t)nr;
+        hipLaunchKernelGGL(k_idx_zero, dim3((unsigned)nr), dim3(256), 0, st, a);
+        hipLaunchKernelGGL((k_idx_score<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+        hipLaunchKernelGGL(k_idx_collect, dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+        hipLaunchKernelGGL(k_idx_final, dim3((unsigned)nr), dim3(kIdxFinalThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_indexer_topk(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st) {
+    const int qf = a.q_fmt, kf = a.key_fmt;
+#define CSA_IDX_CASE(Q, K) if (qf == Q && kf == K) return launch_tpl<Q, K>(a, total_rows, ws_bytes, st);
+    CSA_IDX_CASE(CSA_F32, CSA_F32)
+    CSA_IDX_CASE(CSA_F32, CSA_BF16)
+    CSA_IDX_CASE(CSA_F32, CSA_FP4_E2M1)
+    CSA_IDX_CASE(CSA_BF16, CSA_F32)
+    CSA_IDX_CASE(CSA_BF16, CSA_BF16)
+    CSA_IDX_CASE(CSA_BF16, CSA_FP4_E2M1)
+    CSA_IDX_CASE(CSA_FP4_E2M1, CSA_F32)
+    CSA_IDX_CASE(CSA_FP4_E2M1, CSA_BF16)
+    CSA_IDX_CASE(CSA_FP4_E2M1, CSA_FP4_E2M1)
+#undef CSA_IDX_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace csa

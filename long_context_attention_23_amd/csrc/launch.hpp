@@ -1,0 +1,100 @@
+// launch.hpp -- argument blocks and launchers of the CSA / HCA kernels.
+// Host validation lives in api.cpp; each .hip file defines its launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa_attn.h"
+
+namespace csa {
+
+struct CompressArgs {
+    const void* x;
+    int32_t B, d, m;
+    int64_t T;
+    const int32_t* tok_start;
+    const float* sbias;
+    const float* sproj;
+    const float* gamma;
+    float eps;
+    int32_t dr;
+    float base;
+    int32_t out_kind;   // 0: KV record, 1: indexer row
+    int32_t fmt;
+    uint8_t* out;
+    uint8_t* out_scales;
+    int64_t cap;
+    int32_t ring;
+    int32_t rec_bytes;
+};
+hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st);
+
+// ---- indexer + top-k
+constexpr int kIdxSmallMaxKeys = 4096;   // one workgroup per query row up to this key count
+constexpr int kIdxHistBins = 4096;       // first-level radix histogram (top 12 key bits)
+constexpr int kIdxChunk = 4096;          // keys per workgroup in the large path
+constexpr int kIdxMaxTopk = 2048;
+
+struct IndexerArgs {
+    const void* q;              // [rows][Hi][row bytes]
+    const uint8_t* q_scales;    // [rows][Hi][di/32] (FP4)
+    int32_t q_fmt;
+    const float* w;             // [rows][Hi]
+    const uint8_t* keys;        // [B][cap][row bytes]
+    const uint8_t* key_scales;  // [B][cap][di/32] (FP4)
+    int32_t key_fmt;
+    int64_t cap;
+    int32_t di, Hi, m, topk, Tq;
+    const int32_t* q_pos;       // [rows]
+    int32_t* out;               // [rows][topk]
+    int32_t row0;               // first row of this launch batch
+    int32_t rows;               // rows in this batch
+    uint8_t* ws;                // per-row workspace slabs (large path)
+    int64_t ws_row_bytes;
+};
+int64_t idx_ws_row_bytes(int64_t cap, int32_t topk);
+hipError_t launch_indexer_topk(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st);
+
+// ---- attention
+struct AttnArgs {
+    const void* q;              // [rows][H][d]
+    int32_t q_fmt;
+    const int32_t* q_pos;       // [rows]
+    const int32_t* topk;        // [rows][k] or null (dense)
+    int32_t k;
+    const uint8_t* comp;        // [B][ccap] records
+    int32_t comp_fmt;
+    int64_t ccap;
+    int32_t comp_rec;
+    const uint8_t* win;         // [B][wcap] records (ring)
+    int32_t win_fmt;
+    int64_t wcap;
+    int32_t win_rec;
+    const float* gamma_q;       // [d] or null
+    const float* sink;          // [H]
+    int32_t d, dr, W, m;
+    float base, scale, eps;
+    int32_t Tq, H, rows;
+    void* out;                  // [rows][H][d]
+    int32_t out_fmt;
+    void* ws;
+    int64_t ws_bytes;
+};
+int64_t attn_ws_bytes(int64_t rows, int32_t H, int32_t d, int64_t max_entries, int32_t q_fmt,
+                      int32_t comp_fmt);
+hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st);
+
+// ---- grouped projection
+struct ProjArgs {
+    const void* o;
+    const void* W;
+    void* y;
+    int64_t M;
+    int32_t Hd, D, G;
+    int32_t fmt;                // o / W dtype
+    int32_t y_fmt;
+};
+hipError_t launch_proj(const ProjArgs& a, hipStream_t st);
+
+}  // namespace csa
