@@ -1,0 +1,302 @@
+"""Benchmark: one decode step of an alternating CSA / HCA layer pair at a
+1,048,576-token context (DeepSeek-V4-Pro shape), batch 4, on one MI355X.
+
+A step is the whole hot path for one new token per sequence:
+  CSA layer: window append (m=1) + compress the completed 4-token block +
+             compress its indexer key (FP4) + indexer top-1024 over 262,144
+             blocks + sparse MQA (64 heads x 512, 1024 blocks + 128 window,
+             FP8 cache) + grouped output projection 32768 -> 7168 (8 groups)
+  HCA layer: window append + compress the completed 128-token block + dense
+             MQA over 8,192 entries + window + grouped output projection.
+Inputs are resident in HBM before timing; R copies of every cache, weight and
+workspace are rotated so that consecutive reuse of a buffer is separated by
+more traffic than the 256 MB last-level cache holds.
+
+Prints one JSON line (metric, value = query tokens per second, roofline of the
+dominant kernel from HIP events, CPU-oracle baseline on the host cores).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA/HCA attention query-tokens/s at 1M ctx; decode HBM GB/s & prefill MFMA %"
+HBM_PEAK_GBS = 8000.0
+
+# workload: 1M-context layer pair decode, V4-Pro shaped
+B, L, H, D_HEAD, DR, W = 4, 1 << 20, 64, 512, 64, 128
+HIDDEN, G = 7168, 8
+M_CSA, K_CSA, M_HCA = 4, 1024, 128
+HI, DI = 4, 64
+N_CSA, N_HCA = L // M_CSA, L // M_HCA
+REC = 592                      # FP8 record bytes (448 E4M3 + 64 bf16 + f32 scale + pad)
+REC_ALGO = 580
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=6, help="rotated buffer sets (defeats the last-level cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes():
+    """Bytes the method itself must move per step, per call (sizes of the
+    inputs read and outputs written, each once)."""
+    q = B * H * D_HEAD * 2
+    o = B * H * D_HEAD * 2
+    win = B * W * REC_ALGO
+    return {
+        "csa_compress_kv": B * (1 + M_CSA) * D_HEAD * 2 + B * M_CSA * DI * 2 + 2 * B * REC_ALGO + B * (DI // 2 + DI // 32),
+        "csa_indexer_topk": B * N_CSA * (DI // 2 + DI // 32) + B * HI * (DI // 2 + DI // 32 + 4) + B * K_CSA * 4,
+        "csa_sparse_mqa_attn": q + B * K_CSA * REC_ALGO + win + o + B * K_CSA * 4,
+        "csa_out_proj": G * (HIDDEN // G) * (H * D_HEAD // G) * 2 + B * H * D_HEAD * 2 + B * HIDDEN * 2,
+        "hca_compress_kv": B * (1 + M_HCA) * D_HEAD * 2 + 2 * B * REC_ALGO,
+        "hca_dense_mqa_attn": q + B * N_HCA * REC_ALGO + win + o,
+        "hca_out_proj": G * (HIDDEN // G) * (H * D_HEAD // G) * 2 + B * H * D_HEAD * 2 + B * HIDDEN * 2,
+    }
+
+
+def build_state(torch, api, copies, seed=4004):
+    """Caches, weights and per-step inputs, R copies.  The prefix caches are
+    made by the library's own compression call from seeded random raw tokens."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn(*shape, std=1.0, dtype=torch.bfloat16):
+        return (torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32) * std).to(dtype)
+
+    b_csa = randn(M_CSA, dtype=torch.float32)
+    b_idx = randn(M_CSA, dtype=torch.float32)
+    b_hca = torch.zeros(M_HCA, device=dev)
+    gam = torch.ones(D_HEAD, device=dev)
+    csa_c = api.KVCache(B, N_CSA, D_HEAD, DR, api.FP8_E4M3)
+    hca_c = api.KVCache(B, N_HCA, D_HEAD, DR, api.FP8_E4M3)
+    keys = api.IdxCache(B, N_CSA, DI, api.FP4_E2M1)
+    wins = [api.KVCache(B, W, D_HEAD, DR, api.FP8_E4M3, ring=True) for _ in range(2)]
+    chunk = 1 << 16
+    for c0 in range(0, L, chunk):
+        start = torch.full((B,), c0, dtype=torch.int32, device=dev)
+        x = randn(B, chunk, D_HEAD)
+        api.compress_kv(x, start, M_CSA, b_csa, gamma=gam, rope_dim=DR, kv_out=csa_c)
+        xi = randn(B, chunk, DI)
+        api.compress_kv(xi, start, M_CSA, b_idx, idx_out=keys)
+        x = randn(B, chunk, D_HEAD)
+        api.compress_kv(x, start, M_HCA, b_hca, gamma=gam, rope_dim=DR, kv_out=hca_c)
+        if c0 + chunk == L:
+            ws = torch.full((B,), L - W, dtype=torch.int32, device=dev)
+            for wc in wins:
+                api.compress_kv(x[:, chunk - W:].contiguous(), ws, 1, torch.zeros(1, device=dev), gamma=gam,
+                                rope_dim=DR, kv_out=wc)
+    torch.cuda.synchronize()
+    t = L - 1
+    sets = []
+    for r in range(copies):
+        s = {}
+        if r == 0:
+            s["csa_c"], s["hca_c"], s["keys"], s["win_csa"], s["win_hca"] = csa_c, hca_c, keys, wins[0], wins[1]
+        else:
+            s["csa_c"] = api.KVCache(B, N_CSA, D_HEAD, DR, api.FP8_E4M3, rec=csa_c.rec.clone())
+            s["hca_c"] = api.KVCache(B, N_HCA, D_HEAD, DR, api.FP8_E4M3, rec=hca_c.rec.clone())
+            s["keys"] = api.IdxCache(B, N_CSA, DI, api.FP4_E2M1, codes=keys.codes.clone(), scales=keys.scales.clone())
+            s["win_csa"] = api.KVCache(B, W, D_HEAD, DR, api.FP8_E4M3, ring=True, rec=wins[0].rec.clone())
+            s["win_hca"] = api.KVCache(B, W, D_HEAD, DR, api.FP8_E4M3, ring=True, rec=wins[1].rec.clone())
+        s["Wo_csa"] = randn(G, HIDDEN // G, H * D_HEAD // G, std=0.02)
+        s["Wo_hca"] = randn(G, HIDDEN // G, H * D_HEAD // G, std=0.02)
+        # per-step inputs: the new token's raw KV (and the rest of its block), queries
+        s["x_csa"] = randn(B, M_CSA, D_HEAD)
+        s["xi_csa"] = randn(B, M_CSA, DI)
+        s["x_hca"] = randn(B, M_HCA, D_HEAD)
+        s["x_new_csa"] = s["x_csa"][:, M_CSA - 1:].contiguous()
+        s["x_new_hca"] = s["x_hca"][:, M_HCA - 1:].contiguous()
+        s["q_csa"] = randn(B, 1, H, D_HEAD)
+        s["q_hca"] = randn(B, 1, H, D_HEAD)
+        qc = torch.randint(0, 256, (B, 1, HI, DI // 2), generator=gen, device=dev, dtype=torch.int32).to(torch.uint8)
+        qs = torch.randint(124, 128, (B, 1, HI, DI // 32), generator=gen, device=dev, dtype=torch.int32).to(torch.uint8)
+        s["qI"], s["qI_s"] = qc, qs
+        s["w_idx"] = randn(B, 1, HI, dtype=torch.float32)
+        s["sink_csa"] = randn(H, dtype=torch.float32)
+        s["sink_hca"] = randn(H, dtype=torch.float32)
+        s["top"] = torch.empty((B, 1, K_CSA), dtype=torch.int32, device=dev)
+        s["idx_ws"] = torch.empty(api.indexer_workspace_bytes(B, 1, N_CSA, K_CSA), dtype=torch.uint8, device=dev)
+        s["o_csa"] = torch.empty((B, 1, H, D_HEAD), dtype=torch.bfloat16, device=dev)
+        s["o_hca"] = torch.empty((B, 1, H, D_HEAD), dtype=torch.bfloat16, device=dev)
+        s["y_csa"] = torch.empty((B, HIDDEN), dtype=torch.bfloat16, device=dev)
+        s["y_hca"] = torch.empty((B, HIDDEN), dtype=torch.bfloat16, device=dev)
+        s["attn_ws_csa"] = torch.empty(max(1, api.attn_workspace_bytes(B, 1, H, D_HEAD, K_CSA, W, api.BF16, api.FP8_E4M3)),
+                                       dtype=torch.uint8, device=dev)
+        s["attn_ws_hca"] = torch.empty(max(1, api.attn_workspace_bytes(B, 1, H, D_HEAD, N_HCA, W, api.BF16, api.FP8_E4M3)),
+                                       dtype=torch.uint8, device=dev)
+        sets.append(s)
+    shared = dict(
+        b_csa=b_csa, b_idx=b_idx, b_hca=b_hca, gam=gam, zero1=torch.zeros(1, device=dev),
+        pos=torch.full((B, 1), t, dtype=torch.int32, device=dev),
+        tok_new=torch.full((B,), t, dtype=torch.int32, device=dev),
+        tok_csa=torch.full((B,), t + 1 - M_CSA, dtype=torch.int32, device=dev),
+        tok_hca=torch.full((B,), t + 1 - M_HCA, dtype=torch.int32, device=dev),
+        p_csa=api.attn_params(D_HEAD, DR, W, M_CSA), p_hca=api.attn_params(D_HEAD, DR, W, M_HCA))
+    torch.cuda.synchronize()
+    return sets, shared
+
+
+CALLS = ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_mqa_attn", "csa_out_proj",
+         "hca_compress_kv", "hca_dense_mqa_attn", "hca_out_proj"]
+
+
+def step(api, s, sh, ev=None):
+    """One decode step of the layer pair.  ev: optional list of (start, end)
+    event pairs, one per call, recorded on the current stream."""
+    def mark(i, end):
+        if ev is not None:
+            ev[i][1 if end else 0].record()
+
+    mark(0, False)
+    api.compress_kv(s["x_new_csa"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
+                    kv_out=s["win_csa"])
+    api.compress_kv(s["x_csa"], sh["tok_csa"], M_CSA, sh["b_csa"], gamma=sh["gam"], rope_dim=DR, kv_out=s["csa_c"])
+    api.compress_kv(s["xi_csa"], sh["tok_csa"], M_CSA, sh["b_idx"], idx_out=s["keys"])
+    mark(0, True)
+    mark(1, False)
+    api.indexer_topk(s["qI"], api.FP4_E2M1, s["w_idx"], s["keys"], sh["pos"], M_CSA, K_CSA, q_scales=s["qI_s"],
+                     out=s["top"], workspace=s["idx_ws"])
+    mark(1, True)
+    mark(2, False)
+    api.sparse_mqa_attn(s["q_csa"], sh["pos"], s["top"], s["csa_c"], s["win_csa"], s["sink_csa"], sh["p_csa"],
+                        out=s["o_csa"], workspace=s["attn_ws_csa"])
+    mark(2, True)
+    mark(3, False)
+    api.out_proj_grouped(s["o_csa"].view(B, H * D_HEAD), s["Wo_csa"], y=s["y_csa"])
+    mark(3, True)
+    mark(4, False)
+    api.compress_kv(s["x_new_hca"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
+                    kv_out=s["win_hca"])
+    api.compress_kv(s["x_hca"], sh["tok_hca"], M_HCA, sh["b_hca"], gamma=sh["gam"], rope_dim=DR, kv_out=s["hca_c"])
+    mark(4, True)
+    mark(5, False)
+    api.hca_dense_mqa_attn(s["q_hca"], sh["pos"], s["hca_c"], s["win_hca"], s["sink_hca"], sh["p_hca"],
+                           out=s["o_hca"], workspace=s["attn_ws_hca"])
+    mark(5, True)
+    mark(6, False)
+    api.out_proj_grouped(s["o_hca"].view(B, H * D_HEAD), s["Wo_hca"], y=s["y_hca"])
+    mark(6, True)
+
+
+def cpu_baseline(target_s):
+    """The oracle, as it stands, on one decode step of the same layer pair for
+    the whole batch (synthetic records drawn at the same shapes), repeated up
+    to ~target_s seconds; returns query tokens per second."""
+    import oracle as O
+    from long_context_attention_23_amd import synth
+    g = synth.rng(2004)
+    t = L - 1
+    csa = synth.fp8_records(g, (B, N_CSA), D_HEAD, DR, REC)
+    hca = synth.fp8_records(g, (B, N_HCA), D_HEAD, DR, REC)
+    win = synth.fp8_records(g, (B, W), D_HEAD, DR, REC)
+    kc, ks = synth.fp4_rows(g, (B, N_CSA), DI, -3, 0)
+    qc, qs = synth.fp4_rows(g, (B, 1, HI), DI, -3, 0)
+    w = synth.normal(g, (B, 1, HI))
+    q = synth.bf16_bits(g, (B, 1, H, D_HEAD))
+    x_csa = synth.normal(g, (B, M_CSA, D_HEAD))
+    xi = synth.normal(g, (B, M_CSA, DI))
+    x_hca = synth.normal(g, (B, M_HCA, D_HEAD))
+    sink = synth.normal(g, H)
+    b4 = synth.normal(g, M_CSA)
+    Wo = [synth.bf16_bits(g, (G, HIDDEN // G, H * D_HEAD // G), std=0.02) for _ in range(2)]
+    Wo64 = [O.bf16_decode(x) for x in Wo]
+    gam = np.ones(D_HEAD, np.float32)
+    sc = 1.0 / math.sqrt(D_HEAD)
+    n_steps, t0 = 0, time.perf_counter()
+    while True:
+        for bi in range(B):
+            O.compress(x_csa[bi:bi + 1, -1:], O.F32, [t], 1, [0.0], gamma=gam, dr=DR, out_kind=0, out_fmt=O.FP8_E4M3,
+                       cap=W, ring=True)
+            O.compress(x_csa[bi:bi + 1], O.F32, [t + 1 - M_CSA], M_CSA, b4, gamma=gam, dr=DR, out_kind=0,
+                       out_fmt=O.FP8_E4M3, cap=N_CSA)
+            O.compress(xi[bi:bi + 1], O.F32, [t + 1 - M_CSA], M_CSA, b4, out_kind=1, out_fmt=O.FP4_E2M1, cap=N_CSA)
+            top = O.indexer_topk(qc[bi], qs[bi], O.FP4_E2M1, w[bi], [t], kc[bi], ks[bi], O.FP4_E2M1, M_CSA, K_CSA)
+            oc = O.attention(q[bi], O.BF16, [t], gam, sink, D_HEAD, DR, W, M_CSA, 10000.0, sc, 1e-6, csa[bi],
+                             O.FP8_E4M3, win[bi], O.FP8_E4M3, top)
+            O.out_proj(oc.reshape(1, H * D_HEAD), Wo64[0])
+            O.compress(x_hca[bi:bi + 1, -1:], O.F32, [t], 1, [0.0], gamma=gam, dr=DR, out_kind=0, out_fmt=O.FP8_E4M3,
+                       cap=W, ring=True)
+            O.compress(x_hca[bi:bi + 1], O.F32, [t + 1 - M_HCA], M_HCA, np.zeros(M_HCA), gamma=gam, dr=DR,
+                       out_kind=0, out_fmt=O.FP8_E4M3, cap=N_HCA)
+            oh = O.attention(q[bi], O.BF16, [t], gam, sink, D_HEAD, DR, W, M_HCA, 10000.0, sc, 1e-6, hca[bi],
+                             O.FP8_E4M3, win[bi], O.FP8_E4M3)
+            O.out_proj(oh.reshape(1, H * D_HEAD), Wo64[1])
+        n_steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or n_steps >= 20:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": n_steps * B / el, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_steps} full decode step(s) of the batch-4 layer pair at 1M context (fp64 oracle, "
+                      f"synthetic FP8/FP4 caches of the same shapes), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this path runs on a single "
+              "MI355X; multi-GPU sharding is not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from long_context_attention_23_amd import api
+    api.lib()
+    torch.cuda.set_device(0)
+    sets, sh = build_state(torch, api, args.copies)
+    R = len(sets)
+    for i in range(args.warmup):
+        step(api, sets[i % R], sh)
+    torch.cuda.synchronize()
+    # timed region: exactly K steps, synchronised on both sides
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in CALLS]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(api, sets[i % R], sh, ev[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms_step = el * 1e3 / args.steps
+    per_call = {c: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
+                for j, c in enumerate(CALLS)}
+    algo = algorithmic_bytes()
+    calls = {c: {"us": round(per_call[c] * 1e3, 2), "algo_MB": round(algo[c] / 1e6, 3),
+                 "GBs": round(algo[c] / (per_call[c] * 1e-3) / 1e9, 1)} for c in CALLS}
+    dom = max(CALLS, key=lambda c: per_call[c])
+    achieved = algo[dom] / (per_call[dom] * 1e-3) / 1e9
+    total_algo = sum(algo.values())
+    res = {
+        "metric": METRIC, "value": round(B / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "CSA+HCA layer-pair decode, 1M context, batch 4, V4-Pro shape (hidden 7168, 64 heads "
+                               "x 512, FP8 KV + FP4 indexer, top-1024, window 128)", "global_batch": B,
+                   "seq_len": L, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "step_hbm": {"algo_MB": round(total_algo / 1e6, 2),
+                     "GBs": round(total_algo / (ms_step * 1e-3) / 1e9, 1),
+                     "frac": round(total_algo / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "calls": calls,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -85,7 +85,11 @@ def _check(status):
 
 
 def _ptr(t):
-    return None if t is None else C.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the C ABI must be contiguous")
+    return C.c_void_p(t.data_ptr())
 
 
 def _stream(stream):

@@ -61,3 +61,19 @@ def topk_lists(g, n_visible, k, rows):
         if take > 0:
             out[r, :take] = np.sort(g.choice(n, size=take, replace=False)).astype(np.int32)
     return out
+
+
+def fp8_records(g, prefix, d, dr, rec_bytes):
+    """Random FP8 KV records [prefix..., rec_bytes]: E4M3 codes drawn uniformly
+    over the finite codes, bf16 RoPE dims from a normal draw, a positive fp32
+    row scale, zero padding (layout of include/csa_attn.h)."""
+    prefix = tuple(np.atleast_1d(prefix))
+    dn = d - dr
+    out = np.zeros(prefix + (rec_bytes,), np.uint8)
+    codes = g.integers(0, 254, size=prefix + (dn,), dtype=np.uint8)
+    codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)      # skip 0x7F (NaN); 0xFF unreachable
+    out[..., :dn] = codes
+    out[..., dn:dn + 2 * dr] = bf16_bits(g, prefix + (dr,)).view(np.uint8).reshape(prefix + (2 * dr,))
+    scale = (np.abs(normal(g, prefix)) * np.float32(0.01) + np.float32(1e-3)).astype(np.float32)
+    out[..., dn + 2 * dr:dn + 2 * dr + 4] = scale.view(np.uint8).reshape(prefix + (4,))
+    return out
