@@ -6,6 +6,7 @@
 // GPU).  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -68,6 +69,7 @@ csa_status check_attn_common(const void* q, int32_t q_dtype, const int32_t* q_po
     const int d = p->head_dim, dr = p->rope_dim;
     if (d < 2 || d > 1024 || d % 2) return fail(CSA_ERR_INVALID_ARG, "head_dim %d must be even and in [2, 1024]", d);
     if (dr < 0 || dr > d || dr % 2) return fail(CSA_ERR_INVALID_ARG, "rope_dim %d must be even and <= head_dim", dr);
+    if (dr > 128) return fail(CSA_ERR_UNSUPPORTED, "rope_dim %d > 128", dr);
     if (p->window < 0 || p->m < 1) return fail(CSA_ERR_INVALID_ARG, "window %d / m %d", p->window, p->m);
     if (!is_act_fmt(q_dtype)) return fail(CSA_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
     if (!is_act_fmt(out_dtype)) return fail(CSA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
@@ -134,6 +136,7 @@ csa_status run_attention(const void* q, int32_t q_dtype, const int32_t* q_pos, c
     a.base = p->rope_base;
     a.scale = p->softmax_scale;
     a.eps = p->rms_eps;
+    csa::fill_rope_table(a.rope, a.dr, a.base);
     a.Tq = Tq;
     a.H = H;
     a.rows = (int32_t)rows;
@@ -145,6 +148,13 @@ csa_status run_attention(const void* q, int32_t q_dtype, const int32_t* q_pos, c
 }
 
 }  // namespace
+
+namespace csa {
+// the fp64 inverse RoPE frequencies base^(-2i/dr) of every kernel launch
+void fill_rope_table(RopeTable& t, int dr, float base) {
+    for (int i = 0; i < 64; i++) t.f[i] = (i < dr / 2) ? pow((double)base, -2.0 * i / dr) : 0.0;
+}
+}  // namespace csa
 
 CSA_API size_t csa_kv_record_bytes(int32_t fmt, int32_t d, int32_t d_rope) {
     if (d < 1 || d_rope < 0 || d_rope > d) return 0;
@@ -166,6 +176,7 @@ CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, in
     if (d < 2 || d > 1024 || d % 2) return fail(CSA_ERR_INVALID_ARG, "d %d must be even and in [2, 1024]", d);
     if (m < 1 || m > 1024) return fail(CSA_ERR_INVALID_ARG, "m %d must be in [1, 1024]", m);
     if (rope_dim < 0 || rope_dim > d || rope_dim % 2) return fail(CSA_ERR_INVALID_ARG, "rope_dim %d", rope_dim);
+    if (rope_dim > 128) return fail(CSA_ERR_UNSUPPORTED, "rope_dim %d > 128", rope_dim);
     if (!is_act_fmt(x_dtype)) return fail(CSA_ERR_UNSUPPORTED, "x dtype %d", x_dtype);
     if ((kv_out != nullptr) == (idx_out != nullptr)) return fail(CSA_ERR_INVALID_ARG, "give exactly one of kv_out / idx_out");
     if (T / m > (int64_t)0x7FFFFFFF) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
@@ -211,6 +222,7 @@ CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, in
     a.eps = eps;
     a.dr = rope_dim;
     a.base = rope_base;
+    csa::fill_rope_table(a.rope, rope_dim, rope_base);
     return hip_status(csa::launch_compress(a, x_dtype, static_cast<hipStream_t>(stream)), "compress launch");
 }
 

@@ -85,7 +85,7 @@ __device__ void query_prologue(const AttnArgs& a, int64_t row, int h0, int hg, i
         const int off = d - a.dr;
         for (int p = lane; p < a.dr / 2; p += kWave) {
             float sn, cs;
-            rope_sincos((double)t, p, a.dr, a.base, sn, cs);
+            rope_sincos((double)t, a.rope.f[p], sn, cs);
             float x0 = qs[hh * d + off + 2 * p], x1 = qs[hh * d + off + 2 * p + 1];
             qs[hh * d + off + 2 * p] = x0 * cs - x1 * sn;
             qs[hh * d + off + 2 * p + 1] = x0 * sn + x1 * cs;
@@ -99,7 +99,7 @@ __device__ __forceinline__ void rotate_out(const AttnArgs& a, int64_t t, float* 
     const int d = a.d, off = d - a.dr;
     for (int p = lane0; p < a.dr / 2; p += nthreads) {
         float sn, cs;
-        rope_sincos(-(double)t, p, a.dr, a.base, sn, cs);
+        rope_sincos(-(double)t, a.rope.f[p], sn, cs);
         float x0 = v[off + 2 * p], x1 = v[off + 2 * p + 1];
         v[off + 2 * p] = x0 * cs - x1 * sn;
         v[off + 2 * p + 1] = x0 * sn + x1 * cs;
@@ -235,42 +235,44 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
     }
 }
 
-// merge the splits of (row, head) in split order
+// merge the splits of (row, head): weights exp(m_s - M) with M over the split
+// maxima and the sink, each output dim summed over the splits in split order
 template <typename OT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int nsplit_max, int split) {
     __shared__ float v[kAttnMaxD];
     __shared__ float wsc[1024];
-    __shared__ float sden;
+    __shared__ float red[kAttnThreads / kWave];
     const int h = blockIdx.x;
     const int64_t row = blockIdx.y;
     const int64_t t = a.q_pos[row];
     const int64_t nc = comp_slots(a, t);
     const int64_t ne = nc + a.W;
-    const int64_t nsplit = (ne + split - 1) / split;
+    const int nsplit = (int)((ne + split - 1) / split);
     if (nsplit <= 1) return;
     const float* wo = reinterpret_cast<const float*>(a.ws);
     const float* wml = wo + (size_t)a.rows * nsplit_max * a.H * a.d;
     const int d = a.d;
     const float sk = a.sink[h];
-    if (threadIdx.x == 0) {
-        float M = sk;
-        for (int64_t s = 0; s < nsplit; s++) M = fmaxf(M, wml[(((size_t)row * nsplit_max + s) * a.H + h) * 2]);
-        float den = (M == -INFINITY) ? 0.0f : expf(sk - M);
-        for (int64_t s = 0; s < nsplit; s++) {
-            const size_t i = (((size_t)row * nsplit_max + s) * a.H + h) * 2;
-            const float ms = wml[i], ls = wml[i + 1];
-            const float w = (ms == -INFINITY) ? 0.0f : expf(ms - M);
-            wsc[s] = w;
-            den += ls * w;
-        }
-        sden = den;
+    const size_t mbase = (size_t)row * nsplit_max * a.H + h;     // split s at mbase + s * H
+    float mx = sk;
+    for (int s = threadIdx.x; s < nsplit; s += blockDim.x) mx = fmaxf(mx, wml[(mbase + (size_t)s * a.H) * 2]);
+    const float M = block_max(mx, red);
+    float den = 0.0f;
+    for (int s = threadIdx.x; s < nsplit; s += blockDim.x) {
+        const size_t i = (mbase + (size_t)s * a.H) * 2;
+        const float ms = wml[i];
+        const float w = (ms == -INFINITY) ? 0.0f : expf(ms - M);
+        wsc[s] = w;
+        den += wml[i + 1] * w;
     }
+    den = block_sum(den, red);
+    if (M != -INFINITY) den += expf(sk - M);
     __syncthreads();
-    const float den = sden;
+    const float* wo_h = wo + mbase * d;
     for (int k = threadIdx.x; k < d; k += blockDim.x) {
         float acc = 0.0f;
-        for (int64_t s = 0; s < nsplit; s++)
-            acc = fmaf(wsc[s], wo[(((size_t)row * nsplit_max + s) * a.H + h) * d + k], acc);
+#pragma unroll 8
+        for (int s = 0; s < nsplit; s++) acc = fmaf(wsc[s], wo_h[(size_t)s * a.H * d + k], acc);
         v[k] = den > 0.0f ? acc / den : 0.0f;
     }
     __syncthreads();
@@ -283,26 +285,35 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int n
 int64_t attn_ws_bytes(int64_t rows, int32_t H, int32_t d, int64_t max_entries, int32_t q_fmt, int32_t comp_fmt) {
     (void)q_fmt;
     (void)comp_fmt;
-    const int64_t nsplit = (max_entries + kAttnSplit - 1) / kAttnSplit;
+    // sized for the smaller of the two kernels' split lengths (an upper bound for both)
+    const int split = min(kAttnSplit, attn_mfma_split());
+    const int64_t nsplit = (max_entries + split - 1) / split;
     if (nsplit <= 1) return 0;
     return rows * nsplit * H * ((int64_t)d + 2) * 4;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st) {
     if (a.rows == 0) return hipSuccess;
-    const int64_t nsplit = max((int64_t)1, (max_entries + kAttnSplit - 1) / kAttnSplit);
-    const int HG = min(min(a.H, kAttnQFloats / 64), kAttnQFloats / a.d);
-    const int ngroups = (a.H + HG - 1) / HG;
-    dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)ngroups);
-    const bool qb = a.q_fmt == CSA_BF16, ob = a.out_fmt == CSA_BF16;
-    if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
-    if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
-    if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
-    if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+    const bool mf = attn_mfma_supported(a);
+    const int split = mf ? attn_mfma_split() : kAttnSplit;
+    const int64_t nsplit = max((int64_t)1, (max_entries + split - 1) / split);
+    if (mf) {
+        hipError_t e = launch_attention_mfma(a, max_entries, st);
+        if (e != hipSuccess) return e;
+    } else {
+        const int HG = min(min(a.H, kAttnQFloats / 64), kAttnQFloats / a.d);
+        const int ngroups = (a.H + HG - 1) / HG;
+        dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)ngroups);
+        const bool qb = a.q_fmt == CSA_BF16, ob = a.out_fmt == CSA_BF16;
+        if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+        if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+        if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+        if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+    }
     if (nsplit > 1) {
         dim3 g2((unsigned)a.H, (unsigned)a.rows);
-        if (ob) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, kAttnSplit);
-        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, kAttnSplit);
+        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, split);
+        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, split);
     }
     return hipGetLastError();
 }

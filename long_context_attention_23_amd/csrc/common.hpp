@@ -79,14 +79,17 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 }
 
 // ---------------------------------------------------------------- RoPE
-// angle of pair i at position pos, formed in fp64 (positions reach 2^20 and
-// more, where an fp32 product would be off by tens of milliradians)
-__device__ __forceinline__ void rope_sincos(double pos, int i, int dr, float base, float& s, float& c) {
-    double theta = pos * pow((double)base, -2.0 * (double)i / (double)dr);
-    double sd, cd;
-    sincos(theta, &sd, &cd);
-    s = (float)sd;
-    c = (float)cd;
+// Angle of pair i at position pos: pos * f_i with f_i = base^(-2i/dr) held in
+// fp64 (positions reach 2^20 and more, where an fp32 product would be off by
+// tens of milliradians).  The product is reduced modulo 2*pi exactly enough
+// in fp64 (Cody-Waite, 2*pi split into a double and its remainder, fused
+// multiply-adds), and sin / cos are taken in fp32 of the reduced angle.
+__device__ __forceinline__ void rope_sincos(double pos, double freq, float& s, float& c) {
+    const double x = pos * freq;
+    const double k = rint(x * 0.15915494309189535);           // x / (2 pi)
+    double r = fma(-k, 6.283185307179586, x);                  // 2 pi, leading double
+    r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi - leading double
+    sincosf((float)r, &s, &c);
 }
 
 // ---------------------------------------------------------------- score keys

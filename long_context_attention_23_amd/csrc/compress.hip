@@ -30,6 +30,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     __shared__ float sz[kMaxM];
     __shared__ float red[kCompThreads / kWave];
     __shared__ int se[kMaxD / 32];
+    __shared__ float part[kCompThreads * 8];      // token-group partial sums of the pooling
 
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
@@ -61,27 +62,59 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     for (int r = tid; r < m; r += kCompThreads) sz[r] = expf(sz[r] - zmax) / zsum;
     __syncthreads();
 
-    // ---- pooled vector c = sum_r pi_r x_r (token order), then RMSNorm
-    float c[kMaxD / kCompThreads];
-    float ss = 0.0f;
+    // ---- pooled vector c = sum_r pi_r x_r.  16-byte chunks of the token rows;
+    // the threads of one chunk column split the block's tokens into TG groups
+    // (token order inside a group), and the group sums are added in group order.
+    constexpr int EPC = 16 / (int)sizeof(XT);
+    const int nch = d / EPC;
+    if (d % EPC == 0 && nch <= kCompThreads) {
+        const int TG = kCompThreads / nch;
+        const int c = tid % nch, tg = tid / nch;
+        if (tg < TG) {
+            float acc[EPC];
 #pragma unroll
-    for (int q = 0; q < kMaxD / kCompThreads; q++) {
-        int k = tid + q * kCompThreads;
-        float acc = 0.0f;
-        if (k < d)
+            for (int e = 0; e < EPC; e++) acc[e] = 0.0f;
+#pragma unroll 4
+            for (int r = tg; r < m; r += TG) {
+                const uint4 u = *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC);
+                const float p = sz[r];
+                if constexpr (sizeof(XT) == 2) {
+                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        acc[2 * q] = fmaf(p, __uint_as_float(wd[q] << 16), acc[2 * q]);
+                        acc[2 * q + 1] = fmaf(p, __uint_as_float(wd[q] & 0xFFFF0000u), acc[2 * q + 1]);
+                    }
+                } else {
+                    acc[0] = fmaf(p, __uint_as_float(u.x), acc[0]);
+                    acc[1] = fmaf(p, __uint_as_float(u.y), acc[1]);
+                    acc[2] = fmaf(p, __uint_as_float(u.z), acc[2]);
+                    acc[3] = fmaf(p, __uint_as_float(u.w), acc[3]);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; e++) part[tg * d + c * EPC + e] = acc[e];
+        }
+        __syncthreads();
+        for (int k = tid; k < d; k += kCompThreads) {
+            float v = 0.0f;
+            for (int q = 0; q < TG; q++) v += part[q * d + k];
+            sv[k] = v;
+        }
+    } else {
+        for (int k = tid; k < d; k += kCompThreads) {
+            float acc = 0.0f;
             for (int r = 0; r < m; r++) acc += sz[r] * ld_scalar<XT>(xb, (size_t)r * d + k);
-        c[q] = acc;
-        ss += acc * acc;
+            sv[k] = acc;
+        }
     }
-    float inv = 1.0f;
+    __syncthreads();
+    float ss = 0.0f;
+    for (int k = tid; k < d; k += kCompThreads) ss += sv[k] * sv[k];
     if (a.gamma) {
         ss = block_sum(ss, red);
-        inv = 1.0f / sqrtf(ss / (float)d + a.eps);
-    }
-#pragma unroll
-    for (int q = 0; q < kMaxD / kCompThreads; q++) {
-        int k = tid + q * kCompThreads;
-        if (k < d) sv[k] = a.gamma ? c[q] * inv * a.gamma[k] : c[q];
+        const float inv = 1.0f / sqrtf(ss / (float)d + a.eps);
+        for (int k = tid; k < d; k += kCompThreads) sv[k] = sv[k] * inv * a.gamma[k];
     }
     __syncthreads();
 
@@ -89,7 +122,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     const int off = d - a.dr;
     for (int p = tid; p < a.dr / 2; p += kCompThreads) {
         float sn, cs;
-        rope_sincos((double)(j * m), p, a.dr, a.base, sn, cs);
+        rope_sincos((double)(j * m), a.rope.f[p], sn, cs);
         float x0 = sv[off + 2 * p], x1 = sv[off + 2 * p + 1];
         sv[off + 2 * p] = x0 * cs - x1 * sn;
         sv[off + 2 * p + 1] = x0 * sn + x1 * cs;

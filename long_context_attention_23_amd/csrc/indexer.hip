@@ -292,6 +292,119 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_score(IndexerArgs a) {
         if (lh[i]) atomicAdd(&w.hist[i], lh[i]);
 }
 
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_i __attribute__((ext_vector_type(8)));
+
+constexpr int kIdxMfmaBatch = 8;   // 32-key groups whose loads a wave issues before computing
+
+// Score a chunk of 64-dim keys with the matrix cores.  C[head][key] = Q K^T:
+// the query's Hi rows are the A operand (32 rows, rows >= Hi zero), 32 keys
+// form the B operand, so accumulator lane l < 32 holds heads 0-3, 8-11, ...
+// of key l and lane l + 32 heads 4-7, 12-15, ...; S = sum_h w_h ReLU(C[h][key])
+// is completed with one lane exchange.
+//   KF = FP4: v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 codes, the E8M0 block
+//             scales applied by the instruction (one per 32 values);
+//   KF = BF16: four v_mfma_f32_32x32x16_bf16 (queries FP4 or bf16, exact in bf16).
+// Each wave loads kIdxMfmaBatch groups before computing them, to keep enough
+// bytes in flight.
+template <int QF, int KF>
+__global__ __launch_bounds__(kIdxThreads) void k_idx_score_mfma(IndexerArgs a) {
+    constexpr int DI = 64;
+    constexpr int NKS = KF == CSA_FP4_E2M1 ? 1 : 4;            // K steps per 32-key group
+    constexpr int KROW = KF == CSA_FP4_E2M1 ? DI / 2 : 2 * DI;  // key row bytes
+    __shared__ uint32_t lh[kIdxHistBins];
+    const int64_t r = blockIdx.y, row = a.row0 + r;
+    const int64_t b = row / a.Tq;
+    const int64_t n = visible_blocks(a, row);
+    const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
+    if (n <= a.topk || c0 >= n) return;
+    RowWs ws = row_ws(a, r);
+    for (int i = threadIdx.x; i < kIdxHistBins; i += blockDim.x) lh[i] = 0;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int l32 = lane & 31, half = lane >> 5;
+    const int Hi = a.Hi;
+    float wrow[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const int h = 8 * (i / 4) + 4 * half + (i % 4);
+        wrow[i] = h < Hi ? a.w[row * Hi + h] : 0.0f;
+    }
+    // A fragments: query row l32 (zero beyond Hi)
+    const uint8_t* qbase = reinterpret_cast<const uint8_t*>(a.q) + row * Hi * row_bytes(QF, DI);
+    i32x8_t qa4 = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    int qs4 = 127;
+    bf16x8_i qab[NKS];
+    if constexpr (KF == CSA_FP4_E2M1) {
+        if (l32 < Hi) {
+            const uint4 u = *reinterpret_cast<const uint4*>(qbase + (size_t)l32 * (DI / 2) + 16 * half);
+            qa4[0] = (int)u.x; qa4[1] = (int)u.y; qa4[2] = (int)u.z; qa4[3] = (int)u.w;
+            qs4 = a.q_scales[(row * Hi + l32) * (DI / 32) + half];
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) {
+            float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (l32 < Hi) {
+                const uint8_t* qrow = qbase + (size_t)l32 * row_bytes(QF, DI);
+                const uint8_t* qsc = a.q_scales ? a.q_scales + (row * Hi + l32) * (DI / 32) : nullptr;
+                load8<QF>(qrow, qsc, 16 * ks + 8 * half, v);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; j++) qab[ks][j] = (__bf16)v[j];
+        }
+    }
+    __syncthreads();
+    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
+    const uint8_t* kb = a.keys + (size_t)b * a.cap * KROW;
+    const uint8_t* ksb = KF == CSA_FP4_E2M1 ? a.key_scales + (size_t)b * a.cap * (DI / 32) : nullptr;
+    constexpr int kStride = 32 * (kIdxThreads / 64);
+    for (int64_t gb = c0 + 32 * wv; gb < c1; gb += (int64_t)kStride * kIdxMfmaBatch) {
+        uint4 kc[kIdxMfmaBatch][NKS];
+        int ksc[kIdxMfmaBatch];
+#pragma unroll
+        for (int u = 0; u < kIdxMfmaBatch; u++) {
+            const int64_t key = gb + (int64_t)u * kStride + l32;
+            ksc[u] = 127;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ks++) kc[u][ks] = make_uint4(0u, 0u, 0u, 0u);
+            if (key < c1) {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++)
+                    kc[u][ks] = *reinterpret_cast<const uint4*>(kb + key * KROW + 32 * ks + 16 * half);
+                if constexpr (KF == CSA_FP4_E2M1) ksc[u] = ksb[key * (DI / 32) + half];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kIdxMfmaBatch; u++) {
+            const int64_t key = gb + (int64_t)u * kStride + l32;
+            f32x16_t acc;
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[i] = 0.0f;
+            if constexpr (KF == CSA_FP4_E2M1) {
+                const i32x8_t kf = i32x8_t{(int)kc[u][0].x, (int)kc[u][0].y, (int)kc[u][0].z, (int)kc[u][0].w, 0, 0, 0, 0};
+                acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa4, kf, acc, 4, 4, 0, qs4, 0, ksc[u]);
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qab[ks], __builtin_bit_cast(bf16x8_i, kc[u][ks]), acc, 0, 0, 0);
+            }
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; i++) part = fmaf(wrow[i], fmaxf(acc[i], 0.0f), part);
+            const float sc = part + __shfl_xor(part, 32, kWave);
+            if (half == 0 && key < c1) {
+                const uint32_t k32 = score_key(sc);
+                ws.scores[key] = k32;
+                atomicAdd(&lh[k32 >> 20], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < kIdxHistBins; i += blockDim.x)
+        if (lh[i]) atomicAdd(&ws.hist[i], lh[i]);
+}
+
 // threshold bin of the 4096-bin histogram, computed by one wave
 __device__ __forceinline__ void wave_pick_bin(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -336,13 +449,21 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     const uint32_t tbin = sh[0];
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
-    for (int64_t j0 = c0; j0 < c1; j0 += blockDim.x) {
-        int64_t j = j0 + threadIdx.x;
-        uint32_t key = j < c1 ? w.scores[j] : 0u;
-        uint32_t bin = key >> 20;
-        bool sure = j < c1 && bin > tbin;
-        bool cand = j < c1 && bin == tbin;
-        uint64_t bs = __ballot(sure), bc = __ballot(cand);
+    constexpr int kPer = kIdxChunk / kIdxThreads;
+    uint32_t keys[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {                     // all loads first
+        const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
+        keys[u] = j < c1 ? w.scores[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+        const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
+        const uint32_t key = keys[u];
+        const uint32_t bin = key >> 20;
+        const bool sure = j < c1 && bin > tbin;
+        const bool cand = j < c1 && bin == tbin;
+        const uint64_t bs = __ballot(sure), bc = __ballot(cand);
         uint32_t os = 0, oc = 0;
         if (lane == 0) {
             if (bs) os = atomicAdd(&w.counts[0], (uint32_t)__popcll(bs));
@@ -350,16 +471,20 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
         }
         os = __shfl(os, 0, kWave);
         oc = __shfl(oc, 0, kWave);
-        uint64_t below = (1ull << lane) - 1;
+        const uint64_t below = (1ull << lane) - 1;
         if (sure) w.sel[os + __popcll(bs & below)] = (int32_t)j;
         if (cand) w.cand[oc + __popcll(bc & below)] = make_uint2(key, (uint32_t)j);
     }
 }
 
+constexpr int kIdxBitmapWords = 16384;   // LDS bitmap of selected blocks (caps up to 2^19)
+
 __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
+    __shared__ uint32_t bm[kIdxBitmapWords];
     __shared__ int32_t arr[kIdxMaxTopk];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh[4];
+    __shared__ uint32_t wsum[kIdxFinalThreads / kWave];
     const int64_t r = blockIdx.x, row = a.row0 + r;
     const int64_t n = visible_blocks(a, row);
     int32_t* out = a.out + row * a.topk;
@@ -378,7 +503,52 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
         return ((uint64_t)(c.x & 0xFFFFFu) << jb) | (jmask - (uint64_t)c.y);
     };
     const uint64_t thr = radix_select(get, (int64_t)ncand, 20 + jb, need, hist, sh);
-    // gather the k indices: every "sure" block plus candidates at or above thr
+    const int nwords = (int)((n + 31) / 32);
+    if (nwords <= kIdxBitmapWords) {
+        // mark the k selected blocks, then emit them in block order
+        for (int i = threadIdx.x; i < nwords; i += blockDim.x) bm[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < nsel; i += blockDim.x) {
+            const uint32_t j = (uint32_t)w.sel[i];
+            atomicOr(&bm[j >> 5], 1u << (j & 31));
+        }
+        for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x)
+            if (get(i) >= thr) {
+                const uint32_t j = cand[i].y;
+                atomicOr(&bm[j >> 5], 1u << (j & 31));
+            }
+        __syncthreads();
+        const int per = (nwords + blockDim.x - 1) / blockDim.x;     // consecutive words per thread
+        const int w0 = threadIdx.x * per;
+        uint32_t cnt = 0;
+        for (int q = 0; q < per; q++)
+            if (w0 + q < nwords) cnt += __popc(bm[w0 + q]);
+        // exclusive scan of cnt over the block
+        const int lane = threadIdx.x & (kWave - 1), wvi = threadIdx.x / kWave;
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const uint32_t tv = __shfl_up(incl, o, kWave);
+            if (lane >= o) incl += tv;
+        }
+        if (lane == kWave - 1) wsum[wvi] = incl;
+        __syncthreads();
+        uint32_t off = 0;
+        for (int q = 0; q < wvi; q++) off += wsum[q];
+        off += incl - cnt;
+        for (int q = 0; q < per; q++) {
+            if (w0 + q >= nwords) break;
+            uint32_t bits = bm[w0 + q];
+            while (bits) {
+                const int bpos = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (off < (uint32_t)a.topk) out[off] = (w0 + q) * 32 + bpos;
+                off++;
+            }
+        }
+        return;
+    }
+    // very large caps: gather the k indices and bitonic-sort them
     for (uint32_t i = threadIdx.x; i < nsel && i < (uint32_t)a.topk; i += blockDim.x) arr[i] = w.sel[i];
     if (threadIdx.x == 0) sh[2] = nsel;
     __syncthreads();
@@ -391,7 +561,6 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     while (P < a.topk) P <<= 1;
     for (int i = a.topk + threadIdx.x; i < P; i += blockDim.x) arr[i] = INT32_MAX;
     __syncthreads();
-    // bitonic sort ascending of P entries
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int i = threadIdx.x; i < P / 2; i += blockDim.x) {
@@ -424,7 +593,14 @@ static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes
         a.row0 = (int32_t)r0;
         a.rows = (int32_t)nr;
         hipLaunchKernelGGL(k_idx_zero, dim3((unsigned)nr), dim3(256), 0, st, a);
-        hipLaunchKernelGGL((k_idx_score<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+        const bool mfma_ok = a.di == 64 && a.Hi <= 32 && ((KF == CSA_FP4_E2M1 && QF == CSA_FP4_E2M1) ||
+                                                          (KF == CSA_BF16 && QF != CSA_F32));
+        if constexpr ((KF == CSA_FP4_E2M1 && QF == CSA_FP4_E2M1) || (KF == CSA_BF16 && QF != CSA_F32)) {
+            if (mfma_ok) hipLaunchKernelGGL((k_idx_score_mfma<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+            else hipLaunchKernelGGL((k_idx_score<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+        } else {
+            hipLaunchKernelGGL((k_idx_score<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+        }
         hipLaunchKernelGGL(k_idx_collect, dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
         hipLaunchKernelGGL(k_idx_final, dim3((unsigned)nr), dim3(kIdxFinalThreads), 0, st, a);
         hipError_t e = hipGetLastError();

@@ -9,6 +9,12 @@
 
 namespace csa {
 
+// fp64 inverse frequencies base^(-2i/dr), i < dr/2 (dr <= 128), filled on the host
+struct RopeTable {
+    double f[64];
+};
+void fill_rope_table(RopeTable& t, int dr, float base);
+
 struct CompressArgs {
     const void* x;
     int32_t B, d, m;
@@ -27,6 +33,7 @@ struct CompressArgs {
     int64_t cap;
     int32_t ring;
     int32_t rec_bytes;
+    RopeTable rope;
 };
 hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st);
 
@@ -80,10 +87,14 @@ struct AttnArgs {
     int32_t out_fmt;
     void* ws;
     int64_t ws_bytes;
+    RopeTable rope;
 };
 int64_t attn_ws_bytes(int64_t rows, int32_t H, int32_t d, int64_t max_entries, int32_t q_fmt,
                       int32_t comp_fmt);
 hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st);
+bool attn_mfma_supported(const AttnArgs& a);
+int attn_mfma_split();
+hipError_t launch_attention_mfma(const AttnArgs& a, int64_t max_entries, hipStream_t st);
 
 // ---- grouped projection
 struct ProjArgs {

@@ -157,6 +157,37 @@ def test_indexer_grid_exact(cap, k, Tq, kfmt):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("qkind", ["bf16", "fp4"])
+def test_indexer_bf16_keys_mfma_exact(qkind):
+    """bf16 keys (grid values are exact in bf16) scored on the matrix cores,
+    queries in bf16 or FP4 codes: exact sets."""
+    g = synth.rng(540 if qkind == "bf16" else 541)
+    B, Tq, Hi, di, m, k, cap = 2, 2, 4, 64, 4, 1024, 40000
+    keys = synth.grid(g, (B, cap, di))
+    w = synth.grid(g, (B, Tq, Hi))
+    pos = np.array([[4 * cap - 1, 4 * 7000 + 3], [4 * 100, 4 * cap + 50]], np.int32)
+    if qkind == "bf16":
+        qI = synth.grid(g, (B, Tq, Hi, di))
+        got, ref = run_indexer(bf16_rows(qI), None, O.BF16, w, pos, bf16_rows(keys), None, O.BF16, m, k, di)
+    else:
+        qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+        got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, bf16_rows(keys), None, O.BF16, m, k, di)
+    assert np.array_equal(got, ref)
+
+
+def test_indexer_very_large_cap_exact():
+    """More blocks than the final kernel's LDS bitmap covers (2^19): the
+    sorted-gather fallback."""
+    g = synth.rng(545)
+    B, Tq, Hi, di, m, k, cap = 1, 1, 4, 64, 4, 1024, 600000
+    kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
+    qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+    w = synth.grid(g, (B, Tq, Hi))
+    pos = np.array([[4 * cap - 1]], np.int32)
+    got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
+    assert np.array_equal(got, ref)
+
+
 def test_indexer_fp4_codes_exact():
     """FP4 keys and queries drawn as codes with a narrow exponent range: exact."""
     g = synth.rng(510)
@@ -245,15 +276,23 @@ ATTN_CASES = [
     (False, 1, 33, 8, 64, 16, 5, 3, 0, 40, O.F32, O.F32, O.F32),            # ragged prefill, dense
     (True, 2, 17, 4, 96, 32, 0, 2, 7, 50, O.F32, O.F32, O.BF16),            # no window
     (True, 1, 9, 16, 256, 64, 300, 4, 20, 100, O.BF16, O.F32, O.F32),       # window > split
+    # bf16 queries over bf16 / FP8 caches take the MFMA kernel when d in {128, 256, 512}, H % 16 == 0
+    (True, 2, 5, 16, 128, 64, 37, 4, 100, 300, O.BF16, O.BF16, O.F32),     # d 128, odd window
+    (False, 2, 3, 48, 256, 64, 128, 16, 0, 300, O.FP8_E4M3, O.BF16, O.BF16),  # d 256, 3 waves
+    (True, 1, 2, 96, 512, 64, 0, 4, 700, 5000, O.FP8_E4M3, O.BF16, O.BF16),  # 2 head groups, no window
+    (True, 2, 2, 8, 512, 64, 128, 4, 64, 1000, O.BF16, O.BF16, O.BF16),     # H 8: generic kernel, bf16 q
+    (False, 2, 2, 32, 512, 64, 128, 4, 0, 900, (O.BF16, O.FP8_E4M3), O.BF16, O.BF16),  # mixed cache formats
+    (True, 3, 4, 64, 512, 64, 128, 4, 1024, 8000, O.FP8_E4M3, O.BF16, O.F32),  # prefill-like rows, f32 out
 ]
 
 
 @pytest.mark.parametrize("ci", range(len(ATTN_CASES)), ids=[f"c{i}" for i in range(len(ATTN_CASES))])
 def test_attention_parity(ci):
     sparse, B, Tq, H, d, dr, W, m, k, ccap, cfmt, qfmt, ofmt = ATTN_CASES[ci]
+    cfmt, wfmt = cfmt if isinstance(cfmt, tuple) else (cfmt, cfmt)
     g = synth.rng(600 + ci)
     wcap = W + Tq + 7 if W > 0 else 4
-    comp, win = build_caches(g, B, ccap, wcap, d, dr, cfmt, cfmt)
+    comp, win = build_caches(g, B, ccap, wcap, d, dr, cfmt, wfmt)
     q = synth.normal(g, (B, Tq, H, d))
     gamma = (1 + 0.3 * synth.normal(g, d)).astype(np.float32)
     sink = synth.normal(g, H)
@@ -265,7 +304,7 @@ def test_attention_parity(ci):
         vis = np.minimum((pos.reshape(-1) + 1) // m, ccap)
         topk = synth.topk_lists(g, vis, k, B * Tq).reshape(B, Tq, k)
         topk[..., -1] = np.where(topk[..., -1] >= 0, ccap + 5, -1)   # an invisible index is skipped
-    got, ref = run_attention(sparse, q, qfmt, pos, topk, comp, cfmt, win, cfmt, gamma, sink, d, dr, W, m, ofmt)
+    got, ref = run_attention(sparse, q, qfmt, pos, topk, comp, cfmt, win, wfmt, gamma, sink, d, dr, W, m, ofmt)
     say(f"rel {rel_err(got, ref):.3e} abs {abs_err(got, ref):.3e}")
     if ofmt == O.F32 and qfmt == O.F32 and cfmt == O.F32:
         assert rel_err(got, ref) <= 1e-4
