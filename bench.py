@@ -154,43 +154,59 @@ def build_state(torch, api, copies, seed=4004):
 CALLS = ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_mqa_attn", "csa_out_proj",
          "hca_compress_kv", "hca_dense_mqa_attn", "hca_out_proj"]
 
+# the kernels each call launches (for matching rocprof summaries)
+CALL_KERNELS = {
+    "csa_compress_kv": ["k_compress"],
+    "csa_indexer_topk": ["k_idx_zero", "k_idx_score_mfma", "k_idx_collect", "k_idx_final"],
+    "csa_sparse_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
+    "csa_out_proj": ["k_proj_gemv"],
+    "hca_compress_kv": ["k_compress"],
+    "hca_dense_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
+    "hca_out_proj": ["k_proj_gemv"],
+}
 
-def step(api, s, sh, ev=None):
-    """One decode step of the layer pair.  ev: optional list of (start, end)
-    event pairs, one per call, recorded on the current stream."""
-    def mark(i, end):
-        if ev is not None:
-            ev[i][1 if end else 0].record()
 
-    mark(0, False)
-    api.compress_kv(s["x_new_csa"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
-                    kv_out=s["win_csa"])
-    api.compress_kv(s["x_csa"], sh["tok_csa"], M_CSA, sh["b_csa"], gamma=sh["gam"], rope_dim=DR, kv_out=s["csa_c"])
-    api.compress_kv(s["xi_csa"], sh["tok_csa"], M_CSA, sh["b_idx"], idx_out=s["keys"])
-    mark(0, True)
-    mark(1, False)
-    api.indexer_topk(s["qI"], api.FP4_E2M1, s["w_idx"], s["keys"], sh["pos"], M_CSA, K_CSA, q_scales=s["qI_s"],
-                     out=s["top"], workspace=s["idx_ws"])
-    mark(1, True)
-    mark(2, False)
-    api.sparse_mqa_attn(s["q_csa"], sh["pos"], s["top"], s["csa_c"], s["win_csa"], s["sink_csa"], sh["p_csa"],
-                        out=s["o_csa"], workspace=s["attn_ws_csa"])
-    mark(2, True)
-    mark(3, False)
-    api.out_proj_grouped(s["o_csa"].view(B, H * D_HEAD), s["Wo_csa"], y=s["y_csa"])
-    mark(3, True)
-    mark(4, False)
-    api.compress_kv(s["x_new_hca"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
-                    kv_out=s["win_hca"])
-    api.compress_kv(s["x_hca"], sh["tok_hca"], M_HCA, sh["b_hca"], gamma=sh["gam"], rope_dim=DR, kv_out=s["hca_c"])
-    mark(4, True)
-    mark(5, False)
-    api.hca_dense_mqa_attn(s["q_hca"], sh["pos"], s["hca_c"], s["win_hca"], s["sink_hca"], sh["p_hca"],
-                           out=s["o_hca"], workspace=s["attn_ws_hca"])
-    mark(5, True)
-    mark(6, False)
-    api.out_proj_grouped(s["o_hca"].view(B, H * D_HEAD), s["Wo_hca"], y=s["y_hca"])
-    mark(6, True)
+def call_fns(api):
+    """One function per call of the decode step (each launches that call's kernels)."""
+    def c0(s, sh):
+        api.compress_kv(s["x_new_csa"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
+                        kv_out=s["win_csa"])
+        api.compress_kv(s["x_csa"], sh["tok_csa"], M_CSA, sh["b_csa"], gamma=sh["gam"], rope_dim=DR, kv_out=s["csa_c"])
+        api.compress_kv(s["xi_csa"], sh["tok_csa"], M_CSA, sh["b_idx"], idx_out=s["keys"])
+
+    def c1(s, sh):
+        api.indexer_topk(s["qI"], api.FP4_E2M1, s["w_idx"], s["keys"], sh["pos"], M_CSA, K_CSA, q_scales=s["qI_s"],
+                         out=s["top"], workspace=s["idx_ws"])
+
+    def c2(s, sh):
+        api.sparse_mqa_attn(s["q_csa"], sh["pos"], s["top"], s["csa_c"], s["win_csa"], s["sink_csa"], sh["p_csa"],
+                            out=s["o_csa"], workspace=s["attn_ws_csa"])
+
+    def c3(s, sh):
+        api.out_proj_grouped(s["o_csa"].view(B, H * D_HEAD), s["Wo_csa"], y=s["y_csa"])
+
+    def c4(s, sh):
+        api.compress_kv(s["x_new_hca"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
+                        kv_out=s["win_hca"])
+        api.compress_kv(s["x_hca"], sh["tok_hca"], M_HCA, sh["b_hca"], gamma=sh["gam"], rope_dim=DR, kv_out=s["hca_c"])
+
+    def c5(s, sh):
+        api.hca_dense_mqa_attn(s["q_hca"], sh["pos"], s["hca_c"], s["win_hca"], s["sink_hca"], sh["p_hca"],
+                               out=s["o_hca"], workspace=s["attn_ws_hca"])
+
+    def c6(s, sh):
+        api.out_proj_grouped(s["o_hca"].view(B, H * D_HEAD), s["Wo_hca"], y=s["y_hca"])
+
+    return [c0, c1, c2, c3, c4, c5, c6]
+
+
+def capture(torch, fns, s, sh):
+    """One HIP graph launching fns in order on the capture stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f(s, sh)
+    return g
 
 
 def cpu_baseline(target_s):
@@ -258,27 +274,59 @@ def main():
     torch.cuda.set_device(0)
     sets, sh = build_state(torch, api, args.copies)
     R = len(sets)
-    for i in range(args.warmup):
-        step(api, sets[i % R], sh)
+    fns = call_fns(api)
+    for s_ in sets:                                   # eager warm-up of every call
+        for f in fns:
+            f(s_, sh)
     torch.cuda.synchronize()
-    # timed region: exactly K steps, synchronised on both sides
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in CALLS]
-          for _ in range(args.steps)]
+
+    # calibration: one graph per call, events between them -> per-call GPU time
+    per_call_graphs = [[capture(torch, [f], s_, sh) for f in fns] for s_ in sets]
+    ncal = max(10, min(50, args.steps))
+    evc = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in CALLS]
+           for _ in range(ncal)]
+    for i in range(ncal):
+        for j, g in enumerate(per_call_graphs[i % R]):
+            evc[i][j][0].record()
+            g.replay()
+            evc[i][j][1].record()
+    torch.cuda.synchronize()
+    per_call = {c: float(np.median([evc[i][j][0].elapsed_time(evc[i][j][1]) for i in range(ncal)]))
+                for j, c in enumerate(CALLS)}
+    dom = max(CALLS, key=lambda c: per_call[c])
+    di = CALLS.index(dom)
+
+    # timed region: each step = three graphs (the calls before the dominant one,
+    # the dominant call, the calls after it), events around the dominant call
+    step_graphs = [(capture(torch, fns[:di], s_, sh) if di > 0 else None, capture(torch, [fns[di]], s_, sh),
+                    capture(torch, fns[di + 1:], s_, sh) if di < len(fns) - 1 else None) for s_ in sets]
+    for i in range(args.warmup):
+        for g in step_graphs[i % R]:
+            if g is not None:
+                g.replay()
+    ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(api, sets[i % R], sh, ev[i])
+        pre, mid, post = step_graphs[i % R]
+        if pre is not None:
+            pre.replay()
+        ev[i][0].record()
+        mid.replay()
+        ev[i][1].record()
+        if post is not None:
+            post.replay()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el * 1e3 / args.steps
-    per_call = {c: float(np.mean([ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(args.steps)]))
-                for j, c in enumerate(CALLS)}
+    dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     algo = algorithmic_bytes()
     calls = {c: {"us": round(per_call[c] * 1e3, 2), "algo_MB": round(algo[c] / 1e6, 3),
-                 "GBs": round(algo[c] / (per_call[c] * 1e-3) / 1e9, 1)} for c in CALLS}
-    dom = max(CALLS, key=lambda c: per_call[c])
-    achieved = algo[dom] / (per_call[dom] * 1e-3) / 1e9
+                 "GBs": round(algo[c] / (per_call[c] * 1e-3) / 1e9, 1), "kernels": sorted(set(CALL_KERNELS[c]))}
+             for c in CALLS}
+    achieved = algo[dom] / (dom_ms * 1e-3) / 1e9
     total_algo = sum(algo.values())
+    gpu_ms = sum(per_call.values())
     res = {
         "metric": METRIC, "value": round(B / (ms_step * 1e-3), 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
@@ -286,12 +334,16 @@ def main():
         "config": {"workload": "CSA+HCA layer-pair decode, 1M context, batch 4, V4-Pro shape (hidden 7168, 64 heads "
                                "x 512, FP8 KV + FP4 indexer, top-1024, window 128)", "global_batch": B,
                    "seq_len": L, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
-        "step_hbm": {"algo_MB": round(total_algo / 1e6, 2),
-                     "GBs": round(total_algo / (ms_step * 1e-3) / 1e9, 1),
-                     "frac": round(total_algo / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": dom, "kernels": sorted(set(CALL_KERNELS[dom])),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "us_per_launch": round(dom_ms * 1e3, 2), "algo_MB_per_launch": round(algo[dom] / 1e6, 3)},
+        "step_hbm": {"algo_MB": round(total_algo / 1e6, 2), "gpu_us": round(gpu_ms * 1e3, 2),
+                     "GBs_gpu": round(total_algo / (gpu_ms * 1e-3) / 1e9, 1),
+                     "frac_gpu": round(total_algo / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "calls": calls,
+        "timing": "HIP graphs; value from the wall clock over the timed steps; per-call GPU times from events "
+                  "around per-call graphs (median over a calibration pass)",
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -288,7 +288,9 @@ CSA_API size_t csa_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t
                                        int32_t window, int32_t q_dtype, int32_t comp_fmt) {
     const int64_t rows = (int64_t)(B > 0 ? B : 0) * (Tq > 0 ? Tq : 0);
     if (rows == 0 || H < 1 || head_dim < 1) return 0;
-    return (size_t)csa::attn_ws_bytes(rows, H, head_dim, max_comp_entries + (window > 0 ? window : 0), q_dtype, comp_fmt);
+    (void)q_dtype;
+    (void)comp_fmt;
+    return (size_t)csa::attn_ws_bytes(rows, Tq, H, head_dim, max_comp_entries + (window > 0 ? window : 0));
 }
 
 CSA_API csa_status csa_sparse_mqa_attn(const void* q, int32_t q_dtype, const int32_t* q_pos, const int32_t* topk_idx,

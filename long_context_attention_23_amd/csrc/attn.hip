@@ -10,7 +10,7 @@
 //
 // Decomposition (flash-decoding): a query row's entry list -- its compressed
 // entries (top-k slots, or every visible block) followed by its W window
-// positions -- is cut into fixed splits of kAttnSplit entries; one workgroup
+// positions -- is cut into splits (attn_split_len, launch.hpp); one workgroup
 // per (split, row, head group) keeps a running max / sum / output per head,
 // and a combine kernel merges the splits in split order, adds the sink and
 // applies the output RoPE.  A row whose list fits in one split is finished
@@ -26,7 +26,6 @@ namespace csa {
 
 constexpr int kAttnThreads = 256;
 constexpr int kAttnTile = 8;
-constexpr int kAttnSplit = 256;
 constexpr int kAttnMaxD = 1024;
 constexpr int kAttnQFloats = 4096;
 
@@ -66,7 +65,7 @@ __device__ __forceinline__ float rec_value(const uint8_t* rec, int fmt, int d, i
 
 // q^ = RoPE_t(RMSNorm(q)) for heads [h0, h0+hg) into qs[hh*d + k]; one wave per head
 template <typename QT>
-__device__ void query_prologue(const AttnArgs& a, int64_t row, int h0, int hg, int64_t t, float* qs) {
+__device__ void query_prologue(const AttnArgs& a, int64_t row, int h0, int hg, int64_t t, float* qs, const double* rf) {
     const int d = a.d, lane = threadIdx.x & (kWave - 1), nw = blockDim.x / kWave;
     const QT* q = reinterpret_cast<const QT*>(a.q) + (row * a.H + h0) * d;
     for (int hh = threadIdx.x / kWave; hh < hg; hh += nw) {
@@ -85,7 +84,7 @@ __device__ void query_prologue(const AttnArgs& a, int64_t row, int h0, int hg, i
         const int off = d - a.dr;
         for (int p = lane; p < a.dr / 2; p += kWave) {
             float sn, cs;
-            rope_sincos((double)t, a.rope.f[p], sn, cs);
+            rope_sincos((double)t, rf[p], sn, cs);
             float x0 = qs[hh * d + off + 2 * p], x1 = qs[hh * d + off + 2 * p + 1];
             qs[hh * d + off + 2 * p] = x0 * cs - x1 * sn;
             qs[hh * d + off + 2 * p + 1] = x0 * sn + x1 * cs;
@@ -95,11 +94,12 @@ __device__ void query_prologue(const AttnArgs& a, int64_t row, int h0, int hg, i
 
 // output RoPE_{-t} on the last dr dims of one head's vector v[0..d), by
 // nthreads threads starting at lane0
-__device__ __forceinline__ void rotate_out(const AttnArgs& a, int64_t t, float* v, int lane0, int nthreads) {
+__device__ __forceinline__ void rotate_out(const AttnArgs& a, int64_t t, float* v, int lane0, int nthreads,
+                                           const double* rf) {
     const int d = a.d, off = d - a.dr;
     for (int p = lane0; p < a.dr / 2; p += nthreads) {
         float sn, cs;
-        rope_sincos(-(double)t, a.rope.f[p], sn, cs);
+        rope_sincos(-(double)t, rf[p], sn, cs);
         float x0 = v[off + 2 * p], x1 = v[off + 2 * p + 1];
         v[off + 2 * p] = x0 * cs - x1 * sn;
         v[off + 2 * p + 1] = x0 * sn + x1 * cs;
@@ -113,20 +113,24 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
     __shared__ float pz[kAttnQFloats / 64 * kAttnTile];   // [hg][tile]
     __shared__ float mrun[kAttnQFloats / 64], lrun[kAttnQFloats / 64], alph[kAttnQFloats / 64];
     __shared__ int valid[kAttnTile];
+    __shared__ double rf[64];
 
     const int64_t row = blockIdx.y, b = row / a.Tq;
     const int64_t t = a.q_pos[row];
     const int64_t nc = comp_slots(a, t);
     const int64_t ne = nc + a.W;
-    const int64_t nsplit = (ne + kAttnSplit - 1) / kAttnSplit;
+    const int64_t split = attn_split_len(ne, a.Tq);
+    const int64_t nsplit = attn_nsplit(ne, a.Tq);
     const int64_t s = blockIdx.x;
-    if (s >= nsplit && !(s == 0 && ne == 0)) return;
-    const int64_t e0 = s * kAttnSplit, e1 = min(e0 + (int64_t)kAttnSplit, ne);
+    if (s >= nsplit) return;
+    const int64_t e0 = s * split, e1 = min(e0 + split, ne);
     const int h0 = blockIdx.z * HG, hg = min(HG, a.H - h0);
     const int d = a.d, ld = d + 1;
     const int tid = threadIdx.x;
 
-    query_prologue<QT>(a, row, h0, hg, t, qs);
+    stage_rope(a.rope, rf, a.dr / 2);
+    __syncthreads();
+    query_prologue<QT>(a, row, h0, hg, t, qs, rf);
     for (int hh = tid; hh < hg; hh += blockDim.x) { mrun[hh] = -INFINITY; lrun[hh] = 0.0f; }
     constexpr int kMaxOwn = kAttnQFloats / kAttnThreads;
     float o[kMaxOwn];
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
         }
         __syncthreads();
         const int lane = tid & (kWave - 1), nw = blockDim.x / kWave;
-        for (int hh = tid / kWave; hh < hg; hh += nw) rotate_out(a, t, qs + hh * d, lane, kWave);
+        for (int hh = tid / kWave; hh < hg; hh += nw) rotate_out(a, t, qs + hh * d, lane, kWave, rf);
         __syncthreads();
         OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h0) * d;
         for (int idx = tid; idx < hg * d; idx += blockDim.x) st_scalar<OT>(out, idx, qs[idx]);
@@ -238,21 +242,23 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
 // merge the splits of (row, head): weights exp(m_s - M) with M over the split
 // maxima and the sink, each output dim summed over the splits in split order
 template <typename OT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int nsplit_max, int split) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int nsplit_max) {
     __shared__ float v[kAttnMaxD];
     __shared__ float wsc[1024];
     __shared__ float red[kAttnThreads / kWave];
+    __shared__ double rf[64];
     const int h = blockIdx.x;
     const int64_t row = blockIdx.y;
     const int64_t t = a.q_pos[row];
     const int64_t nc = comp_slots(a, t);
     const int64_t ne = nc + a.W;
-    const int nsplit = (int)((ne + split - 1) / split);
+    const int nsplit = (int)attn_nsplit(ne, a.Tq);
     if (nsplit <= 1) return;
     const float* wo = reinterpret_cast<const float*>(a.ws);
     const float* wml = wo + (size_t)a.rows * nsplit_max * a.H * a.d;
     const int d = a.d;
     const float sk = a.sink[h];
+    stage_rope(a.rope, rf, a.dr / 2);
     const size_t mbase = (size_t)row * nsplit_max * a.H + h;     // split s at mbase + s * H
     float mx = sk;
     for (int s = threadIdx.x; s < nsplit; s += blockDim.x) mx = fmaxf(mx, wml[(mbase + (size_t)s * a.H) * 2]);
@@ -276,44 +282,38 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int n
         v[k] = den > 0.0f ? acc / den : 0.0f;
     }
     __syncthreads();
-    rotate_out(a, t, v, threadIdx.x, blockDim.x);
+    rotate_out(a, t, v, threadIdx.x, blockDim.x, rf);
     __syncthreads();
     OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
     for (int k = threadIdx.x; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
 }
 
-int64_t attn_ws_bytes(int64_t rows, int32_t H, int32_t d, int64_t max_entries, int32_t q_fmt, int32_t comp_fmt) {
-    (void)q_fmt;
-    (void)comp_fmt;
-    // sized for the smaller of the two kernels' split lengths (an upper bound for both)
-    const int split = min(kAttnSplit, attn_mfma_split());
-    const int64_t nsplit = (max_entries + split - 1) / split;
-    if (nsplit <= 1) return 0;
-    return rows * nsplit * H * ((int64_t)d + 2) * 4;
+int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t max_entries) {
+    const int64_t nb = attn_nsplit_bound(max_entries, Tq);
+    if (nb <= 1) return 0;
+    return rows * nb * H * ((int64_t)d + 2) * 4;
 }
 
 hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st) {
     if (a.rows == 0) return hipSuccess;
-    const bool mf = attn_mfma_supported(a);
-    const int split = mf ? attn_mfma_split() : kAttnSplit;
-    const int64_t nsplit = max((int64_t)1, (max_entries + split - 1) / split);
-    if (mf) {
-        hipError_t e = launch_attention_mfma(a, max_entries, st);
+    const int64_t nb = attn_nsplit_bound(max_entries, a.Tq);
+    if (attn_mfma_supported(a)) {
+        hipError_t e = launch_attention_mfma(a, nb, st);
         if (e != hipSuccess) return e;
     } else {
         const int HG = min(min(a.H, kAttnQFloats / 64), kAttnQFloats / a.d);
         const int ngroups = (a.H + HG - 1) / HG;
-        dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)ngroups);
+        dim3 grid((unsigned)nb, (unsigned)a.rows, (unsigned)ngroups);
         const bool qb = a.q_fmt == CSA_BF16, ob = a.out_fmt == CSA_BF16;
-        if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
-        if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
-        if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
-        if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nsplit);
+        if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
+        if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
+        if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
+        if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
     }
-    if (nsplit > 1) {
+    if (nb > 1) {
         dim3 g2((unsigned)a.H, (unsigned)a.rows);
-        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, split);
-        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a, (int)nsplit, split);
+        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a, (int)nb);
+        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a, (int)nb);
     }
     return hipGetLastError();
 }

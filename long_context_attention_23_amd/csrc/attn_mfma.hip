@@ -9,10 +9,13 @@
 //     normalised and rotated queries sit in registers as MFMA A-fragments;
 //   - all heads of the workgroup share one LDS tile of 32 entries (MQA: one
 //     KV vector per entry serves every head); FP8 records are expanded to
-//     bf16 on the way in with the hardware OCP-E4M3 conversion, their per-row
-//     scale kept aside and applied to the logits of the non-RoPE part and to
-//     the probabilities of the non-RoPE output dims (exactly the decoded
-//     value, since scale * <q, code> = <q, scale * code>);
+//     bf16 with the hardware OCP-E4M3 conversion, their per-row scale kept
+//     aside and applied to the logits of the non-RoPE part and to the
+//     probabilities of the non-RoPE output dims (exactly the decoded value,
+//     since scale * <q, code> = <q, scale * code>);
+//   - the tile loop is software-pipelined: each wave loads the raw records of
+//     its 8 entries of tile t+1 into registers (16-byte pieces, one lane per
+//     piece) while tile t is computed, so HBM latency overlaps the MFMAs;
 //   - S = Q K^T and O += P V run as 16x16x32 MFMAs with fp32 accumulation; P
 //     goes through a small per-wave LDS buffer to turn the accumulator layout
 //     into the A-operand layout; the online softmax keeps running max / sum
@@ -26,34 +29,32 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMTE = 32;       // entries per LDS tile
-constexpr int kMSplit = 128;   // entries per workgroup (fixed: results independent of the batch)
+constexpr int kMTE = 32;                  // entries per LDS tile
 constexpr int kPStride = kMTE + 8;
+constexpr int kEntPerWave = kMTE / 4;     // entries of a tile staged by one wave (4 waves per workgroup)
 
 template <int D>
 struct MfmaSmem {
-    uint8_t tile[kMTE][D * 2 + 16];          // bf16 entries, rows padded by 16 bytes
-    const uint8_t* rec[kMTE];
-    int fmt[kMTE];
-    float scale[kMTE];
-    uint16_t p[4][2][16][kPStride];          // per wave: [scaled, plain] P, 16 heads x 32 entries
+    uint8_t tile[kMTE][D * 2 + 16];       // bf16 entries, rows padded by 16 bytes
+    float scale[kMTE];                    // FP8 row scale (1 for bf16 records)
+    int valid[kMTE];
+    uint16_t p[4][2][16][kPStride];       // per wave: [scaled, plain] P, 16 heads x 32 entries
+    double rf[64];                        // RoPE inverse frequencies
 };
 
-// same entry enumeration as the generic kernel
+// record of entry e of a row (nullptr if masked); same enumeration as attn.hip
 __device__ __forceinline__ const uint8_t* mfma_entry_rec(const AttnArgs& a, int64_t row, int64_t b, int64_t t,
-                                                         int64_t nc, int64_t e, int& fmt) {
+                                                         int64_t nc, int64_t vis, int64_t e, int& fmt) {
     if (e < nc) {
         int64_t j = e;
         if (a.topk) {
             j = a.topk[row * a.k + e];
-            int64_t vis = t < 0 ? 0 : (t + 1) / a.m;
-            if (vis > a.ccap) vis = a.ccap;
             if (j < 0 || j >= vis) return nullptr;
         }
         fmt = a.comp_fmt;
         return a.comp + (b * a.ccap + j) * a.comp_rec;
     }
-    int64_t s = t - a.W + 1 + (e - nc);
+    const int64_t s = t - a.W + 1 + (e - nc);
     if (s < 0) return nullptr;
     fmt = a.win_fmt;
     return a.win + (b * a.wcap + s % a.wcap) * a.win_rec;
@@ -65,74 +66,162 @@ __device__ __forceinline__ uint32_t pack_bf16x2(bf16x2_t v) {
     return u;
 }
 
-template <int D, typename OT>
+// raw 16-byte pieces of one wave's entries of a tile, one piece per lane.
+// FP8 records: pieces 0 .. dn/16-1 hold 16 E4M3 codes, the next DR/8 the bf16
+// RoPE dims, the next one the row scale; bf16 records: D/8 pieces of 8 dims.
+struct TileRegs {
+    uint4 piece[kEntPerWave];
+    const uint8_t* rec[kEntPerWave];
+    int fmt[kEntPerWave];
+};
+
+template <int D, int DR>
+__device__ __forceinline__ void tile_load(const AttnArgs& a, int64_t row, int64_t b, int64_t t, int64_t nc,
+                                          int64_t vis, int64_t et, int64_t e1, int w, int lane, TileRegs& R) {
+    constexpr int fp8_pieces = (D - DR) / 16 + DR / 8 + 1;
+#pragma unroll
+    for (int u = 0; u < kEntPerWave; u++) {
+        const int64_t e = et + w + 4 * u;
+        int fmt = 0;
+        const uint8_t* r = e < e1 ? mfma_entry_rec(a, row, b, t, nc, vis, e, fmt) : nullptr;
+        R.rec[u] = r;
+        R.fmt[u] = fmt;
+        R.piece[u] = make_uint4(0u, 0u, 0u, 0u);
+        if (r) {
+            const int npieces = fmt == CSA_FP8_E4M3 ? fp8_pieces : D / 8;
+            if (lane < npieces) R.piece[u] = *reinterpret_cast<const uint4*>(r + 16 * lane);
+        }
+    }
+}
+
+template <int D, int DR>
+__device__ __forceinline__ void tile_store(MfmaSmem<D>& sm, int w, int lane, const TileRegs& R) {
+    constexpr int dn = D - DR;
+#pragma unroll
+    for (int u = 0; u < kEntPerWave; u++) {
+        const int ee = w + 4 * u;
+        uint8_t* dst = sm.tile[ee];
+        const uint4 pc = R.piece[u];
+        if (!R.rec[u]) {
+            // masked entry: a zero row keeps 0 * garbage out of P V
+            if (lane < D / 8) *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
+            if (lane == 0) {
+                sm.scale[ee] = 1.0f;
+                sm.valid[ee] = 0;
+            }
+        } else if (R.fmt[u] == CSA_FP8_E4M3) {
+            if (lane < dn / 16) {
+                uint4 lo, hi;
+                lo.x = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.x, 1.0f, false));
+                lo.y = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.x, 1.0f, true));
+                lo.z = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.y, 1.0f, false));
+                lo.w = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.y, 1.0f, true));
+                hi.x = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.z, 1.0f, false));
+                hi.y = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.z, 1.0f, true));
+                hi.z = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.w, 1.0f, false));
+                hi.w = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc.w, 1.0f, true));
+                *reinterpret_cast<uint4*>(dst + 32 * lane) = lo;
+                *reinterpret_cast<uint4*>(dst + 32 * lane + 16) = hi;
+            } else if (lane < dn / 16 + DR / 8) {
+                *reinterpret_cast<uint4*>(dst + 2 * dn + 16 * (lane - dn / 16)) = pc;
+            } else if (lane == dn / 16 + DR / 8) {
+                sm.scale[ee] = __uint_as_float(pc.x);
+                sm.valid[ee] = 1;
+            }
+        } else {
+            if (lane < D / 8) *reinterpret_cast<uint4*>(dst + 16 * lane) = pc;
+            if (lane == 0) {
+                sm.scale[ee] = 1.0f;
+                sm.valid[ee] = 1;
+            }
+        }
+    }
+}
+
+template <int D, int DR, typename OT>
 __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit_max) {
     constexpr int NS = D / 32;   // QK K-steps
     constexpr int ND = D / 16;   // PV N-tiles
+    constexpr int dn = D - DR;   // non-RoPE dims (multiple of 32)
+    constexpr int nsr = dn / 32, ndr = dn / 16;
     __shared__ MfmaSmem<D> sm;
 
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int64_t row = blockIdx.y, b = row / a.Tq;
     const int64_t t = a.q_pos[row];
-    int64_t nc;
-    if (a.topk) nc = a.k;
-    else {
-        nc = t < 0 ? 0 : (t + 1) / a.m;
-        if (nc > a.ccap) nc = a.ccap;
-    }
+    int64_t vis = t < 0 ? 0 : (t + 1) / a.m;
+    if (vis > a.ccap) vis = a.ccap;
+    const int64_t nc = a.topk ? a.k : vis;
     const int64_t ne = nc + a.W;
-    const int64_t nsplit = (ne + kMSplit - 1) / kMSplit;
+    const int64_t split = attn_split_len(ne, a.Tq);
+    const int64_t nsplit = attn_nsplit(ne, a.Tq);
     const int64_t sp = blockIdx.x;
-    if (sp >= nsplit && !(sp == 0 && ne == 0)) return;
-    const int64_t e0 = sp * kMSplit, e1 = min(e0 + (int64_t)kMSplit, ne);
+    if (sp >= nsplit) return;
+    const int64_t e0 = sp * split, e1 = min(e0 + split, ne);
     const int hw = blockIdx.z * 64 + 16 * w;          // first head of this wave
     const bool active = hw < a.H;
-    const int dn = D - a.dr;                           // non-RoPE dims (multiple of 32)
-    const int nsr = dn / 32, ndr = dn / 16;
 
+    // the first tile's loads go out before the query prologue
+    TileRegs R;
+    tile_load<D, DR>(a, row, b, t, nc, vis, e0, e1, w, lane, R);
+
+    stage_rope(a.rope, sm.rf, a.dr / 2);
+    __syncthreads();
     // ---- query prologue: q^ = RoPE_t(RMSNorm(q)) as bf16 A-fragments
     bf16x8_t qf[NS];
     if (active) {
+        // two passes over this lane's 16-byte chunks of its head row: the sum of
+        // squares, then scale, rotate and round (no large private array)
         const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + (row * a.H + hw + l16) * D;
-        float v[NS][8];
         float ss = 0.0f;
 #pragma unroll
         for (int s = 0; s < NS; s++) {
-            uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g4);
-            uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+            const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g4);
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                v[s][2 * j] = __uint_as_float(wd[j] << 16);
-                v[s][2 * j + 1] = __uint_as_float(wd[j] & 0xFFFF0000u);
+                const float x0 = __uint_as_float(wd[j] << 16), x1 = __uint_as_float(wd[j] & 0xFFFF0000u);
+                ss += x0 * x0 + x1 * x1;
             }
-#pragma unroll
-            for (int j = 0; j < 8; j++) ss += v[s][j] * v[s][j];
         }
         ss += __shfl_xor(ss, 16, kWave);
         ss += __shfl_xor(ss, 32, kWave);
         const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+        // non-RoPE steps, then the RoPE steps (kept apart so both loops unroll)
 #pragma unroll
-        for (int s = 0; s < NS; s++) {
+        for (int s = 0; s < nsr; s++) {
+            const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g4);
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-            for (int j = 0; j < 8; j++) {
-                const int dim = 32 * s + 8 * g4 + j;
-                v[s][j] *= inv;
-                if (a.gamma_q) v[s][j] *= a.gamma_q[dim];
-            }
-            if (s >= nsr) {
-#pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    const int p = (32 * s + 8 * g4 + j - dn) / 2;
-                    float sn, cs;
-                    rope_sincos((double)t, a.rope.f[p], sn, cs);
-                    const float x0 = v[s][j], x1 = v[s][j + 1];
-                    v[s][j] = x0 * cs - x1 * sn;
-                    v[s][j + 1] = x0 * sn + x1 * cs;
+            for (int j = 0; j < 4; j++) {
+                const int dim = 32 * s + 8 * g4 + 2 * j;
+                float x0 = __uint_as_float(wd[j] << 16) * inv, x1 = __uint_as_float(wd[j] & 0xFFFF0000u) * inv;
+                if (a.gamma_q) {
+                    x0 *= a.gamma_q[dim];
+                    x1 *= a.gamma_q[dim + 1];
                 }
+                qf[s][2 * j] = (__bf16)x0;
+                qf[s][2 * j + 1] = (__bf16)x1;
             }
+        }
 #pragma unroll
-            for (int j = 0; j < 8; j++) qf[s][j] = (__bf16)v[s][j];
+        for (int s = nsr; s < NS; s++) {
+            const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * s + 8 * g4);
+            const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int dim = 32 * s + 8 * g4 + 2 * j;
+                float x0 = __uint_as_float(wd[j] << 16) * inv, x1 = __uint_as_float(wd[j] & 0xFFFF0000u) * inv;
+                if (a.gamma_q) {
+                    x0 *= a.gamma_q[dim];
+                    x1 *= a.gamma_q[dim + 1];
+                }
+                float sn, cs;
+                rope_sincos((double)t, sm.rf[(dim - dn) / 2], sn, cs);
+                qf[s][2 * j] = (__bf16)(x0 * cs - x1 * sn);
+                qf[s][2 * j + 1] = (__bf16)(x0 * sn + x1 * cs);
+            }
         }
     }
 
@@ -144,39 +233,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit_max) {
     for (int i = 0; i < 4; i++) { mrun[i] = -INFINITY; lrun[i] = 0.0f; }
 
     for (int64_t et = e0; et < e1; et += kMTE) {
-        const int nt = (int)min((int64_t)kMTE, e1 - et);
         __syncthreads();                                   // previous tile consumed
-        if (tid < kMTE) {
-            int fmt = 0;
-            const uint8_t* r = tid < nt ? mfma_entry_rec(a, row, b, t, nc, et + tid, fmt) : nullptr;
-            sm.rec[tid] = r;
-            sm.fmt[tid] = fmt;
-            float sc = 1.0f;
-            if (r && fmt == CSA_FP8_E4M3) sc = *reinterpret_cast<const float*>(r + dn + 2 * a.dr);
-            sm.scale[tid] = sc;
-        }
+        tile_store<D, DR>(sm, w, lane, R);
         __syncthreads();
-        // ---- stage the tile: 16-byte chunks of 8 bf16 dims
-        for (int idx = tid; idx < kMTE * (D / 8); idx += blockDim.x) {
-            const int ee = idx / (D / 8), c = idx % (D / 8);
-            const uint8_t* r = sm.rec[ee];
-            uint4 out = make_uint4(0u, 0u, 0u, 0u);
-            if (r) {
-                if (sm.fmt[ee] == CSA_BF16) {
-                    out = *reinterpret_cast<const uint4*>(r + 16 * c);
-                } else if (8 * c < dn) {
-                    const uint2 codes = *reinterpret_cast<const uint2*>(r + 8 * c);
-                    out.x = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, 1.0f, false));
-                    out.y = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, 1.0f, true));
-                    out.z = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, 1.0f, false));
-                    out.w = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, 1.0f, true));
-                } else {
-                    out = *reinterpret_cast<const uint4*>(r + dn + 2 * (8 * c - dn));
-                }
-            }
-            *reinterpret_cast<uint4*>(&sm.tile[ee][16 * c]) = out;
-        }
-        __syncthreads();
+        // the next tile's loads are issued after the barrier (whose fence would
+        // otherwise wait for them) and complete while this tile is computed
+        if (et + kMTE < e1) tile_load<D, DR>(a, row, b, t, nc, vis, et + kMTE, e1, w, lane, R);
         if (!active) continue;
 
         // ---- S = Q K^T: two 16-entry N-tiles, split into non-RoPE / RoPE parts
@@ -191,19 +253,26 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit_max) {
                 const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(kr + 64 * s);
                 if (s < nsr) snr[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], kb, snr[n], 0, 0, 0);
                 else sr[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], kb, sr[n], 0, 0, 0);
+                if (s % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
         }
         // ---- online softmax (rows = heads 4*g4 + i; this lane's entries 16n + l16)
         float pz[2][4];
         float alpha[4];
         bool moved = false;
+        float esc[2];
+        int eok[2];
+#pragma unroll
+        for (int n = 0; n < 2; n++) {
+            esc[n] = sm.scale[16 * n + l16];
+            eok[n] = sm.valid[16 * n + l16];
+        }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             float mt = -INFINITY;
 #pragma unroll
             for (int n = 0; n < 2; n++) {
-                const int e = 16 * n + l16;
-                const float z = sm.rec[e] ? a.scale * (sm.scale[e] * snr[n][i] + sr[n][i]) : -INFINITY;
+                const float z = eok[n] ? a.scale * (esc[n] * snr[n][i] + sr[n][i]) : -INFINITY;
                 pz[n][i] = z;
                 mt = fmaxf(mt, z);
             }
@@ -239,10 +308,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit_max) {
 #pragma unroll
         for (int n = 0; n < 2; n++) {
             const int e = 16 * n + l16;
-            const float sc = sm.scale[e];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                const __bf16 ps = (__bf16)(pz[n][i] * sc), pp = (__bf16)pz[n][i];
+                const __bf16 ps = (__bf16)(pz[n][i] * esc[n]), pp = (__bf16)pz[n][i];
                 sm.p[w][0][4 * g4 + i][e] = __builtin_bit_cast(uint16_t, ps);
                 sm.p[w][1][4 * g4 + i][e] = __builtin_bit_cast(uint16_t, pp);
             }
@@ -260,6 +328,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit_max) {
             for (int j = 0; j < 8; j++)
                 vb[j] = *reinterpret_cast<const __bf16*>(&sm.tile[8 * g4 + j][2 * (16 * nd + l16)]);
             o[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nd < ndr ? pa : pb, vb, o[nd], 0, 0, 0);
+            if (nd % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bound the B-fragments kept in flight
         }
     }
     if (!active) return;
@@ -282,7 +351,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit_max) {
         for (int nd = 0; nd < ND; nd++) {
             const int dim = 16 * nd + l16;
             float sn = 0.0f, cs = 1.0f;
-            if (nd >= ndr) rope_sincos(-(double)t, a.rope.f[(dim - dn) / 2], sn, cs);
+            if (nd >= ndr) rope_sincos(-(double)t, sm.rf[(dim - dn) / 2], sn, cs);
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 float v = o[nd][i] * f[i];
@@ -316,26 +385,24 @@ bool attn_mfma_supported(const AttnArgs& a) {
     if (a.comp_fmt == CSA_F32 || (a.W > 0 && a.win_fmt == CSA_F32)) return false;
     if (a.d != 128 && a.d != 256 && a.d != 512) return false;
     if (a.H % 16 != 0) return false;
-    if ((a.d - a.dr) % 32 != 0) return false;
+    if (a.dr != 64) return false;
     return true;
 }
-
-int attn_mfma_split() { return kMSplit; }
 
 template <typename OT>
 static void launch_d(const AttnArgs& a, int nsplit, hipStream_t st) {
     const int groups = (a.H + 63) / 64;
-    const int threads = 64 * min(4, a.H / 16);
     dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)groups);
-    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, OT>), grid, dim3(threads), 0, st, a, nsplit);
-    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, OT>), grid, dim3(threads), 0, st, a, nsplit);
-    else hipLaunchKernelGGL((k_attn_mfma<512, OT>), grid, dim3(threads), 0, st, a, nsplit);
+    // four waves per workgroup always (tile staging is spread over four waves);
+    // waves beyond H stage but do not compute
+    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, OT>), grid, dim3(256), 0, st, a, nsplit);
+    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, OT>), grid, dim3(256), 0, st, a, nsplit);
+    else hipLaunchKernelGGL((k_attn_mfma<512, 64, OT>), grid, dim3(256), 0, st, a, nsplit);
 }
 
-hipError_t launch_attention_mfma(const AttnArgs& a, int64_t max_entries, hipStream_t st) {
-    const int64_t nsplit = max((int64_t)1, (max_entries + kMSplit - 1) / kMSplit);
-    if (a.out_fmt == CSA_BF16) launch_d<uint16_t>(a, (int)nsplit, st);
-    else launch_d<float>(a, (int)nsplit, st);
+hipError_t launch_attention_mfma(const AttnArgs& a, int64_t nsplit_bound, hipStream_t st) {
+    if (a.out_fmt == CSA_BF16) launch_d<uint16_t>(a, (int)nsplit_bound, st);
+    else launch_d<float>(a, (int)nsplit_bound, st);
     return hipGetLastError();
 }
 

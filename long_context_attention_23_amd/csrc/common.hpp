@@ -84,6 +84,18 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 // tens of milliradians).  The product is reduced modulo 2*pi exactly enough
 // in fp64 (Cody-Waite, 2*pi split into a double and its remainder, fused
 // multiply-adds), and sin / cos are taken in fp32 of the reduced angle.
+// Copy a kernel-argument frequency table to LDS with static indices (a
+// per-lane index into a by-value kernel argument would force a private copy
+// of the whole argument block into scratch memory).  Caller synchronises.
+template <typename Table>
+__device__ __forceinline__ void stage_rope(const Table& t, double* lds, int npairs) {
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < 64; i++)
+            if (i < npairs) lds[i] = t.f[i];
+    }
+}
+
 __device__ __forceinline__ void rope_sincos(double pos, double freq, float& s, float& c) {
     const double x = pos * freq;
     const double k = rint(x * 0.15915494309189535);           // x / (2 pi)

@@ -31,6 +31,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     __shared__ float red[kCompThreads / kWave];
     __shared__ int se[kMaxD / 32];
     __shared__ float part[kCompThreads * 8];      // token-group partial sums of the pooling
+    __shared__ double rf[64];
 
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
@@ -40,6 +41,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     if (!a.ring && j >= a.cap) return;
     const int64_t slot = a.ring ? j % a.cap : j;
     const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + i * m) * d;
+    stage_rope(a.rope, rf, a.dr / 2);
 
     // ---- pooling weights: z_r = bias_r + <u, x_r>, softmax over r
     const int lane = tid & (kWave - 1), wv = tid / kWave;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     const int off = d - a.dr;
     for (int p = tid; p < a.dr / 2; p += kCompThreads) {
         float sn, cs;
-        rope_sincos((double)(j * m), a.rope.f[p], sn, cs);
+        rope_sincos((double)(j * m), rf[p], sn, cs);
         float x0 = sv[off + 2 * p], x1 = sv[off + 2 * p + 1];
         sv[off + 2 * p] = x0 * cs - x1 * sn;
         sv[off + 2 * p + 1] = x0 * sn + x1 * cs;

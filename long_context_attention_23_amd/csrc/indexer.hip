@@ -435,6 +435,7 @@ __device__ __forceinline__ void wave_pick_bin(const uint32_t* hist, uint32_t nee
 
 __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     __shared__ uint32_t sh[2];
+    __shared__ uint32_t cnt[2], base[2];
     const int64_t r = blockIdx.y, row = a.row0 + r;
     const int64_t n = visible_blocks(a, row);
     const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     if (threadIdx.x < kWave) {
         uint32_t bin, above;
         wave_pick_bin(w.hist, (uint32_t)a.topk, bin, above);
-        if (threadIdx.x == 0) { sh[0] = bin; sh[1] = above; }
+        if (threadIdx.x == 0) { sh[0] = bin; sh[1] = above; cnt[0] = 0; cnt[1] = 0; }
     }
     __syncthreads();
     const uint32_t tbin = sh[0];
@@ -456,24 +457,39 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
         const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
         keys[u] = j < c1 ? w.scores[j] : 0u;
     }
+    // workgroup-local slots from LDS counters, then one global reservation per list
+    uint32_t slot[kPer];
+    uint32_t kind = 0;                                   // bit u: 1 = sure, bit u+16: candidate
 #pragma unroll
     for (int u = 0; u < kPer; u++) {
         const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
-        const uint32_t key = keys[u];
-        const uint32_t bin = key >> 20;
+        const uint32_t bin = keys[u] >> 20;
         const bool sure = j < c1 && bin > tbin;
         const bool cand = j < c1 && bin == tbin;
         const uint64_t bs = __ballot(sure), bc = __ballot(cand);
         uint32_t os = 0, oc = 0;
         if (lane == 0) {
-            if (bs) os = atomicAdd(&w.counts[0], (uint32_t)__popcll(bs));
-            if (bc) oc = atomicAdd(&w.counts[1], (uint32_t)__popcll(bc));
+            if (bs) os = atomicAdd(&cnt[0], (uint32_t)__popcll(bs));
+            if (bc) oc = atomicAdd(&cnt[1], (uint32_t)__popcll(bc));
         }
         os = __shfl(os, 0, kWave);
         oc = __shfl(oc, 0, kWave);
         const uint64_t below = (1ull << lane) - 1;
-        if (sure) w.sel[os + __popcll(bs & below)] = (int32_t)j;
-        if (cand) w.cand[oc + __popcll(bc & below)] = make_uint2(key, (uint32_t)j);
+        slot[u] = sure ? os + __popcll(bs & below) : oc + __popcll(bc & below);
+        kind |= (sure ? 1u : 0u) << u;
+        kind |= (cand ? 1u : 0u) << (u + 16);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        base[0] = cnt[0] ? atomicAdd(&w.counts[0], cnt[0]) : 0u;
+        base[1] = cnt[1] ? atomicAdd(&w.counts[1], cnt[1]) : 0u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {
+        const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
+        if (kind & (1u << u)) w.sel[base[0] + slot[u]] = (int32_t)j;
+        if (kind & (1u << (u + 16))) w.cand[base[1] + slot[u]] = make_uint2(keys[u], (uint32_t)j);
     }
 }
 

@@ -89,11 +89,32 @@ struct AttnArgs {
     int64_t ws_bytes;
     RopeTable rope;
 };
-int64_t attn_ws_bytes(int64_t rows, int32_t H, int32_t d, int64_t max_entries, int32_t q_fmt,
-                      int32_t comp_fmt);
+int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t max_entries);
+
+// Split policy of the attention kernels: entries per split for a query row
+// with n entries.  It depends only on the row's own entry count and on the
+// chunk length Tq, never on the batch size, so a sequence's result does not
+// depend on the batch it is in.  Chunks of >= 64 queries give one split per
+// row (enough rows to fill the chip); shorter chunks (decode) cut a row into
+// at most 64 splits of at least 64 entries, a multiple of 32.
+__host__ __device__ inline int64_t attn_split_len(int64_t n, int32_t Tq) {
+    if (n <= 0) return 32;
+    if (Tq >= 64) return (n + 31) / 32 * 32;
+    int64_t s = (n + 63) / 64;
+    s = (s + 31) / 32 * 32;
+    return s < 64 ? 64 : s;
+}
+__host__ __device__ inline int64_t attn_nsplit(int64_t n, int32_t Tq) {
+    return n <= 0 ? 1 : (n + attn_split_len(n, Tq) - 1) / attn_split_len(n, Tq);
+}
+// an upper bound of attn_nsplit over rows with at most max_n entries
+inline int64_t attn_nsplit_bound(int64_t max_n, int32_t Tq) {
+    if (Tq >= 64 || max_n <= 0) return 1;
+    int64_t b = (max_n + 63) / 64;
+    return b > 64 ? 64 : b;
+}
 hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st);
 bool attn_mfma_supported(const AttnArgs& a);
-int attn_mfma_split();
 hipError_t launch_attention_mfma(const AttnArgs& a, int64_t max_entries, hipStream_t st);
 
 // ---- grouped projection

@@ -135,27 +135,45 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
     const int i0 = (blockIdx.x % tpg) * rows_wg;
     const T* o = reinterpret_cast<const T*>(a.o);
     const T* W = reinterpret_cast<const T*>(a.W);
-    for (int idx = threadIdx.x; idx < MR * nch; idx += blockDim.x) {
-        const int m = idx / nch, c = idx % nch;
-        osm[idx] = m < a.M ? *reinterpret_cast<const uint4*>(o + (size_t)m * a.Hd + (size_t)g * cg + (size_t)c * EPC)
-                           : make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r0 = i0 + w * R;
     const T* wr = W + ((size_t)g * dg + r0) * cg;
+    // weight chunks are loaded in batches of kIt per lane; the first batch goes
+    // out before the activations are staged, so both sets of loads are in
+    // flight together
+    constexpr int kIt = (32 / R) < 8 ? (32 / R) : 8;
     float acc[R * MR];
 #pragma unroll
     for (int q = 0; q < R * MR; q++) acc[q] = 0.0f;
-    for (int c = lane; c < nch; c += 64) {
-        uint4 wv[R];
+    for (int cb = 0; cb < nch; cb += 64 * kIt) {
+        uint4 wv[kIt][R];
 #pragma unroll
-        for (int r = 0; r < R; r++) wv[r] = *reinterpret_cast<const uint4*>(wr + (size_t)r * cg + (size_t)c * EPC);
+        for (int it = 0; it < kIt; it++) {
+            const int c = cb + lane + 64 * it;
 #pragma unroll
-        for (int m = 0; m < MR; m++) {
-            const uint4 ov = osm[m * nch + c];
+            for (int r = 0; r < R; r++)
+                wv[it][r] = c < nch ? *reinterpret_cast<const uint4*>(wr + (size_t)r * cg + (size_t)c * EPC)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (cb == 0) {
+            for (int idx = threadIdx.x; idx < MR * nch; idx += blockDim.x) {
+                const int m = idx / nch, c = idx % nch;
+                osm[idx] = m < a.M ? *reinterpret_cast<const uint4*>(o + (size_t)m * a.Hd + (size_t)g * cg + (size_t)c * EPC)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+            }
+            __syncthreads();
+        }
 #pragma unroll
-            for (int r = 0; r < R; r++) acc[r * MR + m] = chunk_dot<T>(wv[r], ov, acc[r * MR + m]);
+        for (int it = 0; it < kIt; it++) {
+            const int c = cb + lane + 64 * it;
+            if (c < nch) {
+#pragma unroll
+                for (int m = 0; m < MR; m++) {
+                    const uint4 ov = osm[m * nch + c];
+#pragma unroll
+                    for (int r = 0; r < R; r++) acc[r * MR + m] = chunk_dot<T>(wv[it][r], ov, acc[r * MR + m]);
+                }
+            }
         }
     }
     const float tot = wave_reduce16(acc);
