@@ -81,9 +81,7 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 // ---------------------------------------------------------------- RoPE
 // Angle of pair i at position pos: pos * f_i with f_i = base^(-2i/dr) held in
 // fp64 (positions reach 2^20 and more, where an fp32 product would be off by
-// tens of milliradians).  The product is reduced modulo 2*pi exactly enough
-// in fp64 (Cody-Waite, 2*pi split into a double and its remainder, fused
-// multiply-adds), and sin / cos are taken in fp32 of the reduced angle.
+// tens of milliradians).
 // Copy a kernel-argument frequency table to LDS with static indices (a
 // per-lane index into a by-value kernel argument would force a private copy
 // of the whole argument block into scratch memory).  Caller synchronises.
@@ -96,12 +94,26 @@ __device__ __forceinline__ void stage_rope(const Table& t, double* lds, int npai
     }
 }
 
+// sin and cos of pos * freq.  The angle is reduced in fp64 around the
+// nearest multiple k of pi/2 (Cody-Waite: pi/2 as a double plus the double
+// nearest its remainder, fused multiply-adds) to r in [-pi/4, pi/4]; sin r and
+// cos r come from their Taylor series about 0 in fp32 (through r^9 and r^10:
+// truncation error below 2e-9 on that interval) and k mod 4 picks the
+// quadrant.  Branch-free and table-free.
 __device__ __forceinline__ void rope_sincos(double pos, double freq, float& s, float& c) {
     const double x = pos * freq;
-    const double k = rint(x * 0.15915494309189535);           // x / (2 pi)
-    double r = fma(-k, 6.283185307179586, x);                  // 2 pi, leading double
-    r = fma(-k, 2.4492935982947064e-16, r);                    // 2 pi - leading double
-    sincosf((float)r, &s, &c);
+    const double k = rint(x * 0.6366197723675814);            // x / (pi / 2)
+    double r = fma(-k, 1.5707963267948966, x);                 // pi / 2, leading double
+    r = fma(-k, 6.123233995736766e-17, r);                     // pi / 2 - leading double
+    const float f = (float)r, f2 = f * f;
+    const float sp = f + f * f2 * (-1.0f / 6.0f + f2 * (1.0f / 120.0f + f2 * (-1.0f / 5040.0f + f2 * (1.0f / 362880.0f))));
+    const float cp = 1.0f + f2 * (-0.5f + f2 * (1.0f / 24.0f + f2 * (-1.0f / 720.0f +
+                                   f2 * (1.0f / 40320.0f + f2 * (-1.0f / 3628800.0f)))));
+    const int q = (int)((long long)k & 3);
+    // sin(q pi/2 + r), cos(q pi/2 + r) for q = 0..3: (s, c), (c, -s), (-s, -c), (-c, s)
+    const float ss = (q & 1) ? cp : sp, cc = (q & 1) ? sp : cp;
+    s = (q & 2) ? -ss : ss;
+    c = ((q + 1) & 2) ? -cc : cc;
 }
 
 // ---------------------------------------------------------------- score keys

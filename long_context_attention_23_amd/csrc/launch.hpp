@@ -97,14 +97,17 @@ int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t ma
 // depend on the batch it is in.  Chunks of >= 64 queries give one split per
 // row (enough rows to fill the chip); shorter chunks (decode) cut a row into
 // at most 64 splits of at least 64 entries, a multiple of 32.
-__host__ __device__ inline int64_t attn_split_len(int64_t n, int32_t Tq) {
+// (templated on the integer type: device code uses 32-bit arithmetic)
+template <typename I>
+__host__ __device__ inline I attn_split_len(I n, int32_t Tq) {
     if (n <= 0) return 32;
     if (Tq >= 64) return (n + 31) / 32 * 32;
-    int64_t s = (n + 63) / 64;
+    I s = (n + 63) / 64;
     s = (s + 31) / 32 * 32;
     return s < 64 ? 64 : s;
 }
-__host__ __device__ inline int64_t attn_nsplit(int64_t n, int32_t Tq) {
+template <typename I>
+__host__ __device__ inline I attn_nsplit(I n, int32_t Tq) {
     return n <= 0 ? 1 : (n + attn_split_len(n, Tq) - 1) / attn_split_len(n, Tq);
 }
 // an upper bound of attn_nsplit over rows with at most max_n entries
