@@ -24,11 +24,18 @@
 //     (ds_read_b64_tr_b16).  The P V k index runs over the tile's entries in
 //     a permuted order chosen so that the rows read together fall in disjoint
 //     LDS banks;
-//   - records are fetched straight into an LDS staging area with the gfx950
-//     global-to-LDS load (global_load_lds_dwordx4), one tile ahead, and
-//     expanded into the double-buffered bf16 tile by the wave that fetched
-//     them; record addresses are computed one lane per entry and the top-k
-//     indices are read two tiles ahead; two barriers per tile.
+//   - records are fetched straight into LDS with the gfx950 global-to-LDS
+//     load (global_load_lds_dwordx4) by waves 4..7; record addresses are
+//     computed one lane per entry and the top-k indices are read ahead.
+//     When every record is FP8 (the layout the method stores), the records
+//     stay as fetched in a ring of three tile buffers and the MFMA operands
+//     are converted on the way out of LDS: K rows with 64-bit reads, V
+//     columns with the byte-transposing read (ds_read_b64_tr_b8).  Other
+//     formats go through a staging area and are expanded to bf16 rows;
+//   - software pipeline, two barriers per tile: phase 1 (all waves) runs
+//     P V of tile t-1 and Q K^T of tile t back to back on the matrix cores;
+//     phase 2 runs the softmax of tile t (waves 0..3) beside the fetch work
+//     (waves 4..7).
 #include <stddef.h>
 
 #include "common.hpp"
@@ -43,18 +50,38 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMTE = 32;                  // entries per LDS tile
 constexpr int kNW = 8;                    // waves per workgroup
-constexpr int kEntPerWave = kMTE / kNW;   // entries of a tile fetched by one wave (slots w + 8u)
+constexpr int kFetchers = 4;              // waves 4..7 fetch and expand the tiles
+constexpr int kEntPerWave = kMTE / kFetchers;   // entries of a tile per fetching wave (slots f + 4u)
 constexpr int kPRow = 80;                 // bf16 per P row (64 heads + pad: 160-byte rows)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;          // base-2 headroom before the running max is raised
 
-template <int D>
-struct MfmaSmem {
-    uint8_t tile[2][kMTE][D * 2 + 16];    // bf16 entries (FP8 codes expanded), double-buffered
+// FP8 record bytes: D - DR codes, DR bf16, the f32 scale, padded to 16 bytes
+template <int D, int DR>
+constexpr int fp8_rec_bytes() { return ((D - DR) + 2 * DR + 4 + 15) / 16 * 16; }
+
+template <int D, int DR, bool F8>
+struct MfmaTiles;
+// any record formats: a staging area and double-buffered bf16 rows
+template <int D, int DR>
+struct MfmaTiles<D, DR, false> {
+    static constexpr int kBufs = 2;
+    uint8_t tile[2][kMTE][D * 2 + 16];    // bf16 entries (FP8 codes expanded), 16-byte row pad
     uint8_t raw[kMTE][D * 2];             // records of the next tile as fetched (bf16 records are the largest)
     float scale[2][kMTE];                 // FP8 row scale (1 for bf16 records)
     int valid[2][kMTE];
+};
+// all FP8: the records as fetched, a ring of three tiles
+template <int D, int DR>
+struct MfmaTiles<D, DR, true> {
+    static constexpr int kBufs = 3;
+    uint8_t ring[3][kMTE][fp8_rec_bytes<D, DR>()];
+    int valid[3][kMTE];
+};
+
+template <int D, int DR, bool F8>
+struct MfmaSmem : MfmaTiles<D, DR, F8> {
     float zx[kNW][2][2][64][4];           // partial logits [wave][local head group][n][lane][i]
     uint16_t pt[2][kMTE][kPRow];          // P [scaled, plain] by (k index, head)
     float alpha[64];                      // per-head rescale factor of the current tile
@@ -79,18 +106,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(bf16x2_t v) {
     return u;
 }
 
-// Per-wave fetch state of one tile: lane u < 4 holds the record address of
-// the wave's entry u (tile slot w + 8u); the masks say which entries exist
+// Per-wave fetch state of one tile: lane u < 8 holds the record address of
+// the fetching wave's entry u (tile slot f + 4u); the masks say which entries exist
 // and which are FP8 records.
 struct Fetch {
     uint64_t ptr;         // per lane
     uint32_t vmask, fmask;
 };
 
-// index of this lane's entry in the top-k list (lanes 0..3), read ahead of use
+// index of this lane's entry in the top-k list (lanes 0..7), read ahead of use
 __device__ __forceinline__ int32_t fetch_index(const AttnArgs& a, const RowCtx& c, int32_t et, int32_t e1, int w,
                                                int lane) {
-    const int32_t e = et + w + kNW * lane;
+    const int32_t e = et + w + kFetchers * lane;
     int32_t j = 0;
     if (c.top && lane < kEntPerWave && e < e1 && e < c.nc) j = c.top[e];
     return j;
@@ -99,7 +126,7 @@ __device__ __forceinline__ int32_t fetch_index(const AttnArgs& a, const RowCtx& 
 // record addresses of the wave's entries of the tile at et (j: fetch_index)
 __device__ __forceinline__ Fetch fetch_plan(const AttnArgs& a, const RowCtx& c, int32_t et, int32_t e1, int w,
                                             int lane, int32_t j) {
-    const int32_t e = et + w + kNW * lane;
+    const int32_t e = et + w + kFetchers * lane;
     bool ok = lane < kEntPerWave && e < e1, fp8 = false;
     const uint8_t* p = nullptr;
     if (ok) {
@@ -123,10 +150,26 @@ __device__ __forceinline__ Fetch fetch_plan(const AttnArgs& a, const RowCtx& c, 
     return f;
 }
 
-// issue the global-to-LDS copies of the wave's records into the staging area
+// issue the global-to-LDS copies of the wave's records: entry u to row
+// dst + (w + 4u) * stride
 template <int D, int DR>
-__device__ __forceinline__ void fetch_issue(MfmaSmem<D>& sm, int w, int lane, const Fetch& f) {
+__device__ __forceinline__ void fetch_issue(uint8_t* dst, int stride, int w, int lane, const Fetch& f) {
     constexpr int fp8_pieces = (D - DR) / 16 + DR / 8 + 1;
+    constexpr uint32_t kAll = (1u << kEntPerWave) - 1;
+    if (f.vmask == kAll && f.fmask == kAll) {
+        // every entry present and an FP8 record: one exec mask for all copies
+        if (lane < fp8_pieces) {
+#pragma unroll
+            for (int u = 0; u < kEntPerWave; u++) {
+                const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)f.ptr, u);
+                const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(f.ptr >> 32), u);
+                const uint8_t* rec = (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+                __builtin_amdgcn_global_load_lds(rec + 16 * lane,
+                                                 (__attribute__((address_space(3))) void*)(dst + (w + kFetchers * u) * stride), 16, 0, 0);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < kEntPerWave; u++) {
         if (f.vmask & (1u << u)) {
@@ -136,44 +179,81 @@ __device__ __forceinline__ void fetch_issue(MfmaSmem<D>& sm, int w, int lane, co
             const int npieces = (f.fmask & (1u << u)) ? fp8_pieces : D / 8;
             if (lane < npieces)
                 __builtin_amdgcn_global_load_lds(rec + 16 * lane,
-                                                 (__attribute__((address_space(3))) void*)&sm.raw[w + kNW * u][0], 16, 0, 0);
+                                                 (__attribute__((address_space(3))) void*)(dst + (w + kFetchers * u) * stride), 16, 0, 0);
         }
     }
 }
 
-// expand the wave's fetched records into bf16 tile rows (FP8 codes exactly,
-// RoPE dims copied, row scale and validity aside)
-template <int D, int DR>
-__device__ __forceinline__ void fetch_expand(MfmaSmem<D>& sm, int buf, int w, int lane, const Fetch& f) {
+// expand the wave's fetched records into bf16 tile rows: FP8 codes exactly,
+// RoPE dims copied, row scale and validity aside.  Branch-free over lanes:
+// lane l writes bytes 16l..16l+15 of the row (FP8: codes 8l..8l+7 expanded,
+// or a RoPE piece; bf16: the same bytes of the record); all reads first.
+template <int D, int DR, typename Smem>
+__device__ __forceinline__ void fetch_expand(Smem& sm, int buf, int w, int lane, const Fetch& f) {
     constexpr int dn = D - DR;
+    constexpr uint32_t kAll = (1u << kEntPerWave) - 1;
+    if (f.vmask == kAll && f.fmask == kAll) {
+        // every entry present and an FP8 record: straight-line, selects only
+        const bool code = lane < dn / 8;
+        const int off = code ? 8 * lane : (lane < D / 8 ? dn + 16 * (lane - dn / 8) : 0);
+        uint2 x[kEntPerWave], y[kEntPerWave];
+        float sc[kEntPerWave];
+#pragma unroll
+        for (int u = 0; u < kEntPerWave; u++) {
+            const uint8_t* src = sm.raw[w + kFetchers * u];
+            x[u] = *reinterpret_cast<const uint2*>(src + off);
+            y[u] = *reinterpret_cast<const uint2*>(src + off + 8);
+            sc[u] = *reinterpret_cast<const float*>(src + dn + 2 * DR);
+        }
+        float mysc = sc[0];
+#pragma unroll
+        for (int u = 0; u < kEntPerWave; u++) {
+            const uint32_t c0 = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].x, 1.0f, false));
+            const uint32_t c1 = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].x, 1.0f, true));
+            const uint32_t c2 = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].y, 1.0f, false));
+            const uint32_t c3 = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].y, 1.0f, true));
+            const uint4 o = code ? make_uint4(c0, c1, c2, c3) : make_uint4(x[u].x, x[u].y, y[u].x, y[u].y);
+            if (lane < D / 8) *reinterpret_cast<uint4*>(&sm.tile[buf][w + kFetchers * u][16 * lane]) = o;
+            mysc = lane == u ? sc[u] : mysc;
+        }
+        if (lane < kEntPerWave) {
+            sm.scale[buf][w + kFetchers * lane] = mysc;
+            sm.valid[buf][w + kFetchers * lane] = 1;
+        }
+        return;
+    }
+    uint2 x[kEntPerWave], y[kEntPerWave];
+    float sc[kEntPerWave];
 #pragma unroll
     for (int u = 0; u < kEntPerWave; u++) {
-        const int ee = w + kNW * u;
-        uint8_t* dst = sm.tile[buf][ee];
-        const uint8_t* src = sm.raw[ee];
-        if (!(f.vmask & (1u << u))) {
-            // masked entry: a zero row keeps 0 * garbage out of P V
-            if (lane < D / 8) *reinterpret_cast<uint4*>(dst + 16 * lane) = make_uint4(0u, 0u, 0u, 0u);
-            if (lane == 0) sm.scale[buf][ee] = 1.0f;
-        } else if (f.fmask & (1u << u)) {
-            if (lane < dn / 8) {
-                const uint2 cd = *reinterpret_cast<const uint2*>(src + 8 * lane);
-                uint4 o;
-                o.x = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.x, 1.0f, false));
-                o.y = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.x, 1.0f, true));
-                o.z = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.y, 1.0f, false));
-                o.w = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cd.y, 1.0f, true));
-                *reinterpret_cast<uint4*>(dst + 16 * lane) = o;
-            } else if (lane < dn / 8 + DR / 8) {
-                const int q = lane - dn / 8;
-                *reinterpret_cast<uint4*>(dst + 2 * dn + 16 * q) = *reinterpret_cast<const uint4*>(src + dn + 16 * q);
-            }
-            if (lane == 0) sm.scale[buf][ee] = *reinterpret_cast<const float*>(src + dn + 2 * DR);
+        const bool fp8 = (f.fmask >> u) & 1u;
+        const uint8_t* src = sm.raw[w + kFetchers * u];
+        int off = fp8 ? (lane < dn / 8 ? 8 * lane : dn + 16 * (lane - dn / 8)) : 16 * lane;
+        if (lane >= D / 8) off = 0;
+        x[u] = *reinterpret_cast<const uint2*>(src + off);
+        y[u] = *reinterpret_cast<const uint2*>(src + off + 8);
+        sc[u] = fp8 ? *reinterpret_cast<const float*>(src + dn + 2 * DR) : 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kEntPerWave; u++) {
+        const int ee = w + kFetchers * u;
+        const bool ok = (f.vmask >> u) & 1u, fp8 = (f.fmask >> u) & 1u;
+        uint4 o;
+        if (fp8 && lane < dn / 8) {
+            o.x = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].x, 1.0f, false));
+            o.y = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].x, 1.0f, true));
+            o.z = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].y, 1.0f, false));
+            o.w = pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[u].y, 1.0f, true));
         } else {
-            if (lane < D / 8) *reinterpret_cast<uint4*>(dst + 16 * lane) = *reinterpret_cast<const uint4*>(src + 16 * lane);
-            if (lane == 0) sm.scale[buf][ee] = 1.0f;
+            o = make_uint4(x[u].x, x[u].y, y[u].x, y[u].y);
         }
-        if (lane == 0) sm.valid[buf][ee] = (f.vmask >> u) & 1u;
+        // a masked entry becomes a zero row, which keeps 0 * garbage out of P V
+        if (!ok) o = make_uint4(0u, 0u, 0u, 0u);
+        if (lane < D / 8) *reinterpret_cast<uint4*>(&sm.tile[buf][ee][16 * lane]) = o;
+        if (lane == 0) {
+            sm.scale[buf][ee] = ok ? sc[u] : 1.0f;
+            sm.valid[buf][ee] = ok ? 1 : 0;
+        }
     }
 }
 
@@ -195,6 +275,24 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
 __device__ __forceinline__ bf16x8_t tr_pair(const void* p0, const void* p1) {
     const s16x4_t v0 = lds_read_tr16(p0), v1 = lds_read_tr16(p1);
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// eight E4M3 codes to eight bf16 (exact)
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint2 c) {
+    const uint4 o = make_uint4(pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false)),
+                               pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true)),
+                               pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false)),
+                               pack_bf16x2(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true)));
+    return __builtin_bit_cast(bf16x8_t, o);
+}
+
+// gfx950 byte-transposing LDS read (ds_read_b64_tr_b8).  Within each 16-lane
+// group, lane s points at 8 consecutive bytes; lane i then receives, for
+// j = 0..7, byte i%8 of the 8 bytes addressed by lane i/8 + 2j.
+__device__ __forceinline__ uint2 lds_read_tr8(const void* p) {
+    typedef int v2i __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) v2i lds_v2i;
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)p));
 }
 
 // position of tile entry e in the P V k order: k = 8g + 4h + j holds entry
@@ -223,61 +321,27 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-template <int D, int DR, typename OT>
+template <int D, int DR, bool F8, typename OT>
 __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_max) {
     constexpr int DQ = D / 4;              // dims per quarter
     constexpr int KS = DQ / 32;            // Q K^T K-steps per wave
     constexpr int NT = DQ / 16;            // P V N-tiles per wave
     constexpr int dn = D - DR;             // non-RoPE dims (multiple of 32)
-    constexpr int RS = D * 2 + 16;         // tile row stride in bytes
-    __shared__ MfmaSmem<D> sm;
+    constexpr int RS = D * 2 + 16;         // bf16 tile row stride in bytes
+    constexpr int REC = fp8_rec_bytes<D, DR>();   // FP8 ring row stride in bytes
+    constexpr uint32_t kAll = (1u << kEntPerWave) - 1;
+    __shared__ MfmaSmem<D, DR, F8> sm;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qd = w & 3, hp = w >> 2;                 // dim quarter, head half
     const int l16 = lane & 15, g4 = lane >> 4;
     const int row = blockIdx.y;
-    const int b = row / a.Tq;
-    const int t = a.q_pos[row];
-    RowCtx c;
-    c.vis = t < 0 ? 0 : (t + 1) / a.m;
-    if (c.vis > a.ccap) c.vis = (int32_t)a.ccap;
-    c.nc = a.topk ? a.k : c.vis;
-    c.comp = a.comp + (int64_t)b * a.ccap * a.comp_rec;
-    c.top = a.topk ? a.topk + (int64_t)row * a.k : nullptr;
-    c.win = a.win + (int64_t)b * a.wcap * a.win_rec;
-    {
-        const int32_t s0 = t - a.W + 1;
-        c.slot0 = (a.W > 0 && s0 >= 0) ? s0 % (int32_t)a.wcap : s0;
-    }
-    const int32_t ne = c.nc + a.W;
-    const int32_t split = attn_split_len<int32_t>(ne, a.Tq);
-    const int32_t nsplit = attn_nsplit<int32_t>(ne, a.Tq);
-    const int32_t sp = blockIdx.x;
-    if (sp >= nsplit) return;
-    const int32_t e0 = sp * split, e1 = min(e0 + split, ne);
     const int h0 = blockIdx.z * 64;
     const int MT = min(4, (a.H - h0) / 16);           // 16-head groups in this workgroup
-    const bool active = 2 * hp < MT;                   // this wave's head half exists
-    const bool owner = w < MT;                         // wave w runs the softmax of head group w
     const int dbase = qd * DQ;                         // first dim of this wave's quarter
-    // non-RoPE K-steps / N-tiles of this quarter
-    const int nks = max(0, min(KS, (dn - dbase) / 32));
-    const int nnt = max(0, min(NT, (dn - dbase) / 16));
-    const float zscale = a.scale * kLog2e;             // logits in base-2 units
 
-    // the first tile's records go out before the query prologue; the top-k
-    // indices are read two tiles ahead of their records
-    Fetch fr = fetch_plan(a, c, e0, e1, w, lane, fetch_index(a, c, e0, e1, w, lane));
-    fetch_issue<D, DR>(sm, w, lane, fr);
-    int32_t jn = fetch_index(a, c, e0 + kMTE, e1, w, lane);
-    {
-        // RoPE inverse frequencies, read lane-parallel from the argument block
-        const double* rtab = (const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(AttnArgs, rope));
-        if (tid < a.dr / 2) sm.rf[tid] = rtab[tid];
-    }
-
-    // ---- query prologue: q^ = RoPE_t(RMSNorm(q)), this wave's 32 heads and quarter
+    // ---- the query loads go out first (they do not depend on the position)
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + h0 + 32 * hp) * D;
     uint4 qraw[2][KS];
 #pragma unroll
@@ -299,6 +363,73 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
             gam[ks][1] = gp[1];
         }
     }
+
+    const int b = row / a.Tq;
+    const int t = a.q_pos[row];
+    RowCtx c;
+    c.vis = t < 0 ? 0 : (t + 1) / a.m;
+    if (c.vis > a.ccap) c.vis = (int32_t)a.ccap;
+    c.nc = a.topk ? a.k : c.vis;
+    c.comp = a.comp + (int64_t)b * a.ccap * a.comp_rec;
+    c.top = a.topk ? a.topk + (int64_t)row * a.k : nullptr;
+    c.win = a.win + (int64_t)b * a.wcap * a.win_rec;
+    {
+        const int32_t s0 = t - a.W + 1;
+        c.slot0 = (a.W > 0 && s0 >= 0) ? s0 % (int32_t)a.wcap : s0;
+    }
+    const int32_t ne = c.nc + a.W;
+    const int32_t split = attn_split_len<int32_t>(ne, a.Tq);
+    const int32_t nsplit = attn_nsplit<int32_t>(ne, a.Tq);
+    const int32_t sp = blockIdx.x;
+    if (sp >= nsplit) return;
+    const int32_t e0 = sp * split, e1 = min(e0 + split, ne);
+    const bool active = 2 * hp < MT;                   // this wave's head half exists
+    const bool owner = w < MT;                         // wave w runs the softmax of head group w
+    // non-RoPE K-steps / N-tiles of this quarter
+    const int nks = max(0, min(KS, (dn - dbase) / 32));
+    const int nnt = max(0, min(NT, (dn - dbase) / 16));
+    const float zscale = a.scale * kLog2e;             // logits in base-2 units
+
+    const int fw = w - (kNW - kFetchers);              // fetching wave index (>= 0 for waves 4..7)
+    const bool fetcher = fw >= 0;
+    const int ntiles = (e1 - e0 + kMTE - 1) / kMTE;
+    // the first tile's records go out before the query prologue; the top-k
+    // indices are read two tiles ahead of their records
+    Fetch fr;
+    int32_t jn = 0;
+    // FP8 ring: plan and send tile tt into ring buffer rb; record validity, and
+    // zero the rows of missing entries (no stale codes reach P V)
+    auto ring_issue = [&](int tt, int rb, int32_t j) {
+        if constexpr (F8) {
+            const Fetch f = fetch_plan(a, c, e0 + tt * kMTE, e1, fw, lane, j);
+            fetch_issue<D, DR>(&sm.ring[rb][0][0], REC, fw, lane, f);
+            if (lane < kEntPerWave) sm.valid[rb][fw + kFetchers * lane] = (f.vmask >> lane) & 1u;
+            if (f.vmask != kAll) {
+#pragma unroll
+                for (int u = 0; u < kEntPerWave; u++)
+                    if (!(f.vmask & (1u << u)) && lane < REC / 16)
+                        *reinterpret_cast<uint4*>(&sm.ring[rb][fw + kFetchers * u][16 * lane]) = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    };
+    if (fetcher) {
+        if constexpr (F8) {
+            ring_issue(0, 0, fetch_index(a, c, e0, e1, fw, lane));
+            if (ntiles > 1) ring_issue(1, 1, fetch_index(a, c, e0 + kMTE, e1, fw, lane));
+            jn = fetch_index(a, c, e0 + 2 * kMTE, e1, fw, lane);
+        } else {
+            fr = fetch_plan(a, c, e0, e1, fw, lane, fetch_index(a, c, e0, e1, fw, lane));
+            fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
+            jn = fetch_index(a, c, e0 + kMTE, e1, fw, lane);
+        }
+    }
+    {
+        // RoPE inverse frequencies, read lane-parallel from the argument block
+        const double* rtab = (const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(AttnArgs, rope));
+        if (tid < a.dr / 2) sm.rf[tid] = rtab[tid];
+    }
+
+    // ---- query prologue: q^ = RoPE_t(RMSNorm(q)), this wave's 32 heads and quarter
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
         float ss = 0.0f;
@@ -359,165 +490,238 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
         for (int nd = 0; nd < NT; nd++) o[mt][nd] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // running max (base 2) / sum of the owned heads 16w + 4*g4 + i
+    // running max (base 2) of the owned heads 16w + 4*g4 + i, and this lane's
+    // part of their running sums (the 16 lanes of a row are added at the end)
     float mrun[4], lrun[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) { mrun[i] = -INFINITY; lrun[i] = 0.0f; }
 
-    wait_vm();
-    fetch_expand<D, DR>(sm, 0, w, lane, fr);
-    wait_lgkm();
-    if (e0 + kMTE < e1) {
-        fr = fetch_plan(a, c, e0 + kMTE, e1, w, lane, jn);
-        fetch_issue<D, DR>(sm, w, lane, fr);
-        jn = fetch_index(a, c, e0 + 2 * kMTE, e1, w, lane);
-    }
-    __syncthreads();
-    // per-lane LDS coordinates of the transposing reads
-    const int v_row = 8 * g4 + 2 * (l16 >> 2);
-    const int v_col = 2 * (dbase + 4 * (l16 & 3));
-    const int p_row = 8 * g4 + (l16 >> 2);
-    const int p_col = 32 * hp + 4 * (l16 & 3);
-    int buf = 0;
-    for (int32_t et = e0; et < e1; et += kMTE, buf ^= 1) {
-        // ---- partial logits of this quarter for the wave's head groups, to LDS:
-        // scale * <q, code>_non-RoPE + <q, k>_RoPE
-        if (active) {
+    // expand tile tt into buffer tt % 2 and send the fetch of tile tt + 1
+    // (any formats) expand tile tt into buffer tt % 2, send the fetch of tile tt + 1;
+    // (FP8 ring) wait for tile tt, send the fetch of tile tt + 1 into ring (tt + 1) % 3
+    auto fetch_step = [&](int tt, int rb_next) {
+        if (!fetcher || tt >= ntiles) return;
+        const int32_t et = e0 + tt * kMTE;
+        wait_vm();
+        if constexpr (F8) {
+            if (tt + 1 < ntiles) {
+                ring_issue(tt + 1, rb_next, jn);
+                jn = fetch_index(a, c, et + 2 * kMTE, e1, fw, lane);
+            }
+        } else {
+            fetch_expand<D, DR>(sm, tt & 1, fw, lane, fr);
+            wait_lgkm();
+            if (tt + 1 < ntiles) {
+                fr = fetch_plan(a, c, et + kMTE, e1, fw, lane, jn);
+                fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
+                jn = fetch_index(a, c, et + 2 * kMTE, e1, fw, lane);
+            }
+        }
+    };
+    // partial logits of tile tt (buffer tt % 2), this quarter, the wave's head
+    // groups: scale * <q, code>_non-RoPE + <q, k>_RoPE, to LDS
+    auto qk_step = [&](int bq) {
 #pragma unroll
-            for (int n = 0; n < 2; n++) {
-                const float esc = sm.scale[buf][16 * n + l16];
-                f32x4_t acc[2];
+        for (int n = 0; n < 2; n++) {
+            float esc;
+            const uint8_t* kr;
+            if constexpr (F8) {
+                kr = &sm.ring[bq][16 * n + l16][0];
+                esc = *reinterpret_cast<const float*>(kr + dn + 2 * DR);
+            } else {
+                kr = &sm.tile[bq][16 * n + l16][2 * dbase + 16 * g4];
+                esc = sm.scale[bq][16 * n + l16];
+            }
+            f32x4_t acc[2];
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                const uint8_t* kr = &sm.tile[buf][16 * n + l16][2 * dbase + 16 * g4];
+            for (int mt = 0; mt < 2; mt++) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ks = 0; ks < KS; ks++) {
-                    const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks);
-                    if (ks == nks && ks > 0) {
-#pragma unroll
-                        for (int mt = 0; mt < 2; mt++) acc[mt] *= esc;
-                    }
-#pragma unroll
-                    for (int mt = 0; mt < 2; mt++)
-                        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb, acc[mt], 0, 0, 0);
+            for (int ks = 0; ks < KS; ks++) {
+                bf16x8_t kb;
+                if constexpr (F8) {
+                    const int dim = dbase + 32 * ks + 8 * g4;
+                    if (ks < nks) kb = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(kr + dim));
+                    else kb = *reinterpret_cast<const bf16x8_t*>(kr + dn + 2 * (dim - dn));
+                } else {
+                    kb = *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks);
                 }
-                if (nks == KS) {
+                if (ks == nks && ks > 0) {
 #pragma unroll
                     for (int mt = 0; mt < 2; mt++) acc[mt] *= esc;
                 }
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++)
-                    *reinterpret_cast<f32x4_t*>(&sm.zx[w][mt][n][lane][0]) = acc[mt];
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb, acc[mt], 0, 0, 0);
             }
-        }
-        __syncthreads();
-        // ---- expand the next tile into the other buffer (last read by P V of
-        // the previous tile, which every wave finished before the barrier),
-        // then refill the staging area with the tile after it
-        if (et + kMTE < e1) {
-            wait_vm();
-            fetch_expand<D, DR>(sm, buf ^ 1, w, lane, fr);
-            wait_lgkm();
-            if (et + 2 * kMTE < e1) {
-                fr = fetch_plan(a, c, et + 2 * kMTE, e1, w, lane, jn);
-                fetch_issue<D, DR>(sm, w, lane, fr);
-                jn = fetch_index(a, c, et + 3 * kMTE, e1, w, lane);
+            if (nks == KS) {
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++) acc[mt] *= esc;
             }
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+                *reinterpret_cast<f32x4_t*>(&sm.zx[w][mt][n][lane][0]) = acc[mt];
         }
-        // ---- owner waves: add the quarters in order, online softmax, publish P
-        if (owner) {
-            float esc[2];
-            bool eok[2];
+    };
+    // owner waves: add the quarters of tile tt in order, online softmax, publish P
+    auto softmax_step = [&](int bq) {
+        float esc[2];
+        bool eok[2];
+#pragma unroll
+        for (int n = 0; n < 2; n++) {
+            if constexpr (F8) esc[n] = *reinterpret_cast<const float*>(&sm.ring[bq][16 * n + l16][dn + 2 * DR]);
+            else esc[n] = sm.scale[bq][16 * n + l16];
+            eok[n] = sm.valid[bq][16 * n + l16] != 0;
+        }
+        const int src = 4 * (w >> 1), lg = w & 1;        // waves holding this group's quarters
+        f32x4_t z[2];
+#pragma unroll
+        for (int n = 0; n < 2; n++) {
+            z[n] = *reinterpret_cast<const f32x4_t*>(&sm.zx[src][lg][n][lane][0]);
+#pragma unroll
+            for (int q = 1; q < 4; q++) z[n] += *reinterpret_cast<const f32x4_t*>(&sm.zx[src + q][lg][n][lane][0]);
+        }
+        float zz[2][4];
+        bool over = false;
+#pragma unroll
+        for (int i = 0; i < 4; i++)
 #pragma unroll
             for (int n = 0; n < 2; n++) {
-                esc[n] = sm.scale[buf][16 * n + l16];
-                eok[n] = sm.valid[buf][16 * n + l16] != 0;
+                zz[n][i] = eok[n] ? z[n][i] * zscale : -INFINITY;
+                over |= zz[n][i] > mrun[i] + kLazyMax;
             }
-            const int src = 4 * (w >> 1), lg = w & 1;    // waves holding this group's quarters
-            f32x4_t z[2];
-#pragma unroll
-            for (int n = 0; n < 2; n++) {
-                z[n] = *reinterpret_cast<const f32x4_t*>(&sm.zx[src][lg][n][lane][0]);
-#pragma unroll
-                for (int q = 1; q < 4; q++) z[n] += *reinterpret_cast<const f32x4_t*>(&sm.zx[src + q][lg][n][lane][0]);
-            }
+        // the running max is raised only past the headroom (also for the first
+        // finite logits); then the exact row max is taken and O, l rescaled
+        if (__any(over)) {
             bool moved = false;
-            float pz[2][4];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                float zz[2];
-#pragma unroll
-                for (int n = 0; n < 2; n++) zz[n] = eok[n] ? z[n][i] * zscale : -INFINITY;
-                const float mx = row16_max(fmaxf(zz[0], zz[1]));
-                float mn = mrun[i], al = 1.0f;
-                if (mx > mrun[i] + kLazyMax) {           // also the first finite maximum
-                    mn = mx;
-                    al = exp2f(mrun[i] - mx);            // 0 when mrun was -inf (O and l are 0)
-                    moved |= mrun[i] != -INFINITY;
-                }
-#pragma unroll
-                for (int n = 0; n < 2; n++) pz[n][i] = mn == -INFINITY ? 0.0f : exp2f(zz[n] - mn);
-                const float rs = row16_sum(pz[0][i] + pz[1][i]);
-                lrun[i] = lrun[i] * al + rs;
-                mrun[i] = mn;
+                const float mx = row16_max(fmaxf(zz[0][i], zz[1][i]));
+                const bool up = mx > mrun[i] + kLazyMax;
+                const float al = up ? __builtin_amdgcn_exp2f(mrun[i] - mx) : 1.0f;   // 0 from -inf
+                moved |= up && mrun[i] != -INFINITY;
+                mrun[i] = up ? mx : mrun[i];
+                lrun[i] *= al;
                 if (l16 == 0) sm.alpha[16 * w + 4 * g4 + i] = al;
             }
             const bool any_moved = __any(moved);
             if (lane == 0) sm.moved[w] = any_moved ? 1 : 0;
+        } else if (lane == 0) {
+            sm.moved[w] = 0;
+        }
+        float pz[2][4];
 #pragma unroll
-            for (int n = 0; n < 2; n++) {
-                const int kk = pv_k_of_entry(16 * n + l16);
-                uint2 ps, pp;
-                ps.x = pack_bf16x2(bf16x2_t{(__bf16)(pz[n][0] * esc[n]), (__bf16)(pz[n][1] * esc[n])});
-                ps.y = pack_bf16x2(bf16x2_t{(__bf16)(pz[n][2] * esc[n]), (__bf16)(pz[n][3] * esc[n])});
-                pp.x = pack_bf16x2(bf16x2_t{(__bf16)pz[n][0], (__bf16)pz[n][1]});
-                pp.y = pack_bf16x2(bf16x2_t{(__bf16)pz[n][2], (__bf16)pz[n][3]});
-                *reinterpret_cast<uint2*>(&sm.pt[0][kk][16 * w + 4 * g4]) = ps;
-                *reinterpret_cast<uint2*>(&sm.pt[1][kk][16 * w + 4 * g4]) = pp;
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int n = 0; n < 2; n++)
+                pz[n][i] = mrun[i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(zz[n][i] - mrun[i]);
+            lrun[i] += pz[0][i] + pz[1][i];           // per-lane partial row sums
+        }
+#pragma unroll
+        for (int n = 0; n < 2; n++) {
+            const int kk = pv_k_of_entry(16 * n + l16);
+            uint2 ps, pp;
+            ps.x = pack_bf16x2(bf16x2_t{(__bf16)(pz[n][0] * esc[n]), (__bf16)(pz[n][1] * esc[n])});
+            ps.y = pack_bf16x2(bf16x2_t{(__bf16)(pz[n][2] * esc[n]), (__bf16)(pz[n][3] * esc[n])});
+            pp.x = pack_bf16x2(bf16x2_t{(__bf16)pz[n][0], (__bf16)pz[n][1]});
+            pp.y = pack_bf16x2(bf16x2_t{(__bf16)pz[n][2], (__bf16)pz[n][3]});
+            *reinterpret_cast<uint2*>(&sm.pt[0][kk][16 * w + 4 * g4]) = ps;
+            *reinterpret_cast<uint2*>(&sm.pt[1][kk][16 * w + 4 * g4]) = pp;
+        }
+    };
+    // per-lane LDS coordinates of the transposing reads
+    const int v_row = 8 * g4 + 2 * (l16 >> 2);
+    const int v_col = 2 * (dbase + 4 * (l16 & 3));
+    const int p_row = 8 * g4 + (l16 >> 2);
+    const int p_col = 32 * hp + 4 * (l16 & 3);
+    // rescale O of the head groups whose max moved at tile tt (rare), then O += P V
+    auto pv_step = [&](int bq) {
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+            const int g = 2 * hp + mt;
+            if (g < MT && sm.moved[g]) {
+                const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[16 * g + 4 * g4]);
+#pragma unroll
+                for (int nd = 0; nd < NT; nd++) {
+                    o[mt][nd][0] *= al.x;
+                    o[mt][nd][1] *= al.y;
+                    o[mt][nd][2] *= al.z;
+                    o[mt][nd][3] *= al.w;
+                }
             }
+        }
+        // P A-fragments: scaled P for the non-RoPE dims, plain P for the RoPE dims
+        bf16x8_t pf[2];
+        {
+            const int pa = nnt > 0 ? 0 : 1;
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+                pf[mt] = tr_pair(&sm.pt[pa][p_row][16 * mt + p_col], &sm.pt[pa][p_row + 4][16 * mt + p_col]);
+        }
+#pragma unroll
+        for (int nd = 0; nd < NT; nd++) {
+            if (nd == nnt && nd > 0) {
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++)
+                    pf[mt] = tr_pair(&sm.pt[1][p_row][16 * mt + p_col], &sm.pt[1][p_row + 4][16 * mt + p_col]);
+            }
+            bf16x8_t vb;
+            if constexpr (F8) {
+                // lane (g4, s) addresses entry pi(8*g4 + s/2): bytes of 8 FP8 dims,
+                // or 4 bf16 RoPE dims of rows pi(8*g4 + 4h + s/4)
+                const uint8_t* rb = &sm.ring[bq][0][0];
+                if (nd < nnt) {
+                    const int r = 8 * g4 + (l16 >> 3) + 2 * ((l16 >> 1) & 3);
+                    vb = fp8x8_to_bf16(lds_read_tr8(rb + r * REC + dbase + 16 * nd + 8 * (l16 & 1)));
+                } else {
+                    const int cb = dn + 2 * (dbase + 16 * nd - dn + 4 * (l16 & 3));
+                    vb = tr_pair(rb + v_row * REC + cb, rb + (v_row + 1) * REC + cb);
+                }
+            } else {
+                const uint8_t* vp = &sm.tile[bq][v_row][v_col];
+                vb = tr_pair(vp + 32 * nd, vp + RS + 32 * nd);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
+                o[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[mt], vb, o[mt][nd], 0, 0, 0);
+        }
+    };
+
+    // ---- software pipeline over the tiles; per tile two barriers:
+    //   phase 1 (all waves):   O += P V of tile t-1, partial logits of tile t
+    //   phase 2: waves < MT run the softmax of tile t while the fetching waves
+    //            expand tile t+1 and send the fetch of tile t+2
+    // buffers: any formats, tile t in bf16 buffer t % 2; FP8 ring, tile t in ring t % 3
+    constexpr int NB = MfmaTiles<D, DR, F8>::kBufs;
+    if constexpr (F8) {
+        if (fetcher) wait_vm();
+    } else {
+        fetch_step(0, 0);
+    }
+    __syncthreads();
+    int bcur = 0, bprev = NB - 1;
+    for (int tt = 0; tt < ntiles; tt++) {
+        if (active) {
+            if (tt > 0) pv_step(bprev);
+            qk_step(bcur);
         }
         __syncthreads();
-        if (active) {
-            // ---- rescale O of the head groups whose max moved (rare), then O += P V
-#pragma unroll
-            for (int mt = 0; mt < 2; mt++) {
-                const int g = 2 * hp + mt;
-                if (g < MT && sm.moved[g]) {
-                    const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[16 * g + 4 * g4]);
-#pragma unroll
-                    for (int nd = 0; nd < NT; nd++) {
-                        o[mt][nd][0] *= al.x;
-                        o[mt][nd][1] *= al.y;
-                        o[mt][nd][2] *= al.z;
-                        o[mt][nd][3] *= al.w;
-                    }
-                }
-            }
-            // P A-fragments: scaled P for the non-RoPE dims, plain P for the RoPE dims
-            bf16x8_t pf[2];
-            {
-                const int pa = nnt > 0 ? 0 : 1;
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-                    pf[mt] = tr_pair(&sm.pt[pa][p_row][16 * mt + p_col], &sm.pt[pa][p_row + 4][16 * mt + p_col]);
-            }
-            const uint8_t* vp = &sm.tile[buf][v_row][v_col];
-#pragma unroll
-            for (int nd = 0; nd < NT; nd++) {
-                if (nd == nnt && nd > 0) {
-#pragma unroll
-                    for (int mt = 0; mt < 2; mt++)
-                        pf[mt] = tr_pair(&sm.pt[1][p_row][16 * mt + p_col], &sm.pt[1][p_row + 4][16 * mt + p_col]);
-                }
-                const bf16x8_t vb = tr_pair(vp + 32 * nd, vp + RS + 32 * nd);
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-                    o[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[mt], vb, o[mt][nd], 0, 0, 0);
-            }
+        if (owner) softmax_step(bcur);
+        if constexpr (F8) {
+            int bn2 = bcur + 2;
+            if (bn2 >= NB) bn2 -= NB;
+            fetch_step(tt + 1, bn2);      // waits for tile tt+1, sends tile tt+2
+        } else {
+            fetch_step(tt + 1, 0);
         }
+        __syncthreads();
+        bprev = bcur;
+        bcur = bcur + 1 == NB ? 0 : bcur + 1;
     }
+    if (active && ntiles > 0) pv_step(bprev);
 
     // ---- epilogue
+#pragma unroll
+    for (int i = 0; i < 4; i++) lrun[i] = row16_sum(lrun[i]);
     if (nsplit <= 1) {
         if (owner) {
 #pragma unroll
@@ -562,19 +766,35 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
         }
         return;
     }
-    // partial results of this split: unnormalised O, and (max, sum) in natural-log units
+    // partial results of this split: unnormalised O, and (max, sum) in natural-log units.
+    // O goes through LDS (the tile and logit areas are free now), 32 heads at
+    // a time, so that the global stores are whole 16-byte vectors.
     float* wo = reinterpret_cast<float*>(a.ws);
     float* wml = wo + (size_t)a.rows * nsplit_max * a.H * D;
     const size_t base = ((size_t)row * nsplit_max + sp) * a.H + h0;
-    if (active) {
+    static_assert(sizeof(MfmaTiles<D, DR, F8>) + sizeof(sm.zx) >= 32 * (D + 4) * sizeof(float),
+                  "partial staging does not fit");
+    float* ost = reinterpret_cast<float*>(&sm);     // [32 heads][D + 4]
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++)
-            if (2 * hp + mt < MT)
+    for (int half = 0; half < 2; half++) {
+        if (2 * half >= MT) break;
+        __syncthreads();
+        if (hp == half) {
+#pragma unroll
+            for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int nd = 0; nd < NT; nd++)
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        wo[(base + 16 * (2 * hp + mt) + 4 * g4 + i) * D + dbase + 16 * nd + l16] = o[mt][nd][i];
+                        ost[(16 * mt + 4 * g4 + i) * (D + 4) + dbase + 16 * nd + l16] = o[mt][nd][i];
+        }
+        __syncthreads();
+        const int nv = min(32, 16 * MT - 32 * half) * (D / 4);      // float4s of the valid heads
+        float4* dst = reinterpret_cast<float4*>(wo + (base + 32 * half) * D);
+        for (int v = tid; v < nv; v += kNW * 64) {
+            const int h = v / (D / 4), c4 = v % (D / 4);
+            dst[v] = *reinterpret_cast<const float4*>(&ost[h * (D + 4) + 4 * c4]);
+        }
     }
     if (owner && l16 == 0) {
 #pragma unroll
@@ -595,20 +815,27 @@ bool attn_mfma_supported(const AttnArgs& a) {
     return true;
 }
 
-template <typename OT>
+template <bool F8, typename OT>
 static void launch_d(const AttnArgs& a, int nsplit, hipStream_t st) {
     const int groups = (a.H + 63) / 64;
     dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)groups);
     // eight waves per workgroup always (head halves x dim quarters); a
     // workgroup covers up to 64 heads
-    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
-    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
-    else hipLaunchKernelGGL((k_attn_mfma<512, 64, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
+    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
+    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
+    else hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, int64_t nsplit_bound, hipStream_t st) {
-    if (a.out_fmt == CSA_BF16) launch_d<uint16_t>(a, (int)nsplit_bound, st);
-    else launch_d<float>(a, (int)nsplit_bound, st);
+    // all records FP8: the ring kernel; otherwise the expanding one
+    const bool f8 = a.comp_fmt == CSA_FP8_E4M3 && (a.W == 0 || a.win_fmt == CSA_FP8_E4M3);
+    if (f8) {
+        if (a.out_fmt == CSA_BF16) launch_d<true, uint16_t>(a, (int)nsplit_bound, st);
+        else launch_d<true, float>(a, (int)nsplit_bound, st);
+    } else {
+        if (a.out_fmt == CSA_BF16) launch_d<false, uint16_t>(a, (int)nsplit_bound, st);
+        else launch_d<false, float>(a, (int)nsplit_bound, st);
+    }
     return hipGetLastError();
 }
 
