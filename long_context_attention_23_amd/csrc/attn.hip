@@ -128,7 +128,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
     const int d = a.d, ld = d + 1;
     const int tid = threadIdx.x;
 
-    stage_rope(a.rope, rf, a.dr / 2);
+    stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
     __syncthreads();
     query_prologue<QT>(a, row, h0, hg, t, qs, rf);
     for (int hh = tid; hh < hg; hh += blockDim.x) { mrun[hh] = -INFINITY; lrun[hh] = 0.0f; }
@@ -240,25 +240,28 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
 }
 
 // merge the splits of (row, head): weights exp(m_s - M) with M over the split
-// maxima and the sink, each output dim summed over the splits in split order
+// maxima and the sink.  Thread t sums float4 column t % (d/4) over the splits
+// of group t / (d/4) (splits g, g + G, ... in order, several loads in
+// flight); the groups are then added in group order.
 template <typename OT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int nsplit_max) {
     __shared__ float v[kAttnMaxD];
     __shared__ float wsc[1024];
     __shared__ float red[kAttnThreads / kWave];
     __shared__ double rf[64];
+    __shared__ float4 part[kAttnThreads];
     const int h = blockIdx.x;
     const int64_t row = blockIdx.y;
     const int64_t t = a.q_pos[row];
     const int64_t nc = comp_slots(a, t);
     const int64_t ne = nc + a.W;
-    const int nsplit = (int)attn_nsplit(ne, a.Tq);
+    const int nsplit = (int)attn_nsplit<int64_t>(ne, a.Tq);
     if (nsplit <= 1) return;
     const float* wo = reinterpret_cast<const float*>(a.ws);
     const float* wml = wo + (size_t)a.rows * nsplit_max * a.H * a.d;
     const int d = a.d;
     const float sk = a.sink[h];
-    stage_rope(a.rope, rf, a.dr / 2);
+    stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
     const size_t mbase = (size_t)row * nsplit_max * a.H + h;     // split s at mbase + s * H
     float mx = sk;
     for (int s = threadIdx.x; s < nsplit; s += blockDim.x) mx = fmaxf(mx, wml[(mbase + (size_t)s * a.H) * 2]);
@@ -274,12 +277,60 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int n
     den = block_sum(den, red);
     if (M != -INFINITY) den += expf(sk - M);
     __syncthreads();
-    const float* wo_h = wo + mbase * d;
-    for (int k = threadIdx.x; k < d; k += blockDim.x) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int s = 0; s < nsplit; s++) acc = fmaf(wsc[s], wo_h[(size_t)s * a.H * d + k], acc);
-        v[k] = den > 0.0f ? acc / den : 0.0f;
+    if (d % 4 != 0) {
+        // head dims not a multiple of 4: one dim per thread, splits in order
+        const float* wo_h = wo + mbase * d;
+        for (int k = threadIdx.x; k < d; k += blockDim.x) {
+            float acc = 0.0f;
+            for (int s = 0; s < nsplit; s++) acc = fmaf(wsc[s], wo_h[(size_t)s * a.H * d + k], acc);
+            v[k] = den > 0.0f ? acc / den : 0.0f;
+        }
+        __syncthreads();
+        rotate_out(a, t, v, threadIdx.x, blockDim.x, rf);
+        __syncthreads();
+        OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
+        for (int k = threadIdx.x; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
+        return;
+    }
+    const int nc4 = d / 4;
+    const int G = (int)blockDim.x / nc4;       // split groups
+    const int c = threadIdx.x % nc4, g = threadIdx.x / nc4;
+    const float4* wo4 = reinterpret_cast<const float4*>(wo + mbase * d) + c;
+    const size_t sstride = (size_t)a.H * d / 4;               // float4s between splits
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (g < G) {
+        constexpr int kB = 8;
+        for (int s0 = g; s0 < nsplit; s0 += kB * G) {
+            float4 x[kB];
+#pragma unroll
+            for (int q = 0; q < kB; q++) {
+                const int s = s0 + q * G;
+                x[q] = s < nsplit ? wo4[(size_t)s * sstride] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int q = 0; q < kB; q++) {
+                const int s = s0 + q * G;
+                const float w = s < nsplit ? wsc[s] : 0.0f;
+                acc.x = fmaf(w, x[q].x, acc.x);
+                acc.y = fmaf(w, x[q].y, acc.y);
+                acc.z = fmaf(w, x[q].z, acc.z);
+                acc.w = fmaf(w, x[q].w, acc.w);
+            }
+        }
+        part[threadIdx.x] = acc;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nc4) {
+        float4 r = part[threadIdx.x];
+        for (int q = 1; q < G; q++) {
+            const float4 y = part[q * nc4 + threadIdx.x];
+            r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
+        }
+        const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+        v[4 * threadIdx.x] = den > 0.0f ? r.x * inv : 0.0f;
+        v[4 * threadIdx.x + 1] = den > 0.0f ? r.y * inv : 0.0f;
+        v[4 * threadIdx.x + 2] = den > 0.0f ? r.z * inv : 0.0f;
+        v[4 * threadIdx.x + 3] = den > 0.0f ? r.w * inv : 0.0f;
     }
     __syncthreads();
     rotate_out(a, t, v, threadIdx.x, blockDim.x, rf);

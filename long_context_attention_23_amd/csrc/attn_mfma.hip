@@ -423,11 +423,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
             jn = fetch_index(a, c, e0 + kMTE, e1, fw, lane);
         }
     }
-    {
-        // RoPE inverse frequencies, read lane-parallel from the argument block
-        const double* rtab = (const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(AttnArgs, rope));
-        if (tid < a.dr / 2) sm.rf[tid] = rtab[tid];
-    }
+    stage_rope_arg(offsetof(AttnArgs, rope), sm.rf, a.dr / 2);
 
     // ---- query prologue: q^ = RoPE_t(RMSNorm(q)), this wave's 32 heads and quarter
 #pragma unroll

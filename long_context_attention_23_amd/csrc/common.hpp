@@ -5,6 +5,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/csa_attn.h"
@@ -82,16 +83,15 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
 // Angle of pair i at position pos: pos * f_i with f_i = base^(-2i/dr) held in
 // fp64 (positions reach 2^20 and more, where an fp32 product would be off by
 // tens of milliradians).
-// Copy a kernel-argument frequency table to LDS with static indices (a
-// per-lane index into a by-value kernel argument would force a private copy
-// of the whole argument block into scratch memory).  Caller synchronises.
-template <typename Table>
-__device__ __forceinline__ void stage_rope(const Table& t, double* lds, int npairs) {
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int i = 0; i < 64; i++)
-            if (i < npairs) lds[i] = t.f[i];
-    }
+// Copy the frequency table of the kernel's argument block to LDS, one entry
+// per thread.  The block must be the kernel's first parameter (offset 0 of
+// the kernel-argument segment); offset is offsetof(block, table).  Reading
+// it through the segment pointer keeps a per-lane index off the by-value
+// parameter (which would force a private copy of the whole block).  Needs
+// blockDim >= npairs; the caller synchronises before use.
+__device__ __forceinline__ void stage_rope_arg(size_t offset, double* lds, int npairs) {
+    const double* t = (const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offset);
+    if ((int)threadIdx.x < npairs) lds[threadIdx.x] = t[threadIdx.x];
 }
 
 // sin and cos of pos * freq.  The angle is reduced in fp64 around the

@@ -10,16 +10,20 @@
 // m-position score vector (plus an optional content score), summed over the
 // block's tokens.
 //
-// One workgroup of 256 threads per output block.  The work is streaming and
+// One workgroup of 512 threads per output block.  The work is streaming and
 // memory-bound (m tokens of d values in, one record out); the block's pooled
 // vector lives in LDS between the pooling, normalisation, rotation and
-// quantisation phases.
+// quantisation phases.  A decode step compresses one block per sequence, so
+// a workgroup's own latency is the cost: the token rows are read with many
+// independent 16-byte loads in flight per thread.
+#include <stddef.h>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace csa {
 
-constexpr int kCompThreads = 256;
+constexpr int kCompThreads = 512;
 constexpr int kMaxD = 1024;
 constexpr int kMaxM = 1024;
 
@@ -30,7 +34,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     __shared__ float sz[kMaxM];
     __shared__ float red[kCompThreads / kWave];
     __shared__ int se[kMaxD / 32];
-    __shared__ float part[kCompThreads * 8];      // token-group partial sums of the pooling
+    __shared__ float part[kCompThreads * 8];      // token-group partial sums of the pooling (TG * d <= 8 * threads)
     __shared__ double rf[64];
 
     const int tid = threadIdx.x;
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     if (!a.ring && j >= a.cap) return;
     const int64_t slot = a.ring ? j % a.cap : j;
     const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + i * m) * d;
-    stage_rope(a.rope, rf, a.dr / 2);
+    stage_rope_arg(offsetof(CompressArgs, rope), rf, a.dr / 2);
 
     // ---- pooling weights: z_r = bias_r + <u, x_r>, softmax over r
     const int lane = tid & (kWave - 1), wv = tid / kWave;
@@ -76,22 +80,35 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
             float acc[EPC];
 #pragma unroll
             for (int e = 0; e < EPC; e++) acc[e] = 0.0f;
-#pragma unroll 4
-            for (int r = tg; r < m; r += TG) {
-                const uint4 u = *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC);
-                const float p = sz[r];
-                if constexpr (sizeof(XT) == 2) {
-                    const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+            // batches of kBatch rows: all loads of a batch are issued before any
+            // is consumed (token order is kept inside the group)
+            constexpr int kBatch = 8;
+            for (int r0 = tg; r0 < m; r0 += kBatch * TG) {
+                uint4 u[kBatch];
 #pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        acc[2 * q] = fmaf(p, __uint_as_float(wd[q] << 16), acc[2 * q]);
-                        acc[2 * q + 1] = fmaf(p, __uint_as_float(wd[q] & 0xFFFF0000u), acc[2 * q + 1]);
+                for (int q = 0; q < kBatch; q++) {
+                    const int r = r0 + q * TG;
+                    u[q] = r < m ? *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+                }
+#pragma unroll
+                for (int q = 0; q < kBatch; q++) {
+                    const int r = r0 + q * TG;
+                    if (r >= m) break;
+                    const float p = sz[r];
+                    if constexpr (sizeof(XT) == 2) {
+                        const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            acc[2 * e] = fmaf(p, __uint_as_float(wd[e] << 16), acc[2 * e]);
+                            acc[2 * e + 1] = fmaf(p, __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
+                        }
+                    } else {
+                        acc[0] = fmaf(p, __uint_as_float(u[q].x), acc[0]);
+                        acc[1] = fmaf(p, __uint_as_float(u[q].y), acc[1]);
+                        acc[2] = fmaf(p, __uint_as_float(u[q].z), acc[2]);
+                        acc[3] = fmaf(p, __uint_as_float(u[q].w), acc[3]);
                     }
-                } else {
-                    acc[0] = fmaf(p, __uint_as_float(u.x), acc[0]);
-                    acc[1] = fmaf(p, __uint_as_float(u.y), acc[1]);
-                    acc[2] = fmaf(p, __uint_as_float(u.z), acc[2]);
-                    acc[3] = fmaf(p, __uint_as_float(u.w), acc[3]);
                 }
             }
 #pragma unroll
