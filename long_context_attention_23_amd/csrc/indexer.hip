@@ -152,9 +152,28 @@ __device__ uint64_t radix_select(Get get, int64_t n, int nbits, uint32_t need, u
     for (int shift = ((nbits + 7) / 8) * 8 - 8; shift >= 0; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
         __syncthreads();
-        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-            uint64_t c = get(i);
-            if ((c & pmask) == prefix) atomicAdd(&hist[(c >> shift) & 255u], 1u);
+        for (int64_t i0 = 0; i0 < n; i0 += blockDim.x) {
+            // the whole block runs every round, so each wave's ballots are complete
+            const int64_t i = i0 + threadIdx.x;
+            const uint64_t c = i < n ? get(i) : 0;
+            const bool in = i < n && (c & pmask) == prefix;
+            const uint32_t dg = (uint32_t)(c >> shift) & 255u;
+            // many equal digits (tied scores) would serialise on one LDS
+            // address: a wave whose lanes mostly agree adds per distinct digit
+            const uint64_t act = __ballot(in);
+            const uint32_t d0 = __shfl(dg, act ? __builtin_ctzll(act) : 0, kWave);
+            if (__popcll(__ballot(in && dg == d0)) > 8) {
+                uint64_t todo = act;
+                while (todo) {
+                    const int leader = __builtin_ctzll(todo);
+                    const uint32_t dl = __shfl(dg, leader, kWave);
+                    const uint64_t same = __ballot(in && dg == dl) & todo;
+                    if ((int)(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+                    todo &= ~same;
+                }
+            } else if (in) {
+                atomicAdd(&hist[dg], 1u);
+            }
         }
         __syncthreads();
         if (threadIdx.x < kWave) {
@@ -296,7 +315,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_i __attribute__((ext_vector_type(8)));
 
-constexpr int kIdxMfmaBatch = 8;   // 32-key groups whose loads a wave issues before computing
+constexpr int kIdxScoreThreads = 512;   // 8 waves: every FP4 key load of a chunk in flight at once
 
 // Score a chunk of 64-dim keys with the matrix cores.  C[head][key] = Q K^T:
 // the query's Hi rows are the A operand (32 rows, rows >= Hi zero), 32 keys
@@ -309,9 +328,11 @@ constexpr int kIdxMfmaBatch = 8;   // 32-key groups whose loads a wave issues be
 // Each wave loads kIdxMfmaBatch groups before computing them, to keep enough
 // bytes in flight.
 template <int QF, int KF>
-__global__ __launch_bounds__(kIdxThreads) void k_idx_score_mfma(IndexerArgs a) {
+__global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs a) {
     constexpr int DI = 64;
     constexpr int NKS = KF == CSA_FP4_E2M1 ? 1 : 4;            // K steps per 32-key group
+    // 32-key groups whose loads a wave issues before computing them
+    constexpr int kIdxMfmaBatch = KF == CSA_FP4_E2M1 ? kIdxChunk / kIdxScoreThreads : 4;
     constexpr int KROW = KF == CSA_FP4_E2M1 ? DI / 2 : 2 * DI;  // key row bytes
     __shared__ uint32_t lh[kIdxHistBins];
     const int64_t r = blockIdx.y, row = a.row0 + r;
@@ -358,7 +379,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_score_mfma(IndexerArgs a) {
     const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
     const uint8_t* kb = a.keys + (size_t)b * a.cap * KROW;
     const uint8_t* ksb = KF == CSA_FP4_E2M1 ? a.key_scales + (size_t)b * a.cap * (DI / 32) : nullptr;
-    constexpr int kStride = 32 * (kIdxThreads / 64);
+    constexpr int kStride = 32 * (kIdxScoreThreads / 64);
     for (int64_t gb = c0 + 32 * wv; gb < c1; gb += (int64_t)kStride * kIdxMfmaBatch) {
         uint4 kc[kIdxMfmaBatch][NKS];
         int ksc[kIdxMfmaBatch];
@@ -408,9 +429,15 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_score_mfma(IndexerArgs a) {
 // threshold bin of the 4096-bin histogram, computed by one wave
 __device__ __forceinline__ void wave_pick_bin(const uint32_t* hist, uint32_t need, uint32_t& bin, uint32_t& above) {
     const int lane = threadIdx.x & (kWave - 1);
-    constexpr int per = kIdxHistBins / kWave;   // 64 bins per lane, descending
+    constexpr int per = kIdxHistBins / kWave;   // 64 bins per lane; lane 0 holds the top bins
+    // this lane's bins [4096 - 64(lane+1), 4096 - 64 lane) with all loads in flight
+    const uint4* hv = reinterpret_cast<const uint4*>(hist + kIdxHistBins - per * (lane + 1));
+    uint4 v[per / 4];
+#pragma unroll
+    for (int i = 0; i < per / 4; i++) v[i] = hv[i];
     uint32_t s = 0;
-    for (int q = 0; q < per; q++) s += hist[kIdxHistBins - 1 - per * lane - q];
+#pragma unroll
+    for (int i = 0; i < per / 4; i++) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     uint32_t incl = s;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
@@ -419,18 +446,21 @@ __device__ __forceinline__ void wave_pick_bin(const uint32_t* hist, uint32_t nee
     }
     uint64_t bal = __ballot(incl >= need);
     int L = bal ? __builtin_ctzll(bal) : kWave - 1;
-    uint32_t cum = __shfl(incl - s, L, kWave);
-    uint32_t bb = 0, ab = cum;
-    if (lane == L) {
-        uint32_t c = cum;
-        for (int q = 0; q < per; q++) {
-            uint32_t hb = hist[kIdxHistBins - 1 - per * L - q];
-            if (c + hb >= need) { bb = kIdxHistBins - 1 - per * L - q; ab = c; break; }
-            c += hb;
-        }
+    const uint32_t cum = __shfl(incl - s, L, kWave);
+    // the bins of lane L, one per lane in descending bin order, prefix-summed
+    const int bq = kIdxHistBins - 1 - per * L - lane;
+    const uint32_t hb = hist[bq];
+    uint32_t c = hb;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        uint32_t t = __shfl_up(c, o, kWave);
+        if (lane >= o) c += t;
     }
-    bin = __shfl(bb, L, kWave);
-    above = __shfl(ab, L, kWave);
+    c += cum;
+    const uint64_t hit = __ballot(c >= need);
+    const int q = hit ? __builtin_ctzll(hit) : kWave - 1;
+    bin = (uint32_t)__shfl(bq, q, kWave);
+    above = __shfl(c - hb, q, kWave);
 }
 
 __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
@@ -441,6 +471,15 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
     if (n <= a.topk || c0 >= n) return;
     RowWs w = row_ws(a, r);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
+    constexpr int kPer = kIdxChunk / kIdxThreads;
+    uint32_t keys[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; u++) {                     // score loads go out before the bin search
+        const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
+        keys[u] = j < c1 ? w.scores[j] : 0u;
+    }
     if (threadIdx.x < kWave) {
         uint32_t bin, above;
         wave_pick_bin(w.hist, (uint32_t)a.topk, bin, above);
@@ -448,15 +487,6 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     }
     __syncthreads();
     const uint32_t tbin = sh[0];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
-    constexpr int kPer = kIdxChunk / kIdxThreads;
-    uint32_t keys[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; u++) {                     // all loads first
-        const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
-        keys[u] = j < c1 ? w.scores[j] : 0u;
-    }
     // workgroup-local slots from LDS counters, then one global reservation per list
     uint32_t slot[kPer];
     uint32_t kind = 0;                                   // bit u: 1 = sure, bit u+16: candidate
@@ -495,8 +525,11 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
 
 constexpr int kIdxBitmapWords = 16384;   // LDS bitmap of selected blocks (caps up to 2^19)
 
+constexpr int kIdxFinalLds = 4096;       // candidates kept in LDS across the radix passes
+
 __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     __shared__ uint32_t bm[kIdxBitmapWords];
+    __shared__ uint2 lc[kIdxFinalLds];
     __shared__ int32_t arr[kIdxMaxTopk];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh[4];
@@ -513,7 +546,12 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     const uint32_t need = (uint32_t)a.topk - nsel;     // 1 <= need <= ncand by construction
     const int jb = bits_for(a.cap);
     const uint64_t jmask = ((uint64_t)1 << jb) - 1;
-    const uint2* cand = w.cand;
+    const bool in_lds = ncand <= (uint32_t)kIdxFinalLds;
+    if (in_lds) {
+        for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) lc[i] = w.cand[i];
+        __syncthreads();
+    }
+    const uint2* cand = in_lds ? lc : w.cand;
     auto get = [&](int64_t i) -> uint64_t {
         uint2 c = cand[i];
         return ((uint64_t)(c.x & 0xFFFFFu) << jb) | (jmask - (uint64_t)c.y);
@@ -612,7 +650,7 @@ static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes
         const bool mfma_ok = a.di == 64 && a.Hi <= 32 && ((KF == CSA_FP4_E2M1 && QF == CSA_FP4_E2M1) ||
                                                           (KF == CSA_BF16 && QF != CSA_F32));
         if constexpr ((KF == CSA_FP4_E2M1 && QF == CSA_FP4_E2M1) || (KF == CSA_BF16 && QF != CSA_F32)) {
-            if (mfma_ok) hipLaunchKernelGGL((k_idx_score_mfma<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
+            if (mfma_ok) hipLaunchKernelGGL((k_idx_score_mfma<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxScoreThreads), 0, st, a);
             else hipLaunchKernelGGL((k_idx_score<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
         } else {
             hipLaunchKernelGGL((k_idx_score<QF, KF>), dim3(nchunk, (unsigned)nr), dim3(kIdxThreads), 0, st, a);
