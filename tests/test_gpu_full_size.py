@@ -217,3 +217,40 @@ def test_c4_layer_pair_decode_full_size():
         y, yref = proj_both(o, W, G)
         say(f"c4 {name} projection rel {rel_err(y, yref):.3e}")
         assert rel_err(y, yref) <= 1e-4
+
+
+def test_c5_prefill_chunk_sampled_rows():
+    """CSA chunked prefill at 1M tokens: a chunk of 8,192 queries over a
+    1,048,576-token prefix plus the chunk itself (264,192 blocks), FP4 indexer
+    and FP8 records, 64 heads x 512.  The whole chunk runs on the GPU in the
+    benchmark's configuration (caller workspace, row batches); the oracle
+    checks a spread of query rows one by one."""
+    g = synth.rng(2005)
+    L, T, H, k, Hi, di, m = 1 << 20, 8192, 64, 1024, 4, 64, 4
+    n = (L + T) // m
+    pos = (L + np.arange(T, dtype=np.int32))[None]
+    kc, ks = synth.fp4_rows(g, (1, n), di, -3, 0)
+    qc, qs = synth.fp4_rows(g, (1, T, Hi), di, -3, 0)
+    w = synth.grid(g, (1, T, Hi))
+    keys = api.IdxCache(1, n, di, O.FP4_E2M1, codes=dev(kc), scales=dev(ks))
+    ws = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    say(f"c5 indexer rows={T} keys={n} k={k}")
+    top = api.indexer_topk(dev(qc), O.FP4_E2M1, dev(w), keys, dev(pos), m, k, q_scales=dev(qs), workspace=ws)
+    comp = normed_fp8_records(g, (1, n))
+    win = normed_fp8_records(g, (1, WIN + T))
+    q = synth.bf16_bits(g, (1, T, H, D_HEAD))
+    sink = synth.normal(g, H)
+    cc = api.KVCache(1, n, D_HEAD, DR, O.FP8_E4M3, rec=dev(comp))
+    wc = api.KVCache(1, WIN + T, D_HEAD, DR, O.FP8_E4M3, ring=True, rec=dev(win))
+    say("c5 attention")
+    out = api.sparse_mqa_attn(dev_bf16(q), dev(pos), top, cc, wc, dev(sink), api.attn_params(D_HEAD, DR, WIN, m))
+    torch.cuda.synchronize()
+    top, out = top.cpu().numpy(), out_to_f64(out)
+    rows = np.array([0, 1, 777, 4095, 6001, T - 1])
+    ref_top = O.indexer_topk(qc[0, rows], qs[0, rows], O.FP4_E2M1, w[0, rows], pos[0, rows], kc[0], ks[0],
+                             O.FP4_E2M1, m, k)
+    assert np.array_equal(top[0, rows], ref_top)
+    ref = O.attention(q[0, rows], O.BF16, pos[0, rows], None, sink, D_HEAD, DR, WIN, m, 10000.0, SCALE, 1e-6,
+                      comp[0], O.FP8_E4M3, win[0], O.FP8_E4M3, ref_top)
+    say(f"c5 sampled attention abs {abs_err(out[0, rows], ref):.3e}")
+    assert abs_err(out[0, rows], ref) <= 2e-2
