@@ -14,7 +14,17 @@ more traffic than the 256 MB last-level cache holds.
 
 Prints one JSON line (metric, value = query tokens per second, roofline of the
 dominant kernel from HIP events, CPU-oracle baseline on the host cores).
+
+Profiling helpers (the summaries under profiles/ are made with these):
+  --copy-calibration       a plain 1 GiB device copy, three times (the
+                           reference for FETCH_SIZE / WRITE_SIZE scaling);
+  --summarize DIR          per-kernel duration summary of a rocprofv3
+                           --kernel-trace run written under DIR;
+  --summarize-pmc DIR ...  per-call sums of the counters of rocprofv3 --pmc
+                           runs of this benchmark (one counter per run).
 """
+import glob
+import hashlib
 import argparse
 import json
 import math
@@ -48,6 +58,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=6, help="rotated buffer sets (defeats the last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
+    ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+")
     return ap.parse_args()
 
 
@@ -154,13 +167,13 @@ def build_state(torch, api, copies, seed=4004):
 CALLS = ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_mqa_attn", "csa_out_proj",
          "hca_compress_kv", "hca_dense_mqa_attn", "hca_out_proj"]
 
-# the kernels each call launches (for matching rocprof summaries)
+# the kernels each call launches, in launch order (for matching rocprof traces)
 CALL_KERNELS = {
-    "csa_compress_kv": ["k_compress"],
+    "csa_compress_kv": ["k_compress", "k_compress", "k_compress"],
     "csa_indexer_topk": ["k_idx_zero", "k_idx_score_mfma", "k_idx_collect", "k_idx_final"],
     "csa_sparse_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "csa_out_proj": ["k_proj_gemv"],
-    "hca_compress_kv": ["k_compress"],
+    "hca_compress_kv": ["k_compress", "k_compress"],
     "hca_dense_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "hca_out_proj": ["k_proj_gemv"],
 }
@@ -198,15 +211,6 @@ def call_fns(api):
         api.out_proj_grouped(s["o_hca"].view(B, H * D_HEAD), s["Wo_hca"], y=s["y_hca"])
 
     return [c0, c1, c2, c3, c4, c5, c6]
-
-
-def capture(torch, fns, s, sh):
-    """One HIP graph launching fns in order on the capture stream."""
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for f in fns:
-            f(s, sh)
-    return g
 
 
 def cpu_baseline(target_s):
@@ -254,7 +258,7 @@ def cpu_baseline(target_s):
             O.out_proj(oh.reshape(1, H * D_HEAD), Wo64[1])
         n_steps += 1
         el = time.perf_counter() - t0
-        if el >= target_s or n_steps >= 20:
+        if el >= target_s or n_steps >= 200:
             break
     cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
     return {"value": n_steps * B / el, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
@@ -262,8 +266,149 @@ def cpu_baseline(target_s):
                       f"synthetic FP8/FP4 caches of the same shapes), {el:.1f} s"}
 
 
+# HBM traffic per launch of a call, from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# runs of this benchmark scaled by the copy calibration (profiles/
+# traffic_*.md); valid only while the kernels' sources are unchanged.
+TRAFFIC = {
+    "csa_indexer_topk": {"bytes": 45_482_822, "src": "c090b6af3b5f5673"},
+    "csa_sparse_mqa_attn": {"bytes": 25_352_883, "src": "c090b6af3b5f5673"},
+    "hca_dense_mqa_attn": {"bytes": 78_175_027, "src": "c090b6af3b5f5673"},
+    "csa_out_proj": {"bytes": 61_128_576, "src": "c090b6af3b5f5673"},
+    "hca_out_proj": {"bytes": 61_128_576, "src": "c090b6af3b5f5673"},
+}
+TRAFFIC_SRC = ["long_context_attention_23_amd/csrc/indexer.hip", "long_context_attention_23_amd/csrc/attn_mfma.hip",
+               "long_context_attention_23_amd/csrc/attn.hip", "long_context_attention_23_amd/csrc/proj.hip",
+               "long_context_attention_23_amd/csrc/compress.hip", "long_context_attention_23_amd/csrc/common.hpp"]
+
+
+def src_hash():
+    h = hashlib.sha256()
+    for f in TRAFFIC_SRC:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 1 GiB, three times."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "launches": 3}), flush=True)
+
+
+def _kernel_rows(db):
+    import sqlite3
+    c = sqlite3.connect(db)
+    cols = [r[1] for r in c.execute("pragma table_info(kernels)")]
+    ni = cols.index("name") if "name" in cols else cols.index("kernel_name")
+    st, en = cols.index("start"), cols.index("end")
+    return sorted(((r[ni], r[st], r[en]) for r in c.execute("select * from kernels")), key=lambda r: r[1])
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize(d, last=20):
+    """Per-kernel and per-call durations of a kernel-trace run of this
+    benchmark over its last `last` steps (the timed region).  A step is the
+    fixed sequence of launches of CALL_KERNELS in CALLS order; a call's span
+    runs from its first kernel's start to its last kernel's end."""
+    db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
+    rows = _kernel_rows(db)
+    seq = [k for c in CALLS for k in CALL_KERNELS[c]]
+    first = seq.index("k_idx_zero")
+    zero = [i for i, (n, _, _) in enumerate(rows) if "k_idx_zero" in n]
+    steps = []
+    for z in zero:
+        st = z - first
+        if st < 0 or st + len(seq) > len(rows):
+            continue
+        blk = rows[st:st + len(seq)]
+        if all(k in _short(n) for k, (n, _, _) in zip(seq, blk)):
+            steps.append(blk)
+    steps = steps[-last:]
+    out = [f"steps summarised: {len(steps)} (the last {last} whole steps of the run)", "",
+           "Per kernel:", "",
+           "| kernel | dispatches | avg us | min us | max us | total us |", "|---|---|---|---|---|---|"]
+    agg = {}
+    for blk in steps:
+        for n, a, b in blk:
+            agg.setdefault(_short(n), []).append((b - a) / 1e3)
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"| {k} | {len(v)} | {np.mean(v):.2f} | {min(v):.2f} | {max(v):.2f} | {sum(v):.1f} |")
+    out += ["", "Per call (span = first kernel start to last kernel end, per step):", "",
+            "| call | kernels | avg span us | median span us | avg sum of kernel us |", "|---|---|---|---|---|"]
+    for c in CALLS:
+        i0 = sum(len(CALL_KERNELS[x]) for x in CALLS[:CALLS.index(c)])
+        n = len(CALL_KERNELS[c])
+        spans = [(blk[i0 + n - 1][2] - blk[i0][1]) / 1e3 for blk in steps]
+        sums = [sum(b - a for _, a, b in blk[i0:i0 + n]) / 1e3 for blk in steps]
+        out.append(f"| {c} | {' '.join(CALL_KERNELS[c])} | {np.mean(spans):.2f} | {np.median(spans):.2f} | "
+                   f"{np.mean(sums):.2f} |")
+    wall = [(steps[i + 1][0][1] - steps[i][0][1]) / 1e3 for i in range(len(steps) - 1)]
+    if wall:
+        out += ["", f"step period (start to start): avg {np.mean(wall):.2f} us"]
+    print("\n".join(out))
+
+
+def summarize_pmc(dirs):
+    """Per-call counter sums (mean over the timed steps) from --pmc runs of
+    this benchmark; calls are told apart by their kernels and step order."""
+    import sqlite3
+    res = {}
+    for d in dirs:
+        db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
+        c = sqlite3.connect(db)
+        rows = c.execute("select name, counter_name, counter_value, dispatch_id from pmc_events").fetchall()
+        per = {}
+        for name, cn, v, did in rows:
+            key = (did, _short(name), cn)
+            per[key] = per.get(key, 0.0) + v
+        seq = sorted(per.items())                   # dispatch order
+        counters = sorted({k[2] for k, _ in seq})
+        for cn in counters:
+            ks = [(k[1], v) for k, v in seq if k[2] == cn]
+            sums = {"csa_indexer_topk": [], "csa_sparse_mqa_attn": [], "hca_dense_mqa_attn": [],
+                    "out_proj (one launch)": []}
+            i = 0
+            attn_seen = 0
+            while i < len(ks):
+                n = ks[i][0]
+                if n.endswith("k_idx_zero") and i + 3 < len(ks):
+                    sums["csa_indexer_topk"].append(sum(v for _, v in ks[i:i + 4]))
+                    attn_seen = 0
+                    i += 4
+                    continue
+                if "k_attn_mfma" in n and i + 1 < len(ks) and "k_attn_combine" in ks[i + 1][0]:
+                    key = "csa_sparse_mqa_attn" if attn_seen == 0 else "hca_dense_mqa_attn"
+                    sums[key].append(ks[i][1] + ks[i + 1][1])
+                    attn_seen += 1
+                    i += 2
+                    continue
+                if "k_proj_gemv" in n:
+                    sums["out_proj (one launch)"].append(ks[i][1])
+                i += 1
+            res[cn] = {k: (float(np.mean(v[-10:])) if v else None, len(v)) for k, v in sums.items() if v}
+            if not res[cn]:                         # a --copy-calibration run
+                cp = [v for n, v in ks if "copy" in n.lower() or "elementwise" in n]
+                res[cn]["copy (per launch)"] = (float(np.median(cp)) if cp else None, len(cp))
+    print(json.dumps(res, indent=1))
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        return copy_calibration()
+    if args.summarize:
+        return summarize(args.summarize)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this path runs on a single "
               "MI355X; multi-GPU sharding is not built)", file=sys.stderr)
@@ -280,15 +425,14 @@ def main():
             f(s_, sh)
     torch.cuda.synchronize()
 
-    # calibration: one graph per call, events between them -> per-call GPU time
-    per_call_graphs = [[capture(torch, [f], s_, sh) for f in fns] for s_ in sets]
+    # calibration: events around every call of eagerly launched steps -> per-call GPU time
     ncal = max(10, min(50, args.steps))
     evc = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in CALLS]
            for _ in range(ncal)]
     for i in range(ncal):
-        for j, g in enumerate(per_call_graphs[i % R]):
+        for j, f in enumerate(fns):
             evc[i][j][0].record()
-            g.replay()
+            f(sets[i % R], sh)
             evc[i][j][1].record()
     torch.cuda.synchronize()
     per_call = {c: float(np.median([evc[i][j][0].elapsed_time(evc[i][j][1]) for i in range(ncal)]))
@@ -296,38 +440,23 @@ def main():
     dom = max(CALLS, key=lambda c: per_call[c])
     di = CALLS.index(dom)
 
-    # timed region: per step two graph launches.  A = the dominant call (events
-    # around it); B = the calls after it and, rotated in, the next step's calls
-    # before it.  The first step's leading calls run inside the timed region
-    # too, so exactly K whole steps are timed.
-    def capture_seq(pairs):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for f, s_ in pairs:
-                f(s_, sh)
-        return g
-    pre_fns, post_fns = fns[:di], fns[di + 1:]
-    g_pre = [capture_seq([(f, s_) for f in pre_fns]) if pre_fns else None for s_ in sets]
-    g_dom = [capture_seq([(fns[di], s_)]) for s_ in sets]
-    g_post = [capture_seq([(f, s_) for f in post_fns]) if post_fns else None for s_ in sets]
-    g_rot = [capture_seq([(f, sets[i]) for f in post_fns] + [(f, sets[(i + 1) % R]) for f in pre_fns])
-             if (pre_fns or post_fns) else None for i in range(R)]
+    # timed region: K whole steps launched eagerly on the current stream (the
+    # host stays ahead of the GPU, so the kernels run back to back), with a
+    # pair of events around the dominant call in every step.
     for i in range(args.warmup):
-        for g in (g_pre[i % R], g_dom[i % R], g_post[i % R]):
-            if g is not None:
-                g.replay()
+        for f in fns:
+            f(sets[i % R], sh)
     ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    if g_pre[0] is not None:
-        g_pre[0].replay()
     for i in range(args.steps):
-        ev[i][0].record()
-        g_dom[i % R].replay()
-        ev[i][1].record()
-        last = g_post[i % R] if i == args.steps - 1 else g_rot[i % R]
-        if last is not None:
-            last.replay()
+        s_ = sets[i % R]
+        for j, f in enumerate(fns):
+            if j == di:
+                ev[i][0].record()
+            f(s_, sh)
+            if j == di:
+                ev[i][1].record()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el * 1e3 / args.steps
@@ -348,16 +477,17 @@ def main():
                    "seq_len": L, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dom, "kernels": sorted(set(CALL_KERNELS[dom])),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": (TRAFFIC[dom]["bytes"] if dom in TRAFFIC and TRAFFIC[dom]["src"] == src_hash()
+                                 else None),
                      "us_per_launch": round(dom_ms * 1e3, 2), "algo_MB_per_launch": round(algo[dom] / 1e6, 3)},
         "step_hbm": {"algo_MB": round(total_algo / 1e6, 2), "gpu_us": round(gpu_ms * 1e3, 2),
                      "GBs_gpu": round(total_algo / (gpu_ms * 1e-3) / 1e9, 1),
                      "frac_gpu": round(total_algo / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "calls": calls,
-        "timing": "HIP graphs, two launches per step (the dominant call, then the rest with the next step's "
-                  "leading calls); value from the wall clock over the timed steps; roofline from events around the "
-                  "dominant call in every timed step; per-call GPU times from events around per-call graphs "
-                  "(median over a calibration pass)",
+        "timing": "eager launches on one stream, host ahead of the GPU; value from the wall clock over the "
+                  "timed steps; roofline from events around the dominant call in every timed step; per-call GPU "
+                  "times from events around every call (median over a calibration pass)",
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
