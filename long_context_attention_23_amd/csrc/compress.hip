@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
         for (int k = tid; k < a.dr; k += kCompThreads)
             reinterpret_cast<uint16_t*>(rec + dn)[k] = f32_to_bf16(sv[dn + k]);
         const int tail = dn + 2 * a.dr;
-        for (int k = tail + tid; k < a.rec_bytes; k += kCompThreads) rec[k] = 0;
+        for (int k = tail + 4 + tid; k < a.rec_bytes; k += kCompThreads) rec[k] = 0;
         if (tid == 0) *reinterpret_cast<float*>(rec + tail) = scale;
     } else {  // FP4 E2M1 indexer row with one E8M0 scale per 32 values
         const int nb = d / 32;
@@ -202,12 +202,222 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
     }
 }
 
+// Decode-latency form of the same computation, for position-only pooling
+// scores (no content projection), d % (16-byte chunk) == 0, d <= 1024 and at
+// most QR token rows per thread.  Every global load is issued up front (token
+// rows, pooling biases, gamma); each wave finds the softmax maximum and sum
+// itself; element k of the block belongs to thread k (and k + 512), so RoPE
+// pairs are lane pairs and the whole tail needs three barriers.  The
+// arithmetic and its order are those of k_compress: the softmax over biases
+// reduced by one wave's butterfly, token order inside each token group, group
+// sums in group order, per-thread square sums reduced wave by wave.
+template <typename XT, int QR>
+__global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) {
+    __shared__ float part[kCompThreads * 8];
+    __shared__ float red_ss[kCompThreads / kWave];
+    __shared__ float red_mx[kCompThreads / kWave];
+    __shared__ int se[kMaxD / 32];
+    __shared__ double rf[64];
+    constexpr int EPC = 16 / (int)sizeof(XT);
+    constexpr int KT = kMaxD / kCompThreads;              // elements per thread
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int b = blockIdx.y;
+    const int64_t i = blockIdx.x;
+    const int d = a.d, m = a.m;
+    const int64_t j = (int64_t)a.tok_start[b] / m + i;
+    if (!a.ring && j >= a.cap) return;
+    const int64_t slot = a.ring ? j % a.cap : j;
+    const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + i * m) * d;
+    const int nch = d / EPC, TG = kCompThreads / nch;
+    const int c = tid % nch, tg = tid / nch;
+
+    // ---- every load first: token rows, their biases, the wave's bias sweep, gamma
+    uint4 u[QR];
+    float br[QR];
+#pragma unroll
+    for (int q = 0; q < QR; q++) {
+        const int r = tg + q * TG;
+        const bool ok = tg < TG && r < m;
+        u[q] = ok ? *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC) : make_uint4(0u, 0u, 0u, 0u);
+        br[q] = ok ? a.sbias[r] : 0.0f;
+    }
+    float gk[KT];
+#pragma unroll
+    for (int t = 0; t < KT; t++) {
+        const int k = tid + t * kCompThreads;
+        gk[t] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
+    }
+    float zmax = -INFINITY;
+    for (int r = lane; r < m; r += kWave) zmax = fmaxf(zmax, a.sbias[r]);
+    stage_rope_arg(offsetof(CompressArgs, rope), rf, a.dr / 2);
+    zmax = wave_max(zmax);
+    float zsum = 0.0f;
+    for (int r = lane; r < m; r += kWave) zsum += expf(a.sbias[r] - zmax);
+    zsum = wave_sum(zsum);
+
+    // ---- pooled partial sums of this thread's token group
+    if (tg < TG) {
+        float acc[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; e++) acc[e] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < QR; q++) {
+            if (tg + q * TG >= m) break;
+            const float p = expf(br[q] - zmax) / zsum;
+            if constexpr (sizeof(XT) == 2) {
+                const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    acc[2 * e] = fmaf(p, __uint_as_float(wd[e] << 16), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(p, __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
+                }
+            } else {
+                acc[0] = fmaf(p, __uint_as_float(u[q].x), acc[0]);
+                acc[1] = fmaf(p, __uint_as_float(u[q].y), acc[1]);
+                acc[2] = fmaf(p, __uint_as_float(u[q].z), acc[2]);
+                acc[3] = fmaf(p, __uint_as_float(u[q].w), acc[3]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; e++) part[tg * d + c * EPC + e] = acc[e];
+    }
+    __syncthreads();                                      // barrier 1: partials (and the RoPE table)
+    const int tgu = m < TG ? m : TG;                      // token groups that hold rows
+    float v[KT];
+    float ss = 0.0f;
+#pragma unroll
+    for (int t = 0; t < KT; t++) {
+        const int k = tid + t * kCompThreads;
+        v[t] = 0.0f;
+        if (k < d) {
+            for (int q = 0; q < tgu; q++) v[t] += part[q * d + k];
+            ss += v[t] * v[t];
+        }
+    }
+    if (a.gamma) {                                        // RMSNorm
+        ss = wave_sum(ss);
+        if (lane == 0) red_ss[wv] = ss;
+        __syncthreads();                                  // barrier 2
+        float tot = 0.0f;
+        for (int w = 0; w < kCompThreads / kWave; w++) tot += red_ss[w];
+        const float inv = 1.0f / sqrtf(tot / (float)d + a.eps);
+#pragma unroll
+        for (int t = 0; t < KT; t++) v[t] = v[t] * inv * gk[t];
+    }
+    // ---- RoPE at j*m on the last dr dims: the pair (off + 2p, off + 2p + 1) is a lane pair
+    const int off = d - a.dr;
+#pragma unroll
+    for (int t = 0; t < KT; t++) {
+        const int k = tid + t * kCompThreads;
+        const float other = __shfl_xor(v[t], 1, kWave);
+        if (k < d && k >= off) {
+            float sn, cs;
+            rope_sincos((double)(j * m), rf[(k - off) >> 1], sn, cs);
+            const bool odd = (k - off) & 1;
+            const float x0 = odd ? other : v[t], x1 = odd ? v[t] : other;
+            v[t] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
+        }
+    }
+
+    // ---- quantise into the output record
+    const size_t rrow = (size_t)b * a.cap + slot;
+    uint8_t* rec = a.out + rrow * a.rec_bytes;
+    if (a.fmt == CSA_F32) {
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int k = tid + t * kCompThreads;
+            if (k < d) reinterpret_cast<float*>(rec)[k] = v[t];
+        }
+    } else if (a.fmt == CSA_BF16) {
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int k = tid + t * kCompThreads;
+            if (k < d) reinterpret_cast<uint16_t*>(rec)[k] = f32_to_bf16(v[t]);
+        }
+    } else if (a.fmt == CSA_FP8_E4M3) {
+        const int dn = d - a.dr;
+        float amax = 0.0f;
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int k = tid + t * kCompThreads;
+            if (k < dn) amax = fmaxf(amax, fabsf(v[t]));
+        }
+        amax = wave_max(amax);
+        if (lane == 0) red_mx[wv] = amax;
+        __syncthreads();                                  // barrier 3
+        amax = red_mx[0];
+        for (int w = 1; w < kCompThreads / kWave; w++) amax = fmaxf(amax, red_mx[w]);
+        const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int k = tid + t * kCompThreads;
+            if (k < dn) rec[k] = f32_to_e4m3(v[t] / scale);
+            else if (k < d) reinterpret_cast<uint16_t*>(rec + dn)[k - dn] = f32_to_bf16(v[t]);
+        }
+        const int tail = dn + 2 * a.dr;
+        for (int k = tail + 4 + tid; k < a.rec_bytes; k += kCompThreads) rec[k] = 0;
+        if (tid == 0) *reinterpret_cast<float*>(rec + tail) = scale;
+    } else {  // FP4 E2M1 indexer row with one E8M0 scale per 32 values (32 consecutive lanes)
+        const int nb = d / 32;
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int k = tid + t * kCompThreads;
+            float bm = k < d ? fabsf(v[t]) : 0.0f;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, kWave));
+            if (k < d && (k & 31) == 0) {
+                int e = INT32_MIN;
+                if (bm > 0.0f) {
+                    int ex;
+                    frexpf(bm, &ex);                      // bm in [2^(ex-1), 2^ex)
+                    e = ex - 1 - 2;
+                }
+                se[k >> 5] = e;
+            }
+        }
+        __syncthreads();                                  // barrier 3
+        int emax = INT32_MIN;
+        for (int q = 0; q < nb; q++) emax = max(emax, se[q]);
+#pragma unroll
+        for (int t = 0; t < KT; t++) {
+            const int k = tid + t * kCompThreads;
+            int e = 0;
+            if (k < d) {
+                e = se[k >> 5];
+                if (emax == INT32_MIN) e = 0;             // all-zero row
+                else e = max(e, emax - 14);               // keep FP4 -> FP8 lossless
+                e = min(max(e, -127), 127);
+                if ((k & 31) == 0) a.out_scales[rrow * nb + (k >> 5)] = (uint8_t)(e + 127);
+            }
+            const uint32_t code = k < d ? f32_to_e2m1(ldexpf(v[t], -e)) : 0u;
+            const uint32_t hi = __shfl_xor(code, 1, kWave);
+            if (k < d && (k & 1) == 0) rec[k >> 1] = (uint8_t)(code | (hi << 4));
+        }
+    }
+}
+
+template <typename XT>
+static void launch_compress_t(const CompressArgs& a, dim3 grid, hipStream_t st) {
+    constexpr int EPC = 16 / (int)sizeof(XT);
+    const int nch = a.d / EPC;
+    const bool fast = !a.sproj && a.d % EPC == 0 && a.d <= kMaxD && nch <= kCompThreads && a.dr % 2 == 0 &&
+                      (a.d - a.dr) % 2 == 0 && a.d % 32 == 0;
+    const int TG = fast ? kCompThreads / nch : 1;
+    const int qr = (a.m + TG - 1) / TG;
+    if (fast && qr <= 1) hipLaunchKernelGGL((k_compress_fast<XT, 1>), grid, dim3(kCompThreads), 0, st, a);
+    else if (fast && qr <= 2) hipLaunchKernelGGL((k_compress_fast<XT, 2>), grid, dim3(kCompThreads), 0, st, a);
+    else if (fast && qr <= 4) hipLaunchKernelGGL((k_compress_fast<XT, 4>), grid, dim3(kCompThreads), 0, st, a);
+    else if (fast && qr <= 8) hipLaunchKernelGGL((k_compress_fast<XT, 8>), grid, dim3(kCompThreads), 0, st, a);
+    else if (fast && qr <= 16) hipLaunchKernelGGL((k_compress_fast<XT, 16>), grid, dim3(kCompThreads), 0, st, a);
+    else hipLaunchKernelGGL(k_compress<XT>, grid, dim3(kCompThreads), 0, st, a);
+}
+
 hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st) {
     int64_t nblk = a.T / a.m;
     if (nblk == 0 || a.B == 0) return hipSuccess;
     dim3 grid((unsigned)nblk, (unsigned)a.B);
-    if (x_dtype == CSA_F32) hipLaunchKernelGGL(k_compress<float>, grid, dim3(kCompThreads), 0, st, a);
-    else hipLaunchKernelGGL(k_compress<uint16_t>, grid, dim3(kCompThreads), 0, st, a);
+    if (x_dtype == CSA_F32) launch_compress_t<float>(a, grid, st);
+    else launch_compress_t<uint16_t>(a, grid, st);
     return hipGetLastError();
 }
 

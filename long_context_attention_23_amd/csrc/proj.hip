@@ -8,10 +8,11 @@
 // Two kernels, both keeping every reduction inside one workgroup (no split
 // across workgroups, fixed summation order):
 //   decode (M <= 16): weight streaming.  The group's M activation rows sit in
-//     LDS; each wave walks 16 / M weight rows with 16-byte coalesced loads
-//     (every weight byte read once), accumulates M x rows dot products per
-//     lane (bf16 pairs through v_dot2_f32_bf16), and reduces the 16 partial
-//     sums across the wave by recursive halving (17 lane exchanges);
+//     LDS; the group's weight rows are dealt round-robin to its waves, which
+//     read them with 16-byte coalesced loads (every weight byte read once),
+//     accumulate M x rows dot products per lane (bf16 pairs through
+//     v_dot2_f32_bf16), and reduce the partial sums across the wave by
+//     recursive halving;
 //   otherwise: a TM x TN tile of y per workgroup, walking the reduction
 //     dimension in KC-wide slabs staged in LDS.
 #include "common.hpp"
@@ -101,11 +102,16 @@ __device__ __forceinline__ float chunk_dot<float>(uint4 w, uint4 o, float acc) {
     return acc;
 }
 
-// sum v[0..16) over the 64 lanes; lane 4j..4j+3 end with the total of value j
-__device__ __forceinline__ float wave_reduce16(float* v) {
+// Sum each of v[0..NV) over the 64 lanes (NV a power of two, at most 64):
+// log2(NV) halving exchanges leave one value per lane group, then plain
+// butterflies finish; value j ends in lanes [j * 64 / NV, (j + 1) * 64 / NV).
+template <int NV>
+__device__ __forceinline__ float wave_reduce_n(float* v) {
+    static_assert(NV >= 1 && NV <= 64 && (NV & (NV - 1)) == 0, "NV must be a power of two <= 64");
     const int lane = threadIdx.x & 63;
+    int b = 32;
 #pragma unroll
-    for (int b = 32, n = 16; b >= 4; b >>= 1, n >>= 1) {
+    for (int n = NV; n > 1; n >>= 1, b >>= 1) {
         const bool hi = (lane & b) != 0;
 #pragma unroll
         for (int i = 0; i < n / 2; i++) {
@@ -115,46 +121,62 @@ __device__ __forceinline__ float wave_reduce16(float* v) {
         }
     }
     float r = v[0];
-    r += __shfl_xor(r, 2, 64);
-    r += __shfl_xor(r, 1, 64);
+#pragma unroll
+    for (; b >= 1; b >>= 1) r += __shfl_xor(r, b, 64);
     return r;
 }
 
 constexpr int kGemvLdsBytes = 65536;
 
-template <typename T, typename YT, int MR>
-__global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
-    constexpr int R = 16 / MR;                 // weight rows per wave
+// Decode projection, M <= 16 activation rows.  Workgroup = NW waves of one
+// group g; the group's M activation rows are staged in LDS once.  The group's
+// dg weight rows are dealt to its waves round-robin: wave v of the group
+// (V waves per group) takes rows v, v + V, v + 2V, ... (RT rows), so the grid
+// streams one compact band of every group's weights at a time instead of
+// scattering over all of them.  A wave walks its rows in batches of RB, the
+// next batch's 16-byte loads in flight while the current one is reduced
+// (lane l takes chunks l + 64 it of a row); weights are read once, with
+// non-temporal loads since nothing reuses them.  kFull: the row length is a
+// whole number of passes, so no load or product needs a bounds test (which
+// would otherwise make every wait a full drain).
+template <typename T, typename YT, int MR, int RT, int RB, int NW, bool kFull>
+__global__ __launch_bounds__(64 * NW) void k_proj_gemv(ProjArgs a) {
     constexpr int EPC = 16 / sizeof(T);        // elements per 16-byte chunk
+    constexpr int NV = RT * MR;
+    constexpr int NB = RT / RB;
+    static_assert(RT % RB == 0, "row batches must tile the wave's rows");
     extern __shared__ uint4 osm[];             // [MR][chunks of the group's activation row]
     const int dg = a.D / a.G, cg = a.Hd / a.G;
     const int nch = cg / EPC;
-    const int rows_wg = 4 * R;
-    const int tpg = dg / rows_wg;
-    const int g = blockIdx.x / tpg;
-    const int i0 = (blockIdx.x % tpg) * rows_wg;
-    const T* o = reinterpret_cast<const T*>(a.o);
-    const T* W = reinterpret_cast<const T*>(a.W);
+    const int V = dg / RT;                     // waves per group
+    // consecutive workgroups take different groups: workgroups are dealt to
+    // the 8 XCDs round-robin, so with G = 8 all of group g runs on one XCD
+    const int g = blockIdx.x % a.G;
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r0 = i0 + w * R;
-    const T* wr = W + ((size_t)g * dg + r0) * cg;
-    // weight chunks are loaded in batches of kIt per lane; the first batch goes
-    // out before the activations are staged, so both sets of loads are in
-    // flight together
-    constexpr int kIt = (32 / R) < 8 ? (32 / R) : 8;
-    float acc[R * MR];
+    const int v = (blockIdx.x / a.G) * NW + w;
+    const T* o = reinterpret_cast<const T*>(a.o);
+    const T* W = reinterpret_cast<const T*>(a.W) + ((size_t)g * dg + v) * cg;
+    constexpr int kIt = RB <= 2 ? 8 : 16 / RB;  // chunks per lane per row and pass
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    float acc[NV];
 #pragma unroll
-    for (int q = 0; q < R * MR; q++) acc[q] = 0.0f;
+    for (int q = 0; q < NV; q++) acc[q] = 0.0f;
     for (int cb = 0; cb < nch; cb += 64 * kIt) {
-        uint4 wv[kIt][R];
+        v4u wv[2][RB][kIt];                    // ping-pong batch buffers
+        auto issue = [&](v4u (&dst)[RB][kIt], int bt) {
 #pragma unroll
-        for (int it = 0; it < kIt; it++) {
-            const int c = cb + lane + 64 * it;
+            for (int r = 0; r < RB; r++) {
 #pragma unroll
-            for (int r = 0; r < R; r++)
-                wv[it][r] = c < nch ? *reinterpret_cast<const uint4*>(wr + (size_t)r * cg + (size_t)c * EPC)
-                                    : make_uint4(0u, 0u, 0u, 0u);
-        }
+                for (int it = 0; it < kIt; it++) {
+                    const int c = cb + lane + 64 * it;
+                    const size_t row = (size_t)(bt * RB + r) * V;
+                    dst[r][it] = kFull || c < nch ? __builtin_nontemporal_load(
+                                               reinterpret_cast<const v4u*>(W + row * cg + (size_t)c * EPC))
+                                         : v4u{0u, 0u, 0u, 0u};
+                }
+            }
+        };
+        issue(wv[0], 0);
         if (cb == 0) {
             for (int idx = threadIdx.x; idx < MR * nch; idx += blockDim.x) {
                 const int m = idx / nch, c = idx % nch;
@@ -164,44 +186,64 @@ __global__ __launch_bounds__(256) void k_proj_gemv(ProjArgs a) {
             __syncthreads();
         }
 #pragma unroll
-        for (int it = 0; it < kIt; it++) {
-            const int c = cb + lane + 64 * it;
-            if (c < nch) {
+        for (int bt = 0; bt < NB; bt++) {
+            if (bt + 1 < NB) issue(wv[(bt + 1) & 1], bt + 1);
 #pragma unroll
-                for (int m = 0; m < MR; m++) {
-                    const uint4 ov = osm[m * nch + c];
+            for (int it = 0; it < kIt; it++) {
+                const int c = cb + lane + 64 * it;
+                if (kFull || c < nch) {
 #pragma unroll
-                    for (int r = 0; r < R; r++) acc[r * MR + m] = chunk_dot<T>(wv[it][r], ov, acc[r * MR + m]);
+                    for (int m = 0; m < MR; m++) {
+                        const uint4 ov = osm[m * nch + c];
+#pragma unroll
+                        for (int r = 0; r < RB; r++) {
+                            const v4u x = wv[bt & 1][r][it];
+                            const int q = (bt * RB + r) * MR + m;
+                            acc[q] = chunk_dot<T>(make_uint4(x[0], x[1], x[2], x[3]), ov, acc[q]);
+                        }
+                    }
                 }
             }
         }
     }
-    const float tot = wave_reduce16(acc);
-    if ((lane & 3) == 0) {
-        const int j = lane >> 2, r = j / MR, m = j % MR;
-        if (m < a.M) st_scalar<YT>(reinterpret_cast<YT*>(a.y), (size_t)m * a.D + (size_t)g * dg + r0 + r, tot);
+    const float tot = wave_reduce_n<NV>(acc);
+    if ((lane & (64 / NV - 1)) == 0) {
+        const int j = lane / (64 / NV), r = j / MR, m = j % MR;
+        if (m < a.M) st_scalar<YT>(reinterpret_cast<YT*>(a.y), (size_t)m * a.D + (size_t)g * dg + v + r * V, tot);
     }
+}
+
+// Launch shape, measured on the 8 x [896 x 4096] bf16 decode projection: two
+// rows per wave, one row per batch, eight waves per workgroup (448
+// workgroups) beat fewer, longer waves or all loads in flight at once.
+constexpr int kGemvRows = 2, kGemvBatch = 1, kGemvWaves = 8;
+
+template <typename T, typename YT, int MR>
+static bool launch_gemv(const ProjArgs& a, hipStream_t st) {
+    constexpr int RT = kGemvRows, RB = kGemvBatch, NW = kGemvWaves;
+    const int dg = a.D / a.G, cg = a.Hd / a.G;
+    const size_t lds = (size_t)MR * cg * sizeof(T);
+    if (dg % (NW * RT) || lds > (size_t)kGemvLdsBytes) return false;
+    const unsigned grid = (unsigned)(a.G * (dg / (NW * RT)));
+    constexpr int kIt = RB <= 2 ? 8 : 16 / RB;
+    if ((cg / (16 / (int)sizeof(T))) % (64 * kIt) == 0)
+        hipLaunchKernelGGL((k_proj_gemv<T, YT, MR, RT, RB, NW, true>), dim3(grid), dim3(64 * NW), lds, st, a);
+    else
+        hipLaunchKernelGGL((k_proj_gemv<T, YT, MR, RT, RB, NW, false>), dim3(grid), dim3(64 * NW), lds, st, a);
+    return true;
 }
 
 template <typename T, typename YT>
 static bool try_gemv(const ProjArgs& a, hipStream_t st) {
-    const int dg = a.D / a.G, cg = a.Hd / a.G;
+    const int cg = a.Hd / a.G;
     const int EPC = 16 / (int)sizeof(T);
     if (a.M > 16 || cg % EPC) return false;
-    const int MR = a.M <= 1 ? 1 : a.M <= 2 ? 2 : a.M <= 4 ? 4 : a.M <= 8 ? 8 : 16;
-    const int rows_wg = 4 * (16 / MR);
-    const size_t lds = (size_t)MR * cg * sizeof(T);
-    if (dg % rows_wg || lds > (size_t)kGemvLdsBytes) return false;
     if (((uintptr_t)a.o | (uintptr_t)a.W) & 15) return false;
-    const unsigned grid = (unsigned)(a.G * (dg / rows_wg));
-    switch (MR) {
-        case 1: hipLaunchKernelGGL((k_proj_gemv<T, YT, 1>), dim3(grid), dim3(256), lds, st, a); break;
-        case 2: hipLaunchKernelGGL((k_proj_gemv<T, YT, 2>), dim3(grid), dim3(256), lds, st, a); break;
-        case 4: hipLaunchKernelGGL((k_proj_gemv<T, YT, 4>), dim3(grid), dim3(256), lds, st, a); break;
-        case 8: hipLaunchKernelGGL((k_proj_gemv<T, YT, 8>), dim3(grid), dim3(256), lds, st, a); break;
-        default: hipLaunchKernelGGL((k_proj_gemv<T, YT, 16>), dim3(grid), dim3(256), lds, st, a); break;
-    }
-    return true;
+    if (a.M <= 1) return launch_gemv<T, YT, 1>(a, st);
+    if (a.M <= 2) return launch_gemv<T, YT, 2>(a, st);
+    if (a.M <= 4) return launch_gemv<T, YT, 4>(a, st);
+    if (a.M <= 8) return launch_gemv<T, YT, 8>(a, st);
+    return launch_gemv<T, YT, 16>(a, st);
 }
 
 template <typename T, typename YT>

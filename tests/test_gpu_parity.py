@@ -72,18 +72,23 @@ def decoded(kind, fmt, codes, scales, d, dr):
     return O.idx_decode(codes, scales, fmt, d)
 
 
-@pytest.mark.parametrize("kind,fmt,m,dr,xfmt,ring", [
-    (0, O.FP8_E4M3, 4, 64, O.BF16, False), (0, O.BF16, 128, 64, O.BF16, False), (0, O.F32, 4, 64, O.F32, False),
-    (0, O.FP8_E4M3, 1, 64, O.BF16, True), (0, O.F32, 3, 16, O.F32, True), (1, O.FP4_E2M1, 4, 0, O.BF16, False),
-    (1, O.BF16, 4, 0, O.F32, False), (1, O.F32, 128, 0, O.F32, False)])
-def test_compress_pooled_within_one_code(kind, fmt, m, dr, xfmt, ring):
-    g = synth.rng(400 + m + fmt + 7 * kind)
+@pytest.mark.parametrize("kind,fmt,m,dr,xfmt,ring,content", [
+    (0, O.FP8_E4M3, 4, 64, O.BF16, False, True), (0, O.BF16, 128, 64, O.BF16, False, False),
+    (0, O.F32, 4, 64, O.F32, False, True), (0, O.FP8_E4M3, 1, 64, O.BF16, True, False),
+    (0, O.F32, 3, 16, O.F32, True, True), (1, O.FP4_E2M1, 4, 0, O.BF16, False, True),
+    (1, O.BF16, 4, 0, O.F32, False, True), (1, O.F32, 128, 0, O.F32, False, False),
+    # position-only scores: the latency-oriented kernel (all loads first, lane-pair RoPE)
+    (0, O.FP8_E4M3, 4, 64, O.BF16, False, False), (0, O.FP8_E4M3, 128, 64, O.BF16, False, False),
+    (0, O.FP8_E4M3, 16, 64, O.F32, True, False), (1, O.FP4_E2M1, 4, 0, O.BF16, False, False),
+    (1, O.FP4_E2M1, 128, 0, O.BF16, False, False), (0, O.FP8_E4M3, 200, 64, O.BF16, False, False)])
+def test_compress_pooled_within_one_code(kind, fmt, m, dr, xfmt, ring, content):
+    g = synth.rng(400 + m + fmt + 7 * kind + 1000 * content)
     d = 512 if kind == 0 and fmt != O.F32 else (64 if kind == 1 else 128)
     B = 3
     T = m * 5 + (m - 1 if m > 1 else 0)                # ragged tail ignored
     x = synth.normal(g, (B, T, d))
     b = synth.normal(g, m)
-    u = synth.normal(g, d) * np.float32(0.05) if m in (3, 4) else None
+    u = synth.normal(g, d) * np.float32(0.05) if content else None
     gamma = (1 + 0.2 * synth.normal(g, d)).astype(np.float32) if kind == 0 else None
     tok = [0, m * 3, m * 1000]
     cap = 7 if ring else 1010
@@ -347,7 +352,9 @@ def test_attention_deterministic_and_batch_invariant():
 
 # ====================================================================== projection
 @pytest.mark.parametrize("M,H,d,D,G,fmt", [(2048, 8, 128, 1024, 8, O.F32), (4, 64, 512, 7168, 8, O.BF16),
-                                           (16, 32, 512, 4096, 8, O.BF16), (37, 6, 40, 96, 3, O.F32)])
+                                           (16, 32, 512, 4096, 8, O.BF16), (37, 6, 40, 96, 3, O.F32),
+                                           (1, 16, 256, 1024, 4, O.F32), (8, 64, 512, 7168, 8, O.BF16),
+                                           (2, 8, 128, 384, 2, O.BF16), (3, 8, 64, 200, 8, O.BF16)])
 def test_projection_parity(M, H, d, D, G, fmt):
     g = synth.rng(700 + M)
     Hd = H * d
