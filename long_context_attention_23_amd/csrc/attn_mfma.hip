@@ -300,27 +300,6 @@ __device__ __forceinline__ uint2 lds_read_tr8(const void* p) {
 // (row pitch = 4 banks mod 32: offsets 0, 8, 16, 24 banks)
 __device__ __forceinline__ int pv_k_of_entry(int e) { return (e & ~7) + 4 * (e & 1) + ((e & 7) >> 1); }
 
-// all-reduce over the 16 lanes of a DPP row (rotations, then quad swaps);
-// commutative steps give every lane the same bits
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, dpp_f<0x128>(v));     // row_ror:8
-    v = fmaxf(v, dpp_f<0x124>(v));     // row_ror:4
-    v = fmaxf(v, dpp_f<0x4E>(v));      // quad_perm [2,3,0,1]
-    v = fmaxf(v, dpp_f<0xB1>(v));      // quad_perm [1,0,3,2]
-    return v;
-}
-__device__ __forceinline__ float row16_sum(float v) {
-    v = v + dpp_f<0x128>(v);
-    v = v + dpp_f<0x124>(v);
-    v = v + dpp_f<0x4E>(v);
-    v = v + dpp_f<0xB1>(v);
-    return v;
-}
-
 template <int D, int DR, bool F8, typename OT>
 __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_max) {
     constexpr int DQ = D / 4;              // dims per quarter

@@ -94,6 +94,13 @@ __device__ __forceinline__ void stage_rope_arg(size_t offset, double* lds, int n
     if ((int)threadIdx.x < npairs) lds[threadIdx.x] = t[threadIdx.x];
 }
 
+// the p-th frequency of a RopeTable passed by value at byte `offset` of the
+// kernel arguments, read by one lane from the argument segment
+__device__ __forceinline__ double rope_freq_arg(size_t offset, int p) {
+    return ((const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offset))[p];
+}
+
+
 // sin and cos of pos * freq.  The angle is reduced in fp64 around the
 // nearest multiple k of pi/2 (Cody-Waite: pi/2 as a double plus the double
 // nearest its remainder, fused multiply-adds) to r in [-pi/4, pi/4]; sin r and
@@ -135,6 +142,45 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
     return v;
+}
+
+// all-reduce over the 16 lanes of a DPP row (rotations, then quad swaps);
+// commutative steps give every lane the same bits
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, dpp_f<0x128>(v));     // row_ror:8
+    v = fmaxf(v, dpp_f<0x124>(v));     // row_ror:4
+    v = fmaxf(v, dpp_f<0x4E>(v));      // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_f<0xB1>(v));      // quad_perm [1,0,3,2]
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+    v = v + dpp_f<0x128>(v);
+    v = v + dpp_f<0x124>(v);
+    v = v + dpp_f<0x4E>(v);
+    v = v + dpp_f<0xB1>(v);
+    return v;
+}
+// the same over all 64 lanes: the four row results are read as scalars and
+// combined as (r0 + r1) + (r2 + r3); no LDS round trips
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+    v = row16_sum(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    v = row16_max(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 // block-wide reductions; `red` is LDS scratch of >= blockDim/64 floats

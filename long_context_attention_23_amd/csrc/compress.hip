@@ -207,31 +207,33 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
 // most QR token rows per thread.  Every global load is issued up front (token
 // rows, pooling biases, gamma); each wave finds the softmax maximum and sum
 // itself; element k of the block belongs to thread k (and k + 512), so RoPE
-// pairs are lane pairs and the whole tail needs three barriers.  The
-// arithmetic and its order are those of k_compress: the softmax over biases
-// reduced by one wave's butterfly, token order inside each token group, group
-// sums in group order, per-thread square sums reduced wave by wave.
+// pairs are lane pairs and the whole tail needs three barriers.  The RoPE
+// frequencies come straight from the argument segment, and the destination
+// slot (which depends on the sequence's token start) is found after the loads
+// are out, so the block costs one memory round trip before its arithmetic.  The
+// arithmetic is that of k_compress (token order inside each token group,
+// group sums in group order); the softmax sum and the square sums are reduced
+// in DPP row order instead of a butterfly, so the last bits may differ.
 template <typename XT, int QR>
 __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) {
     __shared__ float part[kCompThreads * 8];
     __shared__ float red_ss[kCompThreads / kWave];
     __shared__ float red_mx[kCompThreads / kWave];
     __shared__ int se[kMaxD / 32];
-    __shared__ double rf[64];
     constexpr int EPC = 16 / (int)sizeof(XT);
     constexpr int KT = kMaxD / kCompThreads;              // elements per thread
+    constexpr int SB = 2 * QR < 16 ? 2 * QR : 16;        // pooling biases per lane (m <= 64 SB)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int b = blockIdx.y;
-    const int64_t i = blockIdx.x;
+    const int i = blockIdx.x;
     const int d = a.d, m = a.m;
-    const int64_t j = (int64_t)a.tok_start[b] / m + i;
-    if (!a.ring && j >= a.cap) return;
-    const int64_t slot = a.ring ? j % a.cap : j;
-    const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + i * m) * d;
+    const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + (int64_t)i * m) * d;
     const int nch = d / EPC, TG = kCompThreads / nch;
     const int c = tid % nch, tg = tid / nch;
+    const int off = d - a.dr;
 
-    // ---- every load first: token rows, their biases, the wave's bias sweep, gamma
+    // ---- every load first: token rows and their biases, the lane's share of
+    // all biases, gamma and the RoPE frequencies of this thread's elements
     uint4 u[QR];
     float br[QR];
 #pragma unroll
@@ -241,19 +243,31 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
         u[q] = ok ? *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC) : make_uint4(0u, 0u, 0u, 0u);
         br[q] = ok ? a.sbias[r] : 0.0f;
     }
+    float sb[SB];
+#pragma unroll
+    for (int s = 0; s < SB; s++) sb[s] = lane + s * kWave < m ? a.sbias[lane + s * kWave] : -INFINITY;
     float gk[KT];
+    double fk[KT];
 #pragma unroll
     for (int t = 0; t < KT; t++) {
         const int k = tid + t * kCompThreads;
         gk[t] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
+        fk[t] = (k < d && k >= off) ? rope_freq_arg(offsetof(CompressArgs, rope), (k - off) >> 1) : 0.0;
     }
+    const int64_t j = (int64_t)(a.tok_start[b] / m) + i;
+    if (!a.ring && j >= a.cap) return;
+    const int64_t slot = a.ring ? j % a.cap : j;
+
+    // ---- softmax of the biases: every wave reduces the same values itself
     float zmax = -INFINITY;
-    for (int r = lane; r < m; r += kWave) zmax = fmaxf(zmax, a.sbias[r]);
-    stage_rope_arg(offsetof(CompressArgs, rope), rf, a.dr / 2);
-    zmax = wave_max(zmax);
+#pragma unroll
+    for (int s = 0; s < SB; s++) zmax = fmaxf(zmax, sb[s]);
+    zmax = wave_max_dpp(zmax);
     float zsum = 0.0f;
-    for (int r = lane; r < m; r += kWave) zsum += expf(a.sbias[r] - zmax);
-    zsum = wave_sum(zsum);
+#pragma unroll
+    for (int s = 0; s < SB; s++)
+        if (lane + s * kWave < m) zsum += expf(sb[s] - zmax);
+    zsum = wave_sum_dpp(zsum);
 
     // ---- pooled partial sums of this thread's token group
     if (tg < TG) {
@@ -281,7 +295,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
 #pragma unroll
         for (int e = 0; e < EPC; e++) part[tg * d + c * EPC + e] = acc[e];
     }
-    __syncthreads();                                      // barrier 1: partials (and the RoPE table)
+    __syncthreads();                                      // barrier 1: partials
     const int tgu = m < TG ? m : TG;                      // token groups that hold rows
     float v[KT];
     float ss = 0.0f;
@@ -295,7 +309,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
         }
     }
     if (a.gamma) {                                        // RMSNorm
-        ss = wave_sum(ss);
+        ss = wave_sum_dpp(ss);
         if (lane == 0) red_ss[wv] = ss;
         __syncthreads();                                  // barrier 2
         float tot = 0.0f;
@@ -305,14 +319,13 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
         for (int t = 0; t < KT; t++) v[t] = v[t] * inv * gk[t];
     }
     // ---- RoPE at j*m on the last dr dims: the pair (off + 2p, off + 2p + 1) is a lane pair
-    const int off = d - a.dr;
 #pragma unroll
     for (int t = 0; t < KT; t++) {
         const int k = tid + t * kCompThreads;
         const float other = __shfl_xor(v[t], 1, kWave);
         if (k < d && k >= off) {
             float sn, cs;
-            rope_sincos((double)(j * m), rf[(k - off) >> 1], sn, cs);
+            rope_sincos((double)(j * m), fk[t], sn, cs);
             const bool odd = (k - off) & 1;
             const float x0 = odd ? other : v[t], x1 = odd ? v[t] : other;
             v[t] = odd ? x0 * sn + x1 * cs : x0 * cs - x1 * sn;
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
             const int k = tid + t * kCompThreads;
             if (k < dn) amax = fmaxf(amax, fabsf(v[t]));
         }
-        amax = wave_max(amax);
+        amax = wave_max_dpp(amax);
         if (lane == 0) red_mx[wv] = amax;
         __syncthreads();                                  // barrier 3
         amax = red_mx[0];
@@ -400,10 +413,12 @@ template <typename XT>
 static void launch_compress_t(const CompressArgs& a, dim3 grid, hipStream_t st) {
     constexpr int EPC = 16 / (int)sizeof(XT);
     const int nch = a.d / EPC;
-    const bool fast = !a.sproj && a.d % EPC == 0 && a.d <= kMaxD && nch <= kCompThreads && a.dr % 2 == 0 &&
-                      (a.d - a.dr) % 2 == 0 && a.d % 32 == 0;
-    const int TG = fast ? kCompThreads / nch : 1;
+    const bool fast0 = !a.sproj && a.d % EPC == 0 && a.d <= kMaxD && nch <= kCompThreads && a.dr % 2 == 0 &&
+                       (a.d - a.dr) % 2 == 0 && a.d % 32 == 0;
+    const int TG = fast0 ? kCompThreads / nch : 1;
     const int qr = (a.m + TG - 1) / TG;
+    const int sb = qr <= 1 ? 2 : qr <= 2 ? 4 : qr <= 4 ? 8 : 16;        // SB of the kernel picked below
+    const bool fast = fast0 && a.m <= kWave * sb;
     if (fast && qr <= 1) hipLaunchKernelGGL((k_compress_fast<XT, 1>), grid, dim3(kCompThreads), 0, st, a);
     else if (fast && qr <= 2) hipLaunchKernelGGL((k_compress_fast<XT, 2>), grid, dim3(kCompThreads), 0, st, a);
     else if (fast && qr <= 4) hipLaunchKernelGGL((k_compress_fast<XT, 4>), grid, dim3(kCompThreads), 0, st, a);

@@ -21,10 +21,12 @@
 //   C  every chunk finds the threshold bin from that histogram and appends
 //      keys above it to the row's "selected" list and keys in it to the
 //      "candidate" list (wave-aggregated appends);
-//   D  one workgroup per row radix-selects the remaining count among the
-//      candidates (8-bit digits over the composite), then bitonic-sorts the k
-//      block indices.  The append order of A/C does not matter: D's result
-//      depends only on the sets.
+//   D  one workgroup per row finds the threshold score suffix among the
+//      candidates (two 10-bit digit passes), takes the tied ones at it by
+//      smallest block index, and emits the k blocks in ascending order from
+//      LDS bitmaps (caps beyond 2^19: composite radix select and a bitonic
+//      sort).  The append order of A/C does not matter: D's result depends
+//      only on the sets.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -315,7 +317,7 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_i __attribute__((ext_vector_type(8)));
 
-constexpr int kIdxScoreThreads = 512;   // 8 waves: every FP4 key load of a chunk in flight at once
+constexpr int kIdxScoreThreads = 1024;  // 16 waves, four 32-key groups each (measured faster than 8 x 8)
 
 // Score a chunk of 64-dim keys with the matrix cores.  C[head][key] = Q K^T:
 // the query's Hi rows are the A operand (32 rows, rows >= Hi zero), 32 keys
@@ -523,17 +525,111 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     }
 }
 
-constexpr int kIdxBitmapWords = 16384;   // LDS bitmap of selected blocks (caps up to 2^19)
+constexpr int kIdxBitmapWords = 16384;   // words per LDS bitmap of blocks (caps up to 2^19)
+constexpr int kIdxFinalLds = 4096;       // candidates kept in LDS across the digit passes
+constexpr int kIdxDigitBins = 1024;      // 10-bit digits of the 20-bit score suffix
 
-constexpr int kIdxFinalLds = 4096;       // candidates kept in LDS across the radix passes
+// wave_pick_digit over 1024 bins (16 per lane, lane 0 holding the top ones)
+__device__ __forceinline__ void wave_pick_digit1024(const uint32_t* hist, uint32_t need, uint32_t& digit,
+                                                    uint32_t& above) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int per = kIdxDigitBins / kWave;
+    uint32_t h[per], s = 0;
+#pragma unroll
+    for (int q = 0; q < per; q++) { h[q] = hist[kIdxDigitBins - 1 - per * lane - q]; s += h[q]; }
+    uint32_t incl = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    const uint64_t bal = __ballot(incl >= need);
+    const int L = bal ? __builtin_ctzll(bal) : kWave - 1;
+    const uint32_t cum = __shfl(incl - s, L, kWave);
+    uint32_t d = 0, ab = cum;
+    if (lane == L) {
+        uint32_t c = cum;
+        d = kIdxDigitBins - per * (L + 1);
+        for (int q = 0; q < per; q++) {
+            if (c + h[q] >= need) { d = kIdxDigitBins - 1 - per * L - q; ab = c; break; }
+            c += h[q];
+        }
+    }
+    digit = __shfl(d, L, kWave);
+    above = __shfl(ab, L, kWave);
+}
 
+// histogram of the 10-bit digit (key >> shift) & 1023 over the candidates
+// whose upper digit equals `upper` (all of them when !filt); a wave whose
+// lanes mostly share one digit (tied scores) adds once per distinct digit
+__device__ __forceinline__ void digit_hist(const uint2* cand, uint32_t ncand, int shift, bool filt, uint32_t upper,
+                                           uint32_t* hist) {
+    for (uint32_t i0 = 0; i0 < ncand; i0 += blockDim.x) {     // block-uniform rounds: complete ballots
+        const uint32_t i = i0 + threadIdx.x;
+        const uint32_t key = i < ncand ? cand[i].x : 0u;
+        const bool in = i < ncand && (!filt || ((key >> 10) & 1023u) == upper);
+        const uint32_t dg = (key >> shift) & 1023u;
+        const uint64_t act = __ballot(in);
+        const uint32_t d0 = __shfl(dg, act ? __builtin_ctzll(act) : 0, kWave);
+        if (__popcll(__ballot(in && dg == d0)) > 8) {
+            uint64_t todo = act;
+            while (todo) {
+                const int leader = __builtin_ctzll(todo);
+                const uint32_t dl = __shfl(dg, leader, kWave);
+                const uint64_t same = __ballot(in && dg == dl) & todo;
+                if ((int)(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+                todo &= ~same;
+            }
+        } else if (in) {
+            atomicAdd(&hist[dg], 1u);
+        }
+    }
+}
+
+// the lowest k set bits of `bits` (k <= 0: none)
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t bits, int k) {
+    uint32_t r = 0;
+    while (k > 0 && bits) {
+        const uint32_t low = bits & (0u - bits);
+        r |= low;
+        bits ^= low;
+        k--;
+    }
+    return r;
+}
+
+// exclusive prefix sum of v over the block (wave scans, then wave totals in order)
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum) {
+    const int lane = threadIdx.x & (kWave - 1), wvi = threadIdx.x / kWave;
+    uint32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += t;
+    }
+    if (lane == kWave - 1) wsum[wvi] = incl;
+    __syncthreads();
+    uint32_t off = 0;
+    for (int q = 0; q < wvi; q++) off += wsum[q];
+    return off + incl - v;
+}
+
+// D: one workgroup per row.  All candidates share the threshold bin (the top
+// 12 key bits), so only the 20-bit score suffix s and the block index j
+// separate them.  Two 10-bit digit passes find the suffix T of the need-th
+// largest candidate; every candidate with s > T is in, and of those with
+// s == T the (need - #{s > T}) smallest j are in (ties to the smaller index).
+// The selected list and these sets are marked in two LDS bitmaps over j
+// (members, ties at T); one pass over the words keeps the lowest tie bits up
+// to the count and emits the members in ascending j.
 __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
-    __shared__ uint32_t bm[kIdxBitmapWords];
-    __shared__ uint2 lc[kIdxFinalLds];
-    __shared__ int32_t arr[kIdxMaxTopk];
+    // candidates during the digit passes, then the two bitmaps
+    __shared__ uint32_t big[2 * kIdxBitmapWords];
+    __shared__ uint32_t hA[kIdxDigitBins], hB[kIdxDigitBins];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh[4];
-    __shared__ uint32_t wsum[kIdxFinalThreads / kWave];
+    __shared__ uint32_t wsum[2][kIdxFinalThreads / kWave];
+    uint2* lc = reinterpret_cast<uint2*>(big);
     const int64_t r = blockIdx.x, row = a.row0 + r;
     const int64_t n = visible_blocks(a, row);
     int32_t* out = a.out + row * a.topk;
@@ -544,9 +640,82 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     RowWs w = row_ws(a, r);
     const uint32_t nsel = w.counts[0], ncand = w.counts[1];
     const uint32_t need = (uint32_t)a.topk - nsel;     // 1 <= need <= ncand by construction
+    const bool in_lds = ncand <= (uint32_t)kIdxFinalLds;
+    const int nwords = (int)((n + 31) / 32);
+    if (nwords <= kIdxBitmapWords) {
+        for (int i = threadIdx.x; i < kIdxDigitBins; i += blockDim.x) { hA[i] = 0u; hB[i] = 0u; }
+        if (in_lds)
+            for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) lc[i] = w.cand[i];
+        __syncthreads();
+        const uint2* cand = in_lds ? lc : w.cand;
+        digit_hist(cand, ncand, 10, false, 0u, hA);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            uint32_t dg, ab;
+            wave_pick_digit1024(hA, need, dg, ab);
+            if (threadIdx.x == 0) { sh[0] = dg; sh[1] = ab; }
+        }
+        __syncthreads();
+        const uint32_t dA = sh[0], needA = need - sh[1];
+        digit_hist(cand, ncand, 0, true, dA, hB);
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            uint32_t dg, ab;
+            wave_pick_digit1024(hB, needA, dg, ab);
+            if (threadIdx.x == 0) { sh[2] = dg; sh[3] = ab; }
+        }
+        __syncthreads();                                  // every read of lc is done
+        const uint32_t T = (dA << 10) | sh[2];
+        const int needT = (int)(needA - sh[3]);           // ties at T to take, >= 1
+        uint32_t* bmA = big;
+        uint32_t* bmT = big + kIdxBitmapWords;
+        for (int i = threadIdx.x; i < nwords; i += blockDim.x) { bmA[i] = 0u; bmT[i] = 0u; }
+        __syncthreads();
+        for (uint32_t i = threadIdx.x; i < nsel; i += blockDim.x) {
+            const uint32_t j = (uint32_t)w.sel[i];
+            atomicOr(&bmA[j >> 5], 1u << (j & 31));
+        }
+        for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) {
+            const uint2 c = w.cand[i];
+            const uint32_t sfx = c.x & 0xFFFFFu;
+            if (sfx >= T) atomicOr(&(sfx > T ? bmA : bmT)[c.y >> 5], 1u << (c.y & 31));
+        }
+        __syncthreads();
+        const int per = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;   // consecutive words per thread
+        const int w0 = (int)threadIdx.x * per;
+        uint32_t ct = 0;
+        for (int q = 0; q < per; q++)
+            if (w0 + q < nwords) ct += __popc(bmT[w0 + q]);
+        const int rt0 = (int)block_exclusive_scan(ct, wsum[0]);   // ties in the words before mine
+        uint32_t cnt = 0;
+        int rt = rt0;
+        for (int q = 0; q < per; q++) {
+            if (w0 + q >= nwords) break;
+            const uint32_t tb = bmT[w0 + q];
+            cnt += __popc(bmA[w0 + q] | lowest_bits(tb, needT - rt));
+            rt += __popc(tb);
+        }
+        uint32_t off = block_exclusive_scan(cnt, wsum[1]);
+        rt = rt0;
+        for (int q = 0; q < per; q++) {
+            if (w0 + q >= nwords) break;
+            const uint32_t tb = bmT[w0 + q];
+            uint32_t bits = bmA[w0 + q] | lowest_bits(tb, needT - rt);
+            rt += __popc(tb);
+            while (bits) {
+                const int bpos = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (off < (uint32_t)a.topk) out[off] = (w0 + q) * 32 + bpos;
+                off++;
+            }
+        }
+        return;
+    }
+    // very large caps: radix-select the composite (score suffix, inverted
+    // block index) among the candidates, gather the k indices, bitonic-sort
+    int32_t* arr = reinterpret_cast<int32_t*>(big + 2 * kIdxFinalLds);
     const int jb = bits_for(a.cap);
     const uint64_t jmask = ((uint64_t)1 << jb) - 1;
-    const bool in_lds = ncand <= (uint32_t)kIdxFinalLds;
     if (in_lds) {
         for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) lc[i] = w.cand[i];
         __syncthreads();
@@ -557,52 +726,6 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
         return ((uint64_t)(c.x & 0xFFFFFu) << jb) | (jmask - (uint64_t)c.y);
     };
     const uint64_t thr = radix_select(get, (int64_t)ncand, 20 + jb, need, hist, sh);
-    const int nwords = (int)((n + 31) / 32);
-    if (nwords <= kIdxBitmapWords) {
-        // mark the k selected blocks, then emit them in block order
-        for (int i = threadIdx.x; i < nwords; i += blockDim.x) bm[i] = 0u;
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < nsel; i += blockDim.x) {
-            const uint32_t j = (uint32_t)w.sel[i];
-            atomicOr(&bm[j >> 5], 1u << (j & 31));
-        }
-        for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x)
-            if (get(i) >= thr) {
-                const uint32_t j = cand[i].y;
-                atomicOr(&bm[j >> 5], 1u << (j & 31));
-            }
-        __syncthreads();
-        const int per = (nwords + blockDim.x - 1) / blockDim.x;     // consecutive words per thread
-        const int w0 = threadIdx.x * per;
-        uint32_t cnt = 0;
-        for (int q = 0; q < per; q++)
-            if (w0 + q < nwords) cnt += __popc(bm[w0 + q]);
-        // exclusive scan of cnt over the block
-        const int lane = threadIdx.x & (kWave - 1), wvi = threadIdx.x / kWave;
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const uint32_t tv = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += tv;
-        }
-        if (lane == kWave - 1) wsum[wvi] = incl;
-        __syncthreads();
-        uint32_t off = 0;
-        for (int q = 0; q < wvi; q++) off += wsum[q];
-        off += incl - cnt;
-        for (int q = 0; q < per; q++) {
-            if (w0 + q >= nwords) break;
-            uint32_t bits = bm[w0 + q];
-            while (bits) {
-                const int bpos = __builtin_ctz(bits);
-                bits &= bits - 1;
-                if (off < (uint32_t)a.topk) out[off] = (w0 + q) * 32 + bpos;
-                off++;
-            }
-        }
-        return;
-    }
-    // very large caps: gather the k indices and bitonic-sort them
     for (uint32_t i = threadIdx.x; i < nsel && i < (uint32_t)a.topk; i += blockDim.x) arr[i] = w.sel[i];
     if (threadIdx.x == 0) sh[2] = nsel;
     __syncthreads();

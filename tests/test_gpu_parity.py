@@ -193,6 +193,24 @@ def test_indexer_very_large_cap_exact():
     assert np.array_equal(got, ref)
 
 
+def test_indexer_tie_heavy_rows_exact():
+    """Rows whose weights are all negative (every key with no positive head
+    product ties at score 0) or all zero (every key ties): more candidates
+    than the final kernel keeps in LDS, and the tie rule (smaller block index)
+    decides most of the set."""
+    g = synth.rng(546)
+    B, Tq, Hi, di, m, k, cap = 2, 2, 4, 64, 4, 1024, 70000
+    kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
+    qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+    w = synth.grid(g, (B, Tq, Hi))
+    w[0, 0] = -np.abs(w[0, 0]) - np.float32(0.125)          # all negative
+    w[1, 1] = 0.0                                            # all zero: every score ties
+    pos = np.array([[4 * cap - 1, 4 * cap - 1], [4 * 50000 + 2, 4 * cap - 1]], np.int32)
+    got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[1, 1], np.arange(k))           # all tied: the first k blocks
+
+
 def test_indexer_fp4_codes_exact():
     """FP4 keys and queries drawn as codes with a narrow exponent range: exact."""
     g = synth.rng(510)
