@@ -107,7 +107,7 @@ __device__ __forceinline__ void rotate_out(const AttnArgs& a, int64_t t, float* 
 }
 
 template <typename QT, typename OT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, int nsplit_max) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG) {
     __shared__ float qs[kAttnQFloats];
     __shared__ float kv[kAttnTile * (kAttnMaxD + 1)];
     __shared__ float pz[kAttnQFloats / 64 * kAttnTile];   // [hg][tile]
@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
     }
     // partials: o (relative to mrun), m, l
     float* wo = reinterpret_cast<float*>(a.ws);
-    float* wml = wo + (size_t)a.rows * nsplit_max * a.H * d;
-    const size_t base = ((size_t)row * nsplit_max + s) * a.H + h0;
+    float* wml = wo + (size_t)a.rows * a.nsplit_max * a.H * d;
+    const size_t base = ((size_t)row * a.nsplit_max + s) * a.H + h0;
 #pragma unroll
     for (int q = 0; q < kMaxOwn; q++) {
         const int idx = tid + q * kAttnThreads;
@@ -244,7 +244,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG, 
 // of group t / (d/4) (splits g, g + G, ... in order, several loads in
 // flight); the groups are then added in group order.
 template <typename OT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int nsplit_max) {
+__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
+    warm_kernargs(offsetof(AttnArgs, rope));
     __shared__ float v[kAttnMaxD];
     __shared__ float wsc[1024];
     __shared__ float red[kAttnThreads / kWave];
@@ -258,11 +259,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a, int n
     const int nsplit = (int)attn_nsplit<int64_t>(ne, a.Tq);
     if (nsplit <= 1) return;
     const float* wo = reinterpret_cast<const float*>(a.ws);
-    const float* wml = wo + (size_t)a.rows * nsplit_max * a.H * a.d;
+    const float* wml = wo + (size_t)a.rows * a.nsplit_max * a.H * a.d;
     const int d = a.d;
     const float sk = a.sink[h];
     stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
-    const size_t mbase = (size_t)row * nsplit_max * a.H + h;     // split s at mbase + s * H
+    const size_t mbase = (size_t)row * a.nsplit_max * a.H + h;     // split s at mbase + s * H
     float mx = sk;
     for (int s = threadIdx.x; s < nsplit; s += blockDim.x) mx = fmaxf(mx, wml[(mbase + (size_t)s * a.H) * 2]);
     const float M = block_max(mx, red);
@@ -345,9 +346,11 @@ int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t ma
     return rows * nb * H * ((int64_t)d + 2) * 4;
 }
 
-hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st) {
-    if (a.rows == 0) return hipSuccess;
-    const int64_t nb = attn_nsplit_bound(max_entries, a.Tq);
+hipError_t launch_attention(const AttnArgs& a0, int64_t max_entries, hipStream_t st) {
+    if (a0.rows == 0) return hipSuccess;
+    const int64_t nb = attn_nsplit_bound(max_entries, a0.Tq);
+    AttnArgs a = a0;
+    a.nsplit_max = (int32_t)nb;
     if (attn_mfma_supported(a)) {
         hipError_t e = launch_attention_mfma(a, nb, st);
         if (e != hipSuccess) return e;
@@ -356,15 +359,15 @@ hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t 
         const int ngroups = (a.H + HG - 1) / HG;
         dim3 grid((unsigned)nb, (unsigned)a.rows, (unsigned)ngroups);
         const bool qb = a.q_fmt == CSA_BF16, ob = a.out_fmt == CSA_BF16;
-        if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
-        if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
-        if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
-        if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG, (int)nb);
+        if (!qb && !ob) hipLaunchKernelGGL((k_attn_valu<float, float>), grid, dim3(kAttnThreads), 0, st, a, HG);
+        if (!qb && ob) hipLaunchKernelGGL((k_attn_valu<float, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG);
+        if (qb && !ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, float>), grid, dim3(kAttnThreads), 0, st, a, HG);
+        if (qb && ob) hipLaunchKernelGGL((k_attn_valu<uint16_t, uint16_t>), grid, dim3(kAttnThreads), 0, st, a, HG);
     }
     if (nb > 1) {
         dim3 g2((unsigned)a.H, (unsigned)a.rows);
-        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a, (int)nb);
-        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a, (int)nb);
+        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -117,32 +117,28 @@ struct Fetch {
 // index of this lane's entry in the top-k list (lanes 0..7), read ahead of use
 __device__ __forceinline__ int32_t fetch_index(const AttnArgs& a, const RowCtx& c, int32_t et, int32_t e1, int w,
                                                int lane) {
+    // unconditional load at a clamped entry (no branch around it, so the
+    // compiler's wait counts stay exact); the value is used only where valid
     const int32_t e = et + w + kFetchers * lane;
-    int32_t j = 0;
-    if (c.top && lane < kEntPerWave && e < e1 && e < c.nc) j = c.top[e];
-    return j;
+    return c.top ? c.top[min(e, c.nc - 1)] : 0;
 }
 
-// record addresses of the wave's entries of the tile at et (j: fetch_index)
+// record addresses of the wave's entries of the tile at et (j: fetch_index).
+// Branch-free over lanes: both the compressed and the window address are
+// formed and one is selected (a per-lane choice between two argument fields
+// would otherwise become a vector load from the argument segment).
 __device__ __forceinline__ Fetch fetch_plan(const AttnArgs& a, const RowCtx& c, int32_t et, int32_t e1, int w,
                                             int lane, int32_t j) {
     const int32_t e = et + w + kFetchers * lane;
-    bool ok = lane < kEntPerWave && e < e1, fp8 = false;
-    const uint8_t* p = nullptr;
-    if (ok) {
-        if (e < c.nc) {
-            const int32_t jj = c.top ? j : e;
-            ok = jj >= 0 && jj < c.vis;
-            p = c.comp + (int64_t)jj * a.comp_rec;
-            fp8 = a.comp_fmt == CSA_FP8_E4M3;
-        } else {
-            int32_t sl = c.slot0 + (e - c.nc);
-            ok = sl >= 0;
-            if (sl >= a.wcap) sl -= (int32_t)a.wcap;
-            p = c.win + (int64_t)sl * a.win_rec;
-            fp8 = a.win_fmt == CSA_FP8_E4M3;
-        }
-    }
+    const bool comp8 = a.comp_fmt == CSA_FP8_E4M3, win8 = a.win_fmt == CSA_FP8_E4M3;
+    const bool inr = lane < kEntPerWave && e < e1;
+    const bool isc = e < c.nc;
+    const int32_t jj = c.top ? j : e;
+    int32_t sl = c.slot0 + (e - c.nc);
+    if (sl >= a.wcap) sl -= (int32_t)a.wcap;
+    const bool ok = inr && (isc ? (jj >= 0 && jj < c.vis) : sl >= 0);
+    const uint8_t* p = isc ? c.comp + (int64_t)jj * a.comp_rec : c.win + (int64_t)sl * a.win_rec;
+    const bool fp8 = isc ? comp8 : win8;
     Fetch f;
     f.ptr = (uint64_t)(uintptr_t)p;
     f.vmask = (uint32_t)__ballot(ok);
@@ -301,7 +297,8 @@ __device__ __forceinline__ uint2 lds_read_tr8(const void* p) {
 __device__ __forceinline__ int pv_k_of_entry(int e) { return (e & ~7) + 4 * (e & 1) + ((e & 7) >> 1); }
 
 template <int D, int DR, bool F8, typename OT>
-__global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_max) {
+__global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
+    warm_kernargs(offsetof(AttnArgs, rope));
     constexpr int DQ = D / 4;              // dims per quarter
     constexpr int KS = DQ / 32;            // Q K^T K-steps per wave
     constexpr int NT = DQ / 16;            // P V N-tiles per wave
@@ -320,27 +317,27 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
     const int MT = min(4, (a.H - h0) / 16);           // 16-head groups in this workgroup
     const int dbase = qd * DQ;                         // first dim of this wave's quarter
 
-    // ---- the query loads go out first (they do not depend on the position)
-    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + h0 + 32 * hp) * D;
+    // ---- the query loads go out first (they do not depend on the position).
+    // No load sits under a branch: a head group beyond MT reads group 0 (its
+    // results are never stored), and without gamma the loads read the query
+    // and are replaced by ones.
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + h0) * D;
     uint4 qraw[2][KS];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < 2; mt++) {
+        const int hg = (2 * hp + mt < MT) ? 32 * hp + 16 * mt : 0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++) {
-            qraw[mt][ks] = make_uint4(0u, 0u, 0u, 0u);
-            if (2 * hp + mt < MT)
-                qraw[mt][ks] = *reinterpret_cast<const uint4*>(qb + (16 * mt + l16) * D + dbase + 32 * ks + 8 * g4);
-        }
+        for (int ks = 0; ks < KS; ks++)
+            qraw[mt][ks] = *reinterpret_cast<const uint4*>(qb + (hg + l16) * D + dbase + 32 * ks + 8 * g4);
+    }
     float4 gam[KS][2];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
-        gam[ks][0] = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        gam[ks][1] = gam[ks][0];
-        if (a.gamma_q) {
-            const float4* gp = reinterpret_cast<const float4*>(a.gamma_q + dbase + 32 * ks + 8 * g4);
-            gam[ks][0] = gp[0];
-            gam[ks][1] = gp[1];
-        }
+        const float* gsrc = a.gamma_q ? a.gamma_q + dbase + 32 * ks + 8 * g4 : reinterpret_cast<const float*>(a.q);
+        const float4 g0 = reinterpret_cast<const float4*>(gsrc)[0], g1 = reinterpret_cast<const float4*>(gsrc)[1];
+        const float4 one = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        gam[ks][0] = a.gamma_q ? g0 : one;
+        gam[ks][1] = a.gamma_q ? g1 : one;
     }
 
     const int b = row / a.Tq;
@@ -391,16 +388,15 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
             }
         }
     };
+    // top-k indices of the first tiles, all in flight together; the records
+    // go out once the query's square sums are published (the fetching waves
+    // would otherwise wait for their records before that barrier)
+    int32_t jf0 = 0, jf1 = 0;
     if (fetcher) {
-        if constexpr (F8) {
-            ring_issue(0, 0, fetch_index(a, c, e0, e1, fw, lane));
-            if (ntiles > 1) ring_issue(1, 1, fetch_index(a, c, e0 + kMTE, e1, fw, lane));
-            jn = fetch_index(a, c, e0 + 2 * kMTE, e1, fw, lane);
-        } else {
-            fr = fetch_plan(a, c, e0, e1, fw, lane, fetch_index(a, c, e0, e1, fw, lane));
-            fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
-            jn = fetch_index(a, c, e0 + kMTE, e1, fw, lane);
-        }
+        jf0 = fetch_index(a, c, e0, e1, fw, lane);
+        jf1 = fetch_index(a, c, e0 + kMTE, e1, fw, lane);
+        if constexpr (F8) jn = fetch_index(a, c, e0 + 2 * kMTE, e1, fw, lane);
+        else jn = jf1;
     }
     stage_rope_arg(offsetof(AttnArgs, rope), sm.rf, a.dr / 2);
 
@@ -420,6 +416,15 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
         ss += __shfl_xor(ss, 16, kWave);
         ss += __shfl_xor(ss, 32, kWave);
         if (g4 == 0) sm.ssq[qd][32 * hp + 16 * mt + l16] = ss;
+    }
+    if (fetcher) {
+        if constexpr (F8) {
+            ring_issue(0, 0, jf0);
+            if (ntiles > 1) ring_issue(1, 1, jf1);
+        } else {
+            fr = fetch_plan(a, c, e0, e1, fw, lane, jf0);
+            fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
+        }
     }
     __syncthreads();
     float inv[2];
@@ -745,8 +750,8 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a, int nsplit_m
     // O goes through LDS (the tile and logit areas are free now), 32 heads at
     // a time, so that the global stores are whole 16-byte vectors.
     float* wo = reinterpret_cast<float*>(a.ws);
-    float* wml = wo + (size_t)a.rows * nsplit_max * a.H * D;
-    const size_t base = ((size_t)row * nsplit_max + sp) * a.H + h0;
+    float* wml = wo + (size_t)a.rows * a.nsplit_max * a.H * D;
+    const size_t base = ((size_t)row * a.nsplit_max + sp) * a.H + h0;
     static_assert(sizeof(MfmaTiles<D, DR, F8>) + sizeof(sm.zx) >= 32 * (D + 4) * sizeof(float),
                   "partial staging does not fit");
     float* ost = reinterpret_cast<float*>(&sm);     // [32 heads][D + 4]
@@ -791,14 +796,16 @@ bool attn_mfma_supported(const AttnArgs& a) {
 }
 
 template <bool F8, typename OT>
-static void launch_d(const AttnArgs& a, int nsplit, hipStream_t st) {
+static void launch_d(const AttnArgs& a0, int nsplit, hipStream_t st) {
+    AttnArgs a = a0;
+    a.nsplit_max = nsplit;
     const int groups = (a.H + 63) / 64;
     dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)groups);
     // eight waves per workgroup always (head halves x dim quarters); a
     // workgroup covers up to 64 heads
-    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
-    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
-    else hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a, nsplit);
+    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a);
+    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, int64_t nsplit_bound, hipStream_t st) {

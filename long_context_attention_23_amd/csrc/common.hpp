@@ -94,6 +94,18 @@ __device__ __forceinline__ void stage_rope_arg(size_t offset, double* lds, int n
     if ((int)threadIdx.x < npairs) lds[threadIdx.x] = t[threadIdx.x];
 }
 
+// Load one dword of every 64-byte line of the first `bytes` of the kernel's
+// argument block, all at once, and wait for them (the empty asm consumes the
+// values).  The scalar loads of the argument fields spread through a kernel
+// otherwise miss the scalar cache one line after another, each costing a
+// memory round trip before the next can be issued; after this they hit.
+__device__ __forceinline__ void warm_kernargs(size_t bytes) {
+    const uint32_t* p = (const uint32_t*)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t acc = 0;
+    for (size_t off = 0; off < bytes; off += 64) acc ^= p[off / 4];
+    asm volatile("" ::"s"(acc));
+}
+
 // the p-th frequency of a RopeTable passed by value at byte `offset` of the
 // kernel arguments, read by one lane from the argument segment
 __device__ __forceinline__ double rope_freq_arg(size_t offset, int p) {
@@ -181,6 +193,30 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
     const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// the value of v in lane `lane` (a wave-uniform index), as a scalar read
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// inclusive prefix sum over the 64 lanes: shifted adds inside each 16-lane
+// DPP row (lanes shifted in from outside the row add 0), then the totals of
+// the rows below, read as scalars
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v) {
+    v += dpp_u<0x111>(v);              // row_shr:1
+    v += dpp_u<0x112>(v);              // row_shr:2
+    v += dpp_u<0x114>(v);              // row_shr:4
+    v += dpp_u<0x118>(v);              // row_shr:8
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const int rw = (threadIdx.x & 63) >> 4;
+    return v + (rw >= 1 ? t0 : 0u) + (rw >= 2 ? t1 : 0u) + (rw >= 3 ? t2 : 0u);
 }
 
 // block-wide reductions; `red` is LDS scratch of >= blockDim/64 floats

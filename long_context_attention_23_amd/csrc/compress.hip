@@ -216,6 +216,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
 // in DPP row order instead of a butterfly, so the last bits may differ.
 template <typename XT, int QR>
 __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) {
+    warm_kernargs(offsetof(CompressArgs, rope));
     __shared__ float part[kCompThreads * 8];
     __shared__ float red_ss[kCompThreads / kWave];
     __shared__ float red_mx[kCompThreads / kWave];

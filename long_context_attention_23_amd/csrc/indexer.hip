@@ -124,14 +124,10 @@ __device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, uint32_t n
 #pragma unroll
     for (int q = 0; q < 4; q++) { h4[q] = hist[255 - 4 * lane - q]; s += h4[q]; }
     uint32_t incl = s;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
+    incl = wave_incl_scan_dpp(incl);
     uint64_t bal = __ballot(incl >= need);
     int L = bal ? __builtin_ctzll(bal) : kWave - 1;
-    uint32_t cum = __shfl(incl - s, L, kWave);
+    uint32_t cum = lane_u32(incl - s, L);
     uint32_t d = 0, ab = cum;
     if (lane == L) {
         uint32_t c = cum;
@@ -142,8 +138,8 @@ __device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, uint32_t n
             c += h4[q];
         }
     }
-    digit = __shfl(d, L, kWave);
-    above = __shfl(ab, L, kWave);
+    digit = lane_u32(d, L);
+    above = lane_u32(ab, L);
 }
 
 // Radix select over n composites get(i) (nbits significant bits): returns the
@@ -163,12 +159,12 @@ __device__ uint64_t radix_select(Get get, int64_t n, int nbits, uint32_t need, u
             // many equal digits (tied scores) would serialise on one LDS
             // address: a wave whose lanes mostly agree adds per distinct digit
             const uint64_t act = __ballot(in);
-            const uint32_t d0 = __shfl(dg, act ? __builtin_ctzll(act) : 0, kWave);
+            const uint32_t d0 = lane_u32(dg, act ? __builtin_ctzll(act) : 0);
             if (__popcll(__ballot(in && dg == d0)) > 8) {
                 uint64_t todo = act;
                 while (todo) {
                     const int leader = __builtin_ctzll(todo);
-                    const uint32_t dl = __shfl(dg, leader, kWave);
+                    const uint32_t dl = lane_u32(dg, leader);
                     const uint64_t same = __ballot(in && dg == dl) & todo;
                     if ((int)(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
                     todo &= ~same;
@@ -280,6 +276,7 @@ int64_t idx_ws_row_bytes(int64_t cap, int32_t topk) {
 }
 
 __global__ void k_idx_zero(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
     const int64_t r = blockIdx.x;
     uint32_t* p = reinterpret_cast<uint32_t*>(a.ws + r * a.ws_row_bytes);
     for (int i = threadIdx.x; i < kIdxHistBins + 4; i += blockDim.x) p[i] = 0;
@@ -331,6 +328,7 @@ constexpr int kIdxScoreThreads = 1024;  // 16 waves, four 32-key groups each (me
 // bytes in flight.
 template <int QF, int KF>
 __global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
     constexpr int DI = 64;
     constexpr int NKS = KF == CSA_FP4_E2M1 ? 1 : 4;            // K steps per 32-key group
     // 32-key groups whose loads a wave issues before computing them
@@ -441,39 +439,33 @@ __device__ __forceinline__ void wave_pick_bin(const uint32_t* hist, uint32_t nee
 #pragma unroll
     for (int i = 0; i < per / 4; i++) s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
     uint32_t incl = s;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
+    incl = wave_incl_scan_dpp(incl);
     uint64_t bal = __ballot(incl >= need);
     int L = bal ? __builtin_ctzll(bal) : kWave - 1;
-    const uint32_t cum = __shfl(incl - s, L, kWave);
+    const uint32_t cum = lane_u32(incl - s, L);
     // the bins of lane L, one per lane in descending bin order, prefix-summed
     const int bq = kIdxHistBins - 1 - per * L - lane;
     const uint32_t hb = hist[bq];
     uint32_t c = hb;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_up(c, o, kWave);
-        if (lane >= o) c += t;
-    }
+    c = wave_incl_scan_dpp(c);
     c += cum;
     const uint64_t hit = __ballot(c >= need);
     const int q = hit ? __builtin_ctzll(hit) : kWave - 1;
-    bin = (uint32_t)__shfl(bq, q, kWave);
-    above = __shfl(c - hb, q, kWave);
+    bin = (uint32_t)lane_u32(bq, q);
+    above = lane_u32(c - hb, q);
 }
 
 __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    constexpr int kWaves = kIdxThreads / kWave;
     __shared__ uint32_t sh[2];
-    __shared__ uint32_t cnt[2], base[2];
+    __shared__ uint32_t wcnt[2][kWaves], base[2];
     const int64_t r = blockIdx.y, row = a.row0 + r;
     const int64_t n = visible_blocks(a, row);
     const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
     if (n <= a.topk || c0 >= n) return;
     RowWs w = row_ws(a, r);
-    const int lane = threadIdx.x & (kWave - 1);
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
     constexpr int kPer = kIdxChunk / kIdxThreads;
     uint32_t keys[kPer];
@@ -485,49 +477,58 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     if (threadIdx.x < kWave) {
         uint32_t bin, above;
         wave_pick_bin(w.hist, (uint32_t)a.topk, bin, above);
-        if (threadIdx.x == 0) { sh[0] = bin; sh[1] = above; cnt[0] = 0; cnt[1] = 0; }
+        if (threadIdx.x == 0) { sh[0] = bin; sh[1] = above; }
     }
     __syncthreads();
     const uint32_t tbin = sh[0];
-    // workgroup-local slots from LDS counters, then one global reservation per list
-    uint32_t slot[kPer];
+    // per-wave counts of the two lists, one global reservation per list for
+    // the workgroup, then slots in (wave, round, lane) order
     uint32_t kind = 0;                                   // bit u: 1 = sure, bit u+16: candidate
+    uint32_t ns = 0, nc = 0;
 #pragma unroll
     for (int u = 0; u < kPer; u++) {
         const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
         const uint32_t bin = keys[u] >> 20;
         const bool sure = j < c1 && bin > tbin;
         const bool cand = j < c1 && bin == tbin;
-        const uint64_t bs = __ballot(sure), bc = __ballot(cand);
-        uint32_t os = 0, oc = 0;
-        if (lane == 0) {
-            if (bs) os = atomicAdd(&cnt[0], (uint32_t)__popcll(bs));
-            if (bc) oc = atomicAdd(&cnt[1], (uint32_t)__popcll(bc));
-        }
-        os = __shfl(os, 0, kWave);
-        oc = __shfl(oc, 0, kWave);
-        const uint64_t below = (1ull << lane) - 1;
-        slot[u] = sure ? os + __popcll(bs & below) : oc + __popcll(bc & below);
+        ns += (uint32_t)__popcll(__ballot(sure));
+        nc += (uint32_t)__popcll(__ballot(cand));
         kind |= (sure ? 1u : 0u) << u;
         kind |= (cand ? 1u : 0u) << (u + 16);
     }
+    if (lane == 0) { wcnt[0][wv] = ns; wcnt[1][wv] = nc; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        base[0] = cnt[0] ? atomicAdd(&w.counts[0], cnt[0]) : 0u;
-        base[1] = cnt[1] ? atomicAdd(&w.counts[1], cnt[1]) : 0u;
+        uint32_t ts = 0, tc = 0;
+        for (int q = 0; q < kWaves; q++) { ts += wcnt[0][q]; tc += wcnt[1][q]; }
+        base[0] = ts ? atomicAdd(&w.counts[0], ts) : 0u;
+        base[1] = tc ? atomicAdd(&w.counts[1], tc) : 0u;
     }
     __syncthreads();
+    uint32_t os = base[0], oc = base[1];
+    for (int q = 0; q < wv; q++) { os += wcnt[0][q]; oc += wcnt[1][q]; }
+    const uint64_t below = (1ull << lane) - 1;
 #pragma unroll
     for (int u = 0; u < kPer; u++) {
         const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
-        if (kind & (1u << u)) w.sel[base[0] + slot[u]] = (int32_t)j;
-        if (kind & (1u << (u + 16))) w.cand[base[1] + slot[u]] = make_uint2(keys[u], (uint32_t)j);
+        const bool sure = (kind >> u) & 1u, cand = (kind >> (u + 16)) & 1u;
+        const uint64_t bs = __ballot(sure), bc = __ballot(cand);
+        if (sure) w.sel[os + __popcll(bs & below)] = (int32_t)j;
+        if (cand) w.cand[oc + __popcll(bc & below)] = make_uint2(keys[u], (uint32_t)j);
+        os += (uint32_t)__popcll(bs);
+        oc += (uint32_t)__popcll(bc);
     }
 }
 
-constexpr int kIdxBitmapWords = 16384;   // words per LDS bitmap of blocks (caps up to 2^19)
-constexpr int kIdxFinalLds = 4096;       // candidates kept in LDS across the digit passes
+constexpr int kIdxBitmapWords = 8192;    // words per LDS bitmap of blocks (caps up to 2^18)
+constexpr int kIdxFinalLds = 4096;       // candidates held in registers across the digit passes
 constexpr int kIdxDigitBins = 1024;      // 10-bit digits of the 20-bit score suffix
+constexpr int kIdxCandPerThread = kIdxFinalLds / kIdxFinalThreads;
+constexpr int kIdxWordsPerThread = kIdxBitmapWords / kIdxFinalThreads;
+constexpr int kIdxSelPerThread = kIdxMaxTopk / kIdxFinalThreads;
+// the large path runs only above kIdxSmallMaxKeys keys, so a row's candidate
+// buffer (one entry per key) always holds kIdxFinalLds entries
+static_assert(kIdxFinalLds <= kIdxSmallMaxKeys, "speculative candidate loads must stay in the buffer");
 
 // wave_pick_digit over 1024 bins (16 per lane, lane 0 holding the top ones)
 __device__ __forceinline__ void wave_pick_digit1024(const uint32_t* hist, uint32_t need, uint32_t& digit,
@@ -538,14 +539,10 @@ __device__ __forceinline__ void wave_pick_digit1024(const uint32_t* hist, uint32
 #pragma unroll
     for (int q = 0; q < per; q++) { h[q] = hist[kIdxDigitBins - 1 - per * lane - q]; s += h[q]; }
     uint32_t incl = s;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
+    incl = wave_incl_scan_dpp(incl);
     const uint64_t bal = __ballot(incl >= need);
     const int L = bal ? __builtin_ctzll(bal) : kWave - 1;
-    const uint32_t cum = __shfl(incl - s, L, kWave);
+    const uint32_t cum = lane_u32(incl - s, L);
     uint32_t d = 0, ab = cum;
     if (lane == L) {
         uint32_t c = cum;
@@ -555,35 +552,40 @@ __device__ __forceinline__ void wave_pick_digit1024(const uint32_t* hist, uint32
             c += h[q];
         }
     }
-    digit = __shfl(d, L, kWave);
-    above = __shfl(ab, L, kWave);
+    digit = lane_u32(d, L);
+    above = lane_u32(ab, L);
 }
 
-// histogram of the 10-bit digit (key >> shift) & 1023 over the candidates
-// whose upper digit equals `upper` (all of them when !filt); a wave whose
-// lanes mostly share one digit (tied scores) adds once per distinct digit
-__device__ __forceinline__ void digit_hist(const uint2* cand, uint32_t ncand, int shift, bool filt, uint32_t upper,
-                                           uint32_t* hist) {
-    for (uint32_t i0 = 0; i0 < ncand; i0 += blockDim.x) {     // block-uniform rounds: complete ballots
-        const uint32_t i = i0 + threadIdx.x;
-        const uint32_t key = i < ncand ? cand[i].x : 0u;
-        const bool in = i < ncand && (!filt || ((key >> 10) & 1023u) == upper);
-        const uint32_t dg = (key >> shift) & 1023u;
-        const uint64_t act = __ballot(in);
-        const uint32_t d0 = __shfl(dg, act ? __builtin_ctzll(act) : 0, kWave);
-        if (__popcll(__ballot(in && dg == d0)) > 8) {
-            uint64_t todo = act;
-            while (todo) {
-                const int leader = __builtin_ctzll(todo);
-                const uint32_t dl = __shfl(dg, leader, kWave);
-                const uint64_t same = __ballot(in && dg == dl) & todo;
-                if ((int)(threadIdx.x & (kWave - 1)) == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
-                todo &= ~same;
-            }
-        } else if (in) {
-            atomicAdd(&hist[dg], 1u);
+// one round of a 10-bit digit histogram: (key >> shift) & 1023 of the
+// candidates `in`.  A wave whose lanes mostly share one digit (tied scores)
+// adds once per distinct digit, and keeps its running count for the digit it
+// meets most (run_dg, run_cnt: wave-uniform) in a register across rounds, so
+// a long run of ties costs one LDS atomic per wave instead of one per round
+// (many waves adding to one address serialise).  Every lane of the wave must
+// take part; flush_digit_run adds the register count at the end.
+__device__ __forceinline__ void digit_hist_round(uint32_t key, bool in, int shift, uint32_t* hist, uint32_t& run_dg,
+                                                 uint32_t& run_cnt) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t dg = (key >> shift) & 1023u;
+    const uint64_t act = __ballot(in);
+    const uint32_t d0 = lane_u32(dg, act ? __builtin_ctzll(act) : 0);
+    if (__popcll(__ballot(in && dg == d0)) > 8) {
+        if (run_cnt == 0) run_dg = d0;
+        uint64_t todo = act;
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const uint32_t dl = lane_u32(dg, leader);
+            const uint64_t same = __ballot(in && dg == dl) & todo;
+            if (dl == run_dg) run_cnt += (uint32_t)__popcll(same);
+            else if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+            todo &= ~same;
         }
+    } else if (in) {
+        atomicAdd(&hist[dg], 1u);
     }
+}
+__device__ __forceinline__ void flush_digit_run(uint32_t* hist, uint32_t run_dg, uint32_t run_cnt) {
+    if (run_cnt && (threadIdx.x & (kWave - 1)) == 0) atomicAdd(&hist[run_dg], run_cnt);
 }
 
 // the lowest k set bits of `bits` (k <= 0: none)
@@ -602,11 +604,7 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t bits, int k) {
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum) {
     const int lane = threadIdx.x & (kWave - 1), wvi = threadIdx.x / kWave;
     uint32_t incl = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += t;
-    }
+    incl = wave_incl_scan_dpp(incl);
     if (lane == kWave - 1) wsum[wvi] = incl;
     __syncthreads();
     uint32_t off = 0;
@@ -620,92 +618,154 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* w
 // largest candidate; every candidate with s > T is in, and of those with
 // s == T the (need - #{s > T}) smallest j are in (ties to the smaller index).
 // The selected list and these sets are marked in two LDS bitmaps over j
-// (members, ties at T); one pass over the words keeps the lowest tie bits up
-// to the count and emits the members in ascending j.
+// (members, ties at T); each thread then owns 8 consecutive words in
+// registers, keeps the lowest tie bits up to the count and emits its members
+// at its offset, so the output is in ascending j.  Up to 4096 candidates live
+// in registers (4 per thread, loaded before the counts are known: the
+// candidate and selected buffers always hold that many entries).
 __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
-    // candidates during the digit passes, then the two bitmaps
-    __shared__ uint32_t big[2 * kIdxBitmapWords];
+    warm_kernargs(sizeof(IndexerArgs));
+    __shared__ uint4 bm4[2][kIdxBitmapWords / 4];        // members, ties at T
+    __shared__ uint2 lc[kIdxFinalLds];                   // very large caps only
     __shared__ uint32_t hA[kIdxDigitBins], hB[kIdxDigitBins];
     __shared__ uint32_t hist[256];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t wsum[2][kIdxFinalThreads / kWave];
-    uint2* lc = reinterpret_cast<uint2*>(big);
+    const int tid = threadIdx.x;
     const int64_t r = blockIdx.x, row = a.row0 + r;
     const int64_t n = visible_blocks(a, row);
     int32_t* out = a.out + row * a.topk;
     if (n <= a.topk) {
-        for (int64_t i = threadIdx.x; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
+        for (int64_t i = tid; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
         return;
     }
     RowWs w = row_ws(a, r);
+    uint2 cv[kIdxCandPerThread];
+#pragma unroll
+    for (int q = 0; q < kIdxCandPerThread; q++) cv[q] = w.cand[tid + q * kIdxFinalThreads];
+    int32_t sv[kIdxSelPerThread];
+#pragma unroll
+    for (int q = 0; q < kIdxSelPerThread; q++) {
+        const int idx = tid + q * kIdxFinalThreads;
+        sv[q] = idx < a.topk ? w.sel[idx] : 0;
+    }
     const uint32_t nsel = w.counts[0], ncand = w.counts[1];
     const uint32_t need = (uint32_t)a.topk - nsel;     // 1 <= need <= ncand by construction
-    const bool in_lds = ncand <= (uint32_t)kIdxFinalLds;
+    const bool in_reg = ncand <= (uint32_t)kIdxFinalLds;
     const int nwords = (int)((n + 31) / 32);
     if (nwords <= kIdxBitmapWords) {
-        for (int i = threadIdx.x; i < kIdxDigitBins; i += blockDim.x) { hA[i] = 0u; hB[i] = 0u; }
-        if (in_lds)
-            for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) lc[i] = w.cand[i];
+        uint32_t* bmA = reinterpret_cast<uint32_t*>(bm4[0]);
+        uint32_t* bmT = reinterpret_cast<uint32_t*>(bm4[1]);
+        for (int i = tid; i < kIdxBitmapWords / 4; i += blockDim.x) {
+            bm4[0][i] = make_uint4(0u, 0u, 0u, 0u);
+            bm4[1][i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        for (int i = tid; i < kIdxDigitBins; i += blockDim.x) { hA[i] = 0u; hB[i] = 0u; }
         __syncthreads();
-        const uint2* cand = in_lds ? lc : w.cand;
-        digit_hist(cand, ncand, 10, false, 0u, hA);
+#pragma unroll
+        for (int q = 0; q < kIdxSelPerThread; q++) {
+            const uint32_t idx = tid + q * kIdxFinalThreads;
+            if (idx < nsel) atomicOr(&bmA[(uint32_t)sv[q] >> 5], 1u << (sv[q] & 31));
+        }
+        // digit passes over the candidates (registers, or global beyond 4096)
+        auto pass = [&](int shift, bool filt, uint32_t upper, uint32_t* h) {
+            uint32_t run_dg = 0, run_cnt = 0;
+            if (in_reg) {
+#pragma unroll
+                for (int q = 0; q < kIdxCandPerThread; q++) {
+                    const uint32_t i = tid + q * kIdxFinalThreads;
+                    const bool in = i < ncand && (!filt || ((cv[q].x >> 10) & 1023u) == upper);
+                    digit_hist_round(cv[q].x, in, shift, h, run_dg, run_cnt);
+                }
+            } else {                                      // batches of 8 rounds, loads first
+                for (uint32_t i0 = 0; i0 < ncand; i0 += 8 * blockDim.x) {
+                    uint32_t kk[8];
+#pragma unroll
+                    for (int q = 0; q < 8; q++) {
+                        const uint32_t i = i0 + q * blockDim.x + tid;
+                        kk[q] = i < ncand ? w.cand[i].x : 0u;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 8; q++) {
+                        const uint32_t i = i0 + q * blockDim.x + tid;
+                        const bool in = i < ncand && (!filt || ((kk[q] >> 10) & 1023u) == upper);
+                        digit_hist_round(kk[q], in, shift, h, run_dg, run_cnt);
+                    }
+                }
+            }
+            flush_digit_run(h, run_dg, run_cnt);
+        };
+        pass(10, false, 0u, hA);
         __syncthreads();
-        if (threadIdx.x < kWave) {
+        if (tid < kWave) {
             uint32_t dg, ab;
             wave_pick_digit1024(hA, need, dg, ab);
-            if (threadIdx.x == 0) { sh[0] = dg; sh[1] = ab; }
+            if (tid == 0) { sh[0] = dg; sh[1] = ab; }
         }
         __syncthreads();
         const uint32_t dA = sh[0], needA = need - sh[1];
-        digit_hist(cand, ncand, 0, true, dA, hB);
+        pass(0, true, dA, hB);
         __syncthreads();
-        if (threadIdx.x < kWave) {
+        if (tid < kWave) {
             uint32_t dg, ab;
             wave_pick_digit1024(hB, needA, dg, ab);
-            if (threadIdx.x == 0) { sh[2] = dg; sh[3] = ab; }
+            if (tid == 0) { sh[2] = dg; sh[3] = ab; }
         }
-        __syncthreads();                                  // every read of lc is done
+        __syncthreads();
         const uint32_t T = (dA << 10) | sh[2];
         const int needT = (int)(needA - sh[3]);           // ties at T to take, >= 1
-        uint32_t* bmA = big;
-        uint32_t* bmT = big + kIdxBitmapWords;
-        for (int i = threadIdx.x; i < nwords; i += blockDim.x) { bmA[i] = 0u; bmT[i] = 0u; }
-        __syncthreads();
-        for (uint32_t i = threadIdx.x; i < nsel; i += blockDim.x) {
-            const uint32_t j = (uint32_t)w.sel[i];
-            atomicOr(&bmA[j >> 5], 1u << (j & 31));
-        }
-        for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) {
-            const uint2 c = w.cand[i];
+        auto mark = [&](uint2 c) {
             const uint32_t sfx = c.x & 0xFFFFFu;
             if (sfx >= T) atomicOr(&(sfx > T ? bmA : bmT)[c.y >> 5], 1u << (c.y & 31));
+        };
+        if (in_reg) {
+#pragma unroll
+            for (int q = 0; q < kIdxCandPerThread; q++)
+                if (tid + q * kIdxFinalThreads < ncand) mark(cv[q]);
+        } else {
+            for (uint32_t i0 = 0; i0 < ncand; i0 += 8 * blockDim.x) {
+                uint2 cc[8];
+#pragma unroll
+                for (int q = 0; q < 8; q++) {
+                    const uint32_t i = i0 + q * blockDim.x + tid;
+                    cc[q] = i < ncand ? w.cand[i] : make_uint2(0u, 0u);
+                }
+#pragma unroll
+                for (int q = 0; q < 8; q++)
+                    if (i0 + q * blockDim.x + tid < ncand) mark(cc[q]);
+            }
         }
         __syncthreads();
-        const int per = (nwords + (int)blockDim.x - 1) / (int)blockDim.x;   // consecutive words per thread
-        const int w0 = (int)threadIdx.x * per;
+        // thread t owns words [8t, 8t + 8): bitmap words past nwords are zero
+        uint32_t am[kIdxWordsPerThread], tm[kIdxWordsPerThread];
+#pragma unroll
+        for (int v = 0; v < kIdxWordsPerThread / 4; v++) {
+            const uint4 x = bm4[0][tid * (kIdxWordsPerThread / 4) + v];
+            const uint4 y = bm4[1][tid * (kIdxWordsPerThread / 4) + v];
+            am[4 * v] = x.x; am[4 * v + 1] = x.y; am[4 * v + 2] = x.z; am[4 * v + 3] = x.w;
+            tm[4 * v] = y.x; tm[4 * v + 1] = y.y; tm[4 * v + 2] = y.z; tm[4 * v + 3] = y.w;
+        }
         uint32_t ct = 0;
-        for (int q = 0; q < per; q++)
-            if (w0 + q < nwords) ct += __popc(bmT[w0 + q]);
-        const int rt0 = (int)block_exclusive_scan(ct, wsum[0]);   // ties in the words before mine
+#pragma unroll
+        for (int q = 0; q < kIdxWordsPerThread; q++) ct += __popc(tm[q]);
+        int rt = (int)block_exclusive_scan(ct, wsum[0]);  // ties in the words before mine
         uint32_t cnt = 0;
-        int rt = rt0;
-        for (int q = 0; q < per; q++) {
-            if (w0 + q >= nwords) break;
-            const uint32_t tb = bmT[w0 + q];
-            cnt += __popc(bmA[w0 + q] | lowest_bits(tb, needT - rt));
+#pragma unroll
+        for (int q = 0; q < kIdxWordsPerThread; q++) {
+            const uint32_t tb = tm[q];
+            am[q] |= lowest_bits(tb, needT - rt);
             rt += __popc(tb);
+            cnt += __popc(am[q]);
         }
         uint32_t off = block_exclusive_scan(cnt, wsum[1]);
-        rt = rt0;
-        for (int q = 0; q < per; q++) {
-            if (w0 + q >= nwords) break;
-            const uint32_t tb = bmT[w0 + q];
-            uint32_t bits = bmA[w0 + q] | lowest_bits(tb, needT - rt);
-            rt += __popc(tb);
+        const int j0 = tid * kIdxWordsPerThread * 32;
+#pragma unroll
+        for (int q = 0; q < kIdxWordsPerThread; q++) {
+            uint32_t bits = am[q];
             while (bits) {
                 const int bpos = __builtin_ctz(bits);
                 bits &= bits - 1;
-                if (off < (uint32_t)a.topk) out[off] = (w0 + q) * 32 + bpos;
+                if (off < (uint32_t)a.topk) out[off] = j0 + 32 * q + bpos;
                 off++;
             }
         }
@@ -713,14 +773,14 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     }
     // very large caps: radix-select the composite (score suffix, inverted
     // block index) among the candidates, gather the k indices, bitonic-sort
-    int32_t* arr = reinterpret_cast<int32_t*>(big + 2 * kIdxFinalLds);
+    int32_t* arr = reinterpret_cast<int32_t*>(bm4[0]);
     const int jb = bits_for(a.cap);
     const uint64_t jmask = ((uint64_t)1 << jb) - 1;
-    if (in_lds) {
+    if (in_reg) {
         for (uint32_t i = threadIdx.x; i < ncand; i += blockDim.x) lc[i] = w.cand[i];
         __syncthreads();
     }
-    const uint2* cand = in_lds ? lc : w.cand;
+    const uint2* cand = in_reg ? lc : w.cand;
     auto get = [&](int64_t i) -> uint64_t {
         uint2 c = cand[i];
         return ((uint64_t)(c.x & 0xFFFFFu) << jb) | (jmask - (uint64_t)c.y);

@@ -181,7 +181,7 @@ def test_indexer_bf16_keys_mfma_exact(qkind):
 
 
 def test_indexer_very_large_cap_exact():
-    """More blocks than the final kernel's LDS bitmap covers (2^19): the
+    """More blocks than the final kernel's LDS bitmaps cover (2^18): the
     sorted-gather fallback."""
     g = synth.rng(545)
     B, Tq, Hi, di, m, k, cap = 1, 1, 4, 64, 4, 1024, 600000
