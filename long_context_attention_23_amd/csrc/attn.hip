@@ -27,6 +27,11 @@ namespace csa {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnTile = 8;
 constexpr int kAttnMaxD = 1024;
+// combine: one workgroup per (head, query row); every thread's partial loads
+// in flight at once (d / 4 columns x groups of splits)
+constexpr int kCombThreads = 1024;
+constexpr int kCombMaxSplits = 64;
+constexpr int kCombLoads = kCombMaxSplits / (kCombThreads / (kAttnMaxD / 4));
 constexpr int kAttnQFloats = 4096;
 
 __device__ __forceinline__ int64_t comp_slots(const AttnArgs& a, int64_t t) {
@@ -241,103 +246,116 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG) 
 
 // merge the splits of (row, head): weights exp(m_s - M) with M over the split
 // maxima and the sink.  Thread t sums float4 column t % (d/4) over the splits
-// of group t / (d/4) (splits g, g + G, ... in order, several loads in
-// flight); the groups are then added in group order.
+// of group t / (d/4) (splits g, g + G, ... in order); every partial load is
+// issued before the weights are known, so the workgroup waits for memory
+// once; the groups are then added in group order.
 template <typename OT>
-__global__ __launch_bounds__(kAttnThreads) void k_attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     warm_kernargs(offsetof(AttnArgs, rope));
     __shared__ float v[kAttnMaxD];
-    __shared__ float wsc[1024];
-    __shared__ float red[kAttnThreads / kWave];
+    __shared__ float wsc[kCombMaxSplits];
+    __shared__ float den_s;
     __shared__ double rf[64];
-    __shared__ float4 part[kAttnThreads];
+    __shared__ float4 part[kCombThreads];
+    const int tid = threadIdx.x;
     const int h = blockIdx.x;
     const int64_t row = blockIdx.y;
-    const int64_t t = a.q_pos[row];
-    const int64_t nc = comp_slots(a, t);
-    const int64_t ne = nc + a.W;
-    const int nsplit = (int)attn_nsplit<int64_t>(ne, a.Tq);
-    if (nsplit <= 1) return;
-    const float* wo = reinterpret_cast<const float*>(a.ws);
-    const float* wml = wo + (size_t)a.rows * a.nsplit_max * a.H * a.d;
+    const int NS = a.nsplit_max;
     const int d = a.d;
-    const float sk = a.sink[h];
-    stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
-    const size_t mbase = (size_t)row * a.nsplit_max * a.H + h;     // split s at mbase + s * H
-    float mx = sk;
-    for (int s = threadIdx.x; s < nsplit; s += blockDim.x) mx = fmaxf(mx, wml[(mbase + (size_t)s * a.H) * 2]);
-    const float M = block_max(mx, red);
-    float den = 0.0f;
-    for (int s = threadIdx.x; s < nsplit; s += blockDim.x) {
-        const size_t i = (mbase + (size_t)s * a.H) * 2;
-        const float ms = wml[i];
-        const float w = (ms == -INFINITY) ? 0.0f : expf(ms - M);
-        wsc[s] = w;
-        den += wml[i + 1] * w;
+    const float* wo = reinterpret_cast<const float*>(a.ws);
+    const float* wml = wo + (size_t)a.rows * NS * a.H * d;
+    const size_t mbase = (size_t)row * NS * a.H + h;           // split s at mbase + s * H
+    // ---- every load first: this thread's partial columns of its splits
+    // (addresses clamped to the buffer; splits past the row's count get weight
+    // 0 and are skipped), the position, the split maxima and sums
+    const int nc4 = d / 4 > 0 ? d / 4 : 1;
+    const int G = (int)blockDim.x / nc4;                        // split groups
+    const int c = tid % nc4, g = tid / nc4;
+    const float4* wo4 = reinterpret_cast<const float4*>(wo + mbase * d) + c;
+    const size_t sstride = (size_t)a.H * d / 4;                 // float4s between splits
+    const bool vec = d % 4 == 0;
+    const int nq = vec ? (NS + G - 1) / G : 0;
+    float4 x[kCombLoads];
+#pragma unroll
+    for (int q = 0; q < kCombLoads; q++) {
+        x[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (q < nq) x[q] = wo4[(size_t)min(g + q * G, NS - 1) * sstride];
     }
-    den = block_sum(den, red);
-    if (M != -INFINITY) den += expf(sk - M);
+    const int64_t t = a.q_pos[row];
+    const int lane = tid & (kWave - 1);
+    float ms = -INFINITY, ls = 0.0f;
+    if (tid < kWave) {
+        const size_t i = (mbase + (size_t)min(lane, NS - 1) * a.H) * 2;
+        ms = wml[i];
+        ls = wml[i + 1];
+    }
+    stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
+    const int64_t nc = comp_slots(a, t);
+    const int nsplit = (int)attn_nsplit<int64_t>(nc + a.W, a.Tq);
+    if (nsplit <= 1) return;
+    // ---- split weights, one wave (at most 64 splits)
+    if (tid < kWave) {
+        const float sk = a.sink[h];
+        const bool live = lane < nsplit;
+        const float M = fmaxf(sk, wave_max_dpp(live ? ms : -INFINITY));
+        const float w = (!live || ms == -INFINITY) ? 0.0f : expf(ms - M);
+        float den = wave_sum_dpp(ls * w);
+        if (M != -INFINITY) den += expf(sk - M);
+        wsc[lane] = w;
+        if (lane == 0) den_s = den;
+    }
     __syncthreads();
-    if (d % 4 != 0) {
+    if (!vec) {
         // head dims not a multiple of 4: one dim per thread, splits in order
+        const float den = den_s;
         const float* wo_h = wo + mbase * d;
-        for (int k = threadIdx.x; k < d; k += blockDim.x) {
+        for (int k = tid; k < d; k += blockDim.x) {
             float acc = 0.0f;
-            for (int s = 0; s < nsplit; s++) acc = fmaf(wsc[s], wo_h[(size_t)s * a.H * d + k], acc);
+            for (int s2 = 0; s2 < nsplit; s2++) acc = fmaf(wsc[s2], wo_h[(size_t)s2 * a.H * d + k], acc);
             v[k] = den > 0.0f ? acc / den : 0.0f;
         }
         __syncthreads();
-        rotate_out(a, t, v, threadIdx.x, blockDim.x, rf);
+        rotate_out(a, t, v, tid, blockDim.x, rf);
         __syncthreads();
         OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
-        for (int k = threadIdx.x; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
+        for (int k = tid; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
         return;
     }
-    const int nc4 = d / 4;
-    const int G = (int)blockDim.x / nc4;       // split groups
-    const int c = threadIdx.x % nc4, g = threadIdx.x / nc4;
-    const float4* wo4 = reinterpret_cast<const float4*>(wo + mbase * d) + c;
-    const size_t sstride = (size_t)a.H * d / 4;               // float4s between splits
+    // ---- this thread's splits in order, then the groups in order
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (g < G) {
-        constexpr int kB = 8;
-        for (int s0 = g; s0 < nsplit; s0 += kB * G) {
-            float4 x[kB];
 #pragma unroll
-            for (int q = 0; q < kB; q++) {
-                const int s = s0 + q * G;
-                x[q] = s < nsplit ? wo4[(size_t)s * sstride] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            }
-#pragma unroll
-            for (int q = 0; q < kB; q++) {
-                const int s = s0 + q * G;
-                const float w = s < nsplit ? wsc[s] : 0.0f;
+        for (int q = 0; q < kCombLoads; q++) {
+            const int s = g + q * G;
+            if (q < nq && s < nsplit) {
+                const float w = wsc[s];
                 acc.x = fmaf(w, x[q].x, acc.x);
                 acc.y = fmaf(w, x[q].y, acc.y);
                 acc.z = fmaf(w, x[q].z, acc.z);
                 acc.w = fmaf(w, x[q].w, acc.w);
             }
         }
-        part[threadIdx.x] = acc;
     }
+    part[tid] = acc;
     __syncthreads();
-    if ((int)threadIdx.x < nc4) {
-        float4 r = part[threadIdx.x];
+    const float den = den_s;
+    if (tid < nc4) {
+        float4 r = part[tid];
         for (int q = 1; q < G; q++) {
-            const float4 y = part[q * nc4 + threadIdx.x];
+            const float4 y = part[q * nc4 + tid];
             r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
         }
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        v[4 * threadIdx.x] = den > 0.0f ? r.x * inv : 0.0f;
-        v[4 * threadIdx.x + 1] = den > 0.0f ? r.y * inv : 0.0f;
-        v[4 * threadIdx.x + 2] = den > 0.0f ? r.z * inv : 0.0f;
-        v[4 * threadIdx.x + 3] = den > 0.0f ? r.w * inv : 0.0f;
+        v[4 * tid] = den > 0.0f ? r.x * inv : 0.0f;
+        v[4 * tid + 1] = den > 0.0f ? r.y * inv : 0.0f;
+        v[4 * tid + 2] = den > 0.0f ? r.z * inv : 0.0f;
+        v[4 * tid + 3] = den > 0.0f ? r.w * inv : 0.0f;
     }
     __syncthreads();
-    rotate_out(a, t, v, threadIdx.x, blockDim.x, rf);
+    rotate_out(a, t, v, tid, blockDim.x, rf);
     __syncthreads();
     OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
-    for (int k = threadIdx.x; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
+    for (int k = tid; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
 }
 
 int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t max_entries) {
@@ -366,8 +384,8 @@ hipError_t launch_attention(const AttnArgs& a0, int64_t max_entries, hipStream_t
     }
     if (nb > 1) {
         dim3 g2((unsigned)a.H, (unsigned)a.rows);
-        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kAttnThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kAttnThreads), 0, st, a);
+        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kCombThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kCombThreads), 0, st, a);
     }
     return hipGetLastError();
 }
