@@ -4,6 +4,7 @@
 // Every argument check runs before the first HIP call, so a non-OK status
 // means nothing was enqueued (and every error path can be exercised without a
 // GPU).  No device memory is allocated here.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -229,7 +230,11 @@ CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, in
 CSA_API size_t csa_indexer_topk_workspace_size(int32_t B, int32_t Tq, int64_t key_cap, int32_t topk) {
     const int64_t rows = (int64_t)(B > 0 ? B : 0) * (Tq > 0 ? Tq : 0);
     if (rows == 0 || key_cap <= csa::kIdxSmallMaxKeys || topk < 1) return 0;
-    return (size_t)(idx_rows_per_batch(rows, key_cap, topk) * csa::idx_ws_row_bytes(key_cap, topk));
+    int64_t need = idx_rows_per_batch(rows, key_cap, topk) * csa::idx_ws_row_bytes(key_cap, topk);
+    // room for the query-batched prefill path too (used for FP4 queries and keys)
+    if (csa::idx_prefill_eligible(64, 4, Tq, key_cap, topk))
+        need = std::max<int64_t>(need, rows * csa::idx_prefill_row_bytes());
+    return (size_t)need;
 }
 
 CSA_API csa_status csa_indexer_topk(const void* q_idx, const uint8_t* q_idx_scales, int32_t q_dtype, const float* w_idx,

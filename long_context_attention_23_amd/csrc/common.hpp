@@ -195,6 +195,9 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// wave ballot of a predicate, straight from its condition mask
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
 // the value of v in lane `lane` (a wave-uniform index), as a scalar read
 __device__ __forceinline__ uint32_t lane_u32(uint32_t v, int lane) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);

@@ -27,6 +27,8 @@
 //      LDS bitmaps (caps beyond 2^19: composite radix select and a bitonic
 //      sort).  The append order of A/C does not matter: D's result depends
 //      only on the sets.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -813,6 +815,597 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     for (int i = threadIdx.x; i < a.topk; i += blockDim.x) out[i] = arr[i];
 }
 
+// ------------------------------------------------------------------ prefill path
+// A chunk of many query rows with FP4 queries and keys (di = 64, Hi = 4):
+// eight queries x four heads fill the 32 rows of one FP4 MFMA, so one
+// 32x32x64 product scores 32 keys for 8 queries (the per-row path pads the
+// four heads to 32 rows).  Kernels:
+//   T  per query, the r-th largest score key of a systematic sample (every
+//      stride-th 32-key tile); r * stride ~ 4k, so about 4k keys of the row
+//      score at or above it;
+//   F  16 queries per workgroup stream every key tile once; keys scoring
+//      above their query's threshold are appended (key, j) to per-(query,
+//      wave) segments, keys tying with it (j) to per-(query, wave) tie
+//      segments that keep each wave's first ties in ascending j (no atomics:
+//      each wave counts its own);
+//   S  per query: with at least k keys above the threshold, three 11-bit
+//      digit passes over their score keys give the k-th largest value T1 and
+//      ties at T1 go to the smaller block index (two 10-bit passes over the
+//      inverted index find the cut); with fewer, all of them are in plus the
+//      smallest j of the threshold ties.  Members are marked in an LDS bitmap
+//      over j and emitted in ascending j.
+//   X  a query whose above-threshold keys overflowed a segment, or whose
+//      candidates are fewer than k (its sample ranked it too high), is flagged
+//      by S and recomputed here exactly: the same digit passes over all its
+//      recomputed scores.
+// S is exact: the top k of a row lie among its keys at or above the
+// threshold whenever those number at least k, and the smallest-j ties needed
+// are among the stored ones (a wave's ties arrive in ascending j).
+constexpr int kPfQ = 8;                  // queries per MFMA row block
+constexpr int kPfRB = 2;                 // row blocks per filter workgroup
+constexpr int kPfQB = kPfQ * kPfRB;      // queries per filter workgroup
+constexpr int kPfThreads = 512;          // threshold, filter and exact workgroups
+constexpr int kPfWaves = kPfThreads / kWave;
+constexpr int kPfSelThreads = 256;       // select workgroups
+constexpr int kPfMaxSampTiles = 128;     // sample tiles per query (LDS: 8 x 4096 keys)
+constexpr int kPfWords = 16384;          // bitmap words: caps up to 2^19 blocks
+constexpr int kPfHdr = 128;              // per-row header: thr, flag, 8 above counts, 8 tie counts
+constexpr int kPfSeg = kIdxPfCands / kPfWaves;     // above-threshold slots per (query, wave)
+constexpr int kPfTieSeg = kIdxPfMaxTopk;           // tie slots per (query, wave)
+static_assert(idx_prefill_row_bytes() == kPfHdr + (int64_t)kIdxPfCands * 8 + (int64_t)kPfWaves * kPfTieSeg * 4,
+              "prefill row layout");
+
+// row layout: header words [0] threshold key, [1] flag, [2..10) above counts
+// per wave, [10..18) tie counts per wave; then the above-threshold (key, j)
+// segments, then the tie j segments (each wave's first kPfTieSeg ties, in
+// ascending j)
+__device__ __forceinline__ uint32_t* pf_hdr(const IndexerArgs& a, int64_t row) {
+    return reinterpret_cast<uint32_t*>(a.ws + row * a.ws_row_bytes);
+}
+__device__ __forceinline__ uint2* pf_cand(const IndexerArgs& a, int64_t row) {
+    return reinterpret_cast<uint2*>(a.ws + row * a.ws_row_bytes + kPfHdr);
+}
+__device__ __forceinline__ uint32_t* pf_ties(const IndexerArgs& a, int64_t row) {
+    return reinterpret_cast<uint32_t*>(a.ws + row * a.ws_row_bytes + kPfHdr + (int64_t)kIdxPfCands * 8);
+}
+
+// A operand of one row block: row l32 = query 4 * (l32 / 4) + head l32 % 4 of
+// the 8 queries from tq (zero codes past Tq)
+__device__ __forceinline__ void pf_load_a(const IndexerArgs& a, int b, int tq, int l32, int half, i32x8_t& qa,
+                                          int& qs) {
+    const int t = tq + l32 / 4, h = l32 & 3;
+    qa = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    qs = 127;
+    if (t < a.Tq) {
+        const int64_t r = ((int64_t)b * a.Tq + t) * 4 + h;
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.q) + r * 32 + 16 * half);
+        qa[0] = (int)u.x; qa[1] = (int)u.y; qa[2] = (int)u.z; qa[3] = (int)u.w;
+        qs = a.q_scales[r * 2 + half];
+    }
+}
+
+// key tile at j0: lane's 16 code bytes and scale of key j0 + l32 (clamped)
+__device__ __forceinline__ void pf_load_keys(const IndexerArgs& a, int b, int64_t j0, int l32, int half, uint4& kc,
+                                             int& ks) {
+    const int64_t j = min(j0 + l32, a.cap - 1);
+    const int64_t r = (int64_t)b * a.cap + j;
+    kc = *reinterpret_cast<const uint4*>(a.keys + r * 32 + 16 * half);
+    ks = a.key_scales[r * 2 + half];
+}
+
+__device__ __forceinline__ f32x16_t pf_mfma(const i32x8_t& qa, int qs, const uint4& kc, int ks) {
+    const i32x8_t kf = i32x8_t{(int)kc.x, (int)kc.y, (int)kc.z, (int)kc.w, 0, 0, 0, 0};
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[i] = 0.0f;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kf, acc, 4, 4, 0, qs, 0, ks);
+}
+
+// score of slot s (query 2s + half of the row block): heads in order, from +0
+__device__ __forceinline__ float pf_score(const f32x16_t& acc, int s, const float* w4) {
+    float v = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 4; h++) v = fmaf(w4[h], fmaxf(acc[4 * s + h], 0.0f), v);
+    return v;
+}
+
+__global__ __launch_bounds__(kPfThreads) void k_idxp_thresh(IndexerArgs a, int32_t stride, int32_t rank) {
+    warm_kernargs(sizeof(IndexerArgs));
+    __shared__ uint32_t ss[kPfQ][kPfMaxSampTiles * 32];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int b = blockIdx.y, tq = blockIdx.x * kPfQ;
+    i32x8_t qa;
+    int qs;
+    pf_load_a(a, b, tq, l32, half, qa, qs);
+    float w[4][4];
+    int32_t nq[4];
+    int32_t nmax = 0;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+        const int t = tq + 2 * s + half;
+        const int64_t row = (int64_t)b * a.Tq + t;
+        nq[s] = t < a.Tq ? (int32_t)visible_blocks(a, row) : 0;
+        nmax = max(nmax, nq[s]);
+#pragma unroll
+        for (int h = 0; h < 4; h++) w[s][h] = t < a.Tq ? a.w[row * 4 + h] : 0.0f;
+    }
+    nmax = (int32_t)wave_max_dpp((float)nmax);          // exact: counts < 2^24
+    const int ntile = (nmax + 31) / 32;
+    const int nst = min((ntile + stride - 1) / stride, kPfMaxSampTiles);
+    for (int i = wv; i < nst; i += kPfWaves) {
+        const int64_t j0 = (int64_t)i * stride * 32;
+        uint4 kc;
+        int ks;
+        pf_load_keys(a, b, j0, l32, half, kc, ks);
+        const f32x16_t acc = pf_mfma(qa, qs, kc, ks);
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const float v = pf_score(acc, s, w[s]);
+            ss[2 * s + half][i * 32 + l32] = j0 + l32 < nq[s] ? score_key(v) : 0u;
+        }
+    }
+    __syncthreads();
+    // wave q: the rank-th largest of query q's samples (largest T with at least
+    // rank samples >= T, built bit by bit); padding counts only at T = 0
+    const int q = wv;
+    const int t = tq + q;
+    uint32_t v[kPfMaxSampTiles * 32 / kWave];
+#pragma unroll
+    for (int i = 0; i < kPfMaxSampTiles * 32 / kWave; i++) {
+        const int idx = lane + kWave * i;
+        v[i] = idx < nst * 32 ? ss[q][idx] : 0u;
+    }
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; bit--) {
+        const uint32_t c = T | (1u << bit);
+        float cnt = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPfMaxSampTiles * 32 / kWave; i++) cnt += v[i] >= c ? 1.0f : 0.0f;
+        if (wave_sum_dpp(cnt) >= (float)rank) T = c;
+    }
+    if (t < a.Tq && lane < kPfHdr / 4) {
+        uint32_t* hd = pf_hdr(a, (int64_t)b * a.Tq + t);
+        hd[lane] = lane == 0 ? T : 0u;                     // thr, flag, counts
+    }
+}
+
+__global__ __launch_bounds__(kPfThreads) void k_idxp_filter(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int b = blockIdx.y, t0 = blockIdx.x * kPfQB;
+    i32x8_t qa[kPfRB];
+    int qs[kPfRB];
+    float w[kPfRB][4][4];
+    float thr[kPfRB][4];                                  // threshold key as a float (NaN for key 0)
+    int32_t nq[kPfRB][4];
+    int32_t nmax = 0;
+#pragma unroll
+    for (int rb = 0; rb < kPfRB; rb++) {
+        pf_load_a(a, b, t0 + kPfQ * rb, l32, half, qa[rb], qs[rb]);
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            const int t = t0 + kPfQ * rb + 2 * s + half;
+            const int64_t row = (int64_t)b * a.Tq + min(t, a.Tq - 1);
+            nq[rb][s] = t < a.Tq ? (int32_t)visible_blocks(a, row) : 0;
+            nmax = max(nmax, nq[rb][s]);
+            {
+                // inverse of score_key: key > T <=> score > thr and key == T <=>
+                // score == thr for every score (NaN and T = 0: neither)
+                const uint32_t T = pf_hdr(a, row)[0];
+                thr[rb][s] = __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
+            }
+#pragma unroll
+            for (int h = 0; h < 4; h++) w[rb][s][h] = t < a.Tq ? a.w[row * 4 + h] : 0.0f;
+        }
+    }
+    nmax = (int32_t)wave_max_dpp((float)nmax);
+    const int ntile = (nmax + 31) / 32;
+    // this wave's running counts per query (above the threshold, at it):
+    // slot (rb, s, half) -> query 8 rb + 2 s + half
+    uint32_t cnt[kPfRB][4][2], tcnt[kPfRB][4][2];
+#pragma unroll
+    for (int rb = 0; rb < kPfRB; rb++)
+#pragma unroll
+        for (int s = 0; s < 4; s++) { cnt[rb][s][0] = cnt[rb][s][1] = tcnt[rb][s][0] = tcnt[rb][s][1] = 0u; }
+    const int64_t rowb = a.ws_row_bytes;
+    uint8_t* wbase = a.ws + ((int64_t)b * a.Tq + t0) * rowb;   // this workgroup's first query row
+    const int64_t hoff = half ? rowb : 0;                        // odd queries of a slot pair
+    uint4 kc;
+    int ks;
+    if (wv < ntile) pf_load_keys(a, b, (int64_t)wv * 32, l32, half, kc, ks);
+    for (int tile = wv; tile < ntile; tile += kPfWaves) {
+        const uint4 kcur = kc;
+        const int kscur = ks;
+        if (tile + kPfWaves < ntile) pf_load_keys(a, b, (int64_t)(tile + kPfWaves) * 32, l32, half, kc, ks);
+        f32x16_t acc[kPfRB];
+#pragma unroll
+        for (int rb = 0; rb < kPfRB; rb++) acc[rb] = pf_mfma(qa[rb], qs[rb], kcur, kscur);
+        const int32_t j = tile * 32 + l32;
+#pragma unroll
+        for (int rb = 0; rb < kPfRB; rb++) {
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const float sc = pf_score(acc[rb], s, w[rb][s]);
+                const bool vis = j < nq[rb][s];
+                const bool above = vis && sc > thr[rb][s], tie = vis && sc == thr[rb][s];
+                const uint64_t bal = ballot64(above), bt = ballot64(tie);
+                if (bal | bt) {
+                    // rank among this half's hits: mbcnt over the whole wave,
+                    // less the lower half's count for the upper half
+                    const uint32_t alo = (uint32_t)bal, ahi = (uint32_t)(bal >> 32);
+                    const uint32_t tlo = (uint32_t)bt, thi = (uint32_t)(bt >> 32);
+                    uint8_t* rp = wbase + (int64_t)(kPfQ * rb + 2 * s) * rowb + hoff;
+                    if (above) {
+                        const uint32_t r = __builtin_amdgcn_mbcnt_hi(ahi, __builtin_amdgcn_mbcnt_lo(alo, 0u));
+                        const uint32_t pos = r + (half ? cnt[rb][s][1] - __popc(alo) : cnt[rb][s][0]);
+                        if (pos < (uint32_t)kPfSeg)
+                            reinterpret_cast<uint2*>(rp + kPfHdr)[wv * kPfSeg + pos] = make_uint2(score_key(sc), (uint32_t)j);
+                    }
+                    if (tie) {
+                        const uint32_t r = __builtin_amdgcn_mbcnt_hi(thi, __builtin_amdgcn_mbcnt_lo(tlo, 0u));
+                        const uint32_t pos = r + (half ? tcnt[rb][s][1] - __popc(tlo) : tcnt[rb][s][0]);
+                        if (pos < (uint32_t)kPfTieSeg)
+                            reinterpret_cast<uint32_t*>(rp + kPfHdr + (int64_t)kIdxPfCands * 8)[wv * kPfTieSeg + pos] = (uint32_t)j;
+                    }
+                    cnt[rb][s][0] += __popc(alo);
+                    cnt[rb][s][1] += __popc(ahi);
+                    tcnt[rb][s][0] += __popc(tlo);
+                    tcnt[rb][s][1] += __popc(thi);
+                }
+            }
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int rb = 0; rb < kPfRB; rb++)
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+#pragma unroll
+                for (int hf = 0; hf < 2; hf++) {
+                    const int t = t0 + kPfQ * rb + 2 * s + hf;
+                    if (t < a.Tq) {
+                        uint32_t* hd = pf_hdr(a, (int64_t)b * a.Tq + t);
+                        hd[2 + wv] = cnt[rb][s][hf];
+                        hd[2 + kPfWaves + wv] = tcnt[rb][s][hf];
+                    }
+                }
+    }
+}
+
+// histogram of the 11-bit (or narrower) digit (v >> shift) & mask of the values
+// `in`, a wave whose lanes mostly agree adding once per distinct digit (as
+// digit_hist_round, without the run register)
+__device__ __forceinline__ void pf_hist_round(uint32_t v, bool in, int shift, uint32_t mask, uint32_t* hist) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t dg = (v >> shift) & mask;
+    const uint64_t act = __ballot(in);
+    const uint32_t d0 = lane_u32(dg, act ? __builtin_ctzll(act) : 0);
+    if (__popcll(__ballot(in && dg == d0)) > 8) {
+        uint64_t todo = act;
+        while (todo) {
+            const int leader = __builtin_ctzll(todo);
+            const uint32_t dl = lane_u32(dg, leader);
+            const uint64_t same = __ballot(in && dg == dl) & todo;
+            if (lane == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+            todo &= ~same;
+        }
+    } else if (in) {
+        atomicAdd(&hist[dg], 1u);
+    }
+}
+
+// in an nb-bin histogram (nb a multiple of 64), the digit whose cumulative
+// count from the top first reaches need, and the count strictly above it;
+// one wave, result in every lane
+template <int NB>
+__device__ __forceinline__ void pf_pick(const uint32_t* hist, uint32_t need, uint32_t& digit, uint32_t& above) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int per = NB / kWave;
+    uint32_t h[per], s = 0;
+#pragma unroll
+    for (int q = 0; q < per; q++) { h[q] = hist[NB - 1 - per * lane - q]; s += h[q]; }
+    const uint32_t incl = wave_incl_scan_dpp(s);
+    const uint64_t bal = __ballot(incl >= need);
+    const int L = bal ? __builtin_ctzll(bal) : kWave - 1;
+    const uint32_t cum = lane_u32(incl - s, L);
+    uint32_t d = 0, ab = cum;
+    if (lane == L) {
+        uint32_t c = cum;
+        d = NB - per * (L + 1);
+        for (int q = 0; q < per; q++) {
+            if (c + h[q] >= need) { d = NB - 1 - per * L - q; ab = c; break; }
+            c += h[q];
+        }
+    }
+    digit = lane_u32(d, L);
+    above = lane_u32(ab, L);
+}
+
+// emit the members marked in bitmap bm (nw words) in ascending j, thread t
+// owning words [t * WPT, (t + 1) * WPT); output padded with -1 to topk
+template <int WPT>
+__device__ __forceinline__ void pf_emit(const uint32_t* bm, int32_t* out, int topk, uint32_t* wsum) {
+    uint32_t am[WPT], cnt = 0;
+#pragma unroll
+    for (int v = 0; v < WPT / 4; v++) {
+        const uint4 x = reinterpret_cast<const uint4*>(bm)[threadIdx.x * (WPT / 4) + v];
+        am[4 * v] = x.x; am[4 * v + 1] = x.y; am[4 * v + 2] = x.z; am[4 * v + 3] = x.w;
+    }
+#pragma unroll
+    for (int q = 0; q < WPT; q++) cnt += __popc(am[q]);
+    uint32_t off = block_exclusive_scan(cnt, wsum);
+    const int j0 = threadIdx.x * WPT * 32;
+#pragma unroll
+    for (int q = 0; q < WPT; q++) {
+        uint32_t bits = am[q];
+        while (bits) {
+            const int bpos = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (off < (uint32_t)topk) out[off] = j0 + 32 * q + bpos;
+            off++;
+        }
+    }
+}
+
+// the need-th smallest j among the slots flagged in ok (CPT per thread): two
+// 10-bit digit passes over 2^20 - 1 - j; ties with j <= the result are in
+template <int CPT>
+__device__ __forceinline__ uint32_t pf_jcut(const uint32_t (&jv)[CPT], const bool (&ok)[CPT], uint32_t nslots,
+                                            uint32_t need, uint32_t* hist, uint32_t* sh) {
+    const uint32_t jm = (1u << 20) - 1u;
+    uint32_t jp = 0, jmsk = 0;
+    const int js[2] = {10, 0};
+    for (int p = 0; p < 2; p++) {
+        for (int i = threadIdx.x; i < 1024; i += blockDim.x) hist[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < CPT; q++) {
+            if (q * (int)blockDim.x >= (int)nslots) break;   // block-uniform
+            const uint32_t iv = jm - jv[q];
+            pf_hist_round(iv, ok[q] && (iv & jmsk) == jp, js[p], 1023u, hist);
+        }
+        __syncthreads();
+        if (threadIdx.x < kWave) {
+            uint32_t dg, ab;
+            pf_pick<1024>(hist, need, dg, ab);
+            if (threadIdx.x == 0) { sh[0] = dg; sh[1] = ab; }
+        }
+        __syncthreads();
+        jp |= sh[0] << js[p];
+        jmsk |= 1023u << js[p];
+        need -= sh[1];
+        __syncthreads();
+    }
+    return jm - jp;
+}
+
+// entry i of the concatenation of NW segments (counts c[], stride seg) -> slot
+template <int NW>
+__device__ __forceinline__ uint32_t pf_slot(uint32_t i, const uint32_t (&c)[NW], int seg) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int s = 0; s < NW - 1; s++)
+        if (w == (uint32_t)s && i >= c[s]) { i -= c[s]; w++; }
+    return w * seg + i;
+}
+
+__global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    constexpr int kCPT = kIdxPfCands / kPfSelThreads;          // candidates per thread
+    constexpr int kWPT = kPfWords / kPfSelThreads;
+    __shared__ uint4 bm4[kPfWords / 4];
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t wsum[kPfSelThreads / kWave];
+    uint32_t* bm = reinterpret_cast<uint32_t*>(bm4);
+    const int tid = threadIdx.x;
+    const int b = blockIdx.y, t = blockIdx.x;
+    const int64_t row = (int64_t)b * a.Tq + t;
+    const int64_t n = visible_blocks(a, row);
+    int32_t* out = a.out + row * a.topk;
+    if (n <= a.topk) {
+        for (int64_t i = tid; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
+        return;
+    }
+    uint32_t* hd = pf_hdr(a, row);
+    uint32_t segc[kPfWaves], tiec[kPfWaves], tot = 0, ttot = 0, tstored = 0;
+    bool over = false;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; w++) {
+        segc[w] = hd[2 + w];
+        tiec[w] = hd[2 + kPfWaves + w];
+        over |= segc[w] > (uint32_t)kPfSeg;
+        tot += segc[w];
+        ttot += tiec[w];
+        tiec[w] = min(tiec[w], (uint32_t)kPfTieSeg);           // entries stored
+        tstored += tiec[w];
+    }
+    const uint32_t k = (uint32_t)a.topk;
+    if (over || tot + ttot < k) {
+        if (tid == 0) hd[1] = 1u;                              // left to the exact kernel
+        return;
+    }
+    const uint2* cand = pf_cand(a, row);
+    uint2 cv[kCPT];
+#pragma unroll
+    for (int q = 0; q < kCPT; q++) {
+        const uint32_t i = tid + q * kPfSelThreads;
+        cv[q] = make_uint2(0u, 0u);
+        if (i < tot) cv[q] = cand[pf_slot(i, segc, kPfSeg)];
+    }
+    for (int i = tid; i < kPfWords / 4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (tot >= k) {
+        // the top k lie among the keys above the threshold: three digit passes
+        // over the 32-bit score key (11, 11, 10 bits), then the smallest j of
+        // the ties at the k-th largest key
+        uint32_t need = k, prefix = 0, pmask = 0;
+        const int shifts[3] = {21, 10, 0};
+        const uint32_t masks[3] = {2047u, 2047u, 1023u};
+        for (int p = 0; p < 3; p++) {
+            for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kCPT; q++) {
+                if (q * kPfSelThreads >= tot) break;              // block-uniform
+                const bool in = tid + q * kPfSelThreads < tot && (cv[q].x & pmask) == prefix;
+                pf_hist_round(cv[q].x, in, shifts[p], masks[p], hist);
+            }
+            __syncthreads();
+            if (tid < kWave) {
+                uint32_t dg, ab;
+                if (p < 2) pf_pick<2048>(hist, need, dg, ab);
+                else pf_pick<1024>(hist, need, dg, ab);
+                if (tid == 0) { sh[0] = dg; sh[1] = ab; }
+            }
+            __syncthreads();
+            prefix |= sh[0] << shifts[p];
+            pmask |= masks[p] << shifts[p];
+            need -= sh[1];
+            __syncthreads();
+        }
+        const uint32_t T1 = prefix;
+        uint32_t jv[kCPT];
+        bool ok[kCPT];
+        uint32_t ntie = 0;
+#pragma unroll
+        for (int q = 0; q < kCPT; q++) {
+            jv[q] = cv[q].y;
+            ok[q] = tid + q * kPfSelThreads < tot && cv[q].x == T1;
+            ntie += ok[q] ? 1u : 0u;
+        }
+        if (tid == 0) sh[2] = 0u;
+        __syncthreads();
+        if (ntie) atomicAdd(&sh[2], ntie);
+        __syncthreads();
+        const uint32_t jcut = sh[2] > need ? pf_jcut<kCPT>(jv, ok, tot, need, hist, sh) : 0xFFFFFFFFu;
+#pragma unroll
+        for (int q = 0; q < kCPT; q++) {
+            const uint2 c = cv[q];
+            if (tid + q * kPfSelThreads < tot && (c.x > T1 || (c.x == T1 && c.y <= jcut)))
+                atomicOr(&bm[c.y >> 5], 1u << (c.y & 31));
+        }
+    } else {
+        // every key above the threshold is in, and the (k - tot) smallest j of
+        // those at it: each wave stored its own first ties, so they are here
+        const uint32_t* ties = pf_ties(a, row);
+        uint32_t jv[kCPT];
+        bool ok[kCPT];
+#pragma unroll
+        for (int q = 0; q < kCPT; q++) {
+            const uint32_t i = tid + q * kPfSelThreads;
+            ok[q] = i < tstored;
+            jv[q] = ok[q] ? ties[pf_slot(i, tiec, kPfTieSeg)] : 0u;
+        }
+        const uint32_t jcut = pf_jcut<kCPT>(jv, ok, tstored, k - tot, hist, sh);
+#pragma unroll
+        for (int q = 0; q < kCPT; q++) {
+            if (tid + q * kPfSelThreads < tot) atomicOr(&bm[cv[q].y >> 5], 1u << (cv[q].y & 31));
+            if (ok[q] && jv[q] <= jcut) atomicOr(&bm[jv[q] >> 5], 1u << (jv[q] & 31));
+        }
+    }
+    __syncthreads();
+    pf_emit<kWPT>(bm, out, a.topk, wsum);
+}
+
+// exact selection of a flagged query row from its recomputed scores: digit
+// passes over the score key, then over the inverted block index of the ties,
+// then the members marked and emitted
+__global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    constexpr int kWPT = kPfWords / kPfThreads;
+    __shared__ uint4 bm4[kPfWords / 4];
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t wsum[kPfWaves];
+    uint32_t* bm = reinterpret_cast<uint32_t*>(bm4);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int b = blockIdx.y, t = blockIdx.x;
+    const int64_t row = (int64_t)b * a.Tq + t;
+    uint32_t* hd = pf_hdr(a, row);
+    if (hd[1] == 0u) return;
+    const int64_t n = visible_blocks(a, row);
+    int32_t* out = a.out + row * a.topk;
+    // A operand: rows 0..3 = the four heads of this query, the rest zero
+    i32x8_t qa = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    int qs = 127;
+    if (l32 < 4) {
+        const int64_t r = row * 4 + l32;
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.q) + r * 32 + 16 * half);
+        qa[0] = (int)u.x; qa[1] = (int)u.y; qa[2] = (int)u.z; qa[3] = (int)u.w;
+        qs = a.q_scales[r * 2 + half];
+    }
+    float w4[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) w4[h] = a.w[row * 4 + h];
+    const int ntile = (int)((n + 31) / 32);
+    // every key of the row, lanes < 32 holding the score key of key j (the
+    // other half of the wave holds zero rows); fn(key, j, valid) per lane
+    auto sweep = [&](auto fn) {
+        for (int tile = wv; tile < ntile; tile += kPfWaves) {
+            uint4 kc;
+            int ks;
+            pf_load_keys(a, b, (int64_t)tile * 32, l32, half, kc, ks);
+            const f32x16_t acc = pf_mfma(qa, qs, kc, ks);
+            const float v = pf_score(acc, 0, w4);
+            const int32_t j = tile * 32 + l32;
+            fn(score_key(v), (uint32_t)j, half == 0 && j < n);
+        }
+    };
+    uint32_t need = (uint32_t)a.topk, prefix = 0, pmask = 0;
+    const int shifts[3] = {21, 10, 0};
+    const uint32_t masks[3] = {2047u, 2047u, 1023u};
+    for (int p = 0; p < 3; p++) {
+        for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;
+        __syncthreads();
+        sweep([&](uint32_t key, uint32_t, bool ok) {
+            pf_hist_round(key, ok && (key & pmask) == prefix, shifts[p], masks[p], hist);
+        });
+        __syncthreads();
+        if (tid < kWave) {
+            uint32_t dg, ab;
+            if (p < 2) pf_pick<2048>(hist, need, dg, ab);
+            else pf_pick<1024>(hist, need, dg, ab);
+            if (tid == 0) { sh[0] = dg; sh[1] = ab; }
+        }
+        __syncthreads();
+        prefix |= sh[0] << shifts[p];
+        pmask |= masks[p] << shifts[p];
+        need -= sh[1];
+        __syncthreads();
+    }
+    const uint32_t T1 = prefix;
+    const uint32_t jm = (1u << 20) - 1u;
+    uint32_t jp = 0, jmsk = 0, jneed = need;
+    const int js[2] = {10, 0};
+    for (int p = 0; p < 2; p++) {
+        for (int i = tid; i < 1024; i += blockDim.x) hist[i] = 0u;
+        __syncthreads();
+        sweep([&](uint32_t key, uint32_t j, bool ok) {
+            const uint32_t iv = jm - j;
+            pf_hist_round(iv, ok && key == T1 && (iv & jmsk) == jp, js[p], 1023u, hist);
+        });
+        __syncthreads();
+        if (tid < kWave) {
+            uint32_t dg, ab;
+            pf_pick<1024>(hist, jneed, dg, ab);
+            if (tid == 0) { sh[0] = dg; sh[1] = ab; }
+        }
+        __syncthreads();
+        jp |= sh[0] << js[p];
+        jmsk |= 1023u << js[p];
+        jneed -= sh[1];
+        __syncthreads();
+    }
+    const uint32_t jcut = jm - jp;
+    for (int i = tid; i < kPfWords / 4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    sweep([&](uint32_t key, uint32_t j, bool ok) {
+        if (ok && (key > T1 || (key == T1 && j <= jcut))) atomicOr(&bm[j >> 5], 1u << (j & 31));
+    });
+    __syncthreads();
+    pf_emit<kWPT>(bm, out, a.topk, wsum);
+}
+
 // ------------------------------------------------------------------ launcher
 template <int QF, int KF>
 static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st) {
@@ -822,6 +1415,24 @@ static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes
         a.rows = (int32_t)total_rows;
         hipLaunchKernelGGL((k_idx_small<QF, KF>), dim3((unsigned)total_rows), dim3(kIdxThreads), 0, st, a);
         return hipGetLastError();
+    }
+    if constexpr (QF == CSA_FP4_E2M1 && KF == CSA_FP4_E2M1) {
+        if (idx_prefill_eligible(a.di, a.Hi, a.Tq, a.cap, a.topk) &&
+            ws_bytes >= total_rows * idx_prefill_row_bytes()) {
+            const unsigned B = (unsigned)(total_rows / a.Tq);
+            const int64_t ntile = (a.cap + 31) / 32;
+            const int64_t stride = std::max<int64_t>(64, (ntile + kPfMaxSampTiles - 1) / kPfMaxSampTiles);
+            const int32_t rank = (int32_t)((4 * (int64_t)a.topk + stride - 1) / stride);
+            a.row0 = 0;
+            a.rows = (int32_t)total_rows;
+            a.ws_row_bytes = idx_prefill_row_bytes();
+            hipLaunchKernelGGL(k_idxp_thresh, dim3((unsigned)((a.Tq + kPfQ - 1) / kPfQ), B), dim3(kPfThreads), 0, st,
+                               a, (int32_t)stride, rank);
+            hipLaunchKernelGGL(k_idxp_filter, dim3((unsigned)((a.Tq + kPfQB - 1) / kPfQB), B), dim3(kPfThreads), 0, st, a);
+            hipLaunchKernelGGL(k_idxp_select, dim3((unsigned)a.Tq, B), dim3(kPfSelThreads), 0, st, a);
+            hipLaunchKernelGGL(k_idxp_exact, dim3((unsigned)a.Tq, B), dim3(kPfThreads), 0, st, a);
+            return hipGetLastError();
+        }
     }
     const int64_t per_batch = ws_bytes / a.ws_row_bytes;
     const unsigned nchunk = (unsigned)((a.cap + kIdxChunk - 1) / kIdxChunk);

@@ -61,6 +61,19 @@ struct IndexerArgs {
     int64_t ws_row_bytes;
 };
 int64_t idx_ws_row_bytes(int64_t cap, int32_t topk);
+// query-batched prefill path of the indexer (FP4 queries and keys): chunks of
+// at least 32 query rows, di 64, four heads, caps up to 2^19 blocks, topk up
+// to 1024; per query row a header, 8192 above-threshold candidate slots and
+// 8 x 1024 tie slots
+constexpr int kIdxPfMinTq = 32;
+constexpr int64_t kIdxPfMaxCap = (int64_t)1 << 19;
+constexpr int kIdxPfMaxTopk = 1024;
+constexpr int kIdxPfCands = 8192;
+inline bool idx_prefill_eligible(int32_t di, int32_t Hi, int32_t Tq, int64_t cap, int32_t topk) {
+    return di == 64 && Hi == 4 && Tq >= kIdxPfMinTq && cap > kIdxSmallMaxKeys && cap <= kIdxPfMaxCap &&
+           topk <= kIdxPfMaxTopk;
+}
+constexpr int64_t idx_prefill_row_bytes() { return 128 + (int64_t)kIdxPfCands * 8 + 8 * kIdxPfMaxTopk * 4; }
 hipError_t launch_indexer_topk(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st);
 
 // ---- attention

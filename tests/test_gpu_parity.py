@@ -211,6 +211,48 @@ def test_indexer_tie_heavy_rows_exact():
     assert np.array_equal(got[1, 1], np.arange(k))           # all tied: the first k blocks
 
 
+@pytest.mark.parametrize("Tq", [96, 40])
+def test_indexer_prefill_chunk_exact(Tq):
+    """A chunk of query rows (FP4 queries and keys, four heads): the
+    query-batched path -- sampled thresholds, candidate filter, exact select.
+    Every row against the oracle, with a ragged chunk (Tq not a multiple of 32)
+    and rows that see fewer blocks than k."""
+    g = synth.rng(560 + Tq)
+    B, Hi, di, m, k, cap = 2, 4, 64, 4, 1024, 20000
+    kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
+    qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+    w = synth.grid(g, (B, Tq, Hi))
+    pos = np.stack([4 * (cap - Tq) + np.arange(Tq, dtype=np.int32) * 4 + 3,
+                    4 * 12000 + np.arange(Tq, dtype=np.int32) * 37]).astype(np.int32)
+    pos[1, :3] = [5, 4 * 1000, 4 * 1023 + 3]                # fewer blocks than k, exactly k
+    got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
+    assert np.array_equal(got, ref)
+
+
+def test_indexer_prefill_fallback_rows_exact():
+    """Rows the sampled threshold cannot serve, recomputed exactly: one with
+    all weights zero (every score ties: candidates overflow) and one whose
+    sampled key tiles score far above the rest (too few candidates)."""
+    g = synth.rng(570)
+    B, Tq, Hi, di, m, k, cap = 1, 64, 4, 64, 4, 1024, 20000
+    kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
+    qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+    w = synth.grid(g, (B, Tq, Hi))
+    w[0, 5] = 0.0
+    # row 9: positive query codes and weights; the keys of every 64th 32-key
+    # tile (the sampled ones) are all +6, so they outrank the rest
+    qc[0, 9] = 0x22                                          # +1.0 in both nibbles
+    qs[0, 9] = 127
+    w[0, 9] = 1.0
+    for t0 in range(0, cap, 64 * 32):
+        kc[0, t0:t0 + 32] = 0x77
+        ks[0, t0:t0 + 32] = 127
+    pos = (4 * (cap - Tq) + np.arange(Tq, dtype=np.int32) * 4 + 3)[None].astype(np.int32)
+    got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[0, 5], np.arange(k))           # all tied: the first k blocks
+
+
 def test_indexer_fp4_codes_exact():
     """FP4 keys and queries drawn as codes with a narrow exponent range: exact."""
     g = synth.rng(510)
