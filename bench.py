@@ -57,6 +57,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--copies", type=int, default=6, help="rotated buffer sets (defeats the last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
@@ -211,6 +212,70 @@ def call_fns(api):
         api.out_proj_grouped(s["o_hca"].view(B, H * D_HEAD), s["Wo_hca"], y=s["y_hca"])
 
     return [c0, c1, c2, c3, c4, c5, c6]
+
+
+# prefill chunk: 8,192 new query tokens of one sequence over a 1,048,576-token
+# prefix (the chunk's own blocks included), m = 4, top-1024, FP4 indexer,
+# FP8 records, 64 heads x 512 -- reported beside the decode line
+PF_T, PF_TOPK = 8192, 1024
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 (the indexer runs the FP4 MFMA)
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16
+
+
+def prefill_measure(torch, api, reps=3, seed=5005):
+    """Times the indexer and the sparse attention of one prefill chunk (events
+    around each call, best of reps after a warm-up) on synthetic inputs of the
+    chunk's shapes, and prices their contractions against the MFMA peaks."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    n = (L + PF_T) // M_CSA
+    u8 = lambda *shape, lo=0, hi=256: torch.randint(lo, hi, shape, generator=gen, device=dev,
+                                                     dtype=torch.int32).to(torch.uint8)
+    keys = api.IdxCache(1, n, DI, api.FP4_E2M1, codes=u8(1, n, DI // 2), scales=u8(1, n, DI // 32, lo=124, hi=128))
+    qc, qsc = u8(1, PF_T, HI, DI // 2), u8(1, PF_T, HI, DI // 32, lo=124, hi=128)
+    w = torch.randn(1, PF_T, HI, generator=gen, device=dev)
+    pos = (torch.arange(PF_T, device=dev, dtype=torch.int32) + L).view(1, PF_T)
+    ws = torch.empty(api.indexer_workspace_bytes(1, PF_T, n, PF_TOPK), dtype=torch.uint8, device=dev)
+    top = torch.empty(1, PF_T, PF_TOPK, dtype=torch.int32, device=dev)
+    comp = api.KVCache(1, n, D_HEAD, DR, api.FP8_E4M3, rec=u8(1, n, REC, hi=0x70))
+    win = api.KVCache(1, W + PF_T, D_HEAD, DR, api.FP8_E4M3, ring=True, rec=u8(1, W + PF_T, REC, hi=0x70))
+    q = torch.randn(1, PF_T, H, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
+    sink = torch.randn(H, generator=gen, device=dev)
+    p = api.attn_params(D_HEAD, DR, W, M_CSA)
+    out = torch.empty(1, PF_T, H, D_HEAD, dtype=torch.bfloat16, device=dev)
+    aws = torch.empty(max(1, api.attn_workspace_bytes(1, PF_T, H, D_HEAD, PF_TOPK, W, api.BF16, api.FP8_E4M3)),
+                      dtype=torch.uint8, device=dev)
+
+    def idx():
+        api.indexer_topk(qc, api.FP4_E2M1, w, keys, pos, M_CSA, PF_TOPK, q_scales=qsc, out=top, workspace=ws)
+
+    def att():
+        api.sparse_mqa_attn(q, pos, top, comp, win, sink, p, out=out, workspace=aws)
+
+    def best(f):
+        f()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t)
+    ti, ta = best(idx), best(att)
+    n_mean = (L + PF_T / 2) / M_CSA                       # blocks visible to the average query
+    fi = 2.0 * PF_T * HI * DI * n_mean                    # indexer q.k products
+    fa = 2.0 * PF_T * H * (PF_TOPK + W) * 2 * D_HEAD      # Q K^T and P V over 1,152 entries
+    return {"workload": "CSA prefill chunk, 8,192 queries over a 1M prefix, 64 heads x 512, top-1024, FP4 indexer, "
+                        "FP8 records", "indexer_ms": round(ti, 3), "attn_ms": round(ta, 3),
+            "query_tokens_per_s": round(PF_T / ((ti + ta) * 1e-3), 1),
+            "indexer_TFLOPs": round(fi / (ti * 1e-3) / 1e12, 1), "indexer_mfma_frac": round(fi / (ti * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
+            "indexer_peak": "fp4 10.1 PFLOP/s",
+            "attn_TFLOPs": round(fa / (ta * 1e-3) / 1e12, 1), "attn_mfma_frac": round(fa / (ta * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "attn_peak": "bf16 2.5 PFLOP/s", "timing": "HIP events around each call, best of 3 after a warm-up"}
 
 
 def cpu_baseline(target_s):
@@ -489,6 +554,8 @@ def main():
                   "timed steps; roofline from events around the dominant call in every timed step; per-call GPU "
                   "times from events around every call (median over a calibration pass)",
     }
+    if not args.no_prefill:
+        res["prefill"] = prefill_measure(torch, api)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(res), flush=True)

@@ -110,7 +110,7 @@ int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t ma
 // chunk length Tq, never on the batch size, so a sequence's result does not
 // depend on the batch it is in.  Chunks of >= 64 queries give one split per
 // row (enough rows to fill the chip); shorter chunks (decode) cut a row into
-// at most 64 splits of at least 64 entries, a multiple of 32.
+// at most 64 splits of at least 32 entries, a multiple of 32.
 // (templated on the integer type: device code uses 32-bit arithmetic)
 template <typename I>
 __host__ __device__ inline I attn_split_len(I n, int32_t Tq) {
@@ -118,7 +118,7 @@ __host__ __device__ inline I attn_split_len(I n, int32_t Tq) {
     if (Tq >= 64) return (n + 31) / 32 * 32;
     I s = (n + 63) / 64;
     s = (s + 31) / 32 * 32;
-    return s < 64 ? 64 : s;
+    return s < 32 ? 32 : s;
 }
 template <typename I>
 __host__ __device__ inline I attn_nsplit(I n, int32_t Tq) {
@@ -127,7 +127,7 @@ __host__ __device__ inline I attn_nsplit(I n, int32_t Tq) {
 // an upper bound of attn_nsplit over rows with at most max_n entries
 inline int64_t attn_nsplit_bound(int64_t max_n, int32_t Tq) {
     if (Tq >= 64 || max_n <= 0) return 1;
-    int64_t b = (max_n + 63) / 64;
+    int64_t b = (max_n + 31) / 32;
     return b > 64 ? 64 : b;
 }
 hipError_t launch_attention(const AttnArgs& a, int64_t max_entries, hipStream_t st);
