@@ -299,7 +299,9 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
         const bool live = lane < nsplit;
         const float M = fmaxf(sk, wave_max_dpp(live ? ms : -INFINITY));
         const float w = (!live || ms == -INFINITY) ? 0.0f : expf(ms - M);
-        float den = wave_sum_dpp(ls * w);
+        // lanes past the row's split count hold whatever the buffer held
+        // (possibly NaN): they add an exact zero, not 0 * ls
+        float den = wave_sum_dpp(live ? ls * w : 0.0f);
         if (M != -INFINITY) den += expf(sk - M);
         wsc[lane] = w;
         if (lane == 0) den_s = den;

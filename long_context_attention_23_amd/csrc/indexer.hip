@@ -412,10 +412,18 @@ __global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs
                 for (int ks = 0; ks < NKS; ks++)
                     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qab[ks], __builtin_bit_cast(bf16x8_i, kc[u][ks]), acc, 0, 0, 0);
             }
+            // rows 8 g + 4 half + (0..3) of group g hold heads; groups with no
+            // head below Hi carry zero weights and are skipped (an fma with a
+            // zero weight leaves the sum as it is), and with Hi <= 4 the upper
+            // half of the wave holds no head at all
             float part = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 16; i++) part = fmaf(wrow[i], fmaxf(acc[i], 0.0f), part);
-            const float sc = part + __shfl_xor(part, 32, kWave);
+            for (int gq = 0; gq < 4; gq++) {
+                if (8 * gq >= Hi) break;                          // wave-uniform
+#pragma unroll
+                for (int h = 0; h < 4; h++) part = fmaf(wrow[4 * gq + h], fmaxf(acc[4 * gq + h], 0.0f), part);
+            }
+            const float sc = Hi > 4 ? part + __shfl_xor(part, 32, kWave) : part;
             if (half == 0 && key < c1) {
                 const uint32_t k32 = score_key(sc);
                 ws.scores[key] = k32;

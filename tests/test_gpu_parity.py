@@ -306,7 +306,8 @@ def build_caches(g, B, ccap, wcap, d, dr, cfmt, wfmt):
     return O.kv_encode(comp_v, cfmt, dr), O.kv_encode(win_v, wfmt, dr)
 
 
-def run_attention(sparse, q32, qfmt, pos, topk, comp, cfmt, win, wfmt, gamma, sink, d, dr, W, m, ofmt):
+def run_attention(sparse, q32, qfmt, pos, topk, comp, cfmt, win, wfmt, gamma, sink, d, dr, W, m, ofmt,
+                  nan_ws=False):
     B, Tq, H, _ = q32.shape
     say(f"attention sparse={sparse} B={B} Tq={Tq} H={H} d={d} dr={dr} W={W} m={m} cfmt={cfmt} wfmt={wfmt} "
         f"qfmt={qfmt} ofmt={ofmt} ccap={comp.shape[1]} wcap={win.shape[1]}")
@@ -320,6 +321,9 @@ def run_attention(sparse, q32, qfmt, pos, topk, comp, cfmt, win, wfmt, gamma, si
     p = api.attn_params(d, dr, W, m)
     kw = dict(gamma_q=None if gamma is None else dev(gamma),
               out_dtype=torch.bfloat16 if ofmt == O.BF16 else torch.float32)
+    if nan_ws:                                    # a workspace full of NaN bit patterns
+        n = api.attn_workspace_bytes(B, Tq, H, d, comp.shape[1] if topk is None else topk.shape[-1], W, qfmt, cfmt)
+        kw["workspace"] = torch.full((max(n, 16),), 0xFF, dtype=torch.uint8, device="cuda")
     if sparse:
         out = api.sparse_mqa_attn(qdev, dev(pos), dev(topk), cc, wc, dev(sink), p, **kw)
     else:
@@ -375,6 +379,28 @@ def test_attention_parity(ci):
         assert rel_err(got, ref) <= 1e-4
     else:
         assert abs_err(got, ref) <= 2e-2
+
+
+@pytest.mark.parametrize("ci", [2, 4, 10])
+def test_attention_split_workspace_holds_nan(ci):
+    """The split partials' workspace starts out as NaN bit patterns: splits a
+    row does not use must not reach its output (the combine's weights of
+    unused splits are exact zeros, not 0 * stale value)."""
+    sparse, B, Tq, H, d, dr, W, m, k, ccap, cfmt, qfmt, ofmt = ATTN_CASES[ci]
+    g = synth.rng(680 + ci)
+    comp, win = build_caches(g, B, ccap, W + Tq + 7, d, dr, cfmt, cfmt)
+    q = synth.normal(g, (B, Tq, H, d))
+    sink = synth.normal(g, H)
+    pos = np.sort(g.integers(0, m * ccap + 40, size=(B, Tq)), axis=1).astype(np.int32)
+    pos[0, 0] = 5                                          # a short row: few of the splits
+    topk = None
+    if sparse:
+        vis = np.minimum((pos.reshape(-1) + 1) // m, ccap)
+        topk = synth.topk_lists(g, vis, k, B * Tq).reshape(B, Tq, k)
+    got, ref = run_attention(sparse, q, qfmt, pos, topk, comp, cfmt, win, cfmt, None, sink, d, dr, W, m, ofmt,
+                             nan_ws=True)
+    assert np.all(np.isfinite(got))
+    assert abs_err(got, ref) <= 2e-2
 
 
 @pytest.mark.parametrize("sink", [-np.inf, 0.0, 30.0])
