@@ -38,6 +38,8 @@
 //     (waves 4..7).
 #include <stddef.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -87,7 +89,7 @@ struct MfmaSmem : MfmaTiles<D, DR, F8> {
     float alpha[64];                      // per-head rescale factor of the current tile
     float fin[64];                        // per-head final factor (single-split rows)
     float ssq[4][64];                     // per-quarter sums of squares of the queries
-    int moved[4];                         // per head group: accumulators need rescaling
+    alignas(8) int moved[4];              // per head group: accumulators need rescaling
     double rf[64];                        // RoPE inverse frequencies
 };
 
@@ -499,43 +501,58 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         }
     };
     // partial logits of tile tt (buffer tt % 2), this quarter, the wave's head
-    // groups: scale * <q, code>_non-RoPE + <q, k>_RoPE, to LDS
-    auto qk_step = [&](int bq) {
+    // groups: scale * <q, code>_non-RoPE + <q, k>_RoPE, to LDS.  The quarter is
+    // a template constant (QD), so the FP8/RoPE split of its K-steps is known at
+    // compile time and every K fragment is read before the first product.
+    auto qk_step = [&](auto qdc, int bq) {
+        constexpr int DB = decltype(qdc)::value * DQ;
+        constexpr int NKS = (dn - DB) / 32 < 0 ? 0 : ((dn - DB) / 32 > KS ? KS : (dn - DB) / 32);
+        float esc[2];
+        bf16x8_t kb[2][KS];
+        if constexpr (F8) {
+            uint2 kc[2][KS];
+#pragma unroll
+            for (int n = 0; n < 2; n++) {
+                const uint8_t* kr = &sm.ring[bq][16 * n + l16][0];
+                esc[n] = *reinterpret_cast<const float*>(kr + dn + 2 * DR);
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) {
+                    const int dim = DB + 32 * ks + 8 * g4;
+                    if (ks < NKS) kc[n][ks] = *reinterpret_cast<const uint2*>(kr + dim);
+                    else kb[n][ks] = *reinterpret_cast<const bf16x8_t*>(kr + dn + 2 * (dim - dn));
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < 2; n++)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ks++) kb[n][ks] = fp8x8_to_bf16(kc[n][ks]);
+        } else {
+#pragma unroll
+            for (int n = 0; n < 2; n++) {
+                const uint8_t* kr = &sm.tile[bq][16 * n + l16][2 * DB + 16 * g4];
+                esc[n] = sm.scale[bq][16 * n + l16];
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++) kb[n][ks] = *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks);
+            }
+        }
 #pragma unroll
         for (int n = 0; n < 2; n++) {
-            float esc;
-            const uint8_t* kr;
-            if constexpr (F8) {
-                kr = &sm.ring[bq][16 * n + l16][0];
-                esc = *reinterpret_cast<const float*>(kr + dn + 2 * DR);
-            } else {
-                kr = &sm.tile[bq][16 * n + l16][2 * dbase + 16 * g4];
-                esc = sm.scale[bq][16 * n + l16];
-            }
             f32x4_t acc[2];
 #pragma unroll
             for (int mt = 0; mt < 2; mt++) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
-                bf16x8_t kb;
-                if constexpr (F8) {
-                    const int dim = dbase + 32 * ks + 8 * g4;
-                    if (ks < nks) kb = fp8x8_to_bf16(*reinterpret_cast<const uint2*>(kr + dim));
-                    else kb = *reinterpret_cast<const bf16x8_t*>(kr + dn + 2 * (dim - dn));
-                } else {
-                    kb = *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks);
-                }
-                if (ks == nks && ks > 0) {
+                if (ks == NKS && ks > 0) {
 #pragma unroll
-                    for (int mt = 0; mt < 2; mt++) acc[mt] *= esc;
+                    for (int mt = 0; mt < 2; mt++) acc[mt] *= esc[n];
                 }
 #pragma unroll
                 for (int mt = 0; mt < 2; mt++)
-                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb, acc[mt], 0, 0, 0);
+                    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb[n][ks], acc[mt], 0, 0, 0);
             }
-            if (nks == KS) {
+            if (NKS == KS) {
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++) acc[mt] *= esc;
+                for (int mt = 0; mt < 2; mt++) acc[mt] *= esc[n];
             }
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
@@ -610,15 +627,50 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     };
     // per-lane LDS coordinates of the transposing reads
     const int v_row = 8 * g4 + 2 * (l16 >> 2);
-    const int v_col = 2 * (dbase + 4 * (l16 & 3));
     const int p_row = 8 * g4 + (l16 >> 2);
     const int p_col = 32 * hp + 4 * (l16 & 3);
-    // rescale O of the head groups whose max moved at tile tt (rare), then O += P V
-    auto pv_step = [&](int bq) {
+    // rescale O of the head groups whose max moved at tile tt (rare), then
+    // O += P V.  The quarter is a template constant: the FP8/RoPE split of its
+    // N-tiles is static, and the flags, P fragments and V fragments are all
+    // read before the first product.
+    auto pv_step = [&](auto qdc, int bq) {
+        constexpr int DB = decltype(qdc)::value * DQ;
+        constexpr int NNT = (dn - DB) / 16 < 0 ? 0 : ((dn - DB) / 16 > NT ? NT : (dn - DB) / 16);
+        const int2 mv = *reinterpret_cast<const int2*>(&sm.moved[2 * hp]);
+        // P A-fragments: scaled P for the non-RoPE dims, plain P for the RoPE dims
+        bf16x8_t pfs[2], pfp[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++) {
+            if (NNT > 0) pfs[mt] = tr_pair(&sm.pt[0][p_row][16 * mt + p_col], &sm.pt[0][p_row + 4][16 * mt + p_col]);
+            if (NNT < NT) pfp[mt] = tr_pair(&sm.pt[1][p_row][16 * mt + p_col], &sm.pt[1][p_row + 4][16 * mt + p_col]);
+        }
+        bf16x8_t vb[NT];
+        if constexpr (F8) {
+            // lane (g4, s) addresses entry pi(8*g4 + s/2): bytes of 8 FP8 dims,
+            // or 4 bf16 RoPE dims of rows pi(8*g4 + 4h + s/4)
+            const uint8_t* rb = &sm.ring[bq][0][0];
+            uint2 vc[NT];
+#pragma unroll
+            for (int nd = 0; nd < NT; nd++) {
+                if (nd < NNT) {
+                    const int r = 8 * g4 + (l16 >> 3) + 2 * ((l16 >> 1) & 3);
+                    vc[nd] = lds_read_tr8(rb + r * REC + DB + 16 * nd + 8 * (l16 & 1));
+                } else {
+                    const int cb = dn + 2 * (DB + 16 * nd - dn + 4 * (l16 & 3));
+                    vb[nd] = tr_pair(rb + v_row * REC + cb, rb + (v_row + 1) * REC + cb);
+                }
+            }
+#pragma unroll
+            for (int nd = 0; nd < NNT; nd++) vb[nd] = fp8x8_to_bf16(vc[nd]);
+        } else {
+            const uint8_t* vp = &sm.tile[bq][v_row][2 * (DB + 4 * (l16 & 3))];
+#pragma unroll
+            for (int nd = 0; nd < NT; nd++) vb[nd] = tr_pair(vp + 32 * nd, vp + RS + 32 * nd);
+        }
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
             const int g = 2 * hp + mt;
-            if (g < MT && sm.moved[g]) {
+            if (g < MT && (mt ? mv.y : mv.x)) {
                 const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[16 * g + 4 * g4]);
 #pragma unroll
                 for (int nd = 0; nd < NT; nd++) {
@@ -629,40 +681,19 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
                 }
             }
         }
-        // P A-fragments: scaled P for the non-RoPE dims, plain P for the RoPE dims
-        bf16x8_t pf[2];
-        {
-            const int pa = nnt > 0 ? 0 : 1;
+#pragma unroll
+        for (int nd = 0; nd < NT; nd++)
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
-                pf[mt] = tr_pair(&sm.pt[pa][p_row][16 * mt + p_col], &sm.pt[pa][p_row + 4][16 * mt + p_col]);
-        }
-#pragma unroll
-        for (int nd = 0; nd < NT; nd++) {
-            if (nd == nnt && nd > 0) {
-#pragma unroll
-                for (int mt = 0; mt < 2; mt++)
-                    pf[mt] = tr_pair(&sm.pt[1][p_row][16 * mt + p_col], &sm.pt[1][p_row + 4][16 * mt + p_col]);
-            }
-            bf16x8_t vb;
-            if constexpr (F8) {
-                // lane (g4, s) addresses entry pi(8*g4 + s/2): bytes of 8 FP8 dims,
-                // or 4 bf16 RoPE dims of rows pi(8*g4 + 4h + s/4)
-                const uint8_t* rb = &sm.ring[bq][0][0];
-                if (nd < nnt) {
-                    const int r = 8 * g4 + (l16 >> 3) + 2 * ((l16 >> 1) & 3);
-                    vb = fp8x8_to_bf16(lds_read_tr8(rb + r * REC + dbase + 16 * nd + 8 * (l16 & 1)));
-                } else {
-                    const int cb = dn + 2 * (dbase + 16 * nd - dn + 4 * (l16 & 3));
-                    vb = tr_pair(rb + v_row * REC + cb, rb + (v_row + 1) * REC + cb);
-                }
-            } else {
-                const uint8_t* vp = &sm.tile[bq][v_row][v_col];
-                vb = tr_pair(vp + 32 * nd, vp + RS + 32 * nd);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; mt++)
-                o[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[mt], vb, o[mt][nd], 0, 0, 0);
+                o[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nd < NNT ? pfs[mt] : pfp[mt], vb[nd], o[mt][nd], 0, 0, 0);
+    };
+    // the steps for this wave's quarter (wave-uniform dispatch)
+    auto with_quarter = [&](auto&& f) {
+        switch (qd) {
+            case 0: f(std::integral_constant<int, 0>{}); break;
+            case 1: f(std::integral_constant<int, 1>{}); break;
+            case 2: f(std::integral_constant<int, 2>{}); break;
+            default: f(std::integral_constant<int, 3>{}); break;
         }
     };
 
@@ -681,8 +712,10 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     int bcur = 0, bprev = NB - 1;
     for (int tt = 0; tt < ntiles; tt++) {
         if (active) {
-            if (tt > 0) pv_step(bprev);
-            qk_step(bcur);
+            with_quarter([&](auto qdc) {
+                if (tt > 0) pv_step(qdc, bprev);
+                qk_step(qdc, bcur);
+            });
         }
         __syncthreads();
         if (owner) softmax_step(bcur);
@@ -697,7 +730,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         bprev = bcur;
         bcur = bcur + 1 == NB ? 0 : bcur + 1;
     }
-    if (active && ntiles > 0) pv_step(bprev);
+    if (active && ntiles > 0) with_quarter([&](auto qdc) { pv_step(qdc, bprev); });
 
     // ---- epilogue
 #pragma unroll
