@@ -170,11 +170,11 @@ CALLS = ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_mqa_attn", "csa_out_
 
 # the kernels each call launches, in launch order (for matching rocprof traces)
 CALL_KERNELS = {
-    "csa_compress_kv": ["k_compress", "k_compress", "k_compress"],
+    "csa_compress_kv": ["k_compress"],
     "csa_indexer_topk": ["k_idx_zero", "k_idx_score_mfma", "k_idx_collect", "k_idx_final"],
     "csa_sparse_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "csa_out_proj": ["k_proj_gemv"],
-    "hca_compress_kv": ["k_compress", "k_compress"],
+    "hca_compress_kv": ["k_compress"],
     "hca_dense_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "hca_out_proj": ["k_proj_gemv"],
 }
@@ -182,11 +182,15 @@ CALL_KERNELS = {
 
 def call_fns(api):
     """One function per call of the decode step (each launches that call's kernels)."""
+    # the step's three CSA compressions (window entry, block, indexer key) and
+    # two HCA ones are each one batched call
     def c0(s, sh):
-        api.compress_kv(s["x_new_csa"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
-                        kv_out=s["win_csa"])
-        api.compress_kv(s["x_csa"], sh["tok_csa"], M_CSA, sh["b_csa"], gamma=sh["gam"], rope_dim=DR, kv_out=s["csa_c"])
-        api.compress_kv(s["xi_csa"], sh["tok_csa"], M_CSA, sh["b_idx"], idx_out=s["keys"])
+        api.compress_kv_batch([
+            dict(x=s["x_new_csa"], tok_start=sh["tok_new"], m=1, score_bias=sh["zero1"], gamma=sh["gam"],
+                 rope_dim=DR, kv_out=s["win_csa"]),
+            dict(x=s["x_csa"], tok_start=sh["tok_csa"], m=M_CSA, score_bias=sh["b_csa"], gamma=sh["gam"],
+                 rope_dim=DR, kv_out=s["csa_c"]),
+            dict(x=s["xi_csa"], tok_start=sh["tok_csa"], m=M_CSA, score_bias=sh["b_idx"], idx_out=s["keys"])])
 
     def c1(s, sh):
         api.indexer_topk(s["qI"], api.FP4_E2M1, s["w_idx"], s["keys"], sh["pos"], M_CSA, K_CSA, q_scales=s["qI_s"],
@@ -200,9 +204,11 @@ def call_fns(api):
         api.out_proj_grouped(s["o_csa"].view(B, H * D_HEAD), s["Wo_csa"], y=s["y_csa"])
 
     def c4(s, sh):
-        api.compress_kv(s["x_new_hca"], sh["tok_new"], 1, sh["zero1"], gamma=sh["gam"], rope_dim=DR,
-                        kv_out=s["win_hca"])
-        api.compress_kv(s["x_hca"], sh["tok_hca"], M_HCA, sh["b_hca"], gamma=sh["gam"], rope_dim=DR, kv_out=s["hca_c"])
+        api.compress_kv_batch([
+            dict(x=s["x_new_hca"], tok_start=sh["tok_new"], m=1, score_bias=sh["zero1"], gamma=sh["gam"],
+                 rope_dim=DR, kv_out=s["win_hca"]),
+            dict(x=s["x_hca"], tok_start=sh["tok_hca"], m=M_HCA, score_bias=sh["b_hca"], gamma=sh["gam"],
+                 rope_dim=DR, kv_out=s["hca_c"])])
 
     def c5(s, sh):
         api.hca_dense_mqa_attn(s["q_hca"], sh["pos"], s["hca_c"], s["win_hca"], s["sink_hca"], sh["p_hca"],

@@ -150,6 +150,40 @@ csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, int64_t T,
                            const csa_idx_cache* idx_out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_compress_kv_batch -- several csa_compress_kv calls enqueued as one
+ * launch (a decode step's window entry, compressed block and indexer key of
+ * the same layer: peacm 3.2 CSA step 1 for each).  Job k has exactly the
+ * arguments and the result of csa_compress_kv(jobs[k].x, x_dtype, ...), so
+ * the semantics, error statuses and rounding are those above.
+ * jobs     : host array of njobs descriptors (read during the call only).
+ * x_dtype  : CSA_F32 or CSA_BF16, shared by every job.
+ * The jobs run concurrently: their outputs must not overlap and no job may
+ * read what another writes.  All jobs are validated before anything is
+ * enqueued.  Up to 4 jobs that take the latency kernel (no content score,
+ * d a multiple of 32, at most 16 token rows per thread) share one launch;
+ * otherwise the jobs are launched one after another on the stream.
+ * Errors: INVALID_ARG (njobs < 0, or jobs NULL with njobs > 0), and those of
+ * csa_compress_kv for any job.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const void* x;
+    int32_t B;
+    int64_t T;
+    int32_t d;
+    const int32_t* tok_start;
+    int32_t m;
+    const float* score_bias;
+    const float* score_proj;
+    const float* gamma;
+    float eps;
+    int32_t rope_dim;
+    float rope_base;
+    const csa_kv_cache* kv_out;
+    const csa_idx_cache* idx_out;
+} csa_compress_job;
+csa_status csa_compress_kv_batch(const csa_compress_job* jobs, int32_t njobs, int32_t x_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_indexer_topk -- CSA step 2 (peacm 3.2: the lightning indexer scores
  * each query against the compressed blocks and keeps the most relevant
  * top-k; digest 3.2: the QK path in FP4).

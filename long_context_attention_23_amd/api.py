@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa_attn
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
 STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_CAPACITY",
           4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_HIP"}
-EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
+EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_compress_kv_batch", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
            "csa_attn_workspace_size", "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "attn_out_proj_grouped",
            "csa_last_error"]
 
@@ -45,6 +45,12 @@ _lib = None
 _V, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
 
 
+class CompressJobT(C.Structure):
+    _fields_ = [("x", _V), ("B", _I32), ("T", _I64), ("d", _I32), ("tok_start", _V), ("m", _I32),
+                ("score_bias", _V), ("score_proj", _V), ("gamma", _V), ("eps", _F), ("rope_dim", _I32),
+                ("rope_base", _F), ("kv_out", C.POINTER(KVCacheT)), ("idx_out", C.POINTER(IdxCacheT))]
+
+
 def lib():
     """Load the HIP library (raises if it has not been built)."""
     global _lib
@@ -60,6 +66,8 @@ def lib():
         L.csa_compress_kv.restype = C.c_int
         L.csa_compress_kv.argtypes = [_V, _I32, _I32, _I64, _I32, _V, _I32, _V, _V, _V, _F, _I32, _F,
                                       C.POINTER(KVCacheT), C.POINTER(IdxCacheT), _V]
+        L.csa_compress_kv_batch.restype = C.c_int
+        L.csa_compress_kv_batch.argtypes = [C.POINTER(CompressJobT), _I32, _I32, _V]
         L.csa_indexer_topk_workspace_size.restype = _SZ
         L.csa_indexer_topk_workspace_size.argtypes = [_I32, _I32, _I64, _I32]
         L.csa_indexer_topk.restype = C.c_int
@@ -149,6 +157,34 @@ def compress_kv(x, tok_start, m, score_bias, *, score_proj=None, gamma=None, eps
     ixs = C.byref(idx_out.struct()) if idx_out is not None else None
     _check(lib().csa_compress_kv(_ptr(x), torch_dtype_code(x), B, T, d, _ptr(tok_start), m, _ptr(score_bias),
                                  _ptr(score_proj), _ptr(gamma), eps, rope_dim, rope_base, kvs, ixs, _stream(stream)))
+
+
+def compress_kv_batch(jobs, stream=None):
+    """csa_compress_kv_batch.  jobs: dicts with compress_kv's arguments (x, tok_start, m, score_bias and
+    its keywords); every x has the same dtype."""
+    n = len(jobs)
+    arr = (CompressJobT * max(n, 1))()
+    keep = []                                   # cache structs referenced by the descriptors
+    dt = torch_dtype_code(jobs[0]["x"]) if n else F32
+    for k, j in enumerate(jobs):
+        x = j["x"]
+        if torch_dtype_code(x) != dt:
+            raise TypeError("every job of a batch needs the same x dtype")
+        B, T, d = x.shape
+        kv = j.get("kv_out")
+        ix = j.get("idx_out")
+        kvs = kv.struct() if kv is not None else None
+        ixs = ix.struct() if ix is not None else None
+        keep += [kvs, ixs]
+        arr[k] = CompressJobT(x.data_ptr(), B, T, d, j["tok_start"].data_ptr(), j["m"], j["score_bias"].data_ptr(),
+                              _ptr(j.get("score_proj")), _ptr(j.get("gamma")), j.get("eps", 1e-6),
+                              j.get("rope_dim", 0), j.get("rope_base", 10000.0),
+                              C.pointer(kvs) if kvs is not None else None,
+                              C.pointer(ixs) if ixs is not None else None)
+        for t in (x, j["tok_start"], j["score_bias"]):
+            if not t.is_contiguous():
+                raise ValueError("tensors passed to the C ABI must be contiguous")
+    _check(lib().csa_compress_kv_batch(arr, n, dt, _stream(stream)))
 
 
 def indexer_workspace_bytes(B, Tq, key_cap, topk):

@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/csa_attn.h"
 #include "launch.hpp"
@@ -167,11 +168,12 @@ CSA_API size_t csa_kv_record_bytes(int32_t fmt, int32_t d, int32_t d_rope) {
 
 CSA_API const char* csa_last_error(void) { return g_err.c_str(); }
 
-CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, int64_t T, int32_t d,
-                                   const int32_t* tok_start, int32_t m, const float* score_bias,
-                                   const float* score_proj, const float* gamma, float eps, int32_t rope_dim,
-                                   float rope_base, const csa_kv_cache* kv_out, const csa_idx_cache* idx_out,
-                                   void* stream) {
+// validates one compression request and fills its launch arguments
+static csa_status compress_args(const void* x, int32_t x_dtype, int32_t B, int64_t T, int32_t d,
+                                const int32_t* tok_start, int32_t m, const float* score_bias,
+                                const float* score_proj, const float* gamma, float eps, int32_t rope_dim,
+                                float rope_base, const csa_kv_cache* kv_out, const csa_idx_cache* idx_out,
+                                csa::CompressArgs& a) {
     if (B < 0 || T < 0) return fail(CSA_ERR_INVALID_ARG, "bad sizes B=%d T=%lld", B, (long long)T);
     if (B > kMaxGridY) return fail(CSA_ERR_UNSUPPORTED, "B=%d > %lld", B, (long long)kMaxGridY);
     if (d < 2 || d > 1024 || d % 2) return fail(CSA_ERR_INVALID_ARG, "d %d must be even and in [2, 1024]", d);
@@ -181,7 +183,7 @@ CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, in
     if (!is_act_fmt(x_dtype)) return fail(CSA_ERR_UNSUPPORTED, "x dtype %d", x_dtype);
     if ((kv_out != nullptr) == (idx_out != nullptr)) return fail(CSA_ERR_INVALID_ARG, "give exactly one of kv_out / idx_out");
     if (T / m > (int64_t)0x7FFFFFFF) return fail(CSA_ERR_UNSUPPORTED, "too many blocks");
-    csa::CompressArgs a{};
+    a = csa::CompressArgs{};
     if (kv_out) {
         if (!is_kv_fmt(kv_out->fmt)) return fail(CSA_ERR_UNSUPPORTED, "kv_out fmt %d", kv_out->fmt);
         if (kv_out->d != d || kv_out->d_rope != rope_dim) return fail(CSA_ERR_INVALID_ARG, "kv_out d/d_rope %d/%d differ from call %d/%d", kv_out->d, kv_out->d_rope, d, rope_dim);
@@ -224,7 +226,35 @@ CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, in
     a.dr = rope_dim;
     a.base = rope_base;
     csa::fill_rope_table(a.rope, rope_dim, rope_base);
+    return CSA_OK;
+}
+
+CSA_API csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, int64_t T, int32_t d,
+                                   const int32_t* tok_start, int32_t m, const float* score_bias,
+                                   const float* score_proj, const float* gamma, float eps, int32_t rope_dim,
+                                   float rope_base, const csa_kv_cache* kv_out, const csa_idx_cache* idx_out,
+                                   void* stream) {
+    csa::CompressArgs a;
+    const csa_status st = compress_args(x, x_dtype, B, T, d, tok_start, m, score_bias, score_proj, gamma, eps,
+                                        rope_dim, rope_base, kv_out, idx_out, a);
+    if (st != CSA_OK) return st;
     return hip_status(csa::launch_compress(a, x_dtype, static_cast<hipStream_t>(stream)), "compress launch");
+}
+
+CSA_API csa_status csa_compress_kv_batch(const csa_compress_job* jobs, int32_t njobs, int32_t x_dtype,
+                                         void* stream) {
+    if (njobs < 0 || (njobs > 0 && !jobs))
+        return fail(CSA_ERR_INVALID_ARG, "njobs %d with jobs %p", njobs, (const void*)jobs);
+    std::vector<csa::CompressArgs> args((size_t)njobs);
+    for (int k = 0; k < njobs; k++) {
+        const csa_compress_job& j = jobs[k];
+        const csa_status st = compress_args(j.x, x_dtype, j.B, j.T, j.d, j.tok_start, j.m, j.score_bias, j.score_proj,
+                                            j.gamma, j.eps, j.rope_dim, j.rope_base, j.kv_out, j.idx_out, args[k]);
+        if (st != CSA_OK) return st;
+    }
+    if (njobs == 0) return CSA_OK;
+    return hip_status(csa::launch_compress_batch(args.data(), njobs, x_dtype, static_cast<hipStream_t>(stream)),
+                      "compress batch launch");
 }
 
 CSA_API size_t csa_indexer_topk_workspace_size(int32_t B, int32_t Tq, int64_t key_cap, int32_t topk) {

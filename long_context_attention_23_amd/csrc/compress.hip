@@ -18,6 +18,8 @@
 // independent 16-byte loads in flight per thread.
 #include <stddef.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -214,19 +216,26 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
 // arithmetic is that of k_compress (token order inside each token group,
 // group sums in group order); the softmax sum and the square sums are reduced
 // in DPP row order instead of a butterfly, so the last bits may differ.
+struct CompFastSmem {
+    float part[kCompThreads * 8];
+    float red_ss[kCompThreads / kWave];
+    float red_mx[kCompThreads / kWave];
+    int se[kMaxD / 32];
+};
+
+// block i of sequence b; `a` lives in the argument segment with its RoPE table
+// at byte rope_off of the segment
 template <typename XT, int QR>
-__global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) {
-    warm_kernargs(offsetof(CompressArgs, rope));
-    __shared__ float part[kCompThreads * 8];
-    __shared__ float red_ss[kCompThreads / kWave];
-    __shared__ float red_mx[kCompThreads / kWave];
-    __shared__ int se[kMaxD / 32];
+__device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t rope_off, CompFastSmem& sm, int b,
+                                                   int i) {
+    float* part = sm.part;
+    float* red_ss = sm.red_ss;
+    float* red_mx = sm.red_mx;
+    int* se = sm.se;
     constexpr int EPC = 16 / (int)sizeof(XT);
     constexpr int KT = kMaxD / kCompThreads;              // elements per thread
     constexpr int SB = 2 * QR < 16 ? 2 * QR : 16;        // pooling biases per lane (m <= 64 SB)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-    const int b = blockIdx.y;
-    const int i = blockIdx.x;
     const int d = a.d, m = a.m;
     const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + (int64_t)i * m) * d;
     const int nch = d / EPC, TG = kCompThreads / nch;
@@ -253,7 +262,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
     for (int t = 0; t < KT; t++) {
         const int k = tid + t * kCompThreads;
         gk[t] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
-        fk[t] = (k < d && k >= off) ? rope_freq_arg(offsetof(CompressArgs, rope), (k - off) >> 1) : 0.0;
+        fk[t] = (k < d && k >= off) ? rope_freq_arg(rope_off, (k - off) >> 1) : 0.0;
     }
     const int64_t j = (int64_t)(a.tok_start[b] / m) + i;
     if (!a.ring && j >= a.cap) return;
@@ -410,16 +419,50 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) 
     }
 }
 
+template <typename XT, int QR>
+__global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) {
+    warm_kernargs(offsetof(CompressArgs, rope));
+    __shared__ CompFastSmem sm;
+    compress_fast_body<XT, QR>(a, offsetof(CompressArgs, rope), sm, blockIdx.y, blockIdx.x);
+}
+
+// Several independent compressions in one launch (blockIdx.z = job): the
+// blocks of one decode step (window entry, compressed block, indexer key)
+// otherwise cost a dispatch each.  Jobs with at most one token row per
+// thread run the QR = 1 body, the others the QRB body.
+template <typename XT, int QRB>
+__global__ __launch_bounds__(kCompThreads) void k_compress_batch(CompressBatch bt) {
+    __shared__ CompFastSmem sm;
+    const int z = blockIdx.z;
+    const CompressArgs& a = bt.job[z];
+    const size_t off = (size_t)z * sizeof(CompressArgs);
+    if ((int64_t)blockIdx.x >= a.T / a.m || (int)blockIdx.y >= a.B) return;
+    constexpr int EPC = 16 / (int)sizeof(XT);
+    const int TG = kCompThreads / (a.d / EPC);
+    if (a.m <= TG) compress_fast_body<XT, 1>(a, off + offsetof(CompressArgs, rope), sm, blockIdx.y, blockIdx.x);
+    else compress_fast_body<XT, QRB>(a, off + offsetof(CompressArgs, rope), sm, blockIdx.y, blockIdx.x);
+}
+
+// token rows per thread of the fast kernel for this job, or 0 when the job
+// needs the general kernel (content scores, d not a whole number of 16-byte
+// chunks, or more pooling biases than the kernel's lanes hold)
 template <typename XT>
-static void launch_compress_t(const CompressArgs& a, dim3 grid, hipStream_t st) {
+static int fast_rows(const CompressArgs& a) {
     constexpr int EPC = 16 / (int)sizeof(XT);
     const int nch = a.d / EPC;
     const bool fast0 = !a.sproj && a.d % EPC == 0 && a.d <= kMaxD && nch <= kCompThreads && a.dr % 2 == 0 &&
                        (a.d - a.dr) % 2 == 0 && a.d % 32 == 0;
-    const int TG = fast0 ? kCompThreads / nch : 1;
+    if (!fast0) return 0;
+    const int TG = kCompThreads / nch;
     const int qr = (a.m + TG - 1) / TG;
-    const int sb = qr <= 1 ? 2 : qr <= 2 ? 4 : qr <= 4 ? 8 : 16;        // SB of the kernel picked below
-    const bool fast = fast0 && a.m <= kWave * sb;
+    const int sb = qr <= 1 ? 2 : qr <= 2 ? 4 : qr <= 4 ? 8 : 16;        // SB of the kernel for qr
+    return (qr <= 16 && a.m <= kWave * sb) ? qr : 0;
+}
+
+template <typename XT>
+static void launch_compress_t(const CompressArgs& a, dim3 grid, hipStream_t st) {
+    const int qr = fast_rows<XT>(a);
+    const bool fast = qr > 0;
     if (fast && qr <= 1) hipLaunchKernelGGL((k_compress_fast<XT, 1>), grid, dim3(kCompThreads), 0, st, a);
     else if (fast && qr <= 2) hipLaunchKernelGGL((k_compress_fast<XT, 2>), grid, dim3(kCompThreads), 0, st, a);
     else if (fast && qr <= 4) hipLaunchKernelGGL((k_compress_fast<XT, 4>), grid, dim3(kCompThreads), 0, st, a);
@@ -435,6 +478,42 @@ hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st) {
     if (x_dtype == CSA_F32) launch_compress_t<float>(a, grid, st);
     else launch_compress_t<uint16_t>(a, grid, st);
     return hipGetLastError();
+}
+
+template <typename XT>
+static hipError_t launch_compress_batch_t(const CompressArgs* jobs, int n, hipStream_t st) {
+    int qmax = 0;
+    int64_t gx = 0, gy = 0;
+    bool one = n <= kCompBatchMax;
+    for (int k = 0; k < n; k++) {
+        const int q = fast_rows<XT>(jobs[k]);
+        one = one && q > 0;
+        qmax = q > qmax ? q : qmax;
+        gx = std::max(gx, jobs[k].T / jobs[k].m);
+        gy = std::max(gy, (int64_t)jobs[k].B);
+    }
+    if (!one) {                                         // one launch per job
+        for (int k = 0; k < n; k++) {
+            const hipError_t e = launch_compress(jobs[k], sizeof(XT) == 4 ? CSA_F32 : CSA_BF16, st);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    if (gx == 0 || gy == 0) return hipSuccess;
+    CompressBatch bt{};
+    for (int k = 0; k < n; k++) bt.job[k] = jobs[k];
+    const dim3 grid((unsigned)gx, (unsigned)gy, (unsigned)n);
+    if (qmax <= 1) hipLaunchKernelGGL((k_compress_batch<XT, 1>), grid, dim3(kCompThreads), 0, st, bt);
+    else if (qmax <= 2) hipLaunchKernelGGL((k_compress_batch<XT, 2>), grid, dim3(kCompThreads), 0, st, bt);
+    else if (qmax <= 4) hipLaunchKernelGGL((k_compress_batch<XT, 4>), grid, dim3(kCompThreads), 0, st, bt);
+    else if (qmax <= 8) hipLaunchKernelGGL((k_compress_batch<XT, 8>), grid, dim3(kCompThreads), 0, st, bt);
+    else hipLaunchKernelGGL((k_compress_batch<XT, 16>), grid, dim3(kCompThreads), 0, st, bt);
+    return hipGetLastError();
+}
+
+hipError_t launch_compress_batch(const CompressArgs* jobs, int n, int x_dtype, hipStream_t st) {
+    if (x_dtype == CSA_F32) return launch_compress_batch_t<float>(jobs, n, st);
+    return launch_compress_batch_t<uint16_t>(jobs, n, st);
 }
 
 }  // namespace csa

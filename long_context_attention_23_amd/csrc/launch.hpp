@@ -36,6 +36,12 @@ struct CompressArgs {
     RopeTable rope;
 };
 hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st);
+// independent compressions of one x dtype; up to kCompBatchMax share a launch
+constexpr int kCompBatchMax = 4;
+struct CompressBatch {
+    CompressArgs job[kCompBatchMax];
+};
+hipError_t launch_compress_batch(const CompressArgs* jobs, int n, int x_dtype, hipStream_t st);
 
 // ---- indexer + top-k
 constexpr int kIdxSmallMaxKeys = 4096;   // one workgroup per query row up to this key count

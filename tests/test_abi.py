@@ -26,7 +26,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 9
+    assert len(names) == 10
     assert sorted(names) == sorted(api.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -99,6 +99,40 @@ def test_compress_idx_validation(L):
 def test_compress_empty_is_ok(L):
     st, msg = compress(L, T=3)          # T < m: no complete block, nothing launched
     assert st == 0 and msg == ""
+
+
+def job(**over):
+    kvs = over.pop("kv_struct", kv())
+    a = dict(x=FAKE.value, B=2, T=8, d=512, tok_start=FAKE.value, m=4, score_bias=FAKE.value, score_proj=None,
+             gamma=None, eps=1e-6, rope_dim=64, rope_base=10000.0, kv_out=C.pointer(kvs), idx_out=None)
+    a.update(over)
+    return api.CompressJobT(**a), kvs
+
+
+def test_compress_batch_validation(L):
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(None, 2, api.BF16, None))
+    assert st == 1 and "njobs" in msg
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(None, -1, api.BF16, None))
+    assert st == 1 and "njobs" in msg
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(None, 0, api.BF16, None))
+    assert st == 0
+    # one bad job among good ones: the whole call fails before any launch
+    good, k0 = job()
+    bad, k1 = job(d=513, kv_struct=kv(d=513))
+    arr = (api.CompressJobT * 2)(good, bad)
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(arr, 2, api.BF16, None))
+    assert st == 1 and "even" in msg
+    bad, k2 = job(m=0)
+    arr = (api.CompressJobT * 2)(good, bad)
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(arr, 2, api.BF16, None))
+    assert st == 1 and "m 0" in msg
+    arr = (api.CompressJobT * 1)(good)
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(arr, 1, api.FP8_E4M3, None))
+    assert st == 2 and "x dtype" in msg
+    empty, k3 = job(T=3)                # T < m: nothing to launch
+    arr = (api.CompressJobT * 2)(empty, empty)
+    st, msg = status_and_msg(L, L.csa_compress_kv_batch(arr, 2, api.BF16, None))
+    assert st == 0
 
 
 def indexer(L, **over):

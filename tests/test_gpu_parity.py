@@ -93,6 +93,12 @@ def test_compress_pooled_within_one_code(kind, fmt, m, dr, xfmt, ring, content):
     tok = [0, m * 3, m * 1000]
     cap = 7 if ring else 1010
     codes, scales, gc, gs = run_compress_both(x, xfmt, tok, m, b, u, gamma, dr, kind, fmt, cap, ring, 0)
+    check_pooled(kind, fmt, d, dr, codes, scales, gc, gs)
+
+
+def check_pooled(kind, fmt, d, dr, codes, scales, gc, gs):
+    """Device record bytes gc/gs against the oracle's codes/scales: within one
+    quantisation step of the stored format."""
     ref = decoded(kind, fmt, codes, scales, d, dr)
     got = decoded(kind, fmt, gc, gs, d, dr)
     written = np.any(codes != 0, axis=-1)
@@ -112,6 +118,63 @@ def test_compress_pooled_within_one_code(kind, fmt, m, dr, xfmt, ring, content):
         e = gs[written].astype(np.int64) - 127
         step = np.repeat(2.0 ** (e + 1), 32, axis=-1)
         assert np.all(np.abs(q - r) <= step)
+
+
+@pytest.mark.parametrize("case", ["decode_step", "multi_block", "five_jobs", "content_score"])
+def test_compress_batch_matches_single_calls(case):
+    """csa_compress_kv_batch: every job's output equals that of its own
+    csa_compress_kv call byte for byte, and the oracle's within one step."""
+    g = synth.rng(4700 + len(case))
+    B = 3
+    # (kind, fmt, m, d, dr, ring, cap, T, content)
+    jobs = [(0, O.FP8_E4M3, 1, 512, 64, True, 9, 1, False),        # window entry
+            (0, O.FP8_E4M3, 4, 512, 64, False, 2100, 4, False),    # CSA block
+            (1, O.FP4_E2M1, 4, 128, 0, False, 2100, 4, False),     # indexer key
+            (0, O.FP8_E4M3, 128, 512, 64, False, 70, 128, False)]  # HCA block
+    if case == "multi_block":
+        jobs = [(0, O.FP8_E4M3, 4, 512, 64, False, 2100, 4 * 5 + 3, False),
+                (1, O.FP4_E2M1, 4, 128, 0, False, 2100, 4 * 7 + 1, False),
+                (0, O.BF16, 16, 256, 64, True, 11, 16 * 3, False)]
+    elif case == "five_jobs":
+        jobs = jobs + [(0, O.BF16, 2, 128, 64, False, 5000, 6, False)]
+    elif case == "content_score":
+        jobs = jobs[:2] + [(1, O.BF16, 4, 128, 0, False, 2100, 8, True)]
+    tok = [0, 128 * 3, 128 * 15]
+    dev_jobs, singles, refs = [], [], []
+    for (kind, fmt, m, d, dr, ring, cap, T, content) in jobs:
+        x32 = synth.normal(g, (B, T, d))
+        bits = (x32.view(np.uint32) >> 16).astype(np.uint16)
+        b = synth.normal(g, m)
+        u = synth.normal(g, d) * np.float32(0.05) if content else None
+        gamma = (1 + 0.2 * synth.normal(g, d)).astype(np.float32) if kind == 0 else None
+        codes, scales, _ = O.compress(bits, O.BF16, tok, m, b, u=u, gamma=gamma, dr=dr, out_kind=kind,
+                                      out_fmt=fmt, cap=cap, ring=ring)
+        refs.append((kind, fmt, d, dr, codes, scales))
+        args = dict(x=dev_bf16(bits), tok_start=dev(np.array(tok, np.int32)), m=m,
+                    score_bias=dev(np.asarray(b, np.float32)), score_proj=None if u is None else dev(u),
+                    gamma=None if gamma is None else dev(gamma), rope_dim=dr)
+        mk = (lambda: api.KVCache(B, cap, d, dr, fmt, ring=ring)) if kind == 0 else (lambda: api.IdxCache(B, cap, d, fmt))
+        one, many = mk(), mk()
+        key = "kv_out" if kind == 0 else "idx_out"
+        api.compress_kv(args["x"], args["tok_start"], m, args["score_bias"], score_proj=args["score_proj"],
+                        gamma=args["gamma"], rope_dim=dr, **{key: one})
+        singles.append(one)
+        dev_jobs.append(dict(args, **{key: many}))
+    say(f"compress batch case={case} jobs={len(jobs)}")
+    api.compress_kv_batch(dev_jobs)
+    torch.cuda.synchronize()
+    for j, one, (kind, fmt, d, dr, codes, scales) in zip(dev_jobs, singles, refs):
+        many = j.get("kv_out") or j.get("idx_out")
+        if kind == 0:
+            gc, gs, oc, osc = many.rec.cpu().numpy(), None, one.rec.cpu().numpy(), None
+        else:
+            gc, oc = many.codes.cpu().numpy(), one.codes.cpu().numpy()
+            gs = None if many.scales is None else many.scales.cpu().numpy()
+            osc = None if one.scales is None else one.scales.cpu().numpy()
+        assert np.array_equal(gc, oc)
+        if gs is not None:
+            assert np.array_equal(gs, osc)
+        check_pooled(kind, fmt, d, dr, codes, scales, gc, gs)
 
 
 # ====================================================================== indexer
