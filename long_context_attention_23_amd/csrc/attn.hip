@@ -272,14 +272,29 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     const int G = (int)blockDim.x / nc4;                        // split groups
     const int c = tid % nc4, g = tid / nc4;
     const float4* wo4 = reinterpret_cast<const float4*>(wo + mbase * d) + c;
-    const size_t sstride = (size_t)a.H * d / 4;                 // float4s between splits
+    const uint2* wb4 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.ws) + mbase * d) + c;
+    const size_t sstride = (size_t)a.H * d / 4;                 // 4-value groups between splits
     const bool vec = d % 4 == 0;
+    const bool pb = a.part_bf16 != 0;                           // partials in bf16
     const int nq = vec ? (NS + G - 1) / G : 0;
     float4 x[kCombLoads];
+    if (pb) {
+        uint2 xb[kCombLoads];
 #pragma unroll
-    for (int q = 0; q < kCombLoads; q++) {
-        x[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (q < nq) x[q] = wo4[(size_t)min(g + q * G, NS - 1) * sstride];
+        for (int q = 0; q < kCombLoads; q++) {
+            xb[q] = make_uint2(0u, 0u);
+            if (q < nq) xb[q] = wb4[(size_t)min(g + q * G, NS - 1) * sstride];
+        }
+#pragma unroll
+        for (int q = 0; q < kCombLoads; q++)
+            x[q] = make_float4(__uint_as_float(xb[q].x << 16), __uint_as_float(xb[q].x & 0xFFFF0000u),
+                               __uint_as_float(xb[q].y << 16), __uint_as_float(xb[q].y & 0xFFFF0000u));
+    } else {
+#pragma unroll
+        for (int q = 0; q < kCombLoads; q++) {
+            x[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (q < nq) x[q] = wo4[(size_t)min(g + q * G, NS - 1) * sstride];
+        }
     }
     const int64_t t = a.q_pos[row];
     const int lane = tid & (kWave - 1);
@@ -311,9 +326,13 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
         // head dims not a multiple of 4: one dim per thread, splits in order
         const float den = den_s;
         const float* wo_h = wo + mbase * d;
+        const uint16_t* wb_h = reinterpret_cast<const uint16_t*>(a.ws) + mbase * d;
         for (int k = tid; k < d; k += blockDim.x) {
             float acc = 0.0f;
-            for (int s2 = 0; s2 < nsplit; s2++) acc = fmaf(wsc[s2], wo_h[(size_t)s2 * a.H * d + k], acc);
+            for (int s2 = 0; s2 < nsplit; s2++) {
+                const size_t i = (size_t)s2 * a.H * d + k;
+                acc = fmaf(wsc[s2], pb ? __uint_as_float((uint32_t)wb_h[i] << 16) : wo_h[i], acc);
+            }
             v[k] = den > 0.0f ? acc / den : 0.0f;
         }
         __syncthreads();
@@ -371,7 +390,11 @@ hipError_t launch_attention(const AttnArgs& a0, int64_t max_entries, hipStream_t
     const int64_t nb = attn_nsplit_bound(max_entries, a0.Tq);
     AttnArgs a = a0;
     a.nsplit_max = (int32_t)nb;
-    if (attn_mfma_supported(a)) {
+    // the matrix-core kernel keeps bf16 partials for bf16 outputs (the partial
+    // store and the combine read agree through this flag)
+    const bool mfma = attn_mfma_supported(a);
+    a.part_bf16 = mfma && a.out_fmt == CSA_BF16 ? 1 : 0;
+    if (mfma) {
         hipError_t e = launch_attention_mfma(a, nb, st);
         if (e != hipSuccess) return e;
     } else {

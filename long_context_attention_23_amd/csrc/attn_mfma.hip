@@ -780,33 +780,59 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         return;
     }
     // partial results of this split: unnormalised O, and (max, sum) in natural-log units.
-    // O goes through LDS (the tile and logit areas are free now), 32 heads at
-    // a time, so that the global stores are whole 16-byte vectors.
+    // O goes through LDS (the tile and logit areas are free now) so that the
+    // global stores are whole 16-byte vectors: in bf16 (bf16 outputs: the
+    // partial is rounded once more, half the bytes of the split round trip)
+    // all heads at once, in fp32 32 heads at a time.
     float* wo = reinterpret_cast<float*>(a.ws);
     float* wml = wo + (size_t)a.rows * a.nsplit_max * a.H * D;
     const size_t base = ((size_t)row * a.nsplit_max + sp) * a.H + h0;
     static_assert(sizeof(MfmaTiles<D, DR, F8>) + sizeof(sm.zx) >= 32 * (D + 4) * sizeof(float),
                   "partial staging does not fit");
-    float* ost = reinterpret_cast<float*>(&sm);     // [32 heads][D + 4]
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-        if (2 * half >= MT) break;
+    static_assert(sizeof(MfmaTiles<D, DR, F8>) + sizeof(sm.zx) >= 64 * (D + 8) * sizeof(uint16_t),
+                  "bf16 partial staging does not fit");
+    if constexpr (sizeof(OT) == 2) {
+        uint16_t* ost = reinterpret_cast<uint16_t*>(&sm);     // [64 heads][D + 8]
         __syncthreads();
-        if (hp == half) {
+        if (active) {
 #pragma unroll
             for (int mt = 0; mt < 2; mt++)
 #pragma unroll
                 for (int nd = 0; nd < NT; nd++)
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        ost[(16 * mt + 4 * g4 + i) * (D + 4) + dbase + 16 * nd + l16] = o[mt][nd][i];
+                        ost[(32 * hp + 16 * mt + 4 * g4 + i) * (D + 8) + dbase + 16 * nd + l16] =
+                            f32_to_bf16(o[mt][nd][i]);
         }
         __syncthreads();
-        const int nv = min(32, 16 * MT - 32 * half) * (D / 4);      // float4s of the valid heads
-        float4* dst = reinterpret_cast<float4*>(wo + (base + 32 * half) * D);
+        const int nv = 16 * MT * (D / 8);                  // 16-byte vectors of the valid heads
+        uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.ws) + base * D);
         for (int v = tid; v < nv; v += kNW * 64) {
-            const int h = v / (D / 4), c4 = v % (D / 4);
-            dst[v] = *reinterpret_cast<const float4*>(&ost[h * (D + 4) + 4 * c4]);
+            const int h = v / (D / 8), c8 = v % (D / 8);
+            dst[v] = *reinterpret_cast<const uint4*>(&ost[h * (D + 8) + 8 * c8]);
+        }
+    } else {
+        float* ost = reinterpret_cast<float*>(&sm);     // [32 heads][D + 4]
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            if (2 * half >= MT) break;
+            __syncthreads();
+            if (hp == half) {
+#pragma unroll
+                for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+                    for (int nd = 0; nd < NT; nd++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            ost[(16 * mt + 4 * g4 + i) * (D + 4) + dbase + 16 * nd + l16] = o[mt][nd][i];
+            }
+            __syncthreads();
+            const int nv = min(32, 16 * MT - 32 * half) * (D / 4);      // float4s of the valid heads
+            float4* dst = reinterpret_cast<float4*>(wo + (base + 32 * half) * D);
+            for (int v = tid; v < nv; v += kNW * 64) {
+                const int h = v / (D / 4), c4 = v % (D / 4);
+                dst[v] = *reinterpret_cast<const float4*>(&ost[h * (D + 4) + 4 * c4]);
+            }
         }
     }
     if (owner && l16 == 0) {
@@ -831,7 +857,7 @@ bool attn_mfma_supported(const AttnArgs& a) {
 template <bool F8, typename OT>
 static void launch_d(const AttnArgs& a0, int nsplit, hipStream_t st) {
     AttnArgs a = a0;
-    a.nsplit_max = nsplit;
+    a.nsplit_max = nsplit;                              // part_bf16: set by launch_attention
     const int groups = (a.H + 63) / 64;
     dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)groups);
     // eight waves per workgroup always (head halves x dim quarters); a

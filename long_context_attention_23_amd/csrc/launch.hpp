@@ -107,6 +107,7 @@ struct AttnArgs {
     void* ws;
     int64_t ws_bytes;
     int32_t nsplit_max;         // splits per row in the partial buffers (set by the launcher)
+    int32_t part_bf16;          // split partials of O stored in bf16 (set by the launcher)
     RopeTable rope;
 };
 int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t max_entries);
