@@ -28,6 +28,7 @@
 //      sort).  The append order of A/C does not matter: D's result depends
 //      only on the sets.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -147,7 +148,7 @@ __device__ __forceinline__ void wave_pick_digit(const uint32_t* hist, uint32_t n
 // Radix select over n composites get(i) (nbits significant bits): returns the
 // composite of the need-th largest.  Block-wide; hist is LDS [256], sh LDS [4].
 template <typename Get>
-__device__ uint64_t radix_select(Get get, int64_t n, int nbits, uint32_t need, uint32_t* hist, uint32_t* sh) {
+__device__ __forceinline__ uint64_t radix_select(Get get, int64_t n, int nbits, uint32_t need, uint32_t* hist, uint32_t* sh) {
     uint64_t prefix = 0, pmask = 0;
     for (int shift = ((nbits + 7) / 8) * 8 - 8; shift >= 0; shift -= 8) {
         for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
@@ -663,7 +664,21 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     const uint32_t need = (uint32_t)a.topk - nsel;     // 1 <= need <= ncand by construction
     const bool in_reg = ncand <= (uint32_t)kIdxFinalLds;
     const int nwords = (int)((n + 31) / 32);
-    if (nwords <= kIdxBitmapWords) {
+    // the bitmap selection, with R candidates per thread held in registers
+    // across its three passes over them (R = 0: read from memory each pass)
+    auto bitmap_select = [&](auto rc) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
+        uint2 cr[R > 0 ? R : 1];
+        if constexpr (R == kIdxCandPerThread) {
+#pragma unroll
+            for (int q = 0; q < R; q++) cr[q] = cv[q];
+        } else if constexpr (R > 0) {
+#pragma unroll
+            for (int q = 0; q < R; q++) {
+                const uint32_t i = tid + q * kIdxFinalThreads;
+                cr[q] = i < ncand ? w.cand[i] : make_uint2(0u, 0u);
+            }
+        }
         uint32_t* bmA = reinterpret_cast<uint32_t*>(bm4[0]);
         uint32_t* bmT = reinterpret_cast<uint32_t*>(bm4[1]);
         for (int i = tid; i < kIdxBitmapWords / 4; i += blockDim.x) {
@@ -677,15 +692,15 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
             const uint32_t idx = tid + q * kIdxFinalThreads;
             if (idx < nsel) atomicOr(&bmA[(uint32_t)sv[q] >> 5], 1u << (sv[q] & 31));
         }
-        // digit passes over the candidates (registers, or global beyond 4096)
+        // digit passes over the candidates (registers, or memory)
         auto pass = [&](int shift, bool filt, uint32_t upper, uint32_t* h) {
             uint32_t run_dg = 0, run_cnt = 0;
-            if (in_reg) {
+            if constexpr (R > 0) {
 #pragma unroll
-                for (int q = 0; q < kIdxCandPerThread; q++) {
+                for (int q = 0; q < R; q++) {
                     const uint32_t i = tid + q * kIdxFinalThreads;
-                    const bool in = i < ncand && (!filt || ((cv[q].x >> 10) & 1023u) == upper);
-                    digit_hist_round(cv[q].x, in, shift, h, run_dg, run_cnt);
+                    const bool in = i < ncand && (!filt || ((cr[q].x >> 10) & 1023u) == upper);
+                    digit_hist_round(cr[q].x, in, shift, h, run_dg, run_cnt);
                 }
             } else {                                      // batches of 8 rounds, loads first
                 for (uint32_t i0 = 0; i0 < ncand; i0 += 8 * blockDim.x) {
@@ -705,33 +720,76 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
             }
             flush_digit_run(h, run_dg, run_cnt);
         };
-        pass(10, false, 0u, hA);
-        __syncthreads();
-        if (tid < kWave) {
-            uint32_t dg, ab;
-            wave_pick_digit1024(hA, need, dg, ab);
-            if (tid == 0) { sh[0] = dg; sh[1] = ab; }
+        // beyond the first size class: the smallest and largest score suffix
+        // among the candidates; when they are equal every candidate ties at T
+        // (e.g. a row whose weights are all negative: the keys left to choose
+        // from all score 0) and the digit passes are skipped
+        uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+        if constexpr (R == kIdxCandPerThread) {
+            kmx = 1u;                                     // always the passes
+        } else if constexpr (R > 0) {
+#pragma unroll
+            for (int q = 0; q < R; q++)
+                if (tid + q * kIdxFinalThreads < ncand) {
+                    kmn = min(kmn, cr[q].x & 0xFFFFFu);
+                    kmx = max(kmx, cr[q].x & 0xFFFFFu);
+                }
+        } else {
+            for (uint32_t i = tid; i < ncand; i += blockDim.x) {
+                const uint32_t x = w.cand[i].x & 0xFFFFFu;
+                kmn = min(kmn, x);
+                kmx = max(kmx, x);
+            }
         }
-        __syncthreads();
-        const uint32_t dA = sh[0], needA = need - sh[1];
-        pass(0, true, dA, hB);
-        __syncthreads();
-        if (tid < kWave) {
-            uint32_t dg, ab;
-            wave_pick_digit1024(hB, needA, dg, ab);
-            if (tid == 0) { sh[2] = dg; sh[3] = ab; }
+        if constexpr (R != kIdxCandPerThread) {
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                kmn = min(kmn, (uint32_t)__shfl_xor((int)kmn, o, kWave));
+                kmx = max(kmx, (uint32_t)__shfl_xor((int)kmx, o, kWave));
+            }
+            if ((tid & (kWave - 1)) == 0) { wsum[0][tid / kWave] = kmn; wsum[1][tid / kWave] = kmx; }
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < kIdxFinalThreads / kWave; v++) {
+                kmn = min(kmn, wsum[0][v]);
+                kmx = max(kmx, wsum[1][v]);
+            }
+            __syncthreads();                              // wsum is reused by the scans below
         }
-        __syncthreads();
-        const uint32_t T = (dA << 10) | sh[2];
-        const int needT = (int)(needA - sh[3]);           // ties at T to take, >= 1
+        uint32_t T;
+        int needT;                                        // ties at T to take, >= 1
+        if (kmn == kmx) {
+            T = kmn;
+            needT = (int)need;
+        } else {
+            pass(10, false, 0u, hA);
+            __syncthreads();
+            if (tid < kWave) {
+                uint32_t dg, ab;
+                wave_pick_digit1024(hA, need, dg, ab);
+                if (tid == 0) { sh[0] = dg; sh[1] = ab; }
+            }
+            __syncthreads();
+            const uint32_t dA = sh[0], needA = need - sh[1];
+            pass(0, true, dA, hB);
+            __syncthreads();
+            if (tid < kWave) {
+                uint32_t dg, ab;
+                wave_pick_digit1024(hB, needA, dg, ab);
+                if (tid == 0) { sh[2] = dg; sh[3] = ab; }
+            }
+            __syncthreads();
+            T = (dA << 10) | sh[2];
+            needT = (int)(needA - sh[3]);
+        }
         auto mark = [&](uint2 c) {
             const uint32_t sfx = c.x & 0xFFFFFu;
             if (sfx >= T) atomicOr(&(sfx > T ? bmA : bmT)[c.y >> 5], 1u << (c.y & 31));
         };
-        if (in_reg) {
+        if constexpr (R > 0) {
 #pragma unroll
-            for (int q = 0; q < kIdxCandPerThread; q++)
-                if (tid + q * kIdxFinalThreads < ncand) mark(cv[q]);
+            for (int q = 0; q < R; q++)
+                if (tid + q * kIdxFinalThreads < ncand) mark(cr[q]);
         } else {
             for (uint32_t i0 = 0; i0 < ncand; i0 += 8 * blockDim.x) {
                 uint2 cc[8];
@@ -779,6 +837,12 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
                 off++;
             }
         }
+    };
+    if (nwords <= kIdxBitmapWords) {
+        if (in_reg) bitmap_select(std::integral_constant<int, kIdxCandPerThread>{});
+        else if (ncand <= 16u * kIdxFinalThreads) bitmap_select(std::integral_constant<int, 16>{});
+        else if (ncand <= 24u * kIdxFinalThreads) bitmap_select(std::integral_constant<int, 24>{});
+        else bitmap_select(std::integral_constant<int, 0>{});
         return;
     }
     // very large caps: radix-select the composite (score suffix, inverted

@@ -274,6 +274,26 @@ def test_indexer_tie_heavy_rows_exact():
     assert np.array_equal(got[1, 1], np.arange(k))           # all tied: the first k blocks
 
 
+def test_indexer_tie_tiers_exact():
+    """Rows where every visible key ties (all weights zero), one per size class
+    of the final selection's candidate storage: 3,000 / 12,000 / 20,000 /
+    40,000 tied candidates (four per thread in registers, sixteen, twenty-four,
+    re-read from memory).  The tie rule gives the first k blocks; an
+    all-negative row beside them mixes ties at 0 with the rest."""
+    g = synth.rng(547)
+    B, Tq, Hi, di, m, k, cap = 1, 5, 4, 64, 4, 1024, 41000
+    kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
+    qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+    w = synth.grid(g, (B, Tq, Hi))
+    w[0, :4] = 0.0
+    w[0, 4] = -np.abs(w[0, 4]) - np.float32(0.125)
+    pos = np.array([[4 * 3000 + 1, 4 * 12000 + 3, 4 * 20000, 4 * 40000 + 2, 4 * cap - 1]], np.int32)
+    got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
+    assert np.array_equal(got, ref)
+    for i in range(4):
+        assert np.array_equal(got[0, i], np.arange(k))
+
+
 @pytest.mark.parametrize("Tq", [96, 40])
 def test_indexer_prefill_chunk_exact(Tq):
     """A chunk of query rows (FP4 queries and keys, four heads): the
