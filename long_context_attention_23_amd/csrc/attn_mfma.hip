@@ -255,6 +255,14 @@ __device__ __forceinline__ void fetch_expand(Smem& sm, int buf, int w, int lane,
     }
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations
+// complete, then s_barrier.  __syncthreads() would also wait for every
+// global-to-LDS copy in flight (they count as LDS writes); the copies of a
+// ring buffer are waited for explicitly (wait_vm) by the waves that issued
+// them, before the barrier that publishes the buffer.  The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // wait for this wave's global-to-LDS copies (vmcnt 0), and for its LDS reads
 // before the staging area is refilled (lgkmcnt 0)
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -343,6 +351,21 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     }
 
     const int b = row / a.Tq;
+    // sparse rows: the entry layout (k top-k entries, then the window) does
+    // not depend on the position, so the fetching waves read the first tiles'
+    // top-k indices before it arrives
+    const int fw = w - (kNW - kFetchers);              // fetching wave index (>= 0 for waves 4..7)
+    const bool fetcher = fw >= 0;
+    const bool sparse = a.topk != nullptr;
+    int32_t jf0 = 0, jf1 = 0, jf2 = 0;
+    if (sparse && fetcher && a.k > 0) {
+        const int32_t split_s = attn_split_len<int32_t>(a.k + a.W, a.Tq);
+        const int32_t eb = (int32_t)blockIdx.x * split_s + fw + kFetchers * lane;
+        const int32_t* top = a.topk + (int64_t)row * a.k;
+        jf0 = top[min(eb, a.k - 1)];
+        jf1 = top[min(eb + kMTE, a.k - 1)];
+        jf2 = top[min(eb + 2 * kMTE, a.k - 1)];
+    }
     const int t = a.q_pos[row];
     RowCtx c;
     c.vis = t < 0 ? 0 : (t + 1) / a.m;
@@ -368,8 +391,6 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const int nnt = max(0, min(NT, (dn - dbase) / 16));
     const float zscale = a.scale * kLog2e;             // logits in base-2 units
 
-    const int fw = w - (kNW - kFetchers);              // fetching wave index (>= 0 for waves 4..7)
-    const bool fetcher = fw >= 0;
     const int ntiles = (e1 - e0 + kMTE - 1) / kMTE;
     // the first tile's records go out before the query prologue; the top-k
     // indices are read two tiles ahead of their records
@@ -390,15 +411,18 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             }
         }
     };
-    // top-k indices of the first tiles, all in flight together; the records
-    // go out once the query's square sums are published (the fetching waves
-    // would otherwise wait for their records before that barrier)
-    int32_t jf0 = 0, jf1 = 0;
+    // the first tiles' records go out as soon as their addresses are known:
+    // the barrier after the query's square sums does not wait for them
     if (fetcher) {
-        jf0 = fetch_index(a, c, e0, e1, fw, lane);
-        jf1 = fetch_index(a, c, e0 + kMTE, e1, fw, lane);
-        if constexpr (F8) jn = fetch_index(a, c, e0 + 2 * kMTE, e1, fw, lane);
-        else jn = jf1;
+        if constexpr (F8) {
+            jn = jf2;
+            ring_issue(0, 0, jf0);
+            if (ntiles > 1) ring_issue(1, 1, jf1);
+        } else {
+            jn = jf1;
+            fr = fetch_plan(a, c, e0, e1, fw, lane, jf0);
+            fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
+        }
     }
     stage_rope_arg(offsetof(AttnArgs, rope), sm.rf, a.dr / 2);
 
@@ -419,16 +443,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         ss += __shfl_xor(ss, 32, kWave);
         if (g4 == 0) sm.ssq[qd][32 * hp + 16 * mt + l16] = ss;
     }
-    if (fetcher) {
-        if constexpr (F8) {
-            ring_issue(0, 0, jf0);
-            if (ntiles > 1) ring_issue(1, 1, jf1);
-        } else {
-            fr = fetch_plan(a, c, e0, e1, fw, lane, jf0);
-            fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
-        }
-    }
-    __syncthreads();
+    lds_barrier();
     float inv[2];
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
