@@ -341,11 +341,11 @@ def cpu_baseline(target_s):
 # runs of this benchmark scaled by the copy calibration (profiles/
 # traffic_*.md); valid only while the kernels' sources are unchanged.
 TRAFFIC = {
-    "csa_indexer_topk": {"bytes": 45_600_874, "src": "bb6c5ff9c46afa85"},
-    "csa_sparse_mqa_attn": {"bytes": 25_417_038, "src": "bb6c5ff9c46afa85"},
-    "hca_dense_mqa_attn": {"bytes": 84_654_647, "src": "bb6c5ff9c46afa85"},
-    "csa_out_proj": {"bytes": 59_134_704, "src": "bb6c5ff9c46afa85"},
-    "hca_out_proj": {"bytes": 59_134_704, "src": "bb6c5ff9c46afa85"},
+    "csa_indexer_topk": {"bytes": 45_554_577, "src": "053954556734fd5d"},
+    "csa_sparse_mqa_attn": {"bytes": 25_884_114, "src": "053954556734fd5d"},
+    "hca_dense_mqa_attn": {"bytes": 54_345_176, "src": "053954556734fd5d"},
+    "csa_out_proj": {"bytes": 59_134_704, "src": "053954556734fd5d"},
+    "hca_out_proj": {"bytes": 59_134_704, "src": "053954556734fd5d"},
 }
 TRAFFIC_SRC = ["long_context_attention_23_amd/csrc/indexer.hip", "long_context_attention_23_amd/csrc/attn_mfma.hip",
                "long_context_attention_23_amd/csrc/attn.hip", "long_context_attention_23_amd/csrc/proj.hip",
