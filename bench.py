@@ -338,8 +338,9 @@ def cpu_baseline(target_s):
 
 
 # HBM traffic per launch of a call, from rocprofv3 FETCH_SIZE and WRITE_SIZE
-# runs of this benchmark scaled by the copy calibration (profiles/
-# traffic_*.md); valid only while the kernels' sources are unchanged.
+# runs of this benchmark scaled by the copy calibration (the summary under
+# profiles/ gives the counts and commands); valid only while the kernels'
+# sources are unchanged (src_hash below).
 TRAFFIC = {
     "csa_indexer_topk": {"bytes": 45_554_577, "src": "053954556734fd5d"},
     "csa_sparse_mqa_attn": {"bytes": 25_884_114, "src": "053954556734fd5d"},
