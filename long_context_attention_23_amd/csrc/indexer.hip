@@ -110,10 +110,12 @@ __device__ __forceinline__ float score_one(const IndexerArgs& a, const uint8_t* 
     return s;
 }
 
-__device__ __forceinline__ int64_t visible_blocks(const IndexerArgs& a, int64_t row) {
-    int64_t t = a.q_pos[row];
-    int64_t n = t < 0 ? 0 : (t + 1) / a.m;
+__device__ __forceinline__ int64_t visible_from(const IndexerArgs& a, int64_t t) {
+    const int64_t n = t < 0 ? 0 : (t + 1) / a.m;
     return n < a.cap ? n : a.cap;
+}
+__device__ __forceinline__ int64_t visible_blocks(const IndexerArgs& a, int64_t row) {
+    return visible_from(a, a.q_pos[row]);
 }
 
 // ------------------------------------------------------------------ radix helpers
@@ -340,9 +342,7 @@ __global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs
     __shared__ uint32_t lh[kIdxHistBins];
     const int64_t r = blockIdx.y, row = a.row0 + r;
     const int64_t b = row / a.Tq;
-    const int64_t n = visible_blocks(a, row);
     const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
-    if (n <= a.topk || c0 >= n) return;
     RowWs ws = row_ws(a, r);
     for (int i = threadIdx.x; i < kIdxHistBins; i += blockDim.x) lh[i] = 0;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -378,27 +378,38 @@ __global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs
             for (int j = 0; j < 8; j++) qab[ks][j] = (__bf16)v[j];
         }
     }
-    __syncthreads();
-    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
     const uint8_t* kb = a.keys + (size_t)b * a.cap * KROW;
     const uint8_t* ksb = KF == CSA_FP4_E2M1 ? a.key_scales + (size_t)b * a.cap * (DI / 32) : nullptr;
     constexpr int kStride = 32 * (kIdxScoreThreads / 64);
-    for (int64_t gb = c0 + 32 * wv; gb < c1; gb += (int64_t)kStride * kIdxMfmaBatch) {
-        uint4 kc[kIdxMfmaBatch][NKS];
-        int ksc[kIdxMfmaBatch];
+    // key loads stay inside the cache's rows (cl); the first batch goes out
+    // before the position arrives, and keys past the visible blocks (c1) are
+    // scored but never stored or counted
+    const int64_t cl = min(c0 + (int64_t)kIdxChunk, a.cap);
+    uint4 kc[kIdxMfmaBatch][NKS];
+    int ksc[kIdxMfmaBatch];
+    auto load_batch = [&](int64_t gb) {
 #pragma unroll
         for (int u = 0; u < kIdxMfmaBatch; u++) {
             const int64_t key = gb + (int64_t)u * kStride + l32;
             ksc[u] = 127;
 #pragma unroll
             for (int ks = 0; ks < NKS; ks++) kc[u][ks] = make_uint4(0u, 0u, 0u, 0u);
-            if (key < c1) {
+            if (key < cl) {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ks++)
                     kc[u][ks] = *reinterpret_cast<const uint4*>(kb + key * KROW + 32 * ks + 16 * half);
                 if constexpr (KF == CSA_FP4_E2M1) ksc[u] = ksb[key * (DI / 32) + half];
             }
         }
+    };
+    const int64_t gb0 = c0 + 32 * wv;
+    load_batch(gb0);
+    const int64_t n = visible_blocks(a, row);
+    if (n <= a.topk || c0 >= n) return;
+    __syncthreads();
+    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
+    for (int64_t gb = gb0; gb < c1; gb += (int64_t)kStride * kIdxMfmaBatch) {
+        if (gb != gb0) load_batch(gb);
 #pragma unroll
         for (int u = 0; u < kIdxMfmaBatch; u++) {
             const int64_t key = gb + (int64_t)u * kStride + l32;
@@ -472,24 +483,29 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
     __shared__ uint32_t sh[2];
     __shared__ uint32_t wcnt[2][kWaves], base[2];
     const int64_t r = blockIdx.y, row = a.row0 + r;
-    const int64_t n = visible_blocks(a, row);
     const int64_t c0 = (int64_t)blockIdx.x * kIdxChunk;
-    if (n <= a.topk || c0 >= n) return;
     RowWs w = row_ws(a, r);
     const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
-    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
     constexpr int kPer = kIdxChunk / kIdxThreads;
+    // every load goes out before the position is needed (they stay inside the
+    // row's workspace; scores past the visible blocks are never used): the
+    // chunk's scores, the position, and wave 0's bin search over the histogram
+    const int64_t cl = min(c0 + (int64_t)kIdxChunk, a.cap);
     uint32_t keys[kPer];
 #pragma unroll
-    for (int u = 0; u < kPer; u++) {                     // score loads go out before the bin search
+    for (int u = 0; u < kPer; u++) {
         const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
-        keys[u] = j < c1 ? w.scores[j] : 0u;
+        keys[u] = j < cl ? w.scores[j] : 0u;
     }
+    const int32_t tpos = a.q_pos[row];
     if (threadIdx.x < kWave) {
         uint32_t bin, above;
         wave_pick_bin(w.hist, (uint32_t)a.topk, bin, above);
         if (threadIdx.x == 0) { sh[0] = bin; sh[1] = above; }
     }
+    const int64_t n = visible_from(a, tpos);
+    if (n <= a.topk || c0 >= n) return;
+    const int64_t c1 = min(c0 + (int64_t)kIdxChunk, n);
     __syncthreads();
     const uint32_t tbin = sh[0];
     // per-wave counts of the two lists, one global reservation per list for
@@ -644,12 +660,9 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     __shared__ uint32_t wsum[2][kIdxFinalThreads / kWave];
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x, row = a.row0 + r;
-    const int64_t n = visible_blocks(a, row);
     int32_t* out = a.out + row * a.topk;
-    if (n <= a.topk) {
-        for (int64_t i = tid; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
-        return;
-    }
+    // the workspace loads go out before the position arrives (a row with
+    // fewer visible blocks than k ignores them)
     RowWs w = row_ws(a, r);
     uint2 cv[kIdxCandPerThread];
 #pragma unroll
@@ -661,6 +674,11 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
         sv[q] = idx < a.topk ? w.sel[idx] : 0;
     }
     const uint32_t nsel = w.counts[0], ncand = w.counts[1];
+    const int64_t n = visible_blocks(a, row);
+    if (n <= a.topk) {
+        for (int64_t i = tid; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
+        return;
+    }
     const uint32_t need = (uint32_t)a.topk - nsel;     // 1 <= need <= ncand by construction
     const bool in_reg = ncand <= (uint32_t)kIdxFinalLds;
     const int nwords = (int)((n + 31) / 32);
@@ -841,7 +859,7 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     if (nwords <= kIdxBitmapWords) {
         if (in_reg) bitmap_select(std::integral_constant<int, kIdxCandPerThread>{});
         else if (ncand <= 16u * kIdxFinalThreads) bitmap_select(std::integral_constant<int, 16>{});
-        else if (ncand <= 24u * kIdxFinalThreads) bitmap_select(std::integral_constant<int, 24>{});
+        else if (ncand <= 20u * kIdxFinalThreads) bitmap_select(std::integral_constant<int, 20>{});
         else bitmap_select(std::integral_constant<int, 0>{});
         return;
     }

@@ -277,7 +277,7 @@ def test_indexer_tie_heavy_rows_exact():
 def test_indexer_tie_tiers_exact():
     """Rows where every visible key ties (all weights zero), one per size class
     of the final selection's candidate storage: 3,000 / 12,000 / 20,000 /
-    40,000 tied candidates (four per thread in registers, sixteen, twenty-four,
+    40,000 tied candidates (four per thread in registers, sixteen, twenty,
     re-read from memory).  The tie rule gives the first k blocks; an
     all-negative row beside them mixes ties at 0 with the rest."""
     g = synth.rng(547)
