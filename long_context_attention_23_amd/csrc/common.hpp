@@ -105,6 +105,20 @@ __device__ __forceinline__ void warm_kernargs(size_t bytes) {
     for (size_t off = 0; off < bytes; off += 64) acc ^= p[off / 4];
     asm volatile("" ::"s"(acc));
 }
+// the same for BYTES bytes starting at a run-time offset: a fixed number of
+// independent loads, one per 64-byte line
+template <size_t BYTES>
+__device__ __forceinline__ void warm_kernargs_at(size_t from) {
+    constexpr int kLines = (int)((BYTES + 63) / 64) + 1;
+    const uint32_t* p = (const uint32_t*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + (from & ~(size_t)63));
+    uint32_t v[kLines];
+#pragma unroll
+    for (int i = 0; i < kLines; i++) v[i] = p[16 * i];
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < kLines; i++) acc ^= v[i];
+    asm volatile("" ::"s"(acc));
+}
 
 // the p-th frequency of a RopeTable passed by value at byte `offset` of the
 // kernel arguments, read by one lane from the argument segment

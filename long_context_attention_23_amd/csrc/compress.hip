@@ -436,7 +436,8 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_batch(CompressBatch b
     const int z = blockIdx.z;
     const CompressArgs& a = bt.job[z];
     const size_t off = (size_t)z * sizeof(CompressArgs);
-    if ((int64_t)blockIdx.x >= a.T / a.m || (int)blockIdx.y >= a.B) return;
+    warm_kernargs_at<offsetof(CompressArgs, rope)>(off);
+    if ((int64_t)(blockIdx.x + 1) * a.m > a.T || (int)blockIdx.y >= a.B) return;   // block x of this job is complete iff (x+1) m <= T
     constexpr int EPC = 16 / (int)sizeof(XT);
     const int TG = kCompThreads / (a.d / EPC);
     if (a.m <= TG) compress_fast_body<XT, 1>(a, off + offsetof(CompressArgs, rope), sm, blockIdx.y, blockIdx.x);
