@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         jf1 = top[min(eb + kMTE, a.k - 1)];
         jf2 = top[min(eb + 2 * kMTE, a.k - 1)];
     }
-    const int t = a.q_pos[row];
+    const int t = load_uniform_i32(a.q_pos + row);
     RowCtx c;
     c.vis = t < 0 ? 0 : (t + 1) / a.m;
     if (c.vis > a.ccap) c.vis = (int32_t)a.ccap;

@@ -120,6 +120,14 @@ __device__ __forceinline__ void warm_kernargs_at(size_t from) {
     asm volatile("" ::"s"(acc));
 }
 
+// A value every lane reads at the same address (a row's position), loaded
+// through the scalar unit: waiting for it does not wait for the vector loads
+// issued before it (they count on a different counter).  The memory is only
+// read during the kernel.
+__device__ __forceinline__ int32_t load_uniform_i32(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // the p-th frequency of a RopeTable passed by value at byte `offset` of the
 // kernel arguments, read by one lane from the argument segment
 __device__ __forceinline__ double rope_freq_arg(size_t offset, int p) {

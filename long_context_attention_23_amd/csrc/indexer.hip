@@ -115,7 +115,7 @@ __device__ __forceinline__ int64_t visible_from(const IndexerArgs& a, int64_t t)
     return n < a.cap ? n : a.cap;
 }
 __device__ __forceinline__ int64_t visible_blocks(const IndexerArgs& a, int64_t row) {
-    return visible_from(a, a.q_pos[row]);
+    return visible_from(a, load_uniform_i32(a.q_pos + row));
 }
 
 // ------------------------------------------------------------------ radix helpers
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(kIdxThreads) void k_idx_collect(IndexerArgs a) {
         const int64_t j = c0 + (int64_t)u * kIdxThreads + threadIdx.x;
         keys[u] = j < cl ? w.scores[j] : 0u;
     }
-    const int32_t tpos = a.q_pos[row];
+    const int32_t tpos = load_uniform_i32(a.q_pos + row);
     if (threadIdx.x < kWave) {
         uint32_t bin, above;
         wave_pick_bin(w.hist, (uint32_t)a.topk, bin, above);
