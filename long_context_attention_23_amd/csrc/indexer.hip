@@ -14,19 +14,21 @@
 // Small path (<= 4096 visible keys, e.g. prefill of a short context): one
 //   workgroup per query row keeps every score in LDS, radix-selects in LDS and
 //   emits the set by a j-ordered compaction.
-// Large path (decode against 10^5..10^6 keys): three kernels over key chunks
-//   and rows --
+// Large path (decode against 10^5..10^6 keys): after a kernel that clears
+//   each row's histogram and counters, three kernels over key chunks and rows --
 //   A  score + 4096-bin LDS histogram of the top 12 key bits, merged into a
 //      per-row global histogram with integer atomics;
 //   C  every chunk finds the threshold bin from that histogram and appends
 //      keys above it to the row's "selected" list and keys in it to the
 //      "candidate" list (wave-aggregated appends);
 //   D  one workgroup per row finds the threshold score suffix among the
-//      candidates (two 10-bit digit passes), takes the tied ones at it by
-//      smallest block index, and emits the k blocks in ascending order from
-//      LDS bitmaps (caps beyond 2^19: composite radix select and a bitonic
-//      sort).  The append order of A/C does not matter: D's result depends
-//      only on the sets.
+//      candidates (two 10-bit digit passes, skipped when all candidates share
+//      one key), takes the tied ones at it by smallest block index, and emits
+//      the k blocks in ascending order from LDS bitmaps (rows with more than
+//      2^18 visible blocks: composite radix select and a bitonic sort).  The
+//      append order of A/C does not matter: D's result depends only on the
+//      sets.
+// Prefill path (chunks of query rows): see the section further down.
 #include <algorithm>
 #include <type_traits>
 
