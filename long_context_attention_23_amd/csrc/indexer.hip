@@ -1061,13 +1061,15 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_thresh(IndexerArgs a, int32
     }
 }
 
-__global__ __launch_bounds__(kPfThreads) void k_idxp_filter(IndexerArgs a) {
+__global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
     const int b = blockIdx.y, t0 = blockIdx.x * kPfQB;
+    // the head weights of the 16 queries sit in LDS (read per tile as one
+    // 16-byte broadcast per query slot), which keeps four waves per SIMD
+    __shared__ float4 wl[kPfRB][4][2];
     i32x8_t qa[kPfRB];
     int qs[kPfRB];
-    float w[kPfRB][4][4];
     float thr[kPfRB][4];                                  // threshold key as a float (NaN for key 0)
     int32_t nq[kPfRB][4];
     int32_t nmax = 0;
@@ -1086,10 +1088,18 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_filter(IndexerArgs a) {
                 const uint32_t T = pf_hdr(a, row)[0];
                 thr[rb][s] = __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
             }
+            if (lane == 0 && wv == 0) {
 #pragma unroll
-            for (int h = 0; h < 4; h++) w[rb][s][h] = t < a.Tq ? a.w[row * 4 + h] : 0.0f;
+                for (int hf = 0; hf < 2; hf++) {
+                    const int tt = t0 + kPfQ * rb + 2 * s + hf;
+                    const int64_t rw = (int64_t)b * a.Tq + min(tt, a.Tq - 1);
+                    wl[rb][s][hf] = tt < a.Tq ? make_float4(a.w[rw * 4], a.w[rw * 4 + 1], a.w[rw * 4 + 2], a.w[rw * 4 + 3])
+                                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
+            }
         }
     }
+    __syncthreads();
     nmax = (int32_t)wave_max_dpp((float)nmax);
     const int ntile = (nmax + 31) / 32;
     // this wave's running counts per query (above the threshold, at it):
@@ -1101,23 +1111,29 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_filter(IndexerArgs a) {
         for (int s = 0; s < 4; s++) { cnt[rb][s][0] = cnt[rb][s][1] = tcnt[rb][s][0] = tcnt[rb][s][1] = 0u; }
     const int64_t rowb = a.ws_row_bytes;
     uint8_t* wbase = a.ws + ((int64_t)b * a.Tq + t0) * rowb;   // this workgroup's first query row
-    const int64_t hoff = half ? rowb : 0;                        // odd queries of a slot pair
     uint4 kc;
     int ks;
     if (wv < ntile) pf_load_keys(a, b, (int64_t)wv * 32, l32, half, kc, ks);
     for (int tile = wv; tile < ntile; tile += kPfWaves) {
+        // odd queries of a slot pair, re-derived every tile (the empty asm
+        // keeps the compiler from hoisting eight 64-bit row addresses out of
+        // the loop, which would not fit in four waves' registers)
+        uint32_t hoff = half ? (uint32_t)rowb : 0u;
+        asm volatile("" : "+v"(hoff));
         const uint4 kcur = kc;
         const int kscur = ks;
         if (tile + kPfWaves < ntile) pf_load_keys(a, b, (int64_t)(tile + kPfWaves) * 32, l32, half, kc, ks);
-        f32x16_t acc[kPfRB];
-#pragma unroll
-        for (int rb = 0; rb < kPfRB; rb++) acc[rb] = pf_mfma(qa[rb], qs[rb], kcur, kscur);
         const int32_t j = tile * 32 + l32;
 #pragma unroll
         for (int rb = 0; rb < kPfRB; rb++) {
+            // one row block's products at a time (fewer live registers: with
+            // four waves per SIMD the others cover the matrix-core latency)
+            const f32x16_t acc = pf_mfma(qa[rb], qs[rb], kcur, kscur);
 #pragma unroll
             for (int s = 0; s < 4; s++) {
-                const float sc = pf_score(acc[rb], s, w[rb][s]);
+                const float4 w4 = wl[rb][s][half];
+                const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
+                const float sc = pf_score(acc, s, wv4);
                 const bool vis = j < nq[rb][s];
                 const bool above = vis && sc > thr[rb][s], tie = vis && sc == thr[rb][s];
                 const uint64_t bal = ballot64(above), bt = ballot64(tie);
@@ -1126,7 +1142,7 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_filter(IndexerArgs a) {
                     // less the lower half's count for the upper half
                     const uint32_t alo = (uint32_t)bal, ahi = (uint32_t)(bal >> 32);
                     const uint32_t tlo = (uint32_t)bt, thi = (uint32_t)(bt >> 32);
-                    uint8_t* rp = wbase + (int64_t)(kPfQ * rb + 2 * s) * rowb + hoff;
+                    uint8_t* rp = wbase + (int64_t)(kPfQ * rb + 2 * s) * rowb + (int64_t)hoff;
                     if (above) {
                         const uint32_t r = __builtin_amdgcn_mbcnt_hi(ahi, __builtin_amdgcn_mbcnt_lo(alo, 0u));
                         const uint32_t pos = r + (half ? cnt[rb][s][1] - __popc(alo) : cnt[rb][s][0]);
