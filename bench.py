@@ -259,6 +259,17 @@ def prefill_measure(torch, api, reps=3, seed=5005):
     def att():
         api.sparse_mqa_attn(q, pos, top, comp, win, sink, p, out=out, workspace=aws)
 
+    # the HCA layer's prefill over the same chunk: every compressed entry of
+    # the 1M prefix (m = 128) plus the window, dense
+    n_h = (L + PF_T) // M_HCA
+    comp_h = api.KVCache(1, n_h, D_HEAD, DR, api.FP8_E4M3, rec=u8(1, n_h, REC, hi=0x70))
+    p_h = api.attn_params(D_HEAD, DR, W, M_HCA)
+    aws_h = torch.empty(max(1, api.attn_workspace_bytes(1, PF_T, H, D_HEAD, n_h, W, api.BF16, api.FP8_E4M3)),
+                        dtype=torch.uint8, device=dev)
+
+    def att_h():
+        api.hca_dense_mqa_attn(q, pos, comp_h, win, sink, p_h, out=out, workspace=aws_h)
+
     def best(f):
         f()
         torch.cuda.synchronize()
@@ -271,17 +282,21 @@ def prefill_measure(torch, api, reps=3, seed=5005):
             torch.cuda.synchronize()
             t.append(e0.elapsed_time(e1))
         return min(t)
-    ti, ta = best(idx), best(att)
+    ti, ta, th = best(idx), best(att), best(att_h)
     n_mean = (L + PF_T / 2) / M_CSA                       # blocks visible to the average query
     fi = 2.0 * PF_T * HI * DI * n_mean                    # indexer q.k products
     fa = 2.0 * PF_T * H * (PF_TOPK + W) * 2 * D_HEAD      # Q K^T and P V over 1,152 entries
+    fh = 2.0 * PF_T * H * ((L + PF_T / 2) / M_HCA + W) * 2 * D_HEAD   # HCA: every block of the prefix + window
     return {"workload": "CSA prefill chunk, 8,192 queries over a 1M prefix, 64 heads x 512, top-1024, FP4 indexer, "
-                        "FP8 records", "indexer_ms": round(ti, 3), "attn_ms": round(ta, 3),
+                        "FP8 records; and the HCA layer's dense attention over the same chunk (8,256 blocks + window)", "indexer_ms": round(ti, 3), "attn_ms": round(ta, 3),
             "query_tokens_per_s": round(PF_T / ((ti + ta) * 1e-3), 1),
             "indexer_TFLOPs": round(fi / (ti * 1e-3) / 1e12, 1), "indexer_mfma_frac": round(fi / (ti * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
             "indexer_peak": "fp4 10.1 PFLOP/s",
             "attn_TFLOPs": round(fa / (ta * 1e-3) / 1e12, 1), "attn_mfma_frac": round(fa / (ta * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "attn_peak": "bf16 2.5 PFLOP/s", "timing": "HIP events around each call, best of 3 after a warm-up"}
+            "attn_peak": "bf16 2.5 PFLOP/s",
+            "hca_attn_ms": round(th, 3), "hca_attn_TFLOPs": round(fh / (th * 1e-3) / 1e12, 1),
+            "hca_attn_mfma_frac": round(fh / (th * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "timing": "HIP events around each call, best of 3 after a warm-up"}
 
 
 def cpu_baseline(target_s):

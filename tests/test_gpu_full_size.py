@@ -11,7 +11,10 @@ policy), and checks every output the oracle can afford:
   - the CSA + HCA layer pair decode at 1M tokens, batch 4 (262,144 CSA and
     8,192 HCA entries, FP8 records, FP4 indexer keys, 64 heads x 512,
     projection 32768 -> 7168 in 8 groups), including the step's cache
-    writes (window append, CSA block, indexer key, HCA block).
+    writes (window append, CSA block, indexer key, HCA block);
+  - the 8,192-query prefill chunk at 1M tokens, in the CSA layer (indexer
+    top-1024 and sparse attention) and in the HCA layer (dense over 8,256
+    blocks), on sampled query rows.
 
 Indexer inputs are exact (grid values or drawn FP4 codes with grid weights),
 so top-k sets must match bit for bit; attention outputs (bf16) within 2e-2
@@ -253,4 +256,34 @@ def test_c5_prefill_chunk_sampled_rows():
     ref = O.attention(q[0, rows], O.BF16, pos[0, rows], None, sink, D_HEAD, DR, WIN, m, 10000.0, SCALE, 1e-6,
                       comp[0], O.FP8_E4M3, win[0], O.FP8_E4M3, ref_top)
     say(f"c5 sampled attention abs {abs_err(out[0, rows], ref):.3e}")
+    assert abs_err(out[0, rows], ref) <= 2e-2
+
+
+def test_c5_hca_prefill_chunk_sampled_rows():
+    """HCA chunked prefill at 1M tokens: the same 8,192-query chunk in the
+    heavily compressed layer (m = 128), each query dense over every block of
+    its prefix (8,192 + q/128 of 8,256) plus its 128-entry window, FP8
+    records, 64 heads x 512, in the benchmark's configuration (caller
+    workspace).  The oracle checks a spread of query rows one by one."""
+    g = synth.rng(2006)
+    L, T, H, m = 1 << 20, 8192, 64, 128
+    n = (L + T) // m
+    pos = (L + np.arange(T, dtype=np.int32))[None]
+    comp = normed_fp8_records(g, (1, n))
+    win = normed_fp8_records(g, (1, WIN + T))
+    q = synth.bf16_bits(g, (1, T, H, D_HEAD))
+    sink = synth.normal(g, H)
+    cc = api.KVCache(1, n, D_HEAD, DR, O.FP8_E4M3, rec=dev(comp))
+    wc = api.KVCache(1, WIN + T, D_HEAD, DR, O.FP8_E4M3, ring=True, rec=dev(win))
+    ws = torch.empty(max(1, api.attn_workspace_bytes(1, T, H, D_HEAD, n, WIN, api.BF16, O.FP8_E4M3)),
+                     dtype=torch.uint8, device="cuda")
+    say(f"c5 hca attention rows={T} blocks={n} ws={ws.numel()}")
+    out = api.hca_dense_mqa_attn(dev_bf16(q), dev(pos), cc, wc, dev(sink), api.attn_params(D_HEAD, DR, WIN, m),
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    out = out_to_f64(out)
+    rows = np.array([0, 127, 128, 3000, 6143, T - 1])        # block boundaries and the chunk's ends
+    ref = O.attention(q[0, rows], O.BF16, pos[0, rows], None, sink, D_HEAD, DR, WIN, m, 10000.0, SCALE, 1e-6,
+                      comp[0], O.FP8_E4M3, win[0], O.FP8_E4M3, None)
+    say(f"c5 hca sampled attention abs {abs_err(out[0, rows], ref):.3e}")
     assert abs_err(out[0, rows], ref) <= 2e-2
