@@ -229,9 +229,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16
 
 
 def prefill_measure(torch, api, reps=3, seed=5005):
-    """Times the indexer and the sparse attention of one prefill chunk (events
-    around each call, best of reps after a warm-up) on synthetic inputs of the
-    chunk's shapes, and prices their contractions against the MFMA peaks."""
+    """Times the indexer, the sparse attention and the grouped output
+    projection of one prefill chunk, and the HCA layer's dense attention over
+    the same chunk (events around each call, best of reps after a warm-up), on
+    synthetic inputs of the chunk's shapes, and prices their contractions
+    against the MFMA peaks."""
     dev = "cuda"
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
@@ -270,6 +272,13 @@ def prefill_measure(torch, api, reps=3, seed=5005):
     def att_h():
         api.hca_dense_mqa_attn(q, pos, comp_h, win, sink, p_h, out=out, workspace=aws_h)
 
+    # the chunk's grouped output projection: [8192, 64 x 512] -> [8192, 7168]
+    wo = (torch.randn(G, HIDDEN // G, H * D_HEAD // G, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    y = torch.empty(PF_T, HIDDEN, dtype=torch.bfloat16, device=dev)
+
+    def proj():
+        api.out_proj_grouped(out.view(PF_T, H * D_HEAD), wo, y=y)
+
     def best(f):
         f()
         torch.cuda.synchronize()
@@ -282,20 +291,26 @@ def prefill_measure(torch, api, reps=3, seed=5005):
             torch.cuda.synchronize()
             t.append(e0.elapsed_time(e1))
         return min(t)
-    ti, ta, th = best(idx), best(att), best(att_h)
+    ti, ta, th, tp = best(idx), best(att), best(att_h), best(proj)
     n_mean = (L + PF_T / 2) / M_CSA                       # blocks visible to the average query
     fi = 2.0 * PF_T * HI * DI * n_mean                    # indexer q.k products
     fa = 2.0 * PF_T * H * (PF_TOPK + W) * 2 * D_HEAD      # Q K^T and P V over 1,152 entries
     fh = 2.0 * PF_T * H * ((L + PF_T / 2) / M_HCA + W) * 2 * D_HEAD   # HCA: every block of the prefix + window
+    fp = 2.0 * PF_T * H * D_HEAD * (HIDDEN // G)         # grouped projection (block-diagonal)
     return {"workload": "CSA prefill chunk, 8,192 queries over a 1M prefix, 64 heads x 512, top-1024, FP4 indexer, "
-                        "FP8 records; and the HCA layer's dense attention over the same chunk (8,256 blocks + window)", "indexer_ms": round(ti, 3), "attn_ms": round(ta, 3),
-            "query_tokens_per_s": round(PF_T / ((ti + ta) * 1e-3), 1),
+                        "FP8 records, grouped projection to 7,168; and the HCA layer's dense attention over the same "
+                        "chunk (8,256 blocks + window)",
+            "indexer_ms": round(ti, 3), "attn_ms": round(ta, 3), "proj_ms": round(tp, 3),
+            "query_tokens_per_s": round(PF_T / ((ti + ta + tp) * 1e-3), 1),
+            "query_tokens_per_s_calls": "CSA indexer + sparse attention + projection",
             "indexer_TFLOPs": round(fi / (ti * 1e-3) / 1e12, 1), "indexer_mfma_frac": round(fi / (ti * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
             "indexer_peak": "fp4 10.1 PFLOP/s",
             "attn_TFLOPs": round(fa / (ta * 1e-3) / 1e12, 1), "attn_mfma_frac": round(fa / (ta * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "attn_peak": "bf16 2.5 PFLOP/s",
             "hca_attn_ms": round(th, 3), "hca_attn_TFLOPs": round(fh / (th * 1e-3) / 1e12, 1),
             "hca_attn_mfma_frac": round(fh / (th * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "proj_TFLOPs": round(fp / (tp * 1e-3) / 1e12, 1),
+            "proj_mfma_frac": round(fp / (tp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "timing": "HIP events around each call, best of 3 after a warm-up"}
 
 

@@ -13,8 +13,12 @@
 //     accumulate M x rows dot products per lane (bf16 pairs through
 //     v_dot2_f32_bf16), and reduce the partial sums across the wave by
 //     recursive halving;
+//   bf16, M > 16 (prefill chunks): a matrix-core GEMM per group, 256 x 128
+//     tiles of y, the reduction walked in 32-wide slabs through LDS;
 //   otherwise: a TM x TN tile of y per workgroup, walking the reduction
 //     dimension in KC-wide slabs staged in LDS.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -233,6 +237,156 @@ static bool launch_gemv(const ProjArgs& a, hipStream_t st) {
     return true;
 }
 
+// ---- bf16 GEMM on the matrix cores (M > 16)
+// y_g[m][n] = sum_c o[m][g cg + c] W[g][n][c]: both operands are read along
+// the reduction dimension, which is what the A (rows of o) and B (rows of W)
+// operands of v_mfma_f32_32x32x16_bf16 want.  Workgroup tile 256 (m) x 128 (n)
+// of one group, four waves each owning 64 rows x all 128 columns (2 x 4
+// accumulators of 32 x 32).  The reduction goes in 32-wide slabs copied
+// straight from global memory into LDS (global_load_lds_dwordx4, no register
+// staging), three slabs in flight: slab s + 2 is sent while slab s is
+// multiplied.  A slab row is 64 bytes (four 16-byte chunks), unpadded; chunk c
+// of row r sits in slot c ^ ((r >> 1) & 3), so the fragment reads of 8
+// consecutive rows hit 8 distinct bank groups.  72 KB of LDS: two workgroups
+// per CU.  Rows past M and columns past D/G load clamped (valid) addresses and
+// are never stored.  Tiles are dealt so that the dispatcher's round-robin over
+// the 8 XCDs gives each XCD a contiguous run of tiles (neighbouring n-tiles
+// share their rows of o in that XCD's L2).
+constexpr int kPmBM = 256, kPmBN = 128, kPmBK = 32;
+constexpr int kPmThreads = 256;
+constexpr int kPmStages = 3;
+constexpr int kPmAq = kPmBM * kPmBK / 8 / kPmThreads;   // 16-byte copies of o per thread and slab
+constexpr int kPmBq = kPmBN * kPmBK / 8 / kPmThreads;   // 16-byte copies of W per thread and slab
+constexpr int kPmSlabBytes = (kPmBM + kPmBN) * kPmBK * 2;
+typedef __bf16 bf16x8_p __attribute__((ext_vector_type(8)));
+typedef float f32x16_p __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int pm_slot(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
+
+template <typename YT>
+__global__ __launch_bounds__(kPmThreads, 2) void k_proj_mfma(ProjArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t sm[kPmStages][kPmSlabBytes];   // [A 256 rows | B 128 rows]
+    const int dg = a.D / a.G, cg = a.Hd / a.G;
+    const int tiles_n = (dg + kPmBN - 1) / kPmBN;
+    const int64_t tiles_m = (a.M + kPmBM - 1) / kPmBM;
+    // XCD-aware deal: workgroup id -> logical tile (n fastest, then m, then g)
+    const int64_t id = blockIdx.x, nwg = gridDim.x, per = nwg / 8;
+    const int64_t L = id < 8 * per ? (id % 8) * per + id / 8 : id;
+    const int tn = (int)(L % tiles_n);
+    const int64_t tm = (L / tiles_n) % tiles_m;
+    const int g = (int)(L / tiles_n / tiles_m);
+    const int64_t m0 = tm * kPmBM;
+    const int n0 = tn * kPmBN;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hl = lane >> 5;
+    const uint16_t* o = reinterpret_cast<const uint16_t*>(a.o) + (size_t)g * cg;
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W) + (size_t)g * dg * cg;
+    // copy q of this wave fills slots [64 (4 q + w), +64) of the A (or B) part;
+    // lane l's slot holds chunk (slot % 4) ^ ((row >> 1) & 3) of row slot / 4
+    const uint16_t* ap[kPmAq];
+    const uint16_t* bp[kPmBq];
+#pragma unroll
+    for (int q = 0; q < kPmAq; q++) {
+        const int sl = 64 * (4 * q + w) + lane, r = sl >> 2;
+        const int c = (sl & 3) ^ ((r >> 1) & 3);
+        ap[q] = o + (size_t)min(m0 + r, a.M - 1) * a.Hd + 8 * c;
+    }
+#pragma unroll
+    for (int q = 0; q < kPmBq; q++) {
+        const int sl = 64 * (4 * q + w) + lane, r = sl >> 2;
+        const int c = (sl & 3) ^ ((r >> 1) & 3);
+        bp[q] = W + (size_t)min(n0 + r, dg - 1) * cg + 8 * c;
+    }
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto issue = [&](int s, int buf) __attribute__((always_inline)) {
+        uint8_t* base = &sm[buf][0];
+#pragma unroll
+        for (int q = 0; q < kPmAq; q++)
+            __builtin_amdgcn_global_load_lds(ap[q] + s * kPmBK, (lds_void*)(base + 1024 * (4 * q + w)), 16, 0, 0);
+#pragma unroll
+        for (int q = 0; q < kPmBq; q++)
+            __builtin_amdgcn_global_load_lds(bp[q] + s * kPmBK,
+                                             (lds_void*)(base + kPmBM * 64 + 1024 * (4 * q + w)), 16, 0, 0);
+    };
+    f32x16_p acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        // every fragment of the slab is read before the first product
+        const uint8_t* base = &sm[buf][0];
+        constexpr int KK = kPmBK / 16;
+        bf16x8_p fa[KK][2], fb[KK][4];
+#pragma unroll
+        for (int kk = 0; kk < KK; kk++) {
+            const int c = 2 * kk + hl;
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+                fa[kk][i] = *reinterpret_cast<const bf16x8_p*>(base + 16 * pm_slot(64 * w + 32 * i + l32, c));
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                fb[kk][j] = *reinterpret_cast<const bf16x8_p*>(base + kPmBM * 64 + 16 * pm_slot(32 * j + l32, c));
+        }
+        // the products take the fragments through an empty asm, so all twelve
+        // reads go out before the first product
+        static_assert(KK == 2, "fragment pinning is written for two K-steps");
+        asm volatile("" : "+v"(fa[0][0]), "+v"(fa[0][1]), "+v"(fb[0][0]), "+v"(fb[0][1]), "+v"(fb[0][2]),
+                     "+v"(fb[0][3]), "+v"(fa[1][0]), "+v"(fa[1][1]), "+v"(fb[1][0]), "+v"(fb[1][1]),
+                     "+v"(fb[1][2]), "+v"(fb[1][3]));
+#pragma unroll
+        for (int kk = 0; kk < KK; kk++)
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+    };
+    // slab s lives in buffer s % 3.  Each thread waits for its own copies of
+    // slab s (leaving those of slab s + 1 in flight); the barrier then makes
+    // every thread's copies visible and frees the buffer of slab s - 1, which
+    // receives slab s + 2.
+    const int ns = cg / kPmBK;
+    issue(0, 0);
+    if (ns > 1) issue(1, 1);
+    int buf = 0, buf2 = 2;
+    for (int s = 0; s < ns; s++) {
+        if (s + 1 < ns) __builtin_amdgcn_s_waitcnt(0x0F70 | (kPmAq + kPmBq));   // vmcnt(copies per slab)
+        else __builtin_amdgcn_s_waitcnt(0x0F70);                               // vmcnt(0)
+        __syncthreads();
+        if (s + 2 < ns) issue(s + 2, buf2);
+        compute(buf);
+        buf = buf == kPmStages - 1 ? 0 : buf + 1;
+        buf2 = buf2 == kPmStages - 1 ? 0 : buf2 + 1;
+    }
+    // accumulator (i, j) element e: row 8 (e / 4) + 4 hl + e % 4, column l32
+    YT* y = reinterpret_cast<YT*>(a.y) + (size_t)g * dg;
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int n = n0 + 32 * j + l32;
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int64_t m = m0 + 64 * w + 32 * i + 8 * (e / 4) + 4 * hl + (e % 4);
+                if (m < a.M && n < dg) st_scalar<YT>(y, (size_t)m * a.D + n, acc[i][j][e]);
+            }
+        }
+}
+
+template <typename YT>
+static bool try_mfma(const ProjArgs& a, hipStream_t st) {
+    const int cg = a.Hd / a.G, dg = a.D / a.G;
+    if (a.fmt != CSA_BF16 || a.M <= 16 || cg % kPmBK) return false;
+    if (((uintptr_t)a.o | (uintptr_t)a.W) & 15) return false;
+    const int64_t tiles = (int64_t)a.G * ((a.M + kPmBM - 1) / kPmBM) * ((dg + kPmBN - 1) / kPmBN);
+    if (tiles > 0x7fffffff) return false;
+    hipLaunchKernelGGL((k_proj_mfma<YT>), dim3((unsigned)tiles), dim3(kPmThreads), 0, st, a);
+    return true;
+}
+
 template <typename T, typename YT>
 static bool try_gemv(const ProjArgs& a, hipStream_t st) {
     const int cg = a.Hd / a.G;
@@ -249,6 +403,9 @@ static bool try_gemv(const ProjArgs& a, hipStream_t st) {
 template <typename T, typename YT>
 static void launch_t(const ProjArgs& a, hipStream_t st) {
     if (try_gemv<T, YT>(a, st)) return;
+    if constexpr (sizeof(T) == 2) {
+        if (try_mfma<YT>(a, st)) return;
+    }
     const int dg = a.D / a.G;
     const unsigned gx = (unsigned)(a.G * ((dg + kProjTN - 1) / kProjTN));
     if (a.M <= 8) {

@@ -287,3 +287,23 @@ def test_c5_hca_prefill_chunk_sampled_rows():
                       comp[0], O.FP8_E4M3, win[0], O.FP8_E4M3, None)
     say(f"c5 hca sampled attention abs {abs_err(out[0, rows], ref):.3e}")
     assert abs_err(out[0, rows], ref) <= 2e-2
+
+
+def test_c5_projection_sampled_rows():
+    """The prefill chunk's grouped output projection at full size: 8,192 rows
+    of 64 x 512 bf16 attention outputs projected to 7,168 in 8 groups
+    (W [8, 896, 4096] bf16, fp32 output) on the matrix cores, in the
+    benchmark's configuration; the oracle checks sampled rows (tile edges and
+    the chunk's ends)."""
+    g = synth.rng(2007)
+    M, Hd, D, G = 8192, 64 * D_HEAD, 7168, 8
+    ob = synth.bf16_bits(g, (M, Hd))
+    Wb = synth.bf16_bits(g, (G, D // G, Hd // G))
+    say(f"c5 projection M={M} Hd={Hd} D={D} G={G}")
+    y = api.out_proj_grouped(dev_bf16(ob), dev_bf16(Wb), y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.array([0, 255, 256, 4097, 6000, M - 1])
+    got = y[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    ref = O.out_proj(O.bf16_decode(ob[rows]), O.bf16_decode(Wb))
+    say(f"c5 projection rel {rel_err(got, ref):.3e}")
+    assert rel_err(got, ref) <= 1e-5

@@ -523,7 +523,12 @@ def test_attention_deterministic_and_batch_invariant():
 @pytest.mark.parametrize("M,H,d,D,G,fmt", [(2048, 8, 128, 1024, 8, O.F32), (4, 64, 512, 7168, 8, O.BF16),
                                            (16, 32, 512, 4096, 8, O.BF16), (37, 6, 40, 96, 3, O.F32),
                                            (1, 16, 256, 1024, 4, O.F32), (8, 64, 512, 7168, 8, O.BF16),
-                                           (2, 8, 128, 384, 2, O.BF16), (3, 8, 64, 200, 8, O.BF16)])
+                                           (2, 8, 128, 384, 2, O.BF16), (3, 8, 64, 200, 8, O.BF16),
+                                           # bf16 with M > 16 runs on the matrix cores: a ragged 256-row
+                                           # tile, ragged 128-column tiles (D/G = 200), a single 32-wide
+                                           # slab, and the prefill chunk's grouping at a smaller M
+                                           (300, 16, 128, 1024, 8, O.BF16), (40, 8, 64, 1600, 8, O.BF16),
+                                           (17, 4, 32, 96, 4, O.BF16), (600, 64, 512, 7168, 8, O.BF16)])
 def test_projection_parity(M, H, d, D, G, fmt):
     g = synth.rng(700 + M)
     Hd = H * d
@@ -540,6 +545,23 @@ def test_projection_parity(M, H, d, D, G, fmt):
         ref = O.out_proj(o.astype(np.float64), W.astype(np.float64))
     torch.cuda.synchronize()
     assert rel_err(out_to_f64(y), ref) <= 1e-5
+
+
+def test_projection_mfma_bf16_out():
+    """The matrix-core projection with a bf16 output: each element is the fp32
+    sum rounded once to bf16 (within half a bf16 ulp of the exact value, plus
+    the fp32 accumulation error)."""
+    g = synth.rng(790)
+    M, Hd, D, G = 333, 2048, 1024, 8
+    ob = synth.bf16_bits(g, (M, Hd))
+    Wb = (synth.normal(g, (G, D // G, Hd // G)).astype(np.float32) * np.float32(0.05)).view(np.uint32)
+    Wb = (Wb >> 16).astype(np.uint16)
+    say(f"projection bf16 out M={M} Hd={Hd} D={D} G={G}")
+    y = api.out_proj_grouped(dev_bf16(ob), dev_bf16(Wb), y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = O.out_proj(O.bf16_decode(ob), O.bf16_decode(Wb))
+    got = out_to_f64(y)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-5 * np.max(np.abs(ref)))
 
 
 # ====================================================================== end to end (C1 shape)
