@@ -157,6 +157,11 @@ __device__ __forceinline__ void rope_sincos(double pos, double freq, float& s, f
     c = ((q + 1) & 2) ? -cc : cc;
 }
 
+// ReLU on the bit pattern: a float with the sign bit set is a negative int32,
+// so one integer max gives max(x, +0) for every non-NaN x, without the
+// canonicalising pass a float max of an unknown value takes.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // ---------------------------------------------------------------- score keys
 // order-preserving map float -> uint32 (larger float, larger key); NaN -> 0; -0 == +0
 __device__ __forceinline__ uint32_t score_key(float s) {

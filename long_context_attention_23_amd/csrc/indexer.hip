@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs
             for (int gq = 0; gq < 4; gq++) {
                 if (8 * gq >= Hi) break;                          // wave-uniform
 #pragma unroll
-                for (int h = 0; h < 4; h++) part = fmaf(wrow[4 * gq + h], fmaxf(acc[4 * gq + h], 0.0f), part);
+                for (int h = 0; h < 4; h++) part = fmaf(wrow[4 * gq + h], relu_bits(acc[4 * gq + h]), part);
             }
             const float sc = Hi > 4 ? part + __shfl_xor(part, 32, kWave) : part;
             if (half == 0 && key < c1) {
@@ -997,7 +997,7 @@ __device__ __forceinline__ f32x16_t pf_mfma(const i32x8_t& qa, int qs, const uin
 __device__ __forceinline__ float pf_score(const f32x16_t& acc, int s, const float* w4) {
     float v = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 4; h++) v = fmaf(w4[h], fmaxf(acc[4 * s + h], 0.0f), v);
+    for (int h = 0; h < 4; h++) v = fmaf(w4[h], relu_bits(acc[4 * s + h]), v);
     return v;
 }
 
