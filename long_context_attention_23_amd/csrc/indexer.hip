@@ -1061,6 +1061,9 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_thresh(IndexerArgs a, int32
     }
 }
 
+// compare predicates of the lane-mask compare builtin (LLVM's numbering)
+constexpr int kFcmpOeq = 1, kFcmpOgt = 2;
+
 __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
@@ -1100,8 +1103,15 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
         }
     }
     __syncthreads();
+    int32_t nmin = nq[0][0];
+#pragma unroll
+    for (int rb = 0; rb < kPfRB; rb++)
+#pragma unroll
+        for (int s = 0; s < 4; s++) nmin = min(nmin, nq[rb][s]);
     nmax = (int32_t)wave_max_dpp((float)nmax);
+    nmin = -(int32_t)wave_max_dpp(-(float)nmin);
     const int ntile = (nmax + 31) / 32;
+    const int nfull = nmin / 32;                          // tiles every query of the workgroup sees whole
     // this wave's running counts per query (above the threshold, at it):
     // slot (rb, s, half) -> query 8 rb + 2 s + half
     uint32_t cnt[kPfRB][4][2], tcnt[kPfRB][4][2];
@@ -1124,6 +1134,9 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
         const int kscur = ks;
         if (tile + kPfWaves < ntile) pf_load_keys(a, b, (int64_t)(tile + kPfWaves) * 32, l32, half, kc, ks);
         const int32_t j = tile * 32 + l32;
+        // tiles below every query's visible count skip the visibility test
+        auto body = [&](auto visc) __attribute__((always_inline)) {
+        constexpr bool kVis = decltype(visc)::value;
 #pragma unroll
         for (int rb = 0; rb < kPfRB; rb++) {
             // one row block's products at a time (fewer live registers: with
@@ -1134,10 +1147,17 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                 const float4 w4 = wl[rb][s][half];
                 const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
                 const float sc = pf_score(acc, s, wv4);
-                const bool vis = j < nq[rb][s];
-                const bool above = vis && sc > thr[rb][s], tie = vis && sc == thr[rb][s];
-                const uint64_t bal = ballot64(above), bt = ballot64(tie);
+                // lane masks straight from the compares (ordered: a NaN score
+                // is neither above nor at the threshold)
+                uint64_t bal = __builtin_amdgcn_fcmpf(sc, thr[rb][s], kFcmpOgt);
+                uint64_t bt = __builtin_amdgcn_fcmpf(sc, thr[rb][s], kFcmpOeq);
+                if constexpr (kVis) {
+                    const uint64_t vm = ballot64(j < nq[rb][s]);
+                    bal &= vm;
+                    bt &= vm;
+                }
                 if (bal | bt) {
+                    const bool above = (bal >> lane) & 1u, tie = (bt >> lane) & 1u;
                     // rank among this half's hits: mbcnt over the whole wave,
                     // less the lower half's count for the upper half
                     const uint32_t alo = (uint32_t)bal, ahi = (uint32_t)(bal >> 32);
@@ -1162,6 +1182,9 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                 }
             }
         }
+        };
+        if (tile < nfull) body(std::false_type{});
+        else body(std::true_type{});
     }
     if (lane == 0) {
 #pragma unroll
