@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+")
+    ap.add_argument("--summarize-prefill", metavar="DIR")
     return ap.parse_args()
 
 
@@ -372,11 +373,11 @@ def cpu_baseline(target_s):
 # profiles/ gives the counts and commands); valid only while the kernels'
 # sources are unchanged (src_hash below).
 TRAFFIC = {
-    "csa_indexer_topk": {"bytes": 45_597_345, "src": "861587c9831846ae"},
-    "csa_sparse_mqa_attn": {"bytes": 25_883_068, "src": "861587c9831846ae"},
-    "hca_dense_mqa_attn": {"bytes": 54_346_446, "src": "861587c9831846ae"},
-    "csa_out_proj": {"bytes": 59_134_577, "src": "861587c9831846ae"},
-    "hca_out_proj": {"bytes": 59_134_577, "src": "861587c9831846ae"},
+    "csa_indexer_topk": {"bytes": 45_592_894, "src": "09aa1c9e818f283f"},
+    "csa_sparse_mqa_attn": {"bytes": 25_883_101, "src": "09aa1c9e818f283f"},
+    "hca_dense_mqa_attn": {"bytes": 54_347_744, "src": "09aa1c9e818f283f"},
+    "csa_out_proj": {"bytes": 59_134_697, "src": "09aa1c9e818f283f"},
+    "hca_out_proj": {"bytes": 59_134_697, "src": "09aa1c9e818f283f"},
 }
 TRAFFIC_SRC = ["long_context_attention_23_amd/csrc/indexer.hip", "long_context_attention_23_amd/csrc/attn_mfma.hip",
                "long_context_attention_23_amd/csrc/attn.hip", "long_context_attention_23_amd/csrc/proj.hip",
@@ -459,6 +460,38 @@ def summarize(d, last=20):
     print("\n".join(out))
 
 
+def summarize_prefill(d):
+    """Per-call kernel durations of the prefill section in a kernel-trace run
+    of this benchmark.  The section runs each call once to warm up, then
+    `reps` times, in the order indexer, CSA attention, HCA attention,
+    projection; the indexer's kernels are k_idxp_*, each attention call is one
+    k_attn_mfma launch (one split per row), the projection k_proj_mfma."""
+    db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
+    rows = [(_short(n), (b - a) / 1e3) for n, a, b in _kernel_rows(db) if "csa::" in n]
+    i0 = next(i for i, (n, _) in enumerate(rows) if "k_idxp_" in n)
+    pre = rows[i0:]
+    att = [t for n, t in pre if "k_attn_mfma" in n]
+    nrep = len(att) // 2
+    calls = {"csa_indexer_topk (k_idxp_*)": None, "csa_sparse_mqa_attn": att[:nrep],
+             "hca_dense_mqa_attn": att[nrep:2 * nrep], "attn_out_proj_grouped": [t for n, t in pre if "k_proj_mfma" in n]}
+    per = {}
+    for n, t in pre:
+        if "k_idxp_" in n:
+            per.setdefault(n.replace("csa::", ""), []).append(t)
+    out = ["Prefill section, per kernel of the indexer call (every launch: warm-up and timed):", "",
+           "| kernel | launches | avg us | min us |", "|---|---|---|---|"]
+    for k, v in per.items():
+        out.append(f"| {k} | {len(v)} | {np.mean(v):.1f} | {min(v):.1f} |")
+    out += ["", "Per call (kernel-only):", "", "| call | launches | avg us | min us |", "|---|---|---|---|"]
+    nidx = len(per.get("k_idxp_filter", []))
+    idx_sum = [sum(v[i] for v in per.values() if len(v) == nidx) for i in range(nidx)]
+    calls["csa_indexer_topk (k_idxp_*)"] = idx_sum
+    for c, v in calls.items():
+        if v:
+            out.append(f"| {c} | {len(v)} | {np.mean(v):.1f} | {min(v):.1f} |")
+    print("\n".join(out))
+
+
 def summarize_pmc(dirs):
     """Per-call counter sums (mean over the timed steps) from --pmc runs of
     this benchmark; calls are told apart by their kernels and step order."""
@@ -511,6 +544,8 @@ def main():
         return summarize(args.summarize)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
+    if args.summarize_prefill:
+        return summarize_prefill(args.summarize_prefill)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this path runs on a single "
               "MI355X; multi-GPU sharding is not built)", file=sys.stderr)
