@@ -1252,28 +1252,31 @@ __device__ __forceinline__ void pf_pick(const uint32_t* hist, uint32_t need, uin
     above = lane_u32(ab, L);
 }
 
-// emit the members marked in bitmap bm (nw words) in ascending j, thread t
-// owning words [t * WPT, (t + 1) * WPT); output padded with -1 to topk
-template <int WPT>
-__device__ __forceinline__ void pf_emit(const uint32_t* bm, int32_t* out, int topk, uint32_t* wsum) {
-    uint32_t am[WPT], cnt = 0;
-#pragma unroll
-    for (int v = 0; v < WPT / 4; v++) {
-        const uint4 x = reinterpret_cast<const uint4*>(bm)[threadIdx.x * (WPT / 4) + v];
-        am[4 * v] = x.x; am[4 * v + 1] = x.y; am[4 * v + 2] = x.z; am[4 * v + 3] = x.w;
+// emit the members marked in the first nw4 16-byte groups of bitmap bm (the
+// words that can hold a visible block) in ascending j: thread t owns groups
+// [t g, (t + 1) g), g = ceil(nw4 / threads), counted in one pass and emitted
+// in a second; output padded with -1 to topk by the caller's initial fill
+__device__ __forceinline__ void pf_emit(const uint4* bm4, int nw4, int32_t* out, int topk, uint32_t* wsum) {
+    const int g = (nw4 + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int v0 = (int)threadIdx.x * g, v1 = min(v0 + g, nw4);
+    uint32_t cnt = 0;
+    for (int v = v0; v < v1; v++) {
+        const uint4 x = bm4[v];
+        cnt += __popc(x.x) + __popc(x.y) + __popc(x.z) + __popc(x.w);
     }
-#pragma unroll
-    for (int q = 0; q < WPT; q++) cnt += __popc(am[q]);
     uint32_t off = block_exclusive_scan(cnt, wsum);
-    const int j0 = threadIdx.x * WPT * 32;
+    for (int v = v0; v < v1; v++) {
+        const uint4 x = bm4[v];
+        const uint32_t wd[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-    for (int q = 0; q < WPT; q++) {
-        uint32_t bits = am[q];
-        while (bits) {
-            const int bpos = __builtin_ctz(bits);
-            bits &= bits - 1;
-            if (off < (uint32_t)topk) out[off] = j0 + 32 * q + bpos;
-            off++;
+        for (int e = 0; e < 4; e++) {
+            uint32_t bits = wd[e];
+            while (bits) {
+                const int bpos = __builtin_ctz(bits);
+                bits &= bits - 1;
+                if (off < (uint32_t)topk) out[off] = 128 * v + 32 * e + bpos;
+                off++;
+            }
         }
     }
 }
@@ -1323,7 +1326,6 @@ __device__ __forceinline__ uint32_t pf_slot(uint32_t i, const uint32_t (&c)[NW],
 __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
     constexpr int kCPT = kIdxPfCands / kPfSelThreads;          // candidates per thread
-    constexpr int kWPT = kPfWords / kPfSelThreads;
     __shared__ uint4 bm4[kPfWords / 4];
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t sh[4];
@@ -1333,6 +1335,7 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
     const int b = blockIdx.y, t = blockIdx.x;
     const int64_t row = (int64_t)b * a.Tq + t;
     const int64_t n = visible_blocks(a, row);
+    const int nw4 = (int)min<int64_t>((n + 127) / 128, kPfWords / 4);   // bitmap groups holding visible blocks
     int32_t* out = a.out + row * a.topk;
     if (n <= a.topk) {
         for (int64_t i = tid; i < a.topk; i += blockDim.x) out[i] = i < n ? (int32_t)i : -1;
@@ -1364,7 +1367,7 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
         cv[q] = make_uint2(0u, 0u);
         if (i < tot) cv[q] = cand[pf_slot(i, segc, kPfSeg)];
     }
-    for (int i = tid; i < kPfWords / 4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < nw4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tot >= k) {
         // the top k lie among the keys above the threshold: three digit passes
         // over the 32-bit score key (11, 11, 10 bits), then the smallest j of
@@ -1435,7 +1438,7 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
         }
     }
     __syncthreads();
-    pf_emit<kWPT>(bm, out, a.topk, wsum);
+    pf_emit(bm4, nw4, out, a.topk, wsum);
 }
 
 // exact selection of a flagged query row from its recomputed scores: digit
@@ -1443,7 +1446,6 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
 // then the members marked and emitted
 __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
-    constexpr int kWPT = kPfWords / kPfThreads;
     __shared__ uint4 bm4[kPfWords / 4];
     __shared__ uint32_t hist[2048];
     __shared__ uint32_t sh[4];
@@ -1455,6 +1457,7 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
     uint32_t* hd = pf_hdr(a, row);
     if (hd[1] == 0u) return;
     const int64_t n = visible_blocks(a, row);
+    const int nw4 = (int)min<int64_t>((n + 127) / 128, kPfWords / 4);   // bitmap groups holding visible blocks
     int32_t* out = a.out + row * a.topk;
     // A operand: rows 0..3 = the four heads of this query, the rest zero
     i32x8_t qa = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
@@ -1528,13 +1531,13 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
         __syncthreads();
     }
     const uint32_t jcut = jm - jp;
-    for (int i = tid; i < kPfWords / 4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < nw4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
     sweep([&](uint32_t key, uint32_t j, bool ok) {
         if (ok && (key > T1 || (key == T1 && j <= jcut))) atomicOr(&bm[j >> 5], 1u << (j & 31));
     });
     __syncthreads();
-    pf_emit<kWPT>(bm, out, a.topk, wsum);
+    pf_emit(bm4, nw4, out, a.topk, wsum);
 }
 
 // ------------------------------------------------------------------ launcher
