@@ -938,7 +938,7 @@ constexpr int kPfRB = 2;                 // row blocks per filter workgroup
 constexpr int kPfQB = kPfQ * kPfRB;      // queries per filter workgroup
 constexpr int kPfThreads = 512;          // threshold, filter and exact workgroups
 constexpr int kPfWaves = kPfThreads / kWave;
-constexpr int kPfSelThreads = 256;       // select workgroups
+constexpr int kPfSelThreads = 512;       // select workgroups (16 candidates per thread: fewer unrolled masks than 32)
 constexpr int kPfMaxSampTiles = 128;     // sample tiles per query (LDS: 8 x 4096 keys)
 constexpr int kPfWords = 16384;          // bitmap words: caps up to 2^19 blocks
 constexpr int kPfHdr = 128;              // per-row header: thr, flag, 8 above counts, 8 tie counts
