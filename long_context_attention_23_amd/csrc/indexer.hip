@@ -1137,11 +1137,14 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
         // tiles below every query's visible count skip the visibility test
         auto body = [&](auto visc) __attribute__((always_inline)) {
         constexpr bool kVis = decltype(visc)::value;
+        // both row blocks' products first, so the second runs on the matrix
+        // core while the first one's scores are formed
+        f32x16_t accs[kPfRB];
+#pragma unroll
+        for (int rb = 0; rb < kPfRB; rb++) accs[rb] = pf_mfma(qa[rb], qs[rb], kcur, kscur);
 #pragma unroll
         for (int rb = 0; rb < kPfRB; rb++) {
-            // one row block's products at a time (fewer live registers: with
-            // four waves per SIMD the others cover the matrix-core latency)
-            const f32x16_t acc = pf_mfma(qa[rb], qs[rb], kcur, kscur);
+            const f32x16_t& acc = accs[rb];
 #pragma unroll
             for (int s = 0; s < 4; s++) {
                 const float4 w4 = wl[rb][s][half];
