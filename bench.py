@@ -315,6 +315,29 @@ def prefill_measure(torch, api, reps=3, seed=5005):
             "timing": "HIP events around each call, best of 3 after a warm-up"}
 
 
+def capture_step_graphs(torch, fns, sets, sh):
+    """One HIP graph per rotated buffer set, each holding one whole decode step
+    (every call's kernels, in order).  The calls allocate nothing and issue no
+    memsets, so the graphs hold only kernel nodes."""
+    side = torch.cuda.Stream()                        # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                     # warm-up on a side stream before capture
+        for s_ in sets:
+            for f in fns:
+                f(s_, sh)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for s_ in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f(s_, sh)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
 def cpu_baseline(target_s):
     """The oracle, as it stands, on one decode step of the same layer pair for
     the whole batch (synthetic records drawn at the same shapes), repeated up
@@ -577,7 +600,7 @@ def main():
     dom = max(CALLS, key=lambda c: per_call[c])
     di = CALLS.index(dom)
 
-    # timed region: K whole steps launched eagerly on the current stream (the
+    # eager pass: K whole steps launched eagerly on the current stream (the
     # host stays ahead of the GPU, so the kernels run back to back), with a
     # pair of events around the dominant call in every step.
     for i in range(args.warmup):
@@ -595,9 +618,20 @@ def main():
             if j == di:
                 ev[i][1].record()
     torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    ms_step = el * 1e3 / args.steps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     dom_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+
+    # timed region: the same K steps as HIP graph replays (graph i % R holds
+    # one whole step on rotated set i % R), W untimed replays first
+    graphs = capture_step_graphs(torch, fns, sets, sh)
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     algo = algorithmic_bytes()
     calls = {c: {"us": round(per_call[c] * 1e3, 2), "algo_MB": round(algo[c] / 1e6, 3),
                  "GBs": round(algo[c] / (per_call[c] * 1e-3) / 1e9, 1), "kernels": sorted(set(CALL_KERNELS[c]))}
@@ -622,10 +656,13 @@ def main():
                      "GBs_gpu": round(total_algo / (gpu_ms * 1e-3) / 1e9, 1),
                      "frac_gpu": round(total_algo / (gpu_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "calls": calls,
-        "timing": "eager launches on one stream, host ahead of the GPU; value from the wall clock over the "
-                  "timed steps; roofline from events around the dominant call in every timed step; per-call GPU "
-                  "times from events around every call (median over a calibration pass)",
+        "timing": "value and ms_per_step: wall clock over K timed steps, each one HIP graph replay holding the "
+                  "step's calls (one graph per rotated buffer set), synchronised before and after; roofline from "
+                  "events around the dominant call in every step of an eager pass over the same steps; per-call "
+                  "GPU times from events around every call (median over an eager calibration pass)",
     }
+    res["eager"] = {"ms_per_step": round(ms_eager, 4), "query_tokens_per_s": round(B / (ms_eager * 1e-3), 1),
+                    "how": "the same steps launched call by call on one stream (dispatch gaps between kernels)"}
     if not args.no_prefill:
         res["prefill"] = prefill_measure(torch, api)
     if not args.no_cpu_baseline:
