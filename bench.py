@@ -396,11 +396,11 @@ def cpu_baseline(target_s):
 # profiles/ gives the counts and commands); valid only while the kernels'
 # sources are unchanged (src_hash below).
 TRAFFIC = {
-    "csa_indexer_topk": {"bytes": 45_599_148, "src": "06e3042d06466cb1"},
-    "csa_sparse_mqa_attn": {"bytes": 25_898_215, "src": "06e3042d06466cb1"},
-    "hca_dense_mqa_attn": {"bytes": 54_348_341, "src": "06e3042d06466cb1"},
-    "csa_out_proj": {"bytes": 59_135_074, "src": "06e3042d06466cb1"},
-    "hca_out_proj": {"bytes": 59_135_074, "src": "06e3042d06466cb1"},
+    "csa_indexer_topk": {"bytes": 45_599_148, "src": "de59d03fe3448def"},
+    "csa_sparse_mqa_attn": {"bytes": 25_898_215, "src": "de59d03fe3448def"},
+    "hca_dense_mqa_attn": {"bytes": 54_348_341, "src": "de59d03fe3448def"},
+    "csa_out_proj": {"bytes": 59_135_074, "src": "de59d03fe3448def"},
+    "hca_out_proj": {"bytes": 59_135_074, "src": "de59d03fe3448def"},
 }
 TRAFFIC_SRC = ["long_context_attention_23_amd/csrc/indexer.hip", "long_context_attention_23_amd/csrc/attn_mfma.hip",
                "long_context_attention_23_amd/csrc/attn.hip", "long_context_attention_23_amd/csrc/proj.hip",

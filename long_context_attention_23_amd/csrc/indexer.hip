@@ -1258,7 +1258,8 @@ __device__ __forceinline__ void pf_pick(const uint32_t* hist, uint32_t need, uin
 // emit the members marked in the first nw4 16-byte groups of bitmap bm (the
 // words that can hold a visible block) in ascending j: thread t owns groups
 // [t g, (t + 1) g), g = ceil(nw4 / threads), counted in one pass and emitted
-// in a second; output padded with -1 to topk by the caller's initial fill
+// in a second (the callers mark exactly topk members, so every output slot
+// is written)
 __device__ __forceinline__ void pf_emit(const uint4* bm4, int nw4, int32_t* out, int topk, uint32_t* wsum) {
     const int g = (nw4 + (int)blockDim.x - 1) / (int)blockDim.x;
     const int v0 = (int)threadIdx.x * g, v1 = min(v0 + g, nw4);
