@@ -262,8 +262,11 @@ csa_status hca_dense_mqa_attn(const void* q, int32_t q_dtype, const int32_t* q_p
  *   y[r][g*(D/G) + i] = sum_c o[r][g*(Hd/G) + c] * W[g][i][c]
  * o: [M][Hd] (o_dtype F32 / BF16), W: [G][D/G][Hd/G] (w_dtype, same as
  * o_dtype), y: [M][D] (y_dtype F32 / BF16).  fp32 accumulation, no split
- * of the reduction across workgroups.
- * Errors: INVALID_ARG (Hd % G, D % G, Hd/G % 8), UNSUPPORTED, HIP.
+ * of the reduction across workgroups; any Hd/G (widths that are not a whole
+ * number of 16-byte vectors, or 32-wide slabs for bf16 with M > 16, take a
+ * scalar kernel).
+ * Errors: INVALID_ARG (sizes < 1, M < 0, Hd % G, D % G, null pointers with
+ * M > 0), UNSUPPORTED (dtypes, M beyond the grid limit), HIP.
  * ------------------------------------------------------------------------- */
 csa_status attn_out_proj_grouped(const void* o, int32_t o_dtype, const void* W, int32_t w_dtype,
                                  int64_t M, int32_t Hd, int32_t D, int32_t G, void* y,
