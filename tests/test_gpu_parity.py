@@ -528,7 +528,9 @@ def test_attention_deterministic_and_batch_invariant():
                                            # tile, ragged 128-column tiles (D/G = 200), a single 32-wide
                                            # slab, and the prefill chunk's grouping at a smaller M
                                            (300, 16, 128, 1024, 8, O.BF16), (40, 8, 64, 1600, 8, O.BF16),
-                                           (17, 4, 32, 96, 4, O.BF16), (600, 64, 512, 7168, 8, O.BF16)])
+                                           (17, 4, 32, 96, 4, O.BF16), (600, 64, 512, 7168, 8, O.BF16),
+                                           # group widths that are not a whole 16-byte vector (scalar kernel)
+                                           (5, 3, 20, 60, 3, O.BF16), (45, 3, 20, 60, 3, O.BF16)])
 def test_projection_parity(M, H, d, D, G, fmt):
     g = synth.rng(700 + M)
     Hd = H * d
