@@ -140,8 +140,10 @@ size_t csa_kv_record_bytes(int32_t fmt, int32_t d, int32_t d_rope);
  * e = floor(log2 amax) - 2 raised to at least (row max e) - 14, codes E2M1
  * saturating at +-6.
  * score_bias: device f32 [m]; score_proj, gamma: device f32 [d] or NULL.
- * Errors: INVALID_ARG (nulls, d not even or > 1024, m < 1, T < 0, both or
- * neither output), UNSUPPORTED (dtypes; FP4 needs di % 32 == 0), HIP.
+ * Errors: INVALID_ARG (nulls, B or T < 0, d odd or outside [2, 1024], m
+ * outside [1, 1024], rope_dim odd or > d, both or neither output, an output
+ * whose d / d_rope differ from the call's, cap < 1), UNSUPPORTED (dtypes,
+ * rope_dim > 128, B beyond the grid limit; FP4 needs di % 32 == 0), HIP.
  * ------------------------------------------------------------------------- */
 csa_status csa_compress_kv(const void* x, int32_t x_dtype, int32_t B, int64_t T, int32_t d,
                            const int32_t* tok_start, int32_t m, const float* score_bias,
