@@ -39,3 +39,44 @@ def test_traffic_sources_exist_and_hash():
         assert os.path.isfile(os.path.join(ROOT, f)), f
     h = bench.src_hash()
     assert len(h) == 16 and all(c in "0123456789abcdef" for c in h)
+
+
+def test_prefill_trace_summary(tmp_path, capsys):
+    """The prefill-section summary groups a kernel trace by call: the
+    indexer's k_idxp_* launches summed per call, the two attention calls told
+    apart by order (CSA launches first, then HCA), the projection's launches."""
+    import sqlite3
+    db = tmp_path / "run" / "trace_results.db"
+    db.parent.mkdir()
+    c = sqlite3.connect(db)
+    c.execute("create table kernels (name text, start integer, end integer)")
+    t = [0]
+
+    def k(name, us):
+        c.execute("insert into kernels values (?, ?, ?)", (name, t[0], t[0] + int(us * 1000)))
+        t[0] += int(us * 1000) + 500
+
+    for _ in range(3):                                 # decode steps before the section are ignored
+        k("csa::k_idx_zero(csa::IndexerArgs)", 2.5)
+        k("void csa::k_attn_mfma<512, 64, true, unsigned short>(csa::AttnArgs)", 20.0)
+    k("void at::native::fill(float)", 5.0)             # framework kernels are ignored
+    for i in range(4):
+        k("csa::k_idxp_thresh(csa::IndexerArgs, int, int)", 100.0 + i)
+        k("csa::k_idxp_filter(csa::IndexerArgs)", 2000.0 + i)
+        k("csa::k_idxp_select(csa::IndexerArgs)", 400.0 + i)
+        k("csa::k_idxp_exact(csa::IndexerArgs)", 7.0)
+    for us in (3000.0, 3010.0, 3020.0, 3030.0, 17600.0, 17610.0, 17620.0, 17630.0):
+        k("void csa::k_attn_mfma<512, 64, true, unsigned short>(csa::AttnArgs)", us)
+    for _ in range(4):
+        k("void csa::k_proj_mfma<unsigned short>(csa::ProjArgs)", 550.0)
+    c.commit()
+    c.close()
+    bench.summarize_prefill(str(tmp_path))
+    out = capsys.readouterr().out
+    rows = {ln.split("|")[1].strip(): [x.strip() for x in ln.split("|")[2:5]] for ln in out.splitlines()
+            if ln.startswith("| ") and not ln.startswith("| kernel") and not ln.startswith("| call")}
+    assert rows["k_idxp_filter"] == ["4", "2001.5", "2000.0"]
+    assert rows["csa_indexer_topk (k_idxp_*)"] == ["4", "2511.5", "2507.0"]   # 2507 + 3 i per launch
+    assert rows["csa_sparse_mqa_attn"] == ["4", "3015.0", "3000.0"]
+    assert rows["hca_dense_mqa_attn"] == ["4", "17615.0", "17600.0"]
+    assert rows["attn_out_proj_grouped"] == ["4", "550.0", "550.0"]
