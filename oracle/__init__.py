@@ -81,10 +81,10 @@ def _declare(L):
     L.orc_indexer_scores.restype = None
     L.orc_indexer_scores.argtypes = [_P, _P, C.c_int, C.c_int, _P, C.c_long, _P]
     L.orc_topk.restype = C.c_int
-    L.orc_topk.argtypes = [_P, C.c_long, C.c_int, C.c_int, _P]
+    L.orc_topk.argtypes = [_P, C.c_long, C.c_int, _P]
     L.orc_indexer_topk.restype = None
     L.orc_indexer_topk.argtypes = [_P, _P, C.c_int, _P, _P, C.c_int, C.c_int, C.c_int, _P, _P,
-                                   C.c_int, C.c_long, C.c_int, C.c_int, C.c_int, _P, _P]
+                                   C.c_int, C.c_long, C.c_int, C.c_int, _P, _P]
     L.orc_attention.restype = C.c_long
     L.orc_attention.argtypes = [_P, C.c_int, _P, C.c_int, C.c_int, _P, _P, C.POINTER(AttnParams),
                                 _P, C.c_int, C.c_long, _P, C.c_int, C.c_long, _P, C.c_int, _P, _P, _P]
@@ -252,15 +252,15 @@ def indexer_scores(qI, w, keys):
     return S
 
 
-def topk(S, k, rank_in_f32=True):
+def topk(S, k):
     S = _c(S, np.float64)
     out = np.empty(k, np.int32)
-    lib().orc_topk(_p(S), S.size, k, 1 if rank_in_f32 else 0, _p(out))
+    lib().orc_topk(_p(S), S.size, k, _p(out))
     return out
 
 
 def indexer_topk(qI, qI_scales, q_fmt, w, q_pos, keys, key_scales, key_fmt, m, k,
-                 rank_in_f32=True, want_scores=False):
+                 want_scores=False):
     """One sequence.  qI [Tq][Hi][row] codes, w [Tq][Hi] f32, q_pos [Tq] int32,
     keys [cap][row] codes (+ scales).  Returns out [Tq][k] int32 (and scores)."""
     qI = _c(qI, np.uint8)
@@ -275,7 +275,7 @@ def indexer_topk(qI, qI_scales, q_fmt, w, q_pos, keys, key_scales, key_fmt, m, k
     out = np.empty((Tq, k), np.int32)
     sc = np.full((Tq, cap), np.nan) if want_scores else None
     lib().orc_indexer_topk(_p(qI), _p(qs), q_fmt, _p(w), _p(q_pos), Tq, Hi, di, _p(keys), _p(ks),
-                           key_fmt, cap, m, k, 1 if rank_in_f32 else 0, _p(out), _p(sc))
+                           key_fmt, cap, m, k, _p(out), _p(sc))
     return (out, sc) if want_scores else out
 
 

@@ -391,8 +391,8 @@ ORC_API void orc_indexer_scores(const double* qI, const double* w, int Hi, int d
 /* Top-k selection (peacm CSA step 2).  Reading: candidates ordered by score
  * descending, ties to the smaller block index; the first min(k, n) are kept
  * and returned in ascending block order, the rest of out[0..k) is -1.
- * If rank_in_f32, scores are rounded to fp32 before ranking (the decision is
- * then taken in the GPU kernel's precision).  NaN ranks below everything. */
+ * Candidates are ranked on the fp64 scores themselves.  NaN ranks below
+ * everything. */
 typedef struct { double s; long j; } orc_cand;
 
 static int cand_order(const void* a, const void* b) {
@@ -408,12 +408,11 @@ static int index_order(const void* a, const void* b) {
     return (x > y) - (x < y);
 }
 
-ORC_API int orc_topk(const double* S, long n, int k, int rank_in_f32, int32_t* out) {
+ORC_API int orc_topk(const double* S, long n, int k, int32_t* out) {
     orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)(n > 0 ? n : 1));
     for (long j = 0; j < n; j++) {
         double s = S[j];
         if (isnan(s)) s = -INFINITY;
-        else if (rank_in_f32) s = (double)(float)s;
         c[j].s = s;
         c[j].j = j;
     }
@@ -433,7 +432,7 @@ ORC_API int orc_topk(const double* S, long n, int k, int rank_in_f32, int32_t* o
 ORC_API void orc_indexer_topk(const uint8_t* qI, const uint8_t* qI_scales, int q_fmt, const float* w,
                               const int32_t* q_pos, int Tq, int Hi, int di,
                               const uint8_t* keys, const uint8_t* key_scales, int key_fmt, long key_cap,
-                              int m, int k, int rank_in_f32, int32_t* out, double* scores_out) {
+                              int m, int k, int32_t* out, double* scores_out) {
     int qrb = idx_row_code_bytes(q_fmt, di), krb = idx_row_code_bytes(key_fmt, di);
     double* kd = (double*)malloc(sizeof(double) * (size_t)key_cap * di);
 #pragma omp parallel for schedule(static)
@@ -453,7 +452,7 @@ ORC_API void orc_indexer_topk(const uint8_t* qI, const uint8_t* qI_scales, int q
         if (nt > key_cap) nt = key_cap;
         orc_indexer_scores(qd, wd, Hi, di, kd, nt, S);
         if (scores_out) memcpy(scores_out + (size_t)i * key_cap, S, sizeof(double) * (size_t)nt);
-        orc_topk(S, nt, k, rank_in_f32, out + (size_t)i * k);
+        orc_topk(S, nt, k, out + (size_t)i * k);
     }
     free(kd); free(qd); free(wd); free(S);
 }

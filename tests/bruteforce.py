@@ -65,12 +65,11 @@ def layer(x, xI, q, qI, w, sink, *, m, k, W, dr, base, eps, b, bI, gamma_kv, gam
         keys = f32(softmax_pool(xI, m, np.asarray(bI, np.float64)))      # [N, di]
         dots = np.einsum("thi,ni->thn", qI.astype(np.float64), keys)
         S = np.einsum("th,thn->tn", w.astype(np.float64), np.maximum(dots, 0.0))
-        S32 = S.astype(np.float32).astype(np.float64)
         sel = np.zeros_like(visible)
         top = np.full((T, k), -1, np.int32)
         for ti in range(T):
             cand = np.nonzero(visible[ti])[0]
-            order = np.lexsort((cand, -S32[ti, cand]))                  # score desc, index asc
+            order = np.lexsort((cand, -S[ti, cand]))                  # score desc, index asc
             chosen = np.sort(cand[order[:k]])
             sel[ti, chosen] = True
             top[ti, :len(chosen)] = chosen

@@ -233,6 +233,31 @@ def test_topk_definition_on_ties(orc):
     assert list(orc.topk(S[:0], 2)) == [-1, -1]
 
 
+def test_topk_ranks_the_scores_themselves(orc):
+    """Selection orders the scores S as they are: scores that differ below
+    fp32 resolution are still distinct, not ties broken by index."""
+    S = np.array([1.0, 1.0 + 2.0 ** -40, 1.0 + 2.0 ** -41, 0.5])
+    assert np.float32(S[0]) == np.float32(S[1]) == np.float32(S[2])
+    assert list(orc.topk(S, 1)) == [1]
+    assert list(orc.topk(S, 2)) == [1, 2]
+
+
+def test_indexer_general_topk_fp64(orc):
+    """General (normal) f32 inputs: the set equals the first k of a full sort
+    of the fp64 scores computed by numpy, (score desc, index asc)."""
+    g = synth.rng(74)
+    n, Hi, di, k = 4000, 4, 64, 100
+    keys = synth.normal(g, (n, di))
+    qI = synth.normal(g, (1, Hi, di))
+    w = synth.normal(g, (1, Hi))
+    out = orc.indexer_topk(f32_bytes(qI).reshape(1, Hi, 4 * di), None, orc.F32, w,
+                           np.array([4 * n - 1], np.int32), f32_bytes(keys).reshape(n, 4 * di),
+                           None, orc.F32, 4, k)
+    ref_S = np.maximum(keys.astype(np.float64) @ qI[0].astype(np.float64).T, 0) @ w[0].astype(np.float64)
+    order = np.lexsort((np.arange(n), -ref_S))
+    assert np.array_equal(out[0], np.sort(order[:k]))
+
+
 def test_indexer_grid_topk_exact(orc):
     """q, w and keys on the 1/8 grid in [-2, 2]: every score is exact, and the
     top-k set equals a full torch sort by (score desc, index asc)."""
