@@ -37,6 +37,12 @@
  *   - Kernels never read or write outside the buffers described below:
  *     block indices beyond a linear cache's capacity are not stored and not
  *     visible; top-k entries that are negative or not visible are skipped.
+ *     Positions are device data, so the host cannot compare them with a
+ *     linear cache's capacity: a compressed or indexer-key cache smaller
+ *     than the positions need is clipped silently (the blocks at or beyond
+ *     cap do not exist for the call), never reported as CSA_ERR_CAPACITY.
+ *     CSA_ERR_CAPACITY is returned only for the window ring, whose needed
+ *     size (window + Tq - 1) the host does know.
  *   - Results are bitwise deterministic and do not depend on the batch size B
  *     (no floating-point atomics; fixed split sizes; fixed-order merges).
  *   - Calls on one stream run in order; calls on different streams that
@@ -54,11 +60,11 @@ extern "C" {
 
 typedef enum {
     CSA_OK = 0,
-    CSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size or inconsistent shape */
-    CSA_ERR_UNSUPPORTED = 2,   /* dtype / shape combination without a kernel */
-    CSA_ERR_CAPACITY = 3,      /* a cache or output too small for the request */
-    CSA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
-    CSA_ERR_HIP = 5            /* a HIP launch failed (message has the HIP error) */
+    CSA_ERR_INVALID_ARG = -1,  /* null pointer, bad size or inconsistent shape */
+    CSA_ERR_UNSUPPORTED = -2,  /* dtype / shape combination without a kernel */
+    CSA_ERR_CAPACITY = -3,     /* the window ring too small for the request */
+    CSA_ERR_WORKSPACE = -4,    /* workspace missing or smaller than required */
+    CSA_ERR_HIP = -5           /* a HIP launch failed (message has the HIP error) */
 } csa_status;
 
 typedef enum {

@@ -13,8 +13,9 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa_attn.so")
 
 F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
-STATUS = {0: "CSA_OK", 1: "CSA_ERR_INVALID_ARG", 2: "CSA_ERR_UNSUPPORTED", 3: "CSA_ERR_CAPACITY",
-          4: "CSA_ERR_WORKSPACE", 5: "CSA_ERR_HIP"}
+CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_CAPACITY, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4, -5
+STATUS = {CSA_OK: "CSA_OK", CSA_ERR_INVALID_ARG: "CSA_ERR_INVALID_ARG", CSA_ERR_UNSUPPORTED: "CSA_ERR_UNSUPPORTED",
+          CSA_ERR_CAPACITY: "CSA_ERR_CAPACITY", CSA_ERR_WORKSPACE: "CSA_ERR_WORKSPACE", CSA_ERR_HIP: "CSA_ERR_HIP"}
 EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_compress_kv_batch", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
            "csa_attn_workspace_size", "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "attn_out_proj_grouped",
            "csa_last_error"]
