@@ -58,11 +58,15 @@ def parse():
     ap.add_argument("--copies", type=int, default=6, help="rotated buffer sets (defeats the last-level cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
+    ap.add_argument("--prefill-only", action="store_true", help="only the prefill-chunk measurement (for profiling)")
+    ap.add_argument("--no-decode-configs", action="store_true", help="skip the HCA b16 / CSA b32 decode workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-prefill-seconds", type=float, default=25.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+")
     ap.add_argument("--summarize-prefill", metavar="DIR")
+    ap.add_argument("--summarize-pmc-kernels", metavar="DIR", nargs="+")
     return ap.parse_args()
 
 
@@ -172,7 +176,7 @@ CALLS = ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_mqa_attn", "csa_out_
 # the kernels each call launches, in launch order (for matching rocprof traces)
 CALL_KERNELS = {
     "csa_compress_kv": ["k_compress"],
-    "csa_indexer_topk": ["k_idx_zero", "k_idx_score_mfma", "k_idx_collect", "k_idx_final"],
+    "csa_indexer_topk": ["k_idxd_filter", "k_idxd_select"],
     "csa_sparse_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "csa_out_proj": ["k_proj_gemv"],
     "hca_compress_kv": ["k_compress"],
@@ -229,26 +233,93 @@ FP4_PEAK_TFLOPS = 10100.0      # MI355X dense FP4 (the indexer runs the FP4 MFMA
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16
 
 
-def prefill_measure(torch, api, reps=3, seed=5005):
+def _pctl(ts):
+    """median, p10 and p90 (ms) of a list of event times."""
+    return {"median": round(float(np.median(ts)), 4), "p10": round(float(np.percentile(ts, 10)), 4),
+            "p90": round(float(np.percentile(ts, 90)), 4)}
+
+
+def _timed(torch, f, reps, flush=None):
+    """Event times (ms) of f over reps runs after one warm-up; flush() (an
+    L2 / last-level-cache eviction) runs before each, outside the events."""
+    f()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        f()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return ts
+
+
+def _compressed_prefix(torch, api, gen, ntok, caches, chunk=1 << 16):
+    """Fill caches with the library's own compression of seeded N(0,1) raw
+    tokens at positions 0 .. ntok-1: caches = [(cache, m, bias, kind)], kind
+    0 a KV cache (RMSNorm + RoPE), 1 an indexer-key cache (no norm)."""
+    dev = "cuda"
+    gam = torch.ones(D_HEAD, device=dev)
+    for c0 in range(0, ntok, chunk):
+        n = min(chunk, ntok - c0)
+        start = torch.full((caches[0][0].B,), c0, dtype=torch.int32, device=dev)
+        x = xi = None
+        for cache, m, bias, kind in caches:
+            if kind == 0:
+                if x is None:
+                    x = torch.randn(cache.B, n, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
+                api.compress_kv(x, start, m, bias, gamma=gam, rope_dim=DR, kv_out=cache)
+            else:
+                if xi is None:
+                    xi = torch.randn(cache.B, n, DI, generator=gen, device=dev).to(torch.bfloat16)
+                api.compress_kv(xi, start, m, bias, idx_out=cache)
+    torch.cuda.synchronize()
+
+
+def fp4_queries(torch, api, gen, B, T, Hi):
+    """FP4 indexer queries quantised by the library from an N(0,1) draw:
+    every (b, t, h) row of di values is one FP4 row (E2M1 codes, E8M0 scales
+    per 32)."""
+    x = torch.randn(1, B * T * Hi, DI, generator=gen, device="cuda").to(torch.bfloat16)
+    c = api.IdxCache(1, B * T * Hi, DI, api.FP4_E2M1)
+    api.compress_kv(x, torch.zeros(1, dtype=torch.int32, device="cuda"), 1, torch.zeros(1, device="cuda"), idx_out=c)
+    torch.cuda.synchronize()
+    return c.codes.view(B, T, Hi, DI // 2), c.scales.view(B, T, Hi, DI // 32)
+
+
+def prefill_measure(torch, api, reps=10, seed=5005):
     """Times the indexer, the sparse attention and the grouped output
     projection of one prefill chunk, and the HCA layer's dense attention over
-    the same chunk (events around each call, best of reps after a warm-up), on
-    synthetic inputs of the chunk's shapes, and prices their contractions
-    against the MFMA peaks."""
+    the same chunk (events around each call; median, p10, p90 over reps runs
+    after a warm-up), and prices their contractions against the MFMA peaks.
+    Caches are the library's own compression of seeded N(0,1) raw tokens (RMS-
+    normalised FP8 records, FP4 keys); the chunk's indexer queries are N(0,1)
+    quantised to FP4 by the same quantiser."""
     dev = "cuda"
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
-    n = (L + PF_T) // M_CSA
-    u8 = lambda *shape, lo=0, hi=256: torch.randint(lo, hi, shape, generator=gen, device=dev,
-                                                     dtype=torch.int32).to(torch.uint8)
-    keys = api.IdxCache(1, n, DI, api.FP4_E2M1, codes=u8(1, n, DI // 2), scales=u8(1, n, DI // 32, lo=124, hi=128))
-    qc, qsc = u8(1, PF_T, HI, DI // 2), u8(1, PF_T, HI, DI // 32, lo=124, hi=128)
+    ntok = L + PF_T
+    n = ntok // M_CSA
+    n_h = ntok // M_HCA
+    keys = api.IdxCache(1, n, DI, api.FP4_E2M1)
+    comp = api.KVCache(1, n, D_HEAD, DR, api.FP8_E4M3)
+    comp_h = api.KVCache(1, n_h, D_HEAD, DR, api.FP8_E4M3)
+    b_csa = torch.randn(M_CSA, generator=gen, device=dev)
+    b_idx = torch.randn(M_CSA, generator=gen, device=dev)
+    _compressed_prefix(torch, api, gen, ntok, [(comp, M_CSA, b_csa, 0), (comp_h, M_HCA, torch.zeros(M_HCA, device=dev), 0),
+                                              (keys, M_CSA, b_idx, 1)])
+    win = api.KVCache(1, W + PF_T, D_HEAD, DR, api.FP8_E4M3, ring=True)
+    xw = torch.randn(1, W + PF_T, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
+    api.compress_kv(xw, torch.full((1,), L - W, dtype=torch.int32, device=dev), 1, torch.zeros(1, device=dev),
+                    gamma=torch.ones(D_HEAD, device=dev), rope_dim=DR, kv_out=win)
+    qc, qsc = fp4_queries(torch, api, gen, 1, PF_T, HI)
     w = torch.randn(1, PF_T, HI, generator=gen, device=dev)
     pos = (torch.arange(PF_T, device=dev, dtype=torch.int32) + L).view(1, PF_T)
     ws = torch.empty(api.indexer_workspace_bytes(1, PF_T, n, PF_TOPK), dtype=torch.uint8, device=dev)
     top = torch.empty(1, PF_T, PF_TOPK, dtype=torch.int32, device=dev)
-    comp = api.KVCache(1, n, D_HEAD, DR, api.FP8_E4M3, rec=u8(1, n, REC, hi=0x70))
-    win = api.KVCache(1, W + PF_T, D_HEAD, DR, api.FP8_E4M3, ring=True, rec=u8(1, W + PF_T, REC, hi=0x70))
     q = torch.randn(1, PF_T, H, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
     sink = torch.randn(H, generator=gen, device=dev)
     p = api.attn_params(D_HEAD, DR, W, M_CSA)
@@ -264,14 +335,13 @@ def prefill_measure(torch, api, reps=3, seed=5005):
 
     # the HCA layer's prefill over the same chunk: every compressed entry of
     # the 1M prefix (m = 128) plus the window, dense
-    n_h = (L + PF_T) // M_HCA
-    comp_h = api.KVCache(1, n_h, D_HEAD, DR, api.FP8_E4M3, rec=u8(1, n_h, REC, hi=0x70))
     p_h = api.attn_params(D_HEAD, DR, W, M_HCA)
     aws_h = torch.empty(max(1, api.attn_workspace_bytes(1, PF_T, H, D_HEAD, n_h, W, api.BF16, api.FP8_E4M3)),
                         dtype=torch.uint8, device=dev)
+    out_h = torch.empty_like(out)
 
     def att_h():
-        api.hca_dense_mqa_attn(q, pos, comp_h, win, sink, p_h, out=out, workspace=aws_h)
+        api.hca_dense_mqa_attn(q, pos, comp_h, win, sink, p_h, out=out_h, workspace=aws_h)
 
     # the chunk's grouped output projection: [8192, 64 x 512] -> [8192, 7168]
     wo = (torch.randn(G, HIDDEN // G, H * D_HEAD // G, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
@@ -280,39 +350,153 @@ def prefill_measure(torch, api, reps=3, seed=5005):
     def proj():
         api.out_proj_grouped(out.view(PF_T, H * D_HEAD), wo, y=y)
 
-    def best(f):
-        f()
-        torch.cuda.synchronize()
-        t = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            f()
-            e1.record()
-            torch.cuda.synchronize()
-            t.append(e0.elapsed_time(e1))
-        return min(t)
-    ti, ta, th, tp = best(idx), best(att), best(att_h), best(proj)
-    n_mean = (L + PF_T / 2) / M_CSA                       # blocks visible to the average query
-    fi = 2.0 * PF_T * HI * DI * n_mean                    # indexer q.k products
-    fa = 2.0 * PF_T * H * (PF_TOPK + W) * 2 * D_HEAD      # Q K^T and P V over 1,152 entries
-    fh = 2.0 * PF_T * H * ((L + PF_T / 2) / M_HCA + W) * 2 * D_HEAD   # HCA: every block of the prefix + window
-    fp = 2.0 * PF_T * H * D_HEAD * (HIDDEN // G)         # grouped projection (block-diagonal)
+    ti, ta, th, tp = (_timed(torch, f, reps) for f in (idx, att, att_h, proj))
+    mi, ma, mh, mp = (float(np.median(t)) for t in (ti, ta, th, tp))
+    fi, fa, fh, fp = prefill_flops()
     return {"workload": "CSA prefill chunk, 8,192 queries over a 1M prefix, 64 heads x 512, top-1024, FP4 indexer, "
                         "FP8 records, grouped projection to 7,168; and the HCA layer's dense attention over the same "
-                        "chunk (8,256 blocks + window)",
-            "indexer_ms": round(ti, 3), "attn_ms": round(ta, 3), "proj_ms": round(tp, 3),
-            "query_tokens_per_s": round(PF_T / ((ti + ta + tp) * 1e-3), 1),
-            "query_tokens_per_s_calls": "CSA indexer + sparse attention + projection",
-            "indexer_TFLOPs": round(fi / (ti * 1e-3) / 1e12, 1), "indexer_mfma_frac": round(fi / (ti * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                        "chunk (8,256 blocks + window); caches compressed by the library from N(0,1) tokens",
+            "indexer_ms": _pctl(ti), "attn_ms": _pctl(ta), "proj_ms": _pctl(tp), "hca_attn_ms": _pctl(th),
+            "query_tokens_per_s": round(PF_T / ((mi + ma + mp) * 1e-3), 1),
+            "query_tokens_per_s_calls": "CSA indexer + sparse attention + projection (medians)",
+            "indexer_TFLOPs": round(fi / (mi * 1e-3) / 1e12, 1),
+            "indexer_mfma_frac": round(fi / (mi * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
             "indexer_peak": "fp4 10.1 PFLOP/s",
-            "attn_TFLOPs": round(fa / (ta * 1e-3) / 1e12, 1), "attn_mfma_frac": round(fa / (ta * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "attn_TFLOPs": round(fa / (ma * 1e-3) / 1e12, 1), "attn_mfma_frac": round(fa / (ma * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "attn_peak": "bf16 2.5 PFLOP/s",
-            "hca_attn_ms": round(th, 3), "hca_attn_TFLOPs": round(fh / (th * 1e-3) / 1e12, 1),
-            "hca_attn_mfma_frac": round(fh / (th * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "proj_TFLOPs": round(fp / (tp * 1e-3) / 1e12, 1),
-            "proj_mfma_frac": round(fp / (tp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "timing": "HIP events around each call, best of 3 after a warm-up"}
+            "hca_attn_TFLOPs": round(fh / (mh * 1e-3) / 1e12, 1),
+            "hca_attn_mfma_frac": round(fh / (mh * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "proj_TFLOPs": round(fp / (mp * 1e-3) / 1e12, 1),
+            "proj_mfma_frac": round(fp / (mp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "timing": f"HIP events around each call, median (p10, p90) of {reps} runs after a warm-up"}
+
+
+def prefill_flops():
+    """Algorithmic flops of the prefill chunk's calls: indexer q.k products,
+    CSA attention (Q K^T and P V over top-k + window), HCA attention (every
+    block of the prefix + window), grouped projection."""
+    n_mean = (L + PF_T / 2) / M_CSA                       # blocks visible to the average query
+    fi = 2.0 * PF_T * HI * DI * n_mean
+    fa = 2.0 * PF_T * H * (PF_TOPK + W) * 2 * D_HEAD
+    fh = 2.0 * PF_T * H * ((L + PF_T / 2) / M_HCA + W) * 2 * D_HEAD
+    fp = 2.0 * PF_T * H * D_HEAD * (HIDDEN // G)
+    return fi, fa, fh, fp
+
+
+def decode_configs_measure(torch, api, reps=20, seed=6006):
+    """The two other decode workloads, each one step per rep with L2 and the
+    last-level cache evicted before it (a 1 GiB write outside the events):
+      HCA decode, bf16, batch 16 at 65,536 tokens: window append + 128-token
+        block compress, dense attention over 512 entries + window (32 heads x
+        512), grouped projection 16384 -> 4096 (8 groups);
+      CSA decode, bf16, batch 32 at 131,072 tokens: window append + block +
+        indexer-key compress, indexer top-1024 over 32,768 bf16 keys, sparse
+        attention over 1,024 entries + window (32 heads x 512), grouped
+        projection 16384 -> 4096.
+    Caches are the library's compression of seeded N(0,1) raw tokens.
+    Returns per-call and per-step medians and the attention-side HBM rate."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)        # 1 GiB
+    flush_out = torch.empty((), dtype=torch.int64, device=dev)
+
+    def flush():
+        # a read of 1 GiB: the caches end up holding clean lines of it, so the
+        # timed kernel neither hits its own data nor pays for dirty write-backs
+        torch.sum(flush_buf, dim=0, out=flush_out)
+
+    res = {}
+    Hq, hid = 32, 4096
+    zero1 = torch.zeros(1, device=dev)
+    gam = torch.ones(D_HEAD, device=dev)
+    for name, Bc, Lc, m, sparse in (("hca_decode_b16_64k_bf16", 16, 65536, 128, False),
+                                    ("csa_decode_b32_128k_bf16", 32, 131072, 4, True)):
+        n = Lc // m
+        t = Lc - 1
+        comp = api.KVCache(Bc, n, D_HEAD, DR, api.BF16)
+        win = api.KVCache(Bc, W, D_HEAD, DR, api.BF16, ring=True)
+        bias = torch.randn(m, generator=gen, device=dev) if sparse else torch.zeros(m, device=dev)
+        caches = [(comp, m, bias, 0)]
+        keys = None
+        if sparse:
+            keys = api.IdxCache(Bc, n, DI, api.BF16)
+            caches.append((keys, m, torch.randn(m, generator=gen, device=dev), 1))
+        _compressed_prefix(torch, api, gen, Lc, caches)
+        xw = torch.randn(Bc, W, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
+        api.compress_kv(xw, torch.full((Bc,), Lc - W, dtype=torch.int32, device=dev), 1, zero1, gamma=gam,
+                        rope_dim=DR, kv_out=win)
+        pos = torch.full((Bc, 1), t, dtype=torch.int32, device=dev)
+        x_blk = torch.randn(Bc, m, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
+        x_new = x_blk[:, m - 1:].contiguous()
+        xi_blk = torch.randn(Bc, m, DI, generator=gen, device=dev).to(torch.bfloat16)
+        tok_new = torch.full((Bc,), t, dtype=torch.int32, device=dev)
+        tok_blk = torch.full((Bc,), t + 1 - m, dtype=torch.int32, device=dev)
+        q = torch.randn(Bc, 1, Hq, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
+        qI = torch.randn(Bc, 1, HI, DI, generator=gen, device=dev).to(torch.bfloat16)
+        wI = torch.randn(Bc, 1, HI, generator=gen, device=dev)
+        sink = torch.randn(Hq, generator=gen, device=dev) * (1.0 if sparse else 0.02)
+        Wo = (torch.randn(G, hid // G, Hq * D_HEAD // G, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+        o = torch.empty(Bc, 1, Hq, D_HEAD, dtype=torch.bfloat16, device=dev)
+        y = torch.empty(Bc, hid, dtype=torch.bfloat16, device=dev)
+        prm = api.attn_params(D_HEAD, DR, W, m)
+        aws = torch.empty(max(1, api.attn_workspace_bytes(Bc, 1, Hq, D_HEAD, K_CSA if sparse else n, W, api.BF16,
+                                                          api.BF16)), dtype=torch.uint8, device=dev)
+        top = torch.empty(Bc, 1, K_CSA, dtype=torch.int32, device=dev)
+        iws = torch.empty(max(1, api.indexer_workspace_bytes(Bc, 1, n, K_CSA)), dtype=torch.uint8, device=dev)
+
+        def comp_call():
+            jobs = [dict(x=x_new, tok_start=tok_new, m=1, score_bias=zero1, gamma=gam, rope_dim=DR, kv_out=win),
+                    dict(x=x_blk, tok_start=tok_blk, m=m, score_bias=bias, gamma=gam, rope_dim=DR, kv_out=comp)]
+            if sparse:
+                jobs.append(dict(x=xi_blk, tok_start=tok_blk, m=m, score_bias=caches[1][2], idx_out=keys))
+            api.compress_kv_batch(jobs)
+
+        def idx_call():
+            api.indexer_topk(qI, api.BF16, wI, keys, pos, m, K_CSA, out=top, workspace=iws)
+
+        def attn_call():
+            if sparse:
+                api.sparse_mqa_attn(q, pos, top, comp, win, sink, prm, out=o, workspace=aws)
+            else:
+                api.hca_dense_mqa_attn(q, pos, comp, win, sink, prm, out=o, workspace=aws)
+
+        def proj_call():
+            api.out_proj_grouped(o.view(Bc, Hq * D_HEAD), Wo, y=y)
+
+        calls = [("compress_kv", comp_call)] + ([("indexer_topk", idx_call)] if sparse else []) + \
+                [("attention", attn_call), ("out_proj", proj_call)]
+
+        def step():
+            for _, f in calls:
+                f()
+        per = {c: float(np.median(_timed(torch, f, reps, flush))) for c, f in calls}
+        st = _timed(torch, step, reps, flush)
+        ms = float(np.median(st))
+        qo = Bc * Hq * D_HEAD * 2
+        ne = (K_CSA if sparse else n) + W
+        algo = {"compress_kv": Bc * (1 + m) * D_HEAD * 2 + 2 * Bc * 2 * D_HEAD + (Bc * m * DI * 2 + Bc * DI * 2 if sparse else 0),
+                "attention": 2 * qo + Bc * ne * 2 * D_HEAD + (Bc * K_CSA * 4 if sparse else 0),
+                "out_proj": G * (hid // G) * (Hq * D_HEAD // G) * 2 + qo + Bc * hid * 2}
+        if sparse:
+            algo["indexer_topk"] = Bc * n * DI * 2 + Bc * HI * (DI * 2 + 4) + Bc * K_CSA * 4
+        attn_side = sum(v for c, v in algo.items() if c != "out_proj")
+        attn_ms = sum(per[c] for c in algo if c != "out_proj")
+        res[name] = {
+            "batch": Bc, "context": Lc, "m": m, "heads": Hq, "entries_per_query": ne,
+            "step_ms": _pctl(st), "query_tokens_per_s": round(Bc / (ms * 1e-3), 1),
+            "calls_us": {c: round(v * 1e3, 2) for c, v in per.items()},
+            "calls_GBs": {c: round(algo[c] / (per[c] * 1e-3) / 1e9, 1) for c in per},
+            "algo_MB": {c: round(v / 1e6, 3) for c, v in algo.items()},
+            "attention_side": {"algo_MB": round(attn_side / 1e6, 2), "ms": round(attn_ms, 4),
+                               "GBs": round(attn_side / (attn_ms * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(attn_side / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "query_tokens_per_s": round(Bc / (attn_ms * 1e-3), 1)},
+            "timing": f"HIP events, median (p10, p90) of {reps} runs, L2 and last-level cache evicted before each "
+                      "(a 1 GiB read)"}
+        del comp, win, keys, aws, iws
+        torch.cuda.empty_cache()
+    return res
 
 
 def capture_step_graphs(torch, fns, sets, sh):
@@ -391,6 +575,45 @@ def cpu_baseline(target_s):
                       f"synthetic FP8/FP4 caches of the same shapes), {el:.1f} s"}
 
 
+def cpu_baseline_prefill(target_s, nq=512):
+    """The oracle on the prefill chunk's CSA calls (indexer top-1024 over
+    264,192 FP4 keys, sparse attention over 1,024 FP8 records + window, and
+    the grouped projection) for nq strided query rows (every 8,192/nq-th),
+    in batches until the sample is done or about target_s seconds have
+    passed; the rate per query row is extrapolated to the chunk."""
+    import oracle as O
+    from long_context_attention_23_amd import synth
+    g = synth.rng(2005)
+    n = (L + PF_T) // M_CSA
+    kc, ks = synth.fp4_rows(g, (n,), DI, -3, 0)
+    comp = synth.fp8_records(g, (n,), D_HEAD, DR, REC)
+    win = synth.fp8_records(g, (W + PF_T,), D_HEAD, DR, REC)
+    Wo = O.bf16_decode(synth.bf16_bits(g, (G, HIDDEN // G, H * D_HEAD // G), std=0.02))
+    sink = synth.normal(g, H)
+    rows = np.arange(0, PF_T, PF_T // nq)[:nq]
+    done, t0 = 0, time.perf_counter()
+    for b0 in range(0, len(rows), 32):
+        r = rows[b0:b0 + 32]
+        qc, qs = synth.fp4_rows(g, (len(r), HI), DI, -3, 0)
+        w = synth.normal(g, (len(r), HI))
+        q = synth.bf16_bits(g, (len(r), H, D_HEAD))
+        pos = (L + r).astype(np.int32)
+        top = O.indexer_topk(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, M_CSA, PF_TOPK)
+        o = O.attention(q, O.BF16, pos, None, sink, D_HEAD, DR, W, M_CSA, 10000.0, 1.0 / math.sqrt(D_HEAD), 1e-6,
+                        comp, O.FP8_E4M3, win, O.FP8_E4M3, top)
+        O.out_proj(o.reshape(len(r), H * D_HEAD), Wo)
+        done += len(r)
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {"value": done / el, "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
+            "extrapolated": True,
+            "sample": f"{done} of the chunk's 8,192 query rows (every {PF_T // nq}th) through the CSA indexer, sparse "
+                      f"attention and projection (fp64 oracle, synthetic FP4 keys and FP8 records of the 1M prefix's "
+                      f"shapes), {el:.1f} s; the per-row rate stands for the whole chunk"}
+
+
 # HBM traffic per launch of a call, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # runs of this benchmark scaled by the copy calibration (the summary under
 # profiles/ gives the counts and commands); valid only while the kernels'
@@ -448,8 +671,9 @@ def summarize(d, last=20):
     db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
     rows = _kernel_rows(db)
     seq = [k for c in CALLS for k in CALL_KERNELS[c]]
-    first = seq.index("k_idx_zero")
-    zero = [i for i, (n, _, _) in enumerate(rows) if "k_idx_zero" in n]
+    anchor = CALL_KERNELS["csa_indexer_topk"][0]
+    first = seq.index(anchor)
+    zero = [i for i, (n, _, _) in enumerate(rows) if anchor in n]
     steps = []
     for z in zero:
         st = z - first
@@ -491,8 +715,12 @@ def summarize_prefill(d):
     k_attn_mfma launch (one split per row), the projection k_proj_mfma."""
     db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
     rows = [(_short(n), (b - a) / 1e3) for n, a, b in _kernel_rows(db) if "csa::" in n]
-    i0 = next(i for i, (n, _) in enumerate(rows) if "k_idxp_" in n)
-    pre = rows[i0:]
+    # the section runs from its first threshold kernel (decode steps use the
+    # decode threshold kernel) to the next compression launch (the caches of
+    # the workloads measured after it)
+    i0 = next(i for i, (n, _) in enumerate(rows) if "k_idxp_thresh" in n)
+    i1 = next((i for i in range(i0, len(rows)) if "k_compress" in rows[i][0]), len(rows))
+    pre = rows[i0:i1]
     att = [t for n, t in pre if "k_attn_mfma" in n]
     nrep = len(att) // 2
     calls = {"csa_indexer_topk (k_idxp_*)": None, "csa_sparse_mqa_attn": att[:nrep],
@@ -538,10 +766,11 @@ def summarize_pmc(dirs):
             attn_seen = 0
             while i < len(ks):
                 n = ks[i][0]
-                if n.endswith("k_idx_zero") and i + 3 < len(ks):
-                    sums["csa_indexer_topk"].append(sum(v for _, v in ks[i:i + 4]))
+                nk = len(CALL_KERNELS["csa_indexer_topk"])
+                if n.endswith(CALL_KERNELS["csa_indexer_topk"][0]) and i + nk - 1 < len(ks):
+                    sums["csa_indexer_topk"].append(sum(v for _, v in ks[i:i + nk]))
                     attn_seen = 0
-                    i += 4
+                    i += nk
                     continue
                 if "k_attn_mfma" in n and i + 1 < len(ks) and "k_attn_combine" in ks[i + 1][0]:
                     key = "csa_sparse_mqa_attn" if attn_seen == 0 else "hca_dense_mqa_attn"
@@ -559,6 +788,51 @@ def summarize_pmc(dirs):
     print(json.dumps(res, indent=1))
 
 
+def summarize_pmc_kernels(dirs, match=("k_idxp_", "k_attn_mfma", "k_proj_mfma")):
+    """Per-kernel counter means (per dispatch) from rocprofv3 --pmc runs of
+    this benchmark (any counters, several runs), for kernels whose name holds
+    one of `match`, with the derived figures:
+      MFMA busy = sum SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE x 1024 SIMDs)
+      MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_* x 512
+      VALU busy = sum SQ_ACTIVE_INST_VALU / 256 CUs / max GRBM_GUI_ACTIVE
+    (per-dispatch sums over the counter's instances; GRBM_GUI_ACTIVE is taken
+    as its largest instance, the busy time of the GPU)."""
+    import sqlite3
+    per = {}                                  # (kernel, counter) -> list of per-dispatch (sum, max)
+    for d in dirs:
+        db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
+        c = sqlite3.connect(db)
+        acc = {}
+        for name, cn, v, did in c.execute("select name, counter_name, counter_value, dispatch_id from pmc_events"):
+            k = _short(name)
+            if not any(mm in k for mm in match):
+                continue
+            a = acc.setdefault((did, k, cn), [0.0, -1e300])
+            a[0] += v
+            a[1] = max(a[1], v)
+        for (did, k, cn), (sm, mx) in acc.items():
+            per.setdefault((k, cn), []).append((sm, mx))
+    kernels = sorted({k for k, _ in per})
+    out = []
+    for k in kernels:
+        cs = {cn: v for (kk, cn), v in per.items() if kk == k}
+        mean = {cn: float(np.mean([a for a, _ in v])) for cn, v in cs.items()}
+        gmax = float(np.mean([b for _, b in cs["GRBM_GUI_ACTIVE"]])) if "GRBM_GUI_ACTIVE" in cs else None
+        row = {"dispatches": max(len(v) for v in cs.values()), "counters": {cn: round(v, 1) for cn, v in mean.items()}}
+        if gmax:
+            row["GRBM_GUI_ACTIVE_max"] = round(gmax, 1)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                row["mfma_busy"] = round(mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (gmax * 1024), 4)
+            if "SQ_ACTIVE_INST_VALU" in mean:
+                row["valu_busy"] = round(mean["SQ_ACTIVE_INST_VALU"] / 256 / gmax, 4)
+        for t in ("BF16", "F6F4", "F8", "F16", "F32"):
+            cn = "SQ_INSTS_VALU_MFMA_MOPS_" + t
+            if cn in mean:
+                row["mfma_flops_" + t] = float(f"{mean[cn] * 512:.4g}")
+        out.append((k, row))
+    print(json.dumps(dict(out), indent=1))
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -569,6 +843,8 @@ def main():
         return summarize_pmc(args.summarize_pmc)
     if args.summarize_prefill:
         return summarize_prefill(args.summarize_prefill)
+    if args.summarize_pmc_kernels:
+        return summarize_pmc_kernels(args.summarize_pmc_kernels)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this path runs on a single "
               "MI355X; multi-GPU sharding is not built)", file=sys.stderr)
@@ -577,6 +853,9 @@ def main():
     from long_context_attention_23_amd import api
     api.lib()
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_measure(torch, api)}), flush=True)
+        return
     sets, sh = build_state(torch, api, args.copies)
     R = len(sets)
     fns = call_fns(api)
@@ -663,10 +942,17 @@ def main():
     }
     res["eager"] = {"ms_per_step": round(ms_eager, 4), "query_tokens_per_s": round(B / (ms_eager * 1e-3), 1),
                     "how": "the same steps launched call by call on one stream (dispatch gaps between kernels)"}
+    del graphs, sets
+    torch.cuda.empty_cache()
     if not args.no_prefill:
         res["prefill"] = prefill_measure(torch, api)
+        torch.cuda.empty_cache()
+    if not args.no_decode_configs:
+        res["decode_configs"] = decode_configs_measure(torch, api)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        if not args.no_prefill:
+            res["prefill"]["cpu_baseline"] = cpu_baseline_prefill(args.cpu_prefill_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -264,6 +264,9 @@ CSA_API size_t csa_indexer_topk_workspace_size(int32_t B, int32_t Tq, int64_t ke
     // room for the query-batched prefill path too (used for FP4 queries and keys)
     if (csa::idx_prefill_eligible(64, 4, Tq, key_cap, topk))
         need = std::max<int64_t>(need, rows * csa::idx_prefill_row_bytes());
+    // and for the decode path (FP4 queries and keys, every row at once)
+    if (csa::idx_decode_eligible(64, 4, Tq, key_cap, topk))
+        need = std::max<int64_t>(need, rows * csa::idx_decode_row_bytes(key_cap));
     return (size_t)need;
 }
 

@@ -1445,24 +1445,16 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
     pf_emit(bm4, nw4, out, a.topk, wsum);
 }
 
-// exact selection of a flagged query row from its recomputed scores: digit
-// passes over the score key, then over the inverted block index of the ties,
-// then the members marked and emitted
-__global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
-    warm_kernargs(sizeof(IndexerArgs));
-    __shared__ uint4 bm4[kPfWords / 4];
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t sh[4];
-    __shared__ uint32_t wsum[kPfWaves];
+// exact selection of one query row from its recomputed scores: digit passes
+// over the score key, then over the inverted block index of the ties, then the
+// members marked in bm4 (LDS, >= (n + 127) / 128 groups) and emitted.  Every
+// thread of the workgroup calls it; the waves take the key tiles in turn.
+__device__ void exact_row(const IndexerArgs& a, int b, int64_t row, int64_t n, int32_t* out, uint4* bm4,
+                          uint32_t* hist, uint32_t* sh, uint32_t* wsum) {
     uint32_t* bm = reinterpret_cast<uint32_t*>(bm4);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
-    const int b = blockIdx.y, t = blockIdx.x;
-    const int64_t row = (int64_t)b * a.Tq + t;
-    uint32_t* hd = pf_hdr(a, row);
-    if (hd[1] == 0u) return;
-    const int64_t n = visible_blocks(a, row);
-    const int nw4 = (int)min<int64_t>((n + 127) / 128, kPfWords / 4);   // bitmap groups holding visible blocks
-    int32_t* out = a.out + row * a.topk;
+    const int nwv = (int)(blockDim.x >> 6);
+    const int nw4 = (int)((n + 127) / 128);
     // A operand: rows 0..3 = the four heads of this query, the rest zero
     i32x8_t qa = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
     int qs = 127;
@@ -1479,7 +1471,7 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
     // every key of the row, lanes < 32 holding the score key of key j (the
     // other half of the wave holds zero rows); fn(key, j, valid) per lane
     auto sweep = [&](auto fn) {
-        for (int tile = wv; tile < ntile; tile += kPfWaves) {
+        for (int tile = wv; tile < ntile; tile += nwv) {
             uint4 kc;
             int ks;
             pf_load_keys(a, b, (int64_t)tile * 32, l32, half, kc, ks);
@@ -1544,6 +1536,461 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
     pf_emit(bm4, nw4, out, a.topk, wsum);
 }
 
+// a query row the select kernel flagged, recomputed exactly
+__global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    __shared__ uint4 bm4[kPfWords / 4];
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t wsum[kPfWaves];
+    const int b = blockIdx.y, t = blockIdx.x;
+    const int64_t row = (int64_t)b * a.Tq + t;
+    if (pf_hdr(a, row)[1] == 0u) return;
+    exact_row(a, b, row, visible_blocks(a, row), a.out + row * a.topk, bm4, hist, sh, wsum);
+}
+
+// ------------------------------------------------------------------ decode path
+// Query rows of short chunks (decode: one or a few queries per sequence) with
+// FP4 queries and keys (di = 64, Hi = 4) against a large key set (up to 2^18
+// blocks).  Two kernels:
+//   F  the row's keys are split over workgroups of kDfChunk consecutive
+//      blocks.  Every workgroup of a row first scores the same systematic
+//      sample of the row's keys (kDsSampTiles 32-key tiles, every stride-th,
+//      stride and rank from the row's visible count: mostly L2 hits) and
+//      takes the 22-bit prefix T of its rank-th largest score key (low bits
+//      zero, so at least rank samples score at or above T; about 4k keys of
+//      the row do), while its own keys are in flight; every workgroup gets
+//      the same T.  Keys scoring above T go (key, j) to the workgroup's own
+//      segment of the row's candidate area, keys equal to T (j) to its tie
+//      segment, both in ascending j; the counts go to the row header.  No
+//      atomics and nothing to clear: each workgroup writes its own counts.
+//   S  one workgroup per row: the above-threshold segments are compacted
+//      into LDS; with at least k of them, three digit passes (11, 11, 10
+//      bits) over their score keys give the k-th largest key T1 and members
+//      are the keys above T1 plus the smallest-j keys at T1; with fewer,
+//      every key above T plus the smallest-j keys at T.  Members and the
+//      ties to choose from are marked in two LDS bitmaps over j; the lowest
+//      tie bits up to the count join the members, emitted in ascending j.
+//      A row with more candidates than LDS holds, or fewer than k at or
+//      above T (a sample ranked too high), is recomputed exactly in place.
+// Every kernel forms a key's score from the same MFMA result and the same
+// fp32 operations, so the score is the same number in all of them.
+// In an nb-bin histogram (nb = BPT x the workgroup's threads), the digit whose
+// cumulative count from the top first reaches need, and the count strictly
+// above it, found by the whole workgroup: thread t sums the BPT bins
+// [nb - BPT (t + 1), nb - BPT t) with one vector read (consecutive threads,
+// consecutive bins: no bank conflicts), a workgroup scan orders the sums from
+// the top, and the thread holding the need-th count writes (digit, above) to
+// sh[0..1].  Every thread calls it; read sh after a barrier.
+template <int BPT>
+__device__ __forceinline__ void block_pick(const uint32_t* hist, uint32_t need, uint32_t* wsum, uint32_t* sh) {
+    static_assert(BPT == 1 || BPT == 2 || BPT == 4, "bins per thread");
+    const int nb = BPT * (int)blockDim.x;
+    const int lo = nb - BPT * ((int)threadIdx.x + 1);            // lowest bin of this thread's range
+    uint32_t h[BPT];
+    if constexpr (BPT == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(hist + lo);
+        h[0] = v.w; h[1] = v.z; h[2] = v.y; h[3] = v.x;            // highest bin first
+    } else if constexpr (BPT == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(hist + lo);
+        h[0] = v.y; h[1] = v.x;
+    } else {
+        h[0] = hist[lo];
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; q++) s += h[q];
+    const uint32_t ex = block_exclusive_scan(s, wsum);            // counts in the bins above mine
+    if (ex < need && ex + s >= need) {
+        uint32_t c = ex;
+#pragma unroll
+        for (int q = 0; q < BPT; q++) {
+            if (c + h[q] >= need) { sh[0] = (uint32_t)(lo + BPT - 1 - q); sh[1] = c; break; }
+            c += h[q];
+        }
+    }
+}
+
+// smallest and largest of v over the workgroup (all threads call; wv is the
+// caller's scratch of one word pair per wave; a barrier inside)
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint2* wv) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) wv[threadIdx.x / kWave] = make_uint2(mn, mx);
+    __syncthreads();
+    const int nw = (int)(blockDim.x / kWave);
+    for (int q = 0; q < nw; q++) {
+        const uint2 x = wv[q];
+        mn = min(mn, x.x);
+        mx = max(mx, x.y);
+    }
+}
+
+// One pass of a radix select over values known to lie in [base, base + 2^width)
+// (width <= 32): the digit is (v - base) >> shift with shift = width - 11 (or
+// 0), so the values spread over up to 2048 bins wherever the range starts --
+// score keys crowd into a few top-bit bins, and LDS atomics on one address
+// serialise.  add(f) calls f(v, in) for this thread's candidates; the bin
+// holding the need-th largest becomes the new range.  hist (2048 bins) must
+// be zero on entry and is zero again on return.
+template <int NT, typename Add>
+__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* hist,
+                                          uint32_t* wsum, uint32_t* sh) {
+    const int shift = width > 11 ? width - 11 : 0;
+    const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
+    add([&](uint32_t v, bool in) {
+        const uint32_t d = v - base;                   // wraps past lim for v below base
+        if (in && d <= lim) atomicAdd(&hist[d >> shift], 1u);
+    });
+    __syncthreads();
+    block_pick<2048 / NT>(hist, need, wsum, sh);
+    __syncthreads();
+    base += sh[0] << shift;
+    need -= sh[1];
+    width = shift;
+    for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0u;
+    __syncthreads();
+}
+
+__device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
+
+constexpr int kDfThreads = 512;
+constexpr int kDfWaves = kDfThreads / kWave;
+constexpr int kDfTiles = 16;                                         // 32-key tiles per wave
+constexpr int kDfChunk = kDfWaves * kDfTiles * 32;                   // keys per filter workgroup
+constexpr int kDfSegCands = 1024;                                    // above-threshold slots per workgroup
+constexpr int kDsSampTiles = 64;                                     // sample tiles per row
+constexpr int kDsSampPerWave = kDsSampTiles / kDfWaves;
+constexpr int kDecMaxSeg = (int)(kIdxDecMaxCap / kDfChunk);          // workgroups per row at most
+constexpr int kDecHdr = 1024;                                        // T, counts per segment
+constexpr int kDsThreads = 1024;
+constexpr int kDsWords = (int)(kIdxDecMaxCap / 32);                  // bitmap words
+constexpr int kDsWPT = kDsWords / kDsThreads;                        // bitmap words per thread
+constexpr int kDsCPT = kIdxPfCands / kDsThreads;                     // compacted candidates per thread
+static_assert(kDecHdr >= 4 * (2 + 2 * kDecMaxSeg), "decode header");
+static_assert(idx_decode_row_bytes(kIdxDecMaxCap) ==
+                  kDecHdr + (int64_t)kDecMaxSeg * (kDfSegCands * 8 + kDfChunk * 4) &&
+              idx_decode_row_bytes(kDfChunk + 1) == kDecHdr + 2 * (kDfSegCands * 8 + kDfChunk * 4), "decode row layout");
+static_assert(kDsWords * 32 >= kIdxDecMaxCap && kDsWords % (4 * kDsThreads) == 0, "decode bitmaps");
+static_assert(kDecMaxSeg <= kWave && kDsThreads % kDecMaxSeg == 0, "decode segments");
+static_assert(2048 % kDfThreads == 0 && 2048 % kDsThreads == 0 && 1024 % kDsThreads == 0, "histogram picks");
+
+// decode row layout (idx_decode_row_bytes): header words [0] T, [2 + s]
+// above count of segment s, [2 + kDecMaxSeg + s] tie count of segment s;
+// then, for the cache's S = ceil(cap / kDfChunk) segments, each segment's
+// above slots (key, j), then each segment's tie slots (j)
+__device__ __forceinline__ uint32_t* dec_hdr(const IndexerArgs& a, int64_t row) {
+    return reinterpret_cast<uint32_t*>(a.ws + row * a.ws_row_bytes);
+}
+__device__ __forceinline__ uint2* dec_cand(const IndexerArgs& a, int64_t row, int seg) {
+    return reinterpret_cast<uint2*>(a.ws + row * a.ws_row_bytes + kDecHdr) + (int64_t)seg * kDfSegCands;
+}
+__device__ __forceinline__ uint32_t* dec_ties(const IndexerArgs& a, int64_t row, int seg) {
+    const int64_t nseg_cap = (a.cap + kDfChunk - 1) / kDfChunk;
+    return reinterpret_cast<uint32_t*>(a.ws + row * a.ws_row_bytes + kDecHdr + nseg_cap * kDfSegCands * 8) +
+           (int64_t)seg * kDfChunk;
+}
+
+// A operand of one query row: rows 0..3 its four heads, the rest zero
+__device__ __forceinline__ void pd_load_a(const IndexerArgs& a, int64_t row, int l32, int half, i32x8_t& qa, int& qs) {
+    qa = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+    qs = 127;
+    if (l32 < 4) {
+        const int64_t r = row * 4 + l32;
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.q) + r * 32 + 16 * half);
+        qa[0] = (int)u.x; qa[1] = (int)u.y; qa[2] = (int)u.z; qa[3] = (int)u.w;
+        qs = a.q_scales[r * 2 + half];
+    }
+}
+
+// score of key l32 of a tile for the row's four heads (lanes of the upper
+// half hold zero rows).  The product reads operands from every lane, so it
+// is kept out of any lane-divergent select that consumes it (the compiler
+// would otherwise issue it under a partial exec mask).
+__device__ __forceinline__ float pd_score(const i32x8_t& qa, int qs, const uint4& kc, int ks, const float* w4) {
+    const f32x16_t acc = pf_mfma(qa, qs, kc, ks);
+    float v = pf_score(acc, 0, w4);
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ uint32_t sh[2];
+    __shared__ uint32_t wcnt[2][kDfWaves];
+    __shared__ uint32_t wsum[kDfWaves];
+    __shared__ uint2 mm[kDfWaves];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int64_t row = blockIdx.y;
+    const int b = (int)(row / a.Tq);
+    const int seg = (int)blockIdx.x;
+    const int64_t t0 = (int64_t)seg * kDfChunk + (int64_t)wv * kDfTiles * 32;    // this wave's first key
+    const int64_t n = visible_blocks(a, row);
+    if (n <= a.topk || (int64_t)seg * kDfChunk >= n) return;                     // workgroup-uniform
+    // the row's sample (stride from its visible count), loaded
+    // before the chunk's keys: loads return in order, and the threshold is
+    // formed while the chunk is still in flight
+    const int ntile = (int)((n + 31) / 32);
+    const int stride = (ntile + kDsSampTiles - 1) / kDsSampTiles;
+    const int nst = (ntile + stride - 1) / stride;                               // sample tiles, <= kDsSampTiles
+    uint4 sc[kDsSampPerWave];
+    int ss[kDsSampPerWave];
+#pragma unroll
+    for (int i = 0; i < kDsSampPerWave; i++)
+        pf_load_keys(a, b, (int64_t)(wv + kDfWaves * i) * stride * 32, l32, half, sc[i], ss[i]);
+    uint4 kc[kDfTiles];
+    int ks[kDfTiles];
+#pragma unroll
+    for (int i = 0; i < kDfTiles; i++) pf_load_keys(a, b, t0 + 32 * i, l32, half, kc[i], ks[i]);
+    i32x8_t qa;
+    int qs;
+    pd_load_a(a, row, l32, half, qa, qs);
+    float w4[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) w4[h] = a.w[row * 4 + h];
+    for (int i = tid; i < 2048; i += kDfThreads) hist[i] = 0u;
+    uint32_t skey[kDsSampPerWave];
+#pragma unroll
+    for (int i = 0; i < kDsSampPerWave; i++) {
+        const int tile = wv + kDfWaves * i;
+        const int64_t j = (int64_t)tile * stride * 32 + l32;
+        const float v = pd_score(qa, qs, sc[i], ss[i], w4);
+        skey[i] = (half == 0 && tile < nst && j < n) ? score_key(v) : 0u;
+    }
+    // T: the rank-th largest sample key itself, by range-adaptive radix
+    // passes over the samples (key 0 marks no sample).  At least rank samples
+    // score at or above T; an exact sample value (not a bin edge) keeps a
+    // mass of equal scores (e.g. the zeros of a row whose weights are all
+    // negative) on the tie list instead of the above-threshold one.
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u, nv = 0u;
+#pragma unroll
+    for (int i = 0; i < kDsSampPerWave; i++) {
+        nv += (uint32_t)__popcll(ballot64(half == 0 && skey[i] != 0u));
+        if (half == 0 && skey[i] != 0u) { mn = min(mn, skey[i]); mx = max(mx, skey[i]); }
+    }
+    if (lane == 0) wcnt[0][wv] = nv;
+    block_minmax(mn, mx, mm);                          // barrier inside: wcnt complete
+    uint32_t valid = 0;
+#pragma unroll
+    for (int q = 0; q < kDfWaves; q++) valid += wcnt[0][q];
+    uint32_t T = score_key(-__builtin_huge_valf());    // no sample: every non-NaN score is above it
+    if (valid > 0) {
+        uint32_t need = (uint32_t)min<int64_t>(max<int64_t>(((int64_t)4 * a.topk * valid + n - 1) / n, 1), valid);
+        uint32_t base = mn;
+        int width = bit_width(mx - mn);
+        while (width > 0)                                                        // workgroup-uniform
+            span_pass<kDfThreads>([&](auto f) {
+#pragma unroll
+                for (int i = 0; i < kDsSampPerWave; i++) f(skey[i], half == 0 && skey[i] != 0u);
+            }, base, width, need, hist, wsum, sh);
+        T = base;
+    }
+    __syncthreads();                                   // wcnt is reused below
+    // key > T <=> score > thr, key == T <=> score == thr
+    const float thr = __uint_as_float((T & 0x80000000u) ? (T & 0x7FFFFFFFu) : ~T);
+    uint64_t ab[kDfTiles], tb[kDfTiles];
+    uint32_t kk[kDfTiles];
+    uint32_t na = 0, nt = 0;
+#pragma unroll
+    for (int i = 0; i < kDfTiles; i++) {
+        const float v = pd_score(qa, qs, kc[i], ks[i], w4);
+        const uint64_t vm = ballot64(half == 0 && t0 + 32 * i + l32 < n);
+        ab[i] = __builtin_amdgcn_fcmpf(v, thr, kFcmpOgt) & vm;
+        tb[i] = __builtin_amdgcn_fcmpf(v, thr, kFcmpOeq) & vm;
+        kk[i] = score_key(v);
+        na += (uint32_t)__popcll(ab[i]);
+        nt += (uint32_t)__popcll(tb[i]);
+    }
+    if (lane == 0) { wcnt[0][wv] = na; wcnt[1][wv] = nt; }
+    __syncthreads();
+    uint32_t oa = 0, ot = 0, ta = 0, tt = 0;
+#pragma unroll
+    for (int q = 0; q < kDfWaves; q++) {
+        const uint32_t ca = wcnt[0][q], ct = wcnt[1][q];
+        if (q < wv) { oa += ca; ot += ct; }
+        ta += ca;
+        tt += ct;
+    }
+    uint32_t* hd = dec_hdr(a, row);
+    if (tid == 0) {
+        hd[2 + seg] = ta;                        // true counts (above may exceed the slots)
+        hd[2 + kDecMaxSeg + seg] = tt;
+        if (seg == 0) hd[0] = T;
+    }
+    uint2* cand = dec_cand(a, row, seg);
+    uint32_t* ties = dec_ties(a, row, seg);
+    const uint64_t below = (1ull << lane) - 1;
+#pragma unroll
+    for (int i = 0; i < kDfTiles; i++) {
+        const uint32_t j = (uint32_t)(t0 + 32 * i + l32);
+        if ((ab[i] >> lane) & 1u) {
+            const uint32_t pos = oa + (uint32_t)__popcll(ab[i] & below);
+            if (pos < (uint32_t)kDfSegCands) cand[pos] = make_uint2(kk[i], j);
+        }
+        if ((tb[i] >> lane) & 1u) ties[ot + (uint32_t)__popcll(tb[i] & below)] = j;   // < kDfChunk
+        oa += (uint32_t)__popcll(ab[i]);
+        ot += (uint32_t)__popcll(tb[i]);
+    }
+}
+
+__global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
+    warm_kernargs(sizeof(IndexerArgs));
+    __shared__ uint4 bmA4[kDsWords / 4];                             // members (also the exact path's bitmap)
+    __shared__ uint4 bmT4[kDsWords / 4];                             // ties to choose from
+    __shared__ uint2 cl[kIdxPfCands];                                // compacted above-threshold candidates
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ uint32_t sh[4];
+    __shared__ uint32_t segoff[2][kDecMaxSeg];
+    __shared__ uint2 mm[kDsThreads / kWave];
+    __shared__ uint32_t wsum[2][kDsThreads / kWave];
+    uint32_t* bmA = reinterpret_cast<uint32_t*>(bmA4);
+    uint32_t* bmT = reinterpret_cast<uint32_t*>(bmT4);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t row = blockIdx.x;
+    const int b = (int)(row / a.Tq);
+    uint32_t* hd = dec_hdr(a, row);
+    // the segment counts go out before the position arrives (always inside the header)
+    uint32_t ca = 0, ct = 0;
+    if (tid < kDecMaxSeg) { ca = hd[2 + tid]; ct = hd[2 + kDecMaxSeg + tid]; }
+    const int64_t n = visible_blocks(a, row);
+    int32_t* out = a.out + row * a.topk;
+    const uint32_t k = (uint32_t)a.topk;
+    if (n <= a.topk) {
+        for (int64_t i = tid; i < a.topk; i += kDsThreads) out[i] = i < n ? (int32_t)i : -1;
+        return;
+    }
+    const int nseg = (int)((n + kDfChunk - 1) / kDfChunk);
+    if (wv == 0) {                                                   // kDecMaxSeg <= 64: one wave
+        if (lane >= nseg) { ca = 0; ct = 0; }
+        const bool over = __ballot(ca > (uint32_t)kDfSegCands) != 0;
+        const uint32_t ia = wave_incl_scan_dpp(ca), it = wave_incl_scan_dpp(ct);
+        if (lane < kDecMaxSeg) { segoff[0][lane] = ia - ca; segoff[1][lane] = it - ct; }
+        if (lane == kWave - 1) { sh[0] = ia; sh[1] = it; sh[2] = over ? 1u : 0u; }
+    }
+    __syncthreads();
+    const uint32_t tot = sh[0], ttot = sh[1];
+    if (sh[2] || tot > (uint32_t)kIdxPfCands || tot + ttot < k) {
+        exact_row(a, b, row, n, out, bmA4, hist, sh, wsum[0]);
+        return;
+    }
+    // compaction: kDsThreads / kDecMaxSeg threads per segment, each copying
+    // every (that many)-th entry, loads batched four deep
+    {
+        constexpr int kTps = kDsThreads / kDecMaxSeg;
+        const int sg = tid / kTps, sub = tid % kTps;
+        const uint32_t c = sg < nseg ? min(hd[2 + sg], (uint32_t)kDfSegCands) : 0u, o = segoff[0][sg];
+        const uint2* src = dec_cand(a, row, sg);
+        for (uint32_t e0 = sub; e0 < c; e0 += 4 * kTps) {
+            uint2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t e = e0 + u * kTps;
+                v[u] = e < c ? src[e] : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if (e0 + u * kTps < c) cl[o + e0 + u * kTps] = v[u];
+        }
+    }
+    const int nwords = (int)((n + 31) / 32);
+    const int nw4 = (nwords + 3) / 4;
+    for (int i = tid; i < nw4; i += kDsThreads) {
+        bmA4[i] = make_uint4(0u, 0u, 0u, 0u);
+        bmT4[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int i = tid; i < 2048; i += kDsThreads) hist[i] = 0u;
+    __syncthreads();
+    uint2 cv[kDsCPT];
+#pragma unroll
+    for (int q = 0; q < kDsCPT; q++) {
+        const uint32_t i = tid + q * kDsThreads;
+        cv[q] = i < tot ? cl[i] : make_uint2(0u, 0u);
+    }
+    uint32_t needT;                                                  // ties to take
+    if (tot >= k) {
+        // the k-th largest key among those above T: range-adaptive radix
+        // passes until the range is one key
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+        for (int q = 0; q < kDsCPT; q++)
+            if (tid + q * kDsThreads < (int)tot) { mn = min(mn, cv[q].x); mx = max(mx, cv[q].x); }
+        block_minmax(mn, mx, mm);
+        uint32_t need = k, prefix = mn;
+        int width = bit_width(mx - mn);
+        while (width > 0)                                            // workgroup-uniform
+            span_pass<kDsThreads>([&](auto f) {
+#pragma unroll
+                for (int q = 0; q < kDsCPT; q++) f(cv[q].x, tid + q * kDsThreads < (int)tot);
+            }, prefix, width, need, hist, wsum[0], sh);
+        const uint32_t T1 = prefix;
+        needT = need;
+#pragma unroll
+        for (int q = 0; q < kDsCPT; q++) {
+            const uint2 c = cv[q];
+            if (tid + q * kDsThreads < (int)tot && c.x >= T1)
+                atomicOr(&(c.x > T1 ? bmA : bmT)[c.y >> 5], 1u << (c.y & 31));
+        }
+    } else {
+        // every key above T is in, and the (k - tot) smallest j of those at T
+        needT = k - tot;
+#pragma unroll
+        for (int q = 0; q < kDsCPT; q++)
+            if (tid + q * kDsThreads < (int)tot) atomicOr(&bmA[cv[q].y >> 5], 1u << (cv[q].y & 31));
+        for (int s = wv; s < nseg; s += kDsThreads / kWave) {
+            const uint32_t c = hd[2 + kDecMaxSeg + s];
+            const uint32_t* src = dec_ties(a, row, s);
+            for (uint32_t e0 = 0; e0 < c; e0 += 4 * kWave) {
+                uint32_t v[4];
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                    const uint32_t e = e0 + u * kWave + lane;
+                    v[u] = e < c ? src[e] : 0u;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; u++)
+                    if (e0 + u * kWave + lane < c) atomicOr(&bmT[v[u] >> 5], 1u << (v[u] & 31));
+            }
+        }
+    }
+    __syncthreads();
+    // thread t owns words [kDsWPT t, kDsWPT (t + 1)); words past nwords are not read
+    uint32_t am[kDsWPT], tm[kDsWPT];
+    const int w0 = tid * kDsWPT;
+#pragma unroll
+    for (int v = 0; v < kDsWPT / 4; v++) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u), y = x;
+        if (w0 + 4 * v < nwords) { x = bmA4[tid * (kDsWPT / 4) + v]; y = bmT4[tid * (kDsWPT / 4) + v]; }
+        am[4 * v] = x.x; am[4 * v + 1] = x.y; am[4 * v + 2] = x.z; am[4 * v + 3] = x.w;
+        tm[4 * v] = y.x; tm[4 * v + 1] = y.y; tm[4 * v + 2] = y.z; tm[4 * v + 3] = y.w;
+    }
+    uint32_t cnt_t = 0;
+#pragma unroll
+    for (int q = 0; q < kDsWPT; q++) cnt_t += __popc(tm[q]);
+    int rt = (int)block_exclusive_scan(cnt_t, wsum[0]);              // ties in the words before mine
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kDsWPT; q++) {
+        am[q] |= lowest_bits(tm[q], (int)needT - rt);
+        rt += __popc(tm[q]);
+        cnt += __popc(am[q]);
+    }
+    uint32_t off = block_exclusive_scan(cnt, wsum[1]);
+#pragma unroll
+    for (int q = 0; q < kDsWPT; q++) {
+        uint32_t bits = am[q];
+        while (bits) {
+            const int bpos = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (off < k) out[off] = (w0 + q) * 32 + bpos;
+            off++;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ launcher
 template <int QF, int KF>
 static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st) {
@@ -1569,6 +2016,17 @@ static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes
             hipLaunchKernelGGL(k_idxp_filter, dim3((unsigned)((a.Tq + kPfQB - 1) / kPfQB), B), dim3(kPfThreads), 0, st, a);
             hipLaunchKernelGGL(k_idxp_select, dim3((unsigned)a.Tq, B), dim3(kPfSelThreads), 0, st, a);
             hipLaunchKernelGGL(k_idxp_exact, dim3((unsigned)a.Tq, B), dim3(kPfThreads), 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (QF == CSA_FP4_E2M1 && KF == CSA_FP4_E2M1) {
+        if (idx_decode_eligible(a.di, a.Hi, a.Tq, a.cap, a.topk) && ws_bytes >= total_rows * idx_decode_row_bytes(a.cap)) {
+            a.row0 = 0;
+            a.rows = (int32_t)total_rows;
+            a.ws_row_bytes = idx_decode_row_bytes(a.cap);
+            hipLaunchKernelGGL(k_idxd_filter, dim3((unsigned)((a.cap + kDfChunk - 1) / kDfChunk), (unsigned)total_rows),
+                               dim3(kDfThreads), 0, st, a);
+            hipLaunchKernelGGL(k_idxd_select, dim3((unsigned)total_rows), dim3(kDsThreads), 0, st, a);
             return hipGetLastError();
         }
     }

@@ -79,7 +79,19 @@ inline bool idx_prefill_eligible(int32_t di, int32_t Hi, int32_t Tq, int64_t cap
     return di == 64 && Hi == 4 && Tq >= kIdxPfMinTq && cap > kIdxSmallMaxKeys && cap <= kIdxPfMaxCap &&
            topk <= kIdxPfMaxTopk;
 }
+// the decode path (short chunks, FP4 queries and keys, caps up to 2^18):
+// sampled thresholds, per-workgroup candidate segments, exact select
+constexpr int64_t kIdxDecMaxCap = (int64_t)1 << 18;
+inline bool idx_decode_eligible(int32_t di, int32_t Hi, int32_t Tq, int64_t cap, int32_t topk) {
+    return di == 64 && Hi == 4 && Tq < kIdxPfMinTq && cap > kIdxSmallMaxKeys && cap <= kIdxDecMaxCap &&
+           topk <= kIdxPfMaxTopk;
+}
 constexpr int64_t idx_prefill_row_bytes() { return 128 + (int64_t)kIdxPfCands * 8 + 8 * kIdxPfMaxTopk * 4; }
+// decode rows: a 1024-byte header, then per 4096-key segment 1024 (key, j)
+// slots, then per segment 4096 tie slots
+constexpr int64_t idx_decode_row_bytes(int64_t cap) {
+    return 1024 + (cap + 4095) / 4096 * (1024 * 8 + 4096 * 4);
+}
 hipError_t launch_indexer_topk(IndexerArgs a, int64_t total_rows, int64_t ws_bytes, hipStream_t st);
 
 // ---- attention

@@ -17,3 +17,14 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Print the error figures the parity tests achieved."""
+    from helpers import FIGURES
+    if not FIGURES:
+        return
+    terminalreporter.write_sep("-", "parity figures achieved")
+    for case, figs in FIGURES:
+        terminalreporter.write_line(case + ": " + ", ".join(
+            f"{k} {v:.3e}" if isinstance(v, float) else f"{k} {v}" for k, v in figs.items()))

@@ -37,6 +37,33 @@ def abs_err(got, ref):
     return float(np.max(np.abs(got - ref)))
 
 
+def norm_rel(got, ref):
+    """Normwise relative error ||got - ref||_2 / ||ref||_2."""
+    d = np.asarray(got, np.float64) - np.asarray(ref, np.float64)
+    return float(np.linalg.norm(d.ravel()) / max(np.linalg.norm(np.asarray(ref, np.float64).ravel()), 1e-300))
+
+
+# figures achieved by the parity tests, printed in pytest's terminal summary
+FIGURES = []
+
+
+def report(case, **figures):
+    """Record the achieved error figures of a parity case (and print them)."""
+    FIGURES.append((case, figures))
+    say(case, " ".join(f"{k}={v:.3e}" if isinstance(v, float) else f"{k}={v}" for k, v in figures.items()))
+
+
+# Bound on the normwise relative error of an attention output computed from
+# bf16 queries and bf16 / FP8 records: the kernel rounds the normalised,
+# rotated query to bf16, the probabilities P to bf16 for the P.V product,
+# split partials of O to bf16 (bf16 outputs), and the output to bf16: four
+# roundings of relative size at most u = 2^-8 each.  Independent rounding
+# errors add in quadrature over the many terms of every sum, so the normwise
+# error stays near sqrt(4) u = 7.8e-3; FP8 records are decoded exactly on
+# both sides and fp32 accumulation adds ~1e-6.
+BF16_NORM_REL = 1e-2
+
+
 def recall(got, ref):
     """mean over rows of |got & ref| / |ref| (ignoring -1 padding)."""
     vals = []

@@ -57,7 +57,8 @@ def test_prefill_trace_summary(tmp_path, capsys):
         t[0] += int(us * 1000) + 500
 
     for _ in range(3):                                 # decode steps before the section are ignored
-        k("csa::k_idx_zero(csa::IndexerArgs)", 2.5)
+        k("csa::k_idxd_filter(csa::IndexerArgs)", 2.5)
+        k("csa::k_idxd_select(csa::IndexerArgs)", 5.0)
         k("void csa::k_attn_mfma<512, 64, true, unsigned short>(csa::AttnArgs)", 20.0)
     k("void at::native::fill(float)", 5.0)             # framework kernels are ignored
     for i in range(4):
@@ -69,6 +70,10 @@ def test_prefill_trace_summary(tmp_path, capsys):
         k("void csa::k_attn_mfma<512, 64, true, unsigned short>(csa::AttnArgs)", us)
     for _ in range(4):
         k("void csa::k_proj_mfma<unsigned short>(csa::ProjArgs)", 550.0)
+    # the decode workloads measured after the section are ignored
+    k("void csa::k_compress<unsigned short>(csa::CompressArgs)", 30.0)
+    k("void csa::k_attn_mfma<512, 64, true, unsigned short>(csa::AttnArgs)", 40.0)
+    k("void csa::k_proj_mfma<unsigned short>(csa::ProjArgs)", 50.0)
     c.commit()
     c.close()
     bench.summarize_prefill(str(tmp_path))

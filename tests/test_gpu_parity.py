@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle as O
-from helpers import abs_err, dev, dev_bf16, host_bf16_bits, out_to_f64, recall, rel_err, say
+from helpers import (BF16_NORM_REL, abs_err, dev, dev_bf16, host_bf16_bits, norm_rel, out_to_f64, recall, rel_err,
+                     report, say)
 from long_context_attention_23_amd import api, synth
 
 pytestmark = pytest.mark.gpu
@@ -336,6 +337,31 @@ def test_indexer_prefill_fallback_rows_exact():
     assert np.array_equal(got[0, 5], np.arange(k))           # all tied: the first k blocks
 
 
+def test_indexer_decode_fallback_rows_exact():
+    """Decode rows (a few queries per sequence, FP4) that a sampled threshold
+    cannot serve, recomputed exactly: all weights zero (every key ties: more
+    ties than the lists hold), and keys of every 32-key tile whose index is a
+    multiple of ceil(tiles / 128) made to outrank the rest (a systematic
+    sample of such tiles ranks its threshold too high: too few candidates)."""
+    g = synth.rng(571)
+    B, Tq, Hi, di, m, k, cap = 2, 3, 4, 64, 4, 1024, 90000
+    kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
+    qc, qs = synth.fp4_rows(g, (B, Tq, Hi), di, -2, 0)
+    w = synth.grid(g, (B, Tq, Hi))
+    w[0, 1] = 0.0
+    qc[1, 2] = 0x22                                          # +1.0 in both nibbles
+    qs[1, 2] = 127
+    w[1, 2] = 1.0
+    stride = max(1, -(-(-(-cap // 32)) // 128))
+    for t0 in range(0, cap, stride * 32):
+        kc[1, t0:t0 + 32] = 0x77
+        ks[1, t0:t0 + 32] = 127
+    pos = np.array([[4 * cap - 1, 4 * cap - 1, 4 * 30000 + 1], [4 * 60000, 4 * cap - 1, 4 * cap - 1]], np.int32)
+    got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(got[0, 1], np.arange(k))           # all tied: the first k blocks
+
+
 def test_indexer_fp4_codes_exact():
     """FP4 keys and queries drawn as codes with a narrow exponent range: exact."""
     g = synth.rng(510)
@@ -457,11 +483,12 @@ def test_attention_parity(ci):
         topk = synth.topk_lists(g, vis, k, B * Tq).reshape(B, Tq, k)
         topk[..., -1] = np.where(topk[..., -1] >= 0, ccap + 5, -1)   # an invisible index is skipped
     got, ref = run_attention(sparse, q, qfmt, pos, topk, comp, cfmt, win, wfmt, gamma, sink, d, dr, W, m, ofmt)
-    say(f"rel {rel_err(got, ref):.3e} abs {abs_err(got, ref):.3e}")
+    report(f"attention c{ci}", max_rel=rel_err(got, ref), abs=abs_err(got, ref), norm_rel=norm_rel(got, ref))
     if ofmt == O.F32 and qfmt == O.F32 and cfmt == O.F32:
         assert rel_err(got, ref) <= 1e-4
     else:
         assert abs_err(got, ref) <= 2e-2
+        assert norm_rel(got, ref) <= BF16_NORM_REL
 
 
 @pytest.mark.parametrize("ci", [2, 4, 10])
@@ -483,7 +510,9 @@ def test_attention_split_workspace_holds_nan(ci):
     got, ref = run_attention(sparse, q, qfmt, pos, topk, comp, cfmt, win, cfmt, None, sink, d, dr, W, m, ofmt,
                              nan_ws=True)
     assert np.all(np.isfinite(got))
+    report(f"attention NaN workspace c{ci}", abs=abs_err(got, ref), norm_rel=norm_rel(got, ref))
     assert abs_err(got, ref) <= 2e-2
+    assert norm_rel(got, ref) <= BF16_NORM_REL
 
 
 @pytest.mark.parametrize("sink", [-np.inf, 0.0, 30.0])
@@ -517,6 +546,116 @@ def test_attention_deterministic_and_batch_invariant():
     w1 = api.KVCache(1, W + 8, d, dr, O.FP8_E4M3, ring=True, rec=dev(win[2:3]))
     c = api.hca_dense_mqa_attn(qb[2:3], dev(pos[2:3]), c1, w1, dev(sink), p)
     assert torch.equal(c[0].view(torch.int16), a[2].view(torch.int16))
+
+
+def test_sparse_attention_deterministic_and_batch_invariant():
+    """The CSA path (top-k lists, FP8 records, decode splits): two runs are
+    bitwise equal, and a sequence computed alone equals the same sequence
+    computed inside a batch."""
+    g = synth.rng(661)
+    B, Tq, H, d, dr, W, m, ccap, k = 3, 1, 64, 512, 64, 128, 4, 6000, 1024
+    comp, win = build_caches(g, B, ccap, W + 8, d, dr, O.FP8_E4M3, O.FP8_E4M3)
+    q = synth.normal(g, (B, Tq, H, d))
+    qb = dev_bf16((q.view(np.uint32) >> 16).astype(np.uint16))
+    pos = np.array([[m * ccap - 1], [m * 3000 + 1], [m * ccap + 17]], np.int32)
+    vis = np.minimum((pos.reshape(-1) + 1) // m, ccap)
+    topk = synth.topk_lists(g, vis, k, B * Tq).reshape(B, Tq, k)
+    sink = synth.normal(g, H)
+    p = api.attn_params(d, dr, W, m)
+    cc = api.KVCache(B, ccap, d, dr, O.FP8_E4M3, rec=dev(comp))
+    wc = api.KVCache(B, W + 8, d, dr, O.FP8_E4M3, ring=True, rec=dev(win))
+    say("sparse attention determinism / batch invariance")
+    a = api.sparse_mqa_attn(qb, dev(pos), dev(topk), cc, wc, dev(sink), p)
+    b = api.sparse_mqa_attn(qb, dev(pos), dev(topk), cc, wc, dev(sink), p)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for i in range(B):
+        c1 = api.KVCache(1, ccap, d, dr, O.FP8_E4M3, rec=dev(comp[i:i + 1]))
+        w1 = api.KVCache(1, W + 8, d, dr, O.FP8_E4M3, ring=True, rec=dev(win[i:i + 1]))
+        c = api.sparse_mqa_attn(qb[i:i + 1], dev(pos[i:i + 1]), dev(topk[i:i + 1]), c1, w1, dev(sink), p)
+        assert torch.equal(c[0].view(torch.int16), a[i].view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", [O.F32, O.BF16, O.FP8_E4M3])
+def test_sparse_with_every_block_equals_dense(fmt):
+    """CSA with a top-k list holding every visible block, in ascending order,
+    is the HCA dense attention at the same m (the full-top-k identity, GPU
+    against GPU).  Rows whose visible count equals k take identical entry
+    lists and must agree bit for bit; rows with fewer visible blocks than k
+    carry -1 padding and agree within rounding."""
+    g = synth.rng(662 + fmt)
+    B, Tq, H, d, dr, W, m, ccap = 2, 3, 64 if fmt != O.F32 else 8, 512 if fmt != O.F32 else 128, 64, 128, 4, 700
+    comp, win = build_caches(g, B, ccap, W + Tq + 7, d, dr, fmt, fmt)
+    q = synth.normal(g, (B, Tq, H, d))
+    qfmt = O.F32 if fmt == O.F32 else O.BF16
+    if qfmt == O.BF16:
+        qdev = dev_bf16((q.view(np.uint32) >> 16).astype(np.uint16))
+    else:
+        qdev = dev(q)
+    pos = np.array([[m * ccap - 1, m * ccap - 1, m * 300 + 2], [m * ccap - 1, 5, m * ccap + 40]], np.int32)
+    vis = np.minimum((pos + 1) // m, ccap)
+    k = ccap
+    topk = np.full((B, Tq, k), -1, np.int32)
+    for b in range(B):
+        for i in range(Tq):
+            topk[b, i, :vis[b, i]] = np.arange(vis[b, i])
+    sink = synth.normal(g, H)
+    p = api.attn_params(d, dr, W, m)
+    cc = api.KVCache(B, ccap, d, dr, fmt, rec=dev(comp))
+    wc = api.KVCache(B, W + Tq + 7, d, dr, fmt, ring=True, rec=dev(win))
+    say(f"full top-k vs dense fmt={fmt}")
+    od = torch.float32 if fmt == O.F32 else torch.bfloat16
+    sp = api.sparse_mqa_attn(qdev, dev(pos), dev(topk), cc, wc, dev(sink), p, out_dtype=od)
+    de = api.hca_dense_mqa_attn(qdev, dev(pos), cc, wc, dev(sink), p, out_dtype=od)
+    torch.cuda.synchronize()
+    full = torch.from_numpy(vis == k).cuda()
+    assert int(full.sum()) == 4
+    assert torch.equal(sp[full].float(), de[full].float())
+    a, b = out_to_f64(sp), out_to_f64(de)
+    report(f"full top-k vs dense fmt={fmt}", max_rel=rel_err(a, b), norm_rel=norm_rel(a, b))
+    if fmt == O.F32:
+        assert rel_err(a, b) <= 1e-5
+    else:
+        assert abs_err(a, b) <= 2e-2 and norm_rel(a, b) <= BF16_NORM_REL
+
+
+def test_relative_position_invariance_f32():
+    """Shifting every position by a multiple of m (the block structure kept)
+    leaves the CSA output unchanged: the caches are written by the GPU's own
+    compression at both offsets, the top-k lists shift by the same number of
+    blocks, and the outputs must agree to 1e-4 (f32)."""
+    g = synth.rng(663)
+    T, H, d, dr, W, m, k = 640, 8, 128, 64, 128, 4, 48
+    x = synth.normal(g, (1, T, d))
+    q = synth.normal(g, (1, 6, H, d))
+    gam = (1 + 0.3 * synth.normal(g, d)).astype(np.float32)
+    gk = (1 + 0.3 * synth.normal(g, d)).astype(np.float32)
+    b = synth.normal(g, m)
+    sink = synth.normal(g, H)
+    t = np.array([[W - 1, 200, 333, 401, 598, T - 1]], np.int32)
+    vis = (t.reshape(-1) + 1) // m
+    top0 = synth.topk_lists(g, vis, k, t.size).reshape(1, 6, k)
+    outs = []
+    for shift in (0, 4 * 250_000, 4 * 262_143):
+        nblk = (shift + T) // m
+        comp = api.KVCache(1, nblk, d, dr, O.F32)
+        win = api.KVCache(1, W + 8, d, dr, O.F32, ring=True)
+        say(f"position shift {shift}")
+        api.compress_kv(dev(x), dev(np.array([shift], np.int32)), m, dev(b), gamma=dev(gk), rope_dim=dr, kv_out=comp)
+        api.compress_kv(dev(x[:, T - W - 8:]), dev(np.array([shift + T - W - 8], np.int32)), 1,
+                        dev(np.zeros(1, np.float32)), gamma=dev(gk), rope_dim=dr, kv_out=win)
+        top = np.where(top0 >= 0, top0 + shift // m, -1).astype(np.int32)
+        # the window ring holds positions shift + T - W - 8 .. shift + T - 1: queries at the last
+        # position only see raw entries inside it; earlier queries see none of them beyond t
+        o = api.sparse_mqa_attn(dev(q[:, -1:]), dev(t[:, -1:] + shift), dev(top[:, -1:]), comp, win, dev(sink),
+                                api.attn_params(d, dr, W, m), gamma_q=dev(gam))
+        p0 = api.attn_params(d, dr, 0, m)
+        o2 = api.sparse_mqa_attn(dev(q[:, :-1]), dev(t[:, :-1] + shift), dev(top[:, :-1]), comp, win, dev(sink), p0,
+                                 gamma_q=dev(gam))
+        torch.cuda.synchronize()
+        outs.append(np.concatenate([out_to_f64(o2), out_to_f64(o)], axis=1))
+    for o in outs[1:]:
+        report("position shift (f32)", max_rel=rel_err(o, outs[0]))
+        assert rel_err(o, outs[0]) <= 1e-4
 
 
 # ====================================================================== projection
