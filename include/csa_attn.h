@@ -218,6 +218,27 @@ csa_status csa_indexer_topk(const void* q_idx, const uint8_t* q_idx_scales, int3
                             int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_indexer_topk_noalloc -- csa_indexer_topk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without the
+ * workspace, the same result, bit for bit.  The scratch is a static device
+ * array of 64 MiB in the library, one per GPU the library runs on, held until
+ * the process ends; its address is looked up (hipGetSymbolAddress) on the
+ * first call with each device current.  Nothing is allocated or freed.
+ * The array is shared by every call on that GPU and keeps the last call's
+ * contents (the kernels need no cleared scratch): calls that overlap on one
+ * GPU (different streams, different threads) race and must be serialised by
+ * the caller.
+ * Errors: those of csa_indexer_topk, and WORKSPACE when the call needs more
+ * than 64 MiB of scratch (csa_indexer_topk_workspace_size of the same
+ * arguments), HIP when the array's address cannot be taken.
+ * ------------------------------------------------------------------------- */
+csa_status csa_indexer_topk_noalloc(const void* q_idx, const uint8_t* q_idx_scales, int32_t q_dtype,
+                                    const float* w_idx, const csa_idx_cache* keys, const int32_t* q_pos,
+                                    int32_t B, int32_t Tq, int32_t Hi, int32_t m, int32_t topk,
+                                    int32_t* out_idx, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_sparse_mqa_attn -- CSA step 3 (peacm 3.2: multi-query attention over
  * the top-k blocks) with the four tricks (query RMSNorm, partial RoPE with
  * the -i output RoPE, the raw window, the sink logit).

@@ -17,6 +17,7 @@ CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_CAPACITY, CSA_ERR_WORK
 STATUS = {CSA_OK: "CSA_OK", CSA_ERR_INVALID_ARG: "CSA_ERR_INVALID_ARG", CSA_ERR_UNSUPPORTED: "CSA_ERR_UNSUPPORTED",
           CSA_ERR_CAPACITY: "CSA_ERR_CAPACITY", CSA_ERR_WORKSPACE: "CSA_ERR_WORKSPACE", CSA_ERR_HIP: "CSA_ERR_HIP"}
 EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_compress_kv_batch", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
+           "csa_indexer_topk_noalloc",
            "csa_attn_workspace_size", "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "attn_out_proj_grouped",
            "csa_last_error"]
 
@@ -74,6 +75,9 @@ def lib():
         L.csa_indexer_topk.restype = C.c_int
         L.csa_indexer_topk.argtypes = [_V, _V, _I32, _V, C.POINTER(IdxCacheT), _V, _I32, _I32, _I32, _I32,
                                        _I32, _V, _V, _SZ, _V]
+        L.csa_indexer_topk_noalloc.restype = C.c_int
+        L.csa_indexer_topk_noalloc.argtypes = [_V, _V, _I32, _V, C.POINTER(IdxCacheT), _V, _I32, _I32, _I32, _I32,
+                                               _I32, _V, _V]
         L.csa_attn_workspace_size.restype = _SZ
         L.csa_attn_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I64, _I32, _I32, _I32]
         L.csa_sparse_mqa_attn.restype = C.c_int
@@ -205,6 +209,17 @@ def indexer_topk(q_idx, q_dtype, w_idx, keys, q_pos, m, topk, *, q_scales=None, 
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().csa_indexer_topk(_ptr(q_idx), _ptr(q_scales), q_dtype, _ptr(w_idx), C.byref(keys.struct()),
                                   _ptr(q_pos), B, Tq, Hi, m, topk, _ptr(out), _ptr(workspace), wsb, _stream(stream)))
+    return out
+
+
+def indexer_topk_noalloc(q_idx, q_dtype, w_idx, keys, q_pos, m, topk, *, q_scales=None, out=None, stream=None):
+    """csa_indexer_topk_noalloc: as indexer_topk, with the library's static
+    scratch in place of a workspace (the output is the caller's)."""
+    B, Tq, Hi = w_idx.shape
+    if out is None:
+        out = torch.empty((B, Tq, topk), dtype=torch.int32, device=w_idx.device)
+    _check(lib().csa_indexer_topk_noalloc(_ptr(q_idx), _ptr(q_scales), q_dtype, _ptr(w_idx), C.byref(keys.struct()),
+                                          _ptr(q_pos), B, Tq, Hi, m, topk, _ptr(out), _stream(stream)))
     return out
 
 

@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -320,6 +321,54 @@ CSA_API csa_status csa_indexer_topk(const void* q_idx, const uint8_t* q_idx_scal
     const int64_t per = batch > kMaxGridY ? kMaxGridY : batch;
     return hip_status(csa::launch_indexer_topk(a, rows, per * a.ws_row_bytes, static_cast<hipStream_t>(stream)),
                       "indexer launch");
+}
+
+// ---- the indexer without a caller workspace: a static device array
+// (kNoAllocScratchBytes on every GPU the library runs on, held until the
+// process ends) takes the workspace's place.  Its address is taken once per
+// device with hipGetSymbolAddress, on the first call with that device
+// current; in host code the array's name is not a device address.
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+csa_status scratch_address(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CSA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(CSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA_OK;
+}
+}  // namespace
+
+CSA_API csa_status csa_indexer_topk_noalloc(const void* q_idx, const uint8_t* q_idx_scales, int32_t q_dtype,
+                                            const float* w_idx, const csa_idx_cache* keys, const int32_t* q_pos,
+                                            int32_t B, int32_t Tq, int32_t Hi, int32_t m, int32_t topk,
+                                            int32_t* out_idx, void* stream) {
+    if (!keys) return fail(CSA_ERR_INVALID_ARG, "keys is null");
+    const size_t need = csa_indexer_topk_workspace_size(B, Tq, keys->cap, topk);
+    if (need > kNoAllocScratchBytes)
+        return fail(CSA_ERR_WORKSPACE, "the call needs %zu bytes of scratch; the static scratch holds %zu", need,
+                    kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if (need > 0) {
+        const csa_status st = scratch_address(&ws);
+        if (st != CSA_OK) return st;
+    }
+    return csa_indexer_topk(q_idx, q_idx_scales, q_dtype, w_idx, keys, q_pos, B, Tq, Hi, m, topk, out_idx, ws,
+                            need > 0 ? kNoAllocScratchBytes : 0, stream);
 }
 
 CSA_API size_t csa_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t head_dim, int64_t max_comp_entries,

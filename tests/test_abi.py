@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     assert sorted(names) == sorted(api.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -247,3 +247,14 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         api.lib()
+
+
+def test_indexer_noalloc_rejects_beyond_its_scratch(L):
+    """The call needing more than the 64 MiB static scratch is refused before
+    any HIP call (100 decode rows at 262,144 keys need about 150 MiB)."""
+    need = L.csa_indexer_topk_workspace_size(100, 1, 262144, 1024)
+    assert need > 64 << 20
+    st = L.csa_indexer_topk_noalloc(FAKE, FAKE, api.FP4_E2M1, FAKE, C.byref(idx(cap=262144)), FAKE, 100, 1, 4, 4,
+                                    1024, FAKE, None)
+    msg = L.csa_last_error().decode()
+    assert st == WSP and str(need) in msg, (st, msg)
