@@ -290,10 +290,13 @@ csa_status hca_dense_mqa_attn(const void* q, int32_t q_dtype, const int32_t* q_p
  * consecutively, no bias:
  *   y[r][g*(D/G) + i] = sum_c o[r][g*(Hd/G) + c] * W[g][i][c]
  * o: [M][Hd] (o_dtype F32 / BF16), W: [G][D/G][Hd/G] (w_dtype, same as
- * o_dtype), y: [M][D] (y_dtype F32 / BF16).  fp32 accumulation, no split
- * of the reduction across workgroups; any Hd/G (widths that are not a whole
- * number of 16-byte vectors, or 32-wide slabs for bf16 with M > 16, take a
- * scalar kernel).
+ * o_dtype), y: [M][D] (y_dtype F32 / BF16).  fp32 accumulation in a fixed
+ * order, no split of the reduction across workgroups; any Hd/G (widths that
+ * are not a whole number of 16-byte vectors, or of 32-wide slabs for bf16
+ * with M > 4, take a scalar kernel).  Rows are computed independently, so a
+ * row's result does not depend on the other rows; the order of its fp32 sum
+ * (hence its last bits) depends on M's size class only: M <= 4, M <= 128
+ * (bf16), larger.
  * Errors: INVALID_ARG (sizes < 1, M < 0, Hd % G, D % G, null pointers with
  * M > 0), UNSUPPORTED (dtypes, M beyond the grid limit), HIP.
  * ------------------------------------------------------------------------- */

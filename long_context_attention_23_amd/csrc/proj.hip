@@ -19,6 +19,8 @@
 //     dimension in KC-wide slabs staged in LDS.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -237,6 +239,103 @@ static bool launch_gemv(const ProjArgs& a, hipStream_t st) {
     return true;
 }
 
+// ---- skinny bf16 projection on the matrix cores (4 < M <= 128 rows)
+// A weight stream with a few activation rows: one workgroup per 16 output
+// columns of one group, all M rows in blocks of 16 (v_mfma_f32_16x16x32_bf16:
+// A = 16 activation rows x 32 k, B = 32 k x 16 weight rows).  The four waves
+// split the group width into quarters; each streams its quarter of the 16
+// weight rows straight into registers, KB K-steps per batch (every load of a
+// batch in flight before its products), and re-reads the activation
+// fragments per K-step (the M rows of o are a few hundred KB, resident in
+// L2).  The parts' sums meet in LDS and are added in wave order, so the
+// result depends neither on timing nor on M.
+constexpr int kSkWaves = 4;                      // waves per workgroup at most
+constexpr int64_t kSkMaxM = 128;                // rows handled by the skinny kernel
+typedef __bf16 bf16x8_s __attribute__((ext_vector_type(8)));
+typedef float f32x4_s __attribute__((ext_vector_type(4)));
+
+template <int MB, typename YT>
+__global__ __launch_bounds__(64 * kSkWaves) void k_proj_skinny(ProjArgs a) {
+    constexpr int KB = MB <= 2 ? 16 : (MB <= 4 ? 8 : 4);   // K-steps per load batch
+    __shared__ f32x4_s part[kSkWaves][MB][64];
+    const int dg = a.D / a.G, cg = a.Hd / a.G;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (int)(blockDim.x >> 6);
+    const int nbk = (dg + 15) / 16;              // 16-column blocks per group
+    const int g = (int)(blockIdx.x / nbk), nb = (int)(blockIdx.x % nbk);
+    const int l16 = lane & 15, kq = 8 * (lane >> 4);
+    const int n = nb * 16 + l16;
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W) + ((size_t)g * dg + min(n, dg - 1)) * cg + kq;
+    const uint16_t* o = reinterpret_cast<const uint16_t*>(a.o) + (size_t)g * cg + kq;
+    const int nks = cg / 32;
+    const int kper = (nks + nw - 1) / nw;
+    const int kb0 = w * kper, kb1 = min(nks, kb0 + kper);     // this wave's K-steps
+    typedef unsigned v4u_s __attribute__((ext_vector_type(4)));
+    f32x4_s acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[mb] = f32x4_s{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = kb0; k0 < kb1; k0 += KB) {
+        bf16x8_s bf[KB], af[MB][KB];
+#pragma unroll
+        for (int u = 0; u < KB; u++) {
+            const bool kin = k0 + u < kb1;
+            const v4u_s v = kin ? __builtin_nontemporal_load(reinterpret_cast<const v4u_s*>(W + (size_t)(k0 + u) * 32))
+                                : v4u_s{0u, 0u, 0u, 0u};
+            bf[u] = __builtin_bit_cast(bf16x8_s, v);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+            const int m = mb * 16 + l16;
+#pragma unroll
+            for (int u = 0; u < KB; u++) {
+                const bool in = m < a.M && k0 + u < kb1;
+                const uint4 v = in ? *reinterpret_cast<const uint4*>(o + (size_t)m * a.Hd + (size_t)(k0 + u) * 32)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+                af[mb][u] = __builtin_bit_cast(bf16x8_s, v);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < KB; u++)
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mb][u], bf[u], acc[mb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) part[w][mb][lane] = acc[mb];
+    __syncthreads();
+    if (w != 0) return;
+    // lane l holds rows 4 (l / 16) + i of each block, column l % 16
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+        f32x4_s r = part[0][mb][lane];
+        for (int q = 1; q < nw; q++) r += part[q][mb][lane];
+        if (n < dg) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int m = mb * 16 + 4 * (lane >> 4) + i;
+                if (m < a.M) st_scalar<YT>(reinterpret_cast<YT*>(a.y), (size_t)m * a.D + (size_t)g * dg + n, r[i]);
+            }
+        }
+    }
+}
+
+template <typename YT>
+static bool try_skinny(const ProjArgs& a, hipStream_t st) {
+    const int cg = a.Hd / a.G, dg = a.D / a.G;
+    if (a.fmt != CSA_BF16 || a.M <= 4 || a.M > kSkMaxM || cg % 32) return false;
+    if (((uintptr_t)a.o | (uintptr_t)a.W) & 15) return false;
+    const unsigned grid = (unsigned)((int64_t)a.G * ((dg + 15) / 16));
+    // the group width split over up to kSkWaves waves, about 16 K-steps (one
+    // load batch) each; fixed by the width alone, so a row's sum order does
+    // not depend on M
+    const int nw = (int)std::min<int64_t>(kSkWaves, std::max<int64_t>(1, (cg / 32 + 15) / 16));
+    const dim3 blk(64 * nw);
+    if (a.M <= 16) hipLaunchKernelGGL((k_proj_skinny<1, YT>), dim3(grid), blk, 0, st, a);
+    else if (a.M <= 32) hipLaunchKernelGGL((k_proj_skinny<2, YT>), dim3(grid), blk, 0, st, a);
+    else if (a.M <= 64) hipLaunchKernelGGL((k_proj_skinny<4, YT>), dim3(grid), blk, 0, st, a);
+    else hipLaunchKernelGGL((k_proj_skinny<8, YT>), dim3(grid), blk, 0, st, a);
+    return true;
+}
+
 // ---- bf16 GEMM on the matrix cores (M > 16)
 // y_g[m][n] = sum_c o[m][g cg + c] W[g][n][c]: both operands are read along
 // the reduction dimension, which is what the A (rows of o) and B (rows of W)
@@ -402,6 +501,9 @@ static bool try_gemv(const ProjArgs& a, hipStream_t st) {
 
 template <typename T, typename YT>
 static void launch_t(const ProjArgs& a, hipStream_t st) {
+    if constexpr (sizeof(T) == 2) {
+        if (try_skinny<YT>(a, st)) return;
+    }
     if (try_gemv<T, YT>(a, st)) return;
     if constexpr (sizeof(T) == 2) {
         if (try_mfma<YT>(a, st)) return;

@@ -669,7 +669,11 @@ def test_relative_position_invariance_f32():
                                            (300, 16, 128, 1024, 8, O.BF16), (40, 8, 64, 1600, 8, O.BF16),
                                            (17, 4, 32, 96, 4, O.BF16), (600, 64, 512, 7168, 8, O.BF16),
                                            # group widths that are not a whole 16-byte vector (scalar kernel)
-                                           (5, 3, 20, 60, 3, O.BF16), (45, 3, 20, 60, 3, O.BF16)])
+                                           (5, 3, 20, 60, 3, O.BF16), (45, 3, 20, 60, 3, O.BF16),
+                                           # the skinny matrix-core path (4 < M <= 64): row blocks of 16
+                                           # with a ragged last block, ragged 16-column blocks
+                                           (33, 8, 256, 520, 4, O.BF16), (64, 16, 128, 1024, 8, O.BF16),
+                                           (32, 32, 512, 4096, 8, O.BF16)])
 def test_projection_parity(M, H, d, D, G, fmt):
     g = synth.rng(700 + M)
     Hd = H * d
