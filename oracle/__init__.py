@@ -90,6 +90,10 @@ def _declare(L):
                                 _P, C.c_int, C.c_long, _P, C.c_int, C.c_long, _P, C.c_int, _P, _P, _P]
     L.orc_out_proj.restype = None
     L.orc_out_proj.argtypes = [_P, _P, C.c_long, C.c_int, C.c_int, C.c_int, _P]
+    L.orc_fp8_rows_quant.restype = None
+    L.orc_fp8_rows_quant.argtypes = [_P, C.c_long, C.c_int, _P, _P]
+    L.orc_linear_fp8.restype = None
+    L.orc_linear_fp8.argtypes = [_P, C.c_long, C.c_int, _P, _P, C.c_int, C.c_int, _P]
 
 
 def _p(a):
@@ -315,3 +319,51 @@ def out_proj(o, W):
     y = np.empty((M, G * dg))
     lib().orc_out_proj(_p(o), _p(W), M, Hd, G * dg, G, _p(y))
     return y
+
+
+# ---------------------------------------------------------- FP8-weight projections
+def fp8_rows_quant(W):
+    """W [N][K] float -> (codes [N][K] uint8, scale [N] float32): per-row E4M3
+    weights (weight preparation for tests, not a step of the path)."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    codes = np.empty((N, K), np.uint8)
+    scale = np.empty(N, np.float32)
+    lib().orc_fp8_rows_quant(_p(W), N, K, _p(codes), _p(scale))
+    return codes, scale
+
+
+def linear_fp8(x, W, scale, G=1):
+    """x [M][K] fp64 values, W [N][K/G] E4M3 codes, scale [N] -> y [M][N] fp64."""
+    x = _c(x, np.float64)
+    W = _c(W, np.uint8)
+    scale = _c(scale, np.float32)
+    M, K = x.shape
+    N = W.shape[0]
+    assert W.shape[1] * G == K and N % G == 0 and scale.shape == (N,)
+    y = np.empty((M, N))
+    lib().orc_linear_fp8(_p(x), M, K, _p(W), _p(scale), N, G, _p(y))
+    return y
+
+
+def layer_in_proj(h, Wq, sq, Wkv, skv, WkI, skI, WqI, sqI, Ww, sw, Hi):
+    """The input projections of one layer from hidden states h [M][D] (values):
+    q = h Wq^T, kv = h Wkv^T (the raw KV token), kI = h WkI^T (the raw indexer
+    key), qI = h WqI^T, w = h Ww^T, every weight FP8 with per-row scales.
+    Roundings of the outputs (the formats the next steps take): the projected
+    value as an fp32 number, then q, kv, kI to bf16 (nearest even), w kept in
+    fp32, qI quantised to FP4 per head row of di values by the indexer-key
+    rule of fp4_quant_row.  Returns (q bf16 bits, kv bits, kI bits, qI codes
+    [M][Hi][di/2], qI scales [M][Hi][di/32], w float32 [M][Hi])."""
+    f32 = lambda W, s: linear_fp8(h, W, s).astype(np.float32)
+    q, kv, kI = (bf16_encode(f32(W, s)) for W, s in ((Wq, sq), (Wkv, skv), (WkI, skI)))
+    w = f32(Ww, sw)
+    qI = f32(WqI, sqI)
+    M = qI.shape[0]
+    di = qI.shape[1] // Hi
+    codes = np.empty((M, Hi, di // 2), np.uint8)
+    scales = np.empty((M, Hi, di // 32), np.uint8)
+    for r in range(M):
+        for hh in range(Hi):
+            codes[r, hh], scales[r, hh] = fp4_quant_row(qI[r, hh * di:(hh + 1) * di])
+    return q, kv, kI, codes, scales, w

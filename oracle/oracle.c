@@ -621,3 +621,51 @@ ORC_API void orc_out_proj(const double* o, const double* W, long M, int Hd, int 
                 y[(size_t)r * D + (size_t)g * dg + i] = s;
             }
 }
+
+/* ======================================================================
+ * Projections with FP8 weights.  The pages fix the precision of every
+ * parameter outside the MoE experts as FP8 ("DeepSeek-V4 preview review"
+ * (deepseek.csdn.net), section 6.2 on precision and deployment; "DeepSeek V4
+ * (Flash & Pro)" (github wiki article), specification table: FP4 + FP8 mixed
+ * precision).  They say nothing of the scaling granularity or of the
+ * activations.  Reading: a weight matrix is stored as E4M3 codes with one
+ * fp32 scale per output row (value = e4m3(code) * scale, the per-row rule of
+ * the FP8 KV records); activations are not quantised; no bias.
+ * ====================================================================== */
+
+/* Preparing weights (test input generation, not a step of the path): row n of
+ * W [N][K] gets scale = max|W[n][:]| / 448 as an fp32 number (1 for an
+ * all-zero row) and codes = nearest E4M3 of W[n][c] / scale. */
+ORC_API void orc_fp8_rows_quant(const float* W, long N, int K, uint8_t* codes, float* scale) {
+    for (long n = 0; n < N; n++) {
+        double amax = 0.0;
+        for (int c = 0; c < K; c++) {
+            double a = fabs((double)W[(size_t)n * K + c]);
+            if (a > amax) amax = a;
+        }
+        float s = amax > 0.0 ? (float)(amax / 448.0) : 1.0f;
+        scale[n] = s;
+        for (int c = 0; c < K; c++)
+            codes[(size_t)n * K + c] = orc_e4m3_encode((float)((double)W[(size_t)n * K + c] / (double)s));
+    }
+}
+
+/* A projection with FP8 weights, G groups of consecutive rows (G = 1: a dense
+ * map, as the input projections; G > 1: the block-diagonal grouped output
+ * projection of CSA step 4):
+ *   y[r][g*(N/G) + i] = scale[g*(N/G) + i]
+ *                       * sum_c x[r][g*(K/G) + c] * e4m3(W[g*(N/G) + i][c])
+ * x [M][K], W [N][K/G] codes, scale [N], y [M][N]. */
+ORC_API void orc_linear_fp8(const double* x, long M, int K, const uint8_t* W, const float* scale, int N,
+                            int G, double* y) {
+    int ng = N / G, kg = K / G;
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < M; r++)
+        for (int n = 0; n < N; n++) {
+            int g = n / ng;
+            double s = 0.0;
+            for (int c = 0; c < kg; c++)
+                s += x[(size_t)r * K + (size_t)g * kg + c] * orc_e4m3_decode(W[(size_t)n * kg + c]);
+            y[(size_t)r * N + n] = (double)scale[n] * s;
+        }
+}
