@@ -304,6 +304,61 @@ csa_status attn_out_proj_grouped(const void* o, int32_t o_dtype, const void* W, 
                                  int64_t M, int32_t Hd, int32_t D, int32_t G, void* y,
                                  int32_t y_dtype, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * csa_linear_fp8 -- a projection with FP8 weights.  The pages store every
+ * parameter outside the MoE experts in FP8 ("DeepSeek-V4 preview review"
+ * (deepseek.csdn.net), section 6.2; "DeepSeek V4 (Flash & Pro)" (github wiki
+ * article), specification table: FP4 + FP8 mixed precision).  Reading: E4M3
+ * codes with one fp32 scale per output row, activations not quantised, no
+ * bias, G groups of consecutive rows (G = 1 a dense map; G > 1 the
+ * block-diagonal grouped output projection of CSA step 4):
+ *   y[r][g*(N/G) + i] = w_scale[g*(N/G) + i]
+ *                       * sum_c x[r][g*(K/G) + c] * e4m3(W[g*(N/G) + i][c])
+ * x: [M][K] bf16 (x_dtype CSA_BF16), W: [N][K/G] E4M3 codes (0x7F / 0xFF are
+ * NaN), w_scale: f32 [N], y: [M][N] in y_dtype (F32 / BF16, nearest even).
+ * The products are exact (every E4M3 value is a bf16 number) and summed in
+ * fp32 in a fixed order with no split across workgroups; the row scale
+ * multiplies the sum.  Rows are independent; the order of a row's sum, hence
+ * its last bits, depends on M's size class only (M <= 64, larger).
+ * Errors: INVALID_ARG (sizes < 1, M < 0, K % G, N % G, null pointers with
+ * M > 0), UNSUPPORTED (x not bf16, y not F32 / BF16, K/G not a multiple of
+ * 64, x or W not 16-byte aligned, shapes beyond one launch's grid), HIP.
+ * ------------------------------------------------------------------------- */
+csa_status csa_linear_fp8(const void* x, int32_t x_dtype, int64_t M, int32_t K, const uint8_t* W,
+                          const float* w_scale, int32_t N, int32_t G, void* y, int32_t y_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * csa_layer_in_proj -- the input projections of one CSA layer from its hidden
+ * states, one FP8-weight product for all of them (weights as in
+ * csa_linear_fp8, one dense map each; the pages name the outputs, not their
+ * maps: the queries of the core attention, the KV token that CSA step 1
+ * compresses and the window keeps, the lightning indexer's queries, head
+ * weights and key token).
+ * h: [M][D] bf16 (h_dtype CSA_BF16).  W: [N][D] E4M3 codes, w_scale: f32
+ * [N], with N = H*d + d + di + Hi*di + Hi and the rows in this order:
+ *   q     : H*d rows  -> q     [M][H][d]   bf16  (input of the attention)
+ *   kv    : d rows    -> kv    [M][d]      bf16  (raw token of csa_compress_kv)
+ *   k_idx : di rows   -> k_idx [M][di]     bf16  (raw indexer-key token)
+ *   q_idx : Hi*di rows-> q_idx [M][Hi][di/2] FP4 codes, q_idx_scales
+ *                        [M][Hi][di/32] E8M0 (csa_indexer_topk's FP4 queries)
+ *   w_idx : Hi rows   -> w_idx [M][Hi]     f32   (indexer head weights)
+ * Each output is the projected value as an fp32 sum times the row scale,
+ * then rounded: bf16 nearest even; q_idx quantised per head row of di values
+ * by the indexer-key FP4 rule of csa_compress_kv (blocks of 32 with
+ * e = floor(log2 amax) - 2 raised to at least (row max e) - 14, E2M1 codes
+ * nearest even, saturating at +-6).
+ * workspace: csa_layer_in_proj_workspace_size(M, Hi, di) bytes, 4-byte
+ * aligned (the fp32 indexer queries before quantisation); need not be zeroed.
+ * Errors: those of csa_linear_fp8 (K = D, G = 1), INVALID_ARG (H, d, di or
+ * Hi < 1, null outputs), UNSUPPORTED (di not a multiple of 32 or > 256),
+ * WORKSPACE, HIP.
+ * ------------------------------------------------------------------------- */
+size_t csa_layer_in_proj_workspace_size(int64_t M, int32_t Hi, int32_t di);
+csa_status csa_layer_in_proj(const void* h, int32_t h_dtype, int64_t M, int32_t D, const uint8_t* W,
+                             const float* w_scale, int32_t H, int32_t d, int32_t di, int32_t Hi, void* q,
+                             void* kv, void* k_idx, uint8_t* q_idx, uint8_t* q_idx_scales, float* w_idx,
+                             void* workspace, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* csa_last_error(void);
 

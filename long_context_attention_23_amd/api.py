@@ -19,7 +19,7 @@ STATUS = {CSA_OK: "CSA_OK", CSA_ERR_INVALID_ARG: "CSA_ERR_INVALID_ARG", CSA_ERR_
 EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_compress_kv_batch", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
            "csa_indexer_topk_noalloc",
            "csa_attn_workspace_size", "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "attn_out_proj_grouped",
-           "csa_last_error"]
+           "csa_linear_fp8", "csa_layer_in_proj_workspace_size", "csa_layer_in_proj", "csa_last_error"]
 
 
 class CsaError(RuntimeError):
@@ -88,6 +88,13 @@ def lib():
                                          C.POINTER(AttnParamsT), _I32, _I32, _I32, _V, _I32, _V, _SZ, _V]
         L.attn_out_proj_grouped.restype = C.c_int
         L.attn_out_proj_grouped.argtypes = [_V, _I32, _V, _I32, _I64, _I32, _I32, _I32, _V, _I32, _V]
+        L.csa_linear_fp8.restype = C.c_int
+        L.csa_linear_fp8.argtypes = [_V, _I32, _I64, _I32, _V, _V, _I32, _I32, _V, _I32, _V]
+        L.csa_layer_in_proj_workspace_size.restype = _SZ
+        L.csa_layer_in_proj_workspace_size.argtypes = [_I64, _I32, _I32]
+        L.csa_layer_in_proj.restype = C.c_int
+        L.csa_layer_in_proj.argtypes = [_V, _I32, _I64, _I32, _V, _V, _I32, _I32, _I32, _I32, _V, _V, _V, _V, _V,
+                                        _V, _V, _SZ, _V]
         _lib = L
     return _lib
 
@@ -276,3 +283,43 @@ def out_proj_grouped(o, W, *, y=None, y_dtype=None, stream=None):
     _check(lib().attn_out_proj_grouped(_ptr(o), torch_dtype_code(o), _ptr(W), torch_dtype_code(W), M, Hd, D, G,
                                        _ptr(y), torch_dtype_code(y), _stream(stream)))
     return y
+
+
+def linear_fp8(x, W, w_scale, *, G=1, y=None, y_dtype=None, stream=None):
+    """csa_linear_fp8.  x: [M, K] bf16; W: [N, K/G] uint8 E4M3 codes; w_scale: [N] f32.
+    Returns y [M, N] (bf16 unless y or y_dtype says otherwise)."""
+    M, K = x.shape
+    N = W.shape[0]
+    if y is None:
+        y = torch.empty((M, N), dtype=y_dtype or torch.bfloat16, device=x.device)
+    _check(lib().csa_linear_fp8(_ptr(x), torch_dtype_code(x), M, K, _ptr(W), _ptr(w_scale), N, G, _ptr(y),
+                                torch_dtype_code(y), _stream(stream)))
+    return y
+
+
+def layer_in_proj_workspace_size(M, Hi, di):
+    return int(lib().csa_layer_in_proj_workspace_size(M, Hi, di))
+
+
+def layer_in_proj(h, W, w_scale, H, d, di, Hi, *, out=None, workspace=None, stream=None):
+    """csa_layer_in_proj.  h: [M, D] bf16; W: [H*d + d + di + Hi*di + Hi, D] E4M3 codes
+    (rows q | kv | k_idx | q_idx | w_idx); w_scale: f32 per row.  Returns a dict
+    q [M, H, d] bf16, kv [M, d] bf16, k_idx [M, di] bf16, q_idx [M, Hi, di/2] uint8,
+    q_idx_scales [M, Hi, di/32] uint8, w_idx [M, Hi] f32."""
+    M, D = h.shape
+    dev = h.device
+    if out is None:
+        out = dict(q=torch.empty((M, H, d), dtype=torch.bfloat16, device=dev),
+                   kv=torch.empty((M, d), dtype=torch.bfloat16, device=dev),
+                   k_idx=torch.empty((M, di), dtype=torch.bfloat16, device=dev),
+                   q_idx=torch.empty((M, Hi, di // 2), dtype=torch.uint8, device=dev),
+                   q_idx_scales=torch.empty((M, Hi, max(di // 32, 1)), dtype=torch.uint8, device=dev),
+                   w_idx=torch.empty((M, Hi), dtype=torch.float32, device=dev))
+    ws_bytes = layer_in_proj_workspace_size(M, Hi, di)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    _check(lib().csa_layer_in_proj(_ptr(h), torch_dtype_code(h), M, D, _ptr(W), _ptr(w_scale), H, d, di, Hi,
+                                   _ptr(out["q"]), _ptr(out["kv"]), _ptr(out["k_idx"]), _ptr(out["q_idx"]),
+                                   _ptr(out["q_idx_scales"]), _ptr(out["w_idx"]), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

@@ -6,7 +6,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libcsa_attn.so")
-SOURCES = ["api.hip", "compress.hip", "indexer.hip", "attn.hip", "attn_mfma.hip", "proj.hip"]
+SOURCES = ["api.hip", "compress.hip", "indexer.hip", "attn.hip", "attn_mfma.hip", "proj.hip", "lin8.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",

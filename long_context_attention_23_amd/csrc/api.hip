@@ -423,3 +423,87 @@ CSA_API csa_status attn_out_proj_grouped(const void* o, int32_t o_dtype, const v
     a.y_fmt = y_dtype;
     return hip_status(csa::launch_proj(a, static_cast<hipStream_t>(stream)), "projection launch");
 }
+
+namespace {
+
+// shape checks shared by the FP8-weight projections
+csa_status check_lin8(const void* x, int32_t x_dtype, int64_t M, int32_t K, const uint8_t* W, const float* w_scale,
+                      int64_t N, int32_t G) {
+    if (M < 0 || K < 1 || N < 1 || G < 1) return fail(CSA_ERR_INVALID_ARG, "bad sizes M=%lld K=%d N=%lld G=%d", (long long)M, K, (long long)N, G);
+    if (K % G || N % G) return fail(CSA_ERR_INVALID_ARG, "K %d and N %lld must be multiples of G %d", K, (long long)N, G);
+    if (N > 0x7fffffff) return fail(CSA_ERR_UNSUPPORTED, "N=%lld too large", (long long)N);
+    if (x_dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "x dtype %d (bf16 activations only)", x_dtype);
+    if ((K / G) % 64) return fail(CSA_ERR_UNSUPPORTED, "group width K/G=%d is not a multiple of 64", K / G);
+    if (M > 0 && (!x || !W || !w_scale)) return fail(CSA_ERR_INVALID_ARG, "x / W / w_scale is null");
+    if (M > 0 && (!aligned16(x) || !aligned16(W))) return fail(CSA_ERR_UNSUPPORTED, "x and W must be 16-byte aligned");
+    const int64_t grid = M <= csa::kLinSkinnyMaxM ? (int64_t)G * ((N / G + 15) / 16) : csa::lin8_max_tiles(M, (int32_t)N, G);
+    if (grid > 0x7fffffff) return fail(CSA_ERR_UNSUPPORTED, "M=%lld N=%lld too large for one launch", (long long)M, (long long)N);
+    return CSA_OK;
+}
+
+}  // namespace
+
+CSA_API csa_status csa_linear_fp8(const void* x, int32_t x_dtype, int64_t M, int32_t K, const uint8_t* W,
+                                  const float* w_scale, int32_t N, int32_t G, void* y, int32_t y_dtype, void* stream) {
+    const csa_status st = check_lin8(x, x_dtype, M, K, W, w_scale, N, G);
+    if (st != CSA_OK) return st;
+    if (!is_act_fmt(y_dtype)) return fail(CSA_ERR_UNSUPPORTED, "y dtype %d", y_dtype);
+    if (M > 0 && !y) return fail(CSA_ERR_INVALID_ARG, "y is null");
+    csa::LinArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.G = G;
+    a.W = W;
+    a.scale = w_scale;
+    a.nseg = 1;
+    a.seg[0] = csa::LinSeg{0, y_dtype, N, y};
+    return hip_status(csa::launch_lin8(a, static_cast<hipStream_t>(stream)), "fp8 projection launch");
+}
+
+CSA_API size_t csa_layer_in_proj_workspace_size(int64_t M, int32_t Hi, int32_t di) {
+    if (M < 0 || Hi < 1 || di < 1) return 0;
+    return (size_t)M * Hi * di * sizeof(float);
+}
+
+CSA_API csa_status csa_layer_in_proj(const void* h, int32_t h_dtype, int64_t M, int32_t D, const uint8_t* W,
+                                     const float* w_scale, int32_t H, int32_t d, int32_t di, int32_t Hi, void* q,
+                                     void* kv, void* k_idx, uint8_t* q_idx, uint8_t* q_idx_scales, float* w_idx,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+    if (H < 1 || d < 1 || di < 1 || Hi < 1) return fail(CSA_ERR_INVALID_ARG, "bad sizes H=%d d=%d di=%d Hi=%d", H, d, di, Hi);
+    const int64_t nq = (int64_t)H * d, nqi = (int64_t)Hi * di;
+    const int64_t N = nq + d + di + nqi + Hi;
+    const csa_status st = check_lin8(h, h_dtype, M, D, W, w_scale, N, 1);
+    if (st != CSA_OK) return st;
+    if (di % 32 || di > 256) return fail(CSA_ERR_UNSUPPORTED, "di=%d: FP4 queries need a multiple of 32, at most 256", di);
+    if (M > 0 && (!q || !kv || !k_idx || !q_idx || !q_idx_scales || !w_idx))
+        return fail(CSA_ERR_INVALID_ARG, "an output pointer is null");
+    const size_t need = csa_layer_in_proj_workspace_size(M, Hi, di);
+    if (M > 0 && (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 3u)))
+        return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes (need %zu, 4-byte aligned)", ws_bytes, need);
+    if (M == 0) return ok();
+    csa::LinArgs a{};
+    a.x = static_cast<const uint16_t*>(h);
+    a.M = M;
+    a.K = D;
+    a.N = (int32_t)N;
+    a.G = 1;
+    a.W = W;
+    a.scale = w_scale;
+    a.nseg = 5;
+    int32_t n0 = 0;
+    a.seg[0] = csa::LinSeg{n0, CSA_BF16, nq, q};
+    n0 += (int32_t)nq;
+    a.seg[1] = csa::LinSeg{n0, CSA_BF16, d, kv};
+    n0 += d;
+    a.seg[2] = csa::LinSeg{n0, CSA_BF16, di, k_idx};
+    n0 += di;
+    a.seg[3] = csa::LinSeg{n0, CSA_F32, nqi, workspace};
+    n0 += (int32_t)nqi;
+    a.seg[4] = csa::LinSeg{n0, CSA_F32, Hi, w_idx};
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = csa::launch_lin8(a, s);
+    if (e == hipSuccess) e = csa::launch_fp4_rows(static_cast<const float*>(workspace), M * Hi, di, q_idx, q_idx_scales, s);
+    return hip_status(e, "input projection launch");
+}

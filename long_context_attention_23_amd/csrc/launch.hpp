@@ -165,4 +165,29 @@ struct ProjArgs {
 };
 hipError_t launch_proj(const ProjArgs& a, hipStream_t st);
 
+// ---- projections with FP8 weights (csa_linear_fp8, csa_layer_in_proj)
+// Output columns [n0, next segment's n0) go to out[m * ld + (n - n0)] in fmt
+// (CSA_F32 or CSA_BF16); segments sorted by n0, the first at 0.
+constexpr int kLinMaxSeg = 5;
+constexpr int64_t kLinSkinnyMaxM = 64;   // rows handled by the weight-stream kernel
+struct LinSeg {
+    int32_t n0;
+    int32_t fmt;
+    int64_t ld;
+    void* out;
+};
+struct LinArgs {
+    const uint16_t* x;          // [M][K] bf16
+    int64_t M;
+    int32_t K, N, G;
+    const uint8_t* W;           // [N][K/G] E4M3 codes
+    const float* scale;         // [N]
+    int32_t nseg;
+    LinSeg seg[kLinMaxSeg];
+};
+hipError_t launch_lin8(const LinArgs& a, hipStream_t st);
+int64_t lin8_max_tiles(int64_t M, int32_t N, int32_t G);
+// FP4 quantisation of rows of n f32 values (the indexer-key rule)
+hipError_t launch_fp4_rows(const float* x, int64_t rows, int n, uint8_t* codes, uint8_t* scales, hipStream_t st);
+
 }  // namespace csa

@@ -77,3 +77,24 @@ def fp8_records(g, prefix, d, dr, rec_bytes):
     scale = (np.abs(normal(g, prefix)) * np.float32(0.01) + np.float32(1e-3)).astype(np.float32)
     out[..., dn + 2 * dr:dn + 2 * dr + 4] = scale.view(np.uint8).reshape(prefix + (4,))
     return out
+
+
+def e4m3_codes(g, shape, std=64.0):
+    """FP8 weight codes: a normal draw times std, clipped to +-448 and cast to
+    E4M3 by torch's float8_e4m3fn conversion (a format cast), as uint8."""
+    import torch
+    x = np.clip(normal(g, shape, std), -448.0, 448.0).astype(np.float32)
+    return torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+# E4M3 codes of 0, 0.25, 0.5 and 1 (exponent field 5, 6, 7; mantissa 0)
+E4M3_POW2 = np.array([0x00, 0x28, 0x30, 0x38], np.uint8)
+
+
+def e4m3_pow2_codes(g, shape, p_zero=0.5):
+    """FP8 weight codes drawn from {0, +-0.25, +-0.5, +-1}: products with grid
+    activations and their fp32 sums stay exact (zero with probability p_zero)."""
+    mag = g.integers(1, 4, size=shape)
+    mag = np.where(g.random(size=shape) < p_zero, 0, mag)
+    sign = (g.integers(0, 2, size=shape) * 0x80).astype(np.uint8)
+    return (E4M3_POW2[mag] | np.where(mag > 0, sign, 0)).astype(np.uint8)

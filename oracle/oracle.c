@@ -659,7 +659,7 @@ ORC_API void orc_fp8_rows_quant(const float* W, long N, int K, uint8_t* codes, f
 ORC_API void orc_linear_fp8(const double* x, long M, int K, const uint8_t* W, const float* scale, int N,
                             int G, double* y) {
     int ng = N / G, kg = K / G;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for collapse(2) schedule(static)
     for (long r = 0; r < M; r++)
         for (int n = 0; n < N; n++) {
             int g = n / ng;

@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     assert sorted(names) == sorted(api.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -258,3 +258,51 @@ def test_indexer_noalloc_rejects_beyond_its_scratch(L):
                                     1024, FAKE, None)
     msg = L.csa_last_error().decode()
     assert st == WSP and str(need) in msg, (st, msg)
+
+
+@pytest.mark.parametrize("args,code,frag", [
+    ((FAKE, 1, 0, 7168, FAKE, FAKE, 32768, 1, FAKE, 1), OK, ""),            # M = 0: nothing to do
+    ((FAKE, 0, 4, 7168, FAKE, FAKE, 32768, 1, FAKE, 1), UNS, "bf16 activations"),
+    ((FAKE, 1, 4, 7168, FAKE, FAKE, 32768, 7, FAKE, 1), INV, "multiples"),
+    ((FAKE, 1, 4, 7200, FAKE, FAKE, 32768, 1, FAKE, 1), UNS, "multiple of 64"),
+    ((FAKE, 1, 4, 32768, FAKE, FAKE, 7168, 8, FAKE, 2), UNS, "y dtype"),
+    ((None, 1, 4, 7168, FAKE, FAKE, 32768, 1, FAKE, 1), INV, "is null"),
+    ((FAKE, 1, 4, 7168, FAKE, None, 32768, 1, FAKE, 1), INV, "is null"),
+    ((FAKE, 1, 4, 7168, FAKE, FAKE, 32768, 1, None, 1), INV, "y is null"),
+    ((C.c_void_p(4104), 1, 4, 7168, FAKE, FAKE, 32768, 1, FAKE, 1), UNS, "aligned"),
+    ((FAKE, 1, -1, 7168, FAKE, FAKE, 32768, 1, FAKE, 1), INV, "bad sizes"),
+    ((FAKE, 1, 4, 7168, FAKE, FAKE, 0, 1, FAKE, 1), INV, "bad sizes"),
+])
+def test_linear_fp8_validation(L, args, code, frag):
+    st, msg = status_and_msg(L, L.csa_linear_fp8(*args, None))
+    assert st == code and frag in msg, (st, msg)
+
+
+def in_proj(L, **over):
+    a = dict(h=FAKE, h_dtype=api.BF16, M=4, D=7168, W=FAKE, s=FAKE, H=64, d=512, di=64, Hi=4, q=FAKE, kv=FAKE,
+             ki=FAKE, qi=FAKE, qs=FAKE, w=FAKE, ws=FAKE, ws_bytes=4 * 4 * 64 * 4)
+    a.update(over)
+    return status_and_msg(L, L.csa_layer_in_proj(*a.values(), None))
+
+
+@pytest.mark.parametrize("over,code,frag", [
+    (dict(M=0), OK, ""),
+    (dict(H=0), INV, "bad sizes"),
+    (dict(di=48), UNS, "multiple of 32"),
+    (dict(di=288), UNS, "at most 256"),
+    (dict(D=7000), UNS, "multiple of 64"),
+    (dict(h_dtype=api.F32), UNS, "bf16"),
+    (dict(qs=None), INV, "null"),
+    (dict(w=None), INV, "null"),
+    (dict(ws_bytes=4 * 4 * 64 * 4 - 1), WSP, "need 4096"),
+    (dict(ws=None), WSP, "workspace"),
+    (dict(ws=C.c_void_p(4098)), WSP, "aligned"),
+])
+def test_layer_in_proj_validation(L, over, code, frag):
+    st, msg = in_proj(L, **over)
+    assert st == code and frag in msg, (st, msg)
+
+
+def test_layer_in_proj_workspace_size(L):
+    assert L.csa_layer_in_proj_workspace_size(4, 4, 64) == 4 * 4 * 64 * 4
+    assert L.csa_layer_in_proj_workspace_size(-1, 4, 64) == 0
