@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill-chunk measurement")
     ap.add_argument("--prefill-only", action="store_true", help="only the prefill-chunk measurement (for profiling)")
     ap.add_argument("--no-decode-configs", action="store_true", help="skip the HCA b16 / CSA b32 decode workloads")
+    ap.add_argument("--no-layer-proj", action="store_true", help="skip the FP8-weight projection measurement")
+    ap.add_argument("--layer-proj-only", action="store_true", help="only the FP8-weight projections (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-prefill-seconds", type=float, default=25.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -499,6 +501,81 @@ def decode_configs_measure(torch, api, reps=20, seed=6006):
     return res
 
 
+def layer_proj_measure(torch, api, reps=20, seed=7007):
+    """The projections either side of the attention with FP8 weights (E4M3
+    codes, one f32 scale per output row; bf16 activations), at the 1M model
+    widths (hidden 7168, 64 heads x 512, indexer 4 x 64):
+      in_proj : csa_layer_in_proj, one launch for q, the raw KV token, the
+                raw indexer key, the FP4 indexer queries and the head weights
+                (33,604 weight rows), plus the FP4 quantisation of the queries;
+      out_proj: csa_linear_fp8, the grouped output projection 32768 -> 7168
+                in 8 groups.
+    At a 4-sequence decode step (M = 4: weight streams, HBM-bound; caches
+    evicted before each run by a 1 GiB read) and at the 8,192-token prefill
+    chunk (matrix-core bound: bf16 MFMA on the widened weights)."""
+    dev = "cuda"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    flush_buf = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    flush_out = torch.empty((), dtype=torch.int64, device=dev)
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_out)
+
+    def codes(n, k):
+        x = (torch.randn(n, k, generator=gen, device=dev) * 64.0).clamp_(-448.0, 448.0)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    N_in = H * D_HEAD + D_HEAD + DI + HI * DI + HI
+    K_out = H * D_HEAD
+    W_in, s_in = codes(N_in, HIDDEN), torch.full((N_in,), 1e-3, device=dev)
+    W_out, s_out = codes(HIDDEN, K_out // G), torch.full((HIDDEN,), 1e-3, device=dev)
+    res = {"weights_MB": {"in_proj": round(N_in * HIDDEN / 1e6, 2), "out_proj": round(HIDDEN * K_out // G / 1e6, 2)}}
+    for name, M in (("decode_b4", B), ("prefill_chunk_8192", PF_T)):
+        h = (torch.randn(M, HIDDEN, generator=gen, device=dev)).to(torch.bfloat16)
+        o = (torch.randn(M, K_out, generator=gen, device=dev) * 0.05).to(torch.bfloat16)
+        out = dict(q=torch.empty((M, H, D_HEAD), dtype=torch.bfloat16, device=dev),
+                   kv=torch.empty((M, D_HEAD), dtype=torch.bfloat16, device=dev),
+                   k_idx=torch.empty((M, DI), dtype=torch.bfloat16, device=dev),
+                   q_idx=torch.empty((M, HI, DI // 2), dtype=torch.uint8, device=dev),
+                   q_idx_scales=torch.empty((M, HI, DI // 32), dtype=torch.uint8, device=dev),
+                   w_idx=torch.empty((M, HI), dtype=torch.float32, device=dev))
+        ws = torch.empty(api.layer_in_proj_workspace_size(M, HI, DI), dtype=torch.uint8, device=dev)
+        y = torch.empty((M, HIDDEN), dtype=torch.bfloat16, device=dev)
+
+        def fin():
+            api.layer_in_proj(h, W_in, s_in, H, D_HEAD, DI, HI, out=out, workspace=ws)
+
+        def fout():
+            api.linear_fp8(o, W_out, s_out, G=G, y=y)
+
+        decode = M <= 64
+        t_in = _timed(torch, fin, reps, flush if decode else None)
+        t_out = _timed(torch, fout, reps, flush if decode else None)
+        r = {"rows": M, "in_proj_ms": _pctl(t_in), "out_proj_ms": _pctl(t_out)}
+        mi, mo = float(np.median(t_in)), float(np.median(t_out))
+        if decode:
+            bytes_in = N_in * HIDDEN + 4 * N_in + M * HIDDEN * 2 + M * (H * D_HEAD * 2 + D_HEAD * 2 + DI * 2 +
+                                                                        HI * DI // 2 + HI * DI // 32 + HI * 4) \
+                + 2 * M * HI * DI * 4
+            bytes_out = HIDDEN * K_out // G + 4 * HIDDEN + M * K_out * 2 + M * HIDDEN * 2
+            r["algo_MB"] = {"in_proj": round(bytes_in / 1e6, 2), "out_proj": round(bytes_out / 1e6, 2)}
+            r["GBs"] = {"in_proj": round(bytes_in / (mi * 1e-3) / 1e9, 1),
+                        "out_proj": round(bytes_out / (mo * 1e-3) / 1e9, 1)}
+            r["frac_hbm"] = {k: round(v / HBM_PEAK_GBS, 4) for k, v in r["GBs"].items()}
+        else:
+            f_in, f_out = 2.0 * M * HIDDEN * N_in, 2.0 * M * K_out // G * HIDDEN
+            r["tflop"] = {"in_proj": round(f_in / 1e12, 3), "out_proj": round(f_out / 1e12, 3)}
+            r["tflops"] = {"in_proj": round(f_in / (mi * 1e-3) / 1e12, 1),
+                           "out_proj": round(f_out / (mo * 1e-3) / 1e12, 1)}
+            r["frac_bf16_peak"] = {k: round(v / BF16_PEAK_TFLOPS, 4) for k, v in r["tflops"].items()}
+        res[name] = r
+        del h, o, out, ws, y
+    res["timing"] = (f"HIP events, median (p10, p90) of {reps} runs; decode runs with L2 and the last-level "
+                     "cache evicted before each (a 1 GiB read)")
+    return res
+
+
 def capture_step_graphs(torch, fns, sets, sh):
     """One HIP graph per rotated buffer set, each holding one whole decode step
     (every call's kernels, in order).  The calls allocate nothing and issue no
@@ -856,6 +933,9 @@ def main():
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_measure(torch, api)}), flush=True)
         return
+    if args.layer_proj_only:
+        print(json.dumps({"layer_proj_fp8": layer_proj_measure(torch, api)}), flush=True)
+        return
     sets, sh = build_state(torch, api, args.copies)
     R = len(sets)
     fns = call_fns(api)
@@ -949,6 +1029,9 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_decode_configs:
         res["decode_configs"] = decode_configs_measure(torch, api)
+        torch.cuda.empty_cache()
+    if not args.no_layer_proj:
+        res["layer_proj_fp8"] = layer_proj_measure(torch, api)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         if not args.no_prefill:

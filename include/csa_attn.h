@@ -319,7 +319,8 @@ csa_status attn_out_proj_grouped(const void* o, int32_t o_dtype, const void* W, 
  * The products are exact (every E4M3 value is a bf16 number) and summed in
  * fp32 in a fixed order with no split across workgroups; the row scale
  * multiplies the sum.  Rows are independent; the order of a row's sum, hence
- * its last bits, depends on M's size class only (M <= 64, larger).
+ * its last bits, depends only on the weight shape and on M's size class
+ * (M <= 32, M <= 64, larger).  Activations are finite numbers.
  * Errors: INVALID_ARG (sizes < 1, M < 0, K % G, N % G, null pointers with
  * M > 0), UNSUPPORTED (x not bf16, y not F32 / BF16, K/G not a multiple of
  * 64, x or W not 16-byte aligned, shapes beyond one launch's grid), HIP.

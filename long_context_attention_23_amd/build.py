@@ -43,7 +43,7 @@ def build_library(verbose=False, jobs=None):
     if failed:
         raise RuntimeError("hipcc failed for: " + ", ".join(failed))
     tmp = LIB_PATH + ".tmp"
-    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = ["hipcc", "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH

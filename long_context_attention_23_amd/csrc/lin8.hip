@@ -13,17 +13,19 @@
 // the bf16 matrix cores; the row scale is applied to the fp32 sum.  Weights
 // cross HBM as one byte each, which is what the decode shapes are bound by.
 //
-// Two kernels, each keeping every reduction inside one workgroup:
-//   M <= 64 (decode): a weight stream.  A workgroup owns 16 NB output columns
-//     of one group; its four waves split the group width into quarters, each
-//     streams its quarter of the weight rows into registers and multiplies
+// Three kernels, each keeping every reduction inside one workgroup:
+//   M <= 32 (decode): a weight stream.  A workgroup owns 16 output columns of
+//     one group; its waves split the group width, each copies its share of
+//     the 16 weight rows global -> LDS in 128-byte row runs and multiplies
 //     with v_mfma_f32_16x16x32_bf16 (A = 16 activation rows, B = 16 weight
-//     rows); the four partial sums meet in LDS and are added in wave order;
+//     rows); the partial sums meet in LDS and are added in wave order;
+//   32 < M <= 64: the same split with the weights loaded straight into
+//     registers, 32 output columns per workgroup;
 //   M > 64 (prefill): a GEMM with 256 x 128 tiles (v_mfma_f32_32x32x16_bf16),
 //     the reduction walked in 32-wide slabs copied global -> LDS, the weight
 //     bytes widened when each wave reads its fragments.
-// Both order a row's sum by the group width alone, so a row's result does not
-// depend on the other rows; the two kernels order it differently.
+// A row's sum is ordered by the weight shape and M's size class alone, so a
+// row's result does not depend on the other rows.
 // The epilogue multiplies by the row scale and writes each output column to
 // the segment that owns it (the fused input projection writes five outputs
 // from one launch).
@@ -70,7 +72,7 @@ __device__ __forceinline__ void lin_store(const SegSel& s, int64_t m, int n, flo
     else reinterpret_cast<float*>(s.out)[off] = v;
 }
 
-// ---- decode: the weight stream (M <= 64)
+// ---- 32 < M <= 64: the weight stream into registers
 // K-mapping of one 64-wide "double step": lane group q = lane / 16 owns
 // reduction indices 16 q .. 16 q + 15 of the step; the first product takes
 // the lower eight of them, the second the upper eight.  A lane's weight bytes
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(64 * kL8Waves) void k_lin8_skinny(LinArgs a) {
         for (int u = 0; u < KB; u++)
 #pragma unroll
             for (int nb = 0; nb < NB; nb++)
-                wv[nb][u] = s0 + u < d1 ? __builtin_nontemporal_load(reinterpret_cast<const v4u_l*>(wp[nb] + (size_t)(s0 + u) * 64))
+                wv[nb][u] = s0 + u < d1 ? *reinterpret_cast<const v4u_l*>(wp[nb] + (size_t)(s0 + u) * 64)
                                         : v4u_l{0u, 0u, 0u, 0u};
         bf16x8_l af[MB][KB][2];
 #pragma unroll
@@ -147,6 +149,165 @@ __global__ __launch_bounds__(64 * kL8Waves) void k_lin8_skinny(LinArgs a) {
 #pragma unroll
         for (int v = 1; v < kL8Waves; v++) r += part[v][b][lane];
         const int c = c0 + 16 * nb + l16;
+        if (c < ng) {
+            const int n = g * ng + c;
+            const float sc = a.scale[n];
+            const SegSel sg = lin_seg(a, n);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int64_t m = 16 * mb + 4 * q + i;
+                if (m < a.M) lin_store(sg, m, n, r[i] * sc);
+            }
+        }
+    }
+}
+
+// ---- decode, M <= 32: the weight stream through LDS
+// The same products as above (16 output columns per workgroup, the group
+// width split over four waves, partial sums added in wave order), with the
+// weights copied global -> LDS (non-temporal: nothing re-reads them) in runs
+// of 128 bytes per row: one 2 KB slab = 16 rows x 2 double steps per wave,
+// two slabs in flight per wave, each wave on a ring of its own, so no barrier
+// in the loop.  A plain 16-byte load per lane in the matrix-core layout would
+// touch only 64 bytes of each row per instruction.  Slab row r keeps its
+// chunks (16 bytes) in a permuted order (st_swz) so that the fragment reads
+// of the 16 rows hit 16 different bank groups.  The activation fragments of
+// slab s + 1 are loaded while slab s is multiplied, through a buffer
+// resource: rows past M read as zero without touching memory.  Load order
+// per iteration: activations of slab s + 1, then the weight copies of slab
+// s + 2.  (Measured on the 4-row, 7168 x 33,604 input projection: 128-byte
+// runs with six workgroups per CU beat 256-byte runs with three.)
+constexpr int kStSD = 2;                        // double steps per slab
+constexpr int kStStages = 3;
+constexpr int kStMaxMB = 2;
+constexpr int64_t kLinStreamMaxM = 16 * kStMaxMB;
+
+// slot permutation of a slab row (CPR chunks): the fragment reads of rows
+// 0..15 at one chunk land in 16 different 16-byte bank groups
+template <int CPR>
+__device__ __forceinline__ int st_swz(int r) { return (r * CPR / 16) % CPR; }
+
+template <int MB, int NW>
+__global__ __launch_bounds__(64 * NW) void k_lin8_stream(LinArgs a) {
+    constexpr int SD = kStSD, ST = kStStages;
+    constexpr int kCPR = 4 * SD;                 // 16-byte chunks per slab row
+    constexpr int kNI = SD;                      // 1 KB copies per slab
+    constexpr int kSlab = 1024 * kNI;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NW][ST][kSlab];
+    static_assert(sizeof(f32x4_l) * NW * MB * 64 <= sizeof(ring), "partial sums reuse the ring");
+    const int ng = a.N / a.G, kg = a.K / a.G;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int tiles = (ng + 15) / 16;
+    const int g = (int)(blockIdx.x / tiles), c0 = (int)(blockIdx.x % tiles) * 16;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int nds = kg / 64, per = (nds + NW - 1) / NW;
+    const int d0 = min(nds, w * per), d1 = min(nds, d0 + per);
+    const int nsl = (d1 - d0 + SD - 1) / SD;
+    // copy i of a slab fills slots 64 i + lane: slab row r = slot / kCPR gets
+    // its chunk c = (slot % kCPR) ^ swz(r) (double step c / 4, 16-byte part
+    // c % 4); swz spreads the fragment reads of the 16 rows over 16 bank groups
+    const uint8_t* wsrc[kNI];
+    int wdu[kNI];
+#pragma unroll
+    for (int i = 0; i < kNI; i++) {
+        const int slot = 64 * i + lane, r = slot / kCPR, c = (slot % kCPR) ^ st_swz<kCPR>(r);
+        const int n = min(c0 + r, ng - 1);
+        wsrc[i] = a.W + ((size_t)g * ng + n) * kg + 16 * (c & 3);
+        wdu[i] = c >> 2;
+    }
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto issue = [&](int sl, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kNI; i++) {
+            const int ds = min(d0 + sl * SD + wdu[i], d1 - 1);
+            __builtin_amdgcn_global_load_lds(wsrc[i] + (size_t)ds * 64, (lds_void*)(&ring[w][buf][0] + 1024 * i), 16,
+                                             0, 2);                // non-temporal
+        }
+    };
+    // activations through a buffer resource over x (M K bf16, below 2 GiB:
+    // checked by the launcher); a row past M gets an offset past the end and
+    // reads zero, with no memory access and no branch
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, (int)(a.M * a.K * 2), 0x00020000);
+    bf16x8_l af[2][MB][SD][2];
+    auto load_act = [&](int sl, bf16x8_l (&dst)[MB][SD][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) {
+            const int m = 16 * mb + l16;
+#pragma unroll
+            for (int u = 0; u < SD; u++) {
+                // a double step past the range re-reads the last one (it meets
+                // zero weights below)
+                const int ds = min(d0 + sl * SD + u, d1 - 1);
+                const int off = m < a.M ? 2 * (m * a.K + g * kg + ds * 64 + 16 * q) : 0x7FFFFFF0;
+                dst[mb][u][0] = __builtin_bit_cast(bf16x8_l, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+                dst[mb][u][1] = __builtin_bit_cast(bf16x8_l, __builtin_amdgcn_raw_buffer_load_b128(xr, off + 16, 0, 0));
+            }
+        }
+    };
+    f32x4_l acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[mb] = f32x4_l{0.0f, 0.0f, 0.0f, 0.0f};
+    // Every step issues its loads unconditionally (addresses clamped to the
+    // wave's last valid slab, whose re-reads hit L2), so the loop is straight
+    // code; a slab past the range meets zero weights.  Then the only loads
+    // issued after slab s's activations are the copies of slab s + 1, and
+    // vmcnt(copies per slab) is exact.
+    int buf = 0;
+    if (nsl > 0) {
+        issue(0, 0);
+        load_act(0, af[0]);
+#pragma unroll
+        for (int b = 1; b < ST - 1; b++) issue(b, b);
+    }
+    // one slab: af_cur holds its activations, af_nxt receives the next slab's
+    auto step = [&](int sl, bf16x8_l (&af_cur)[MB][SD][2], bf16x8_l (&af_nxt)[MB][SD][2])
+        __attribute__((always_inline)) {
+        // nothing of the previous slab may move below this point: the
+        // scheduler would otherwise hoist the wait above its products
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kNI);                   // vmcnt: only the copies of slab s + 1 in flight
+        load_act(sl + 1, af_nxt);
+        // the copies of slab s + 2 overwrite the buffer of slab s - 1: its
+        // fragment reads must have completed (the compiler may interleave
+        // them with this step)
+        __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0)
+        issue(sl + ST - 1, buf == 0 ? ST - 1 : buf - 1);
+        const uint8_t* base = &ring[w][buf][0];
+#pragma unroll
+        for (int u = 0; u < SD; u++) {
+            // a double step past the wave's range (its copies re-read the last
+            // valid step) multiplies zero weights
+            const bool live = d0 + sl * SD + u < d1;
+            v4u_l fw = *reinterpret_cast<const v4u_l*>(base + 16 * (kCPR * l16 + ((4 * u + q) ^ st_swz<kCPR>(l16))));
+            fw = live ? fw : v4u_l{0u, 0u, 0u, 0u};
+            const bf16x8_l b0 = e4m3x8_to_bf16x8(fw[0], fw[1]);
+            const bf16x8_l b1 = e4m3x8_to_bf16x8(fw[2], fw[3]);
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++) {
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af_cur[mb][u][0], b0, acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af_cur[mb][u][1], b1, acc[mb], 0, 0, 0);
+            }
+        }
+        buf = buf == ST - 1 ? 0 : buf + 1;
+    };
+    // two slabs per trip, so the activation buffers are named statically
+    for (int sl = 0; sl < nsl; sl += 2) {
+        step(sl, af[0], af[1]);
+        step(sl + 1, af[1], af[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);                              // drain the trailing copies
+    __syncthreads();                             // every wave is done with its ring
+    f32x4_l (*part)[MB][64] = reinterpret_cast<f32x4_l (*)[MB][64]>(&ring[0][0][0]);
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) part[w][mb][lane] = acc[mb];
+    __syncthreads();
+    // wave v finishes row block v (lane l: rows 4 (l / 16) + i, column l % 16)
+    for (int mb = w; mb < MB; mb += NW) {
+        f32x4_l r = part[0][mb][lane];
+#pragma unroll
+        for (int v = 1; v < NW; v++) r += part[v][mb][lane];
+        const int c = c0 + l16;
         if (c < ng) {
             const int n = g * ng + c;
             const float sc = a.scale[n];
@@ -349,9 +510,14 @@ static void launch_skinny(const LinArgs& a, hipStream_t st) {
 
 hipError_t launch_lin8(const LinArgs& a, hipStream_t st) {
     if (a.M == 0) return hipSuccess;
-    if (a.M <= 16) launch_skinny<1, 1, 8>(a, st);
-    else if (a.M <= 32) launch_skinny<2, 2, 4>(a, st);
-    else if (a.M <= kLinSkinnyMaxM) launch_skinny<4, 2, 2>(a, st);
+    if (a.M <= kLinStreamMaxM && a.M * a.K * 2 < ((int64_t)1 << 31)) {
+        const int ng = a.N / a.G;
+        const unsigned grid = (unsigned)((int64_t)a.G * ((ng + 15) / 16));
+        // (splitting the group width over eight waves for small grids was
+        // measured slower on the 32768 -> 7168 grouped projection)
+        if (a.M <= 16) hipLaunchKernelGGL((k_lin8_stream<1, kL8Waves>), dim3(grid), dim3(64 * kL8Waves), 0, st, a);
+        else hipLaunchKernelGGL((k_lin8_stream<2, kL8Waves>), dim3(grid), dim3(64 * kL8Waves), 0, st, a);
+    } else if (a.M <= kLinSkinnyMaxM) launch_skinny<4, 2, 2>(a, st);
     else {
         const int ng = a.N / a.G;
         const int64_t tiles = (int64_t)a.G * ((a.M + kL8BM - 1) / kL8BM) * ((ng + kL8BN - 1) / kL8BN);

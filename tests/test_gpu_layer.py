@@ -107,16 +107,20 @@ def test_linear_fp8_parity(case, out):
 
 
 def test_linear_fp8_rows_independent_of_batch():
-    """A row's bits depend only on the row and the size class (M <= 64,
-    larger): rows of one call equal the same rows computed in other calls."""
+    """A row's bits depend only on the row, the weights and M's size class
+    (M <= 32, M <= 64, larger): rows of one call equal the same rows computed
+    in other calls of the same class, for a small and a large grid."""
     g = synth.rng(3150)
-    K, N = 1024, 96
-    xb = synth.bf16_bits(g, (300, K))
-    W = synth.e4m3_codes(g, (N, K))
-    s = np.full(N, 1e-3, np.float32)
-    full_small = run_linear(xb[:64], W, s, 1, torch.float32)
-    for M in (1, 5, 17, 33):
-        assert np.array_equal(run_linear(xb[:M], W, s, 1, torch.float32), full_small[:M]), M
+    xb = synth.bf16_bits(g, (300, 1024))
+    for K, N in ((1024, 96), (1024, 20000)):
+        W = synth.e4m3_codes(g, (N, K))
+        s = np.full(N, 1e-3, np.float32)
+        ref32 = run_linear(xb[:32], W, s, 1, torch.float32)
+        for M in (1, 5, 17):
+            assert np.array_equal(run_linear(xb[:M], W, s, 1, torch.float32), ref32[:M]), (N, M)
+        ref64 = run_linear(xb[:64], W, s, 1, torch.float32)
+        for M in (33, 50):
+            assert np.array_equal(run_linear(xb[:M], W, s, 1, torch.float32), ref64[:M]), (N, M)
     full_big = run_linear(xb, W, s, 1, torch.float32)
     for lo, hi in ((0, 65), (100, 300), (37, 290)):
         assert np.array_equal(run_linear(np.ascontiguousarray(xb[lo:hi]), W, s, 1, torch.float32), full_big[lo:hi])
