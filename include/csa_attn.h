@@ -112,7 +112,19 @@ typedef struct {
  * W raw tokens (0 disables the window), m = compression ratio of `comp`,
  * rope_base = RoPE base (frequency of pair i is base^(-2i/dr)),
  * softmax_scale = logit scale (1/sqrt(d) in the method), rms_eps = RMSNorm
- * epsilon of the query prologue. */
+ * epsilon of the query prologue.
+ * split_policy (the technical-report digest, section 5.3: batch-invariant,
+ * deterministic kernels, a high-throughput and a low-latency one with the
+ * same accumulation order):
+ *   CSA_SPLIT_BY_CHUNK (0): chunks of fewer than 64 queries (decode) cut a
+ *     row's entry list into fixed-size splits merged in split order; longer
+ *     chunks (prefill) take the row in one pass.  A row's result then depends
+ *     on whether its chunk is shorter than 64 queries (within rounding);
+ *   CSA_SPLIT_FIXED (1): every chunk takes the decode splits and merge, so a
+ *     row's bits depend only on the row and the caches, whatever the chunk
+ *     length and the batch; a long chunk then needs the split partials'
+ *     workspace (csa_attn_workspace_size) and their memory traffic. */
+enum { CSA_SPLIT_BY_CHUNK = 0, CSA_SPLIT_FIXED = 1 };
 typedef struct {
     int32_t head_dim;
     int32_t rope_dim;
@@ -121,6 +133,7 @@ typedef struct {
     float rope_base;
     float softmax_scale;
     float rms_eps;
+    int32_t split_policy;
 } csa_attn_params;
 
 /* Bytes of one KV record of format fmt (see csa_kv_cache); 0 if invalid. */
@@ -257,13 +270,14 @@ csa_status csa_indexer_topk_noalloc(const void* q_idx, const uint8_t* q_idx_scal
  * sink    : f32 [H].   topk_idx: int32 [B][Tq][topk].
  * comp    : linear compressed cache with p->m; win: ring window cache.
  * out     : [B][Tq][H][d], out_dtype F32 or BF16.
- * workspace: csa_attn_workspace_size(...) bytes with max_entries = topk.
- * Errors: INVALID_ARG (incl. cache d / dr differing from p), UNSUPPORTED,
- * CAPACITY (win->cap < window + Tq - 1), WORKSPACE, HIP.
+ * workspace: csa_attn_workspace_size(...) bytes with max_entries = topk and
+ *           the call's split_policy.
+ * Errors: INVALID_ARG (incl. cache d / dr differing from p, split_policy not
+ * 0 or 1), UNSUPPORTED, CAPACITY (win->cap < window + Tq - 1), WORKSPACE, HIP.
  * ------------------------------------------------------------------------- */
 size_t csa_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t head_dim,
                                int64_t max_comp_entries, int32_t window, int32_t q_dtype,
-                               int32_t comp_fmt);
+                               int32_t comp_fmt, int32_t split_policy);
 csa_status csa_sparse_mqa_attn(const void* q, int32_t q_dtype, const int32_t* q_pos,
                                const int32_t* topk_idx, int32_t topk, const csa_kv_cache* comp,
                                const csa_kv_cache* win, const float* gamma_q, const float* sink,

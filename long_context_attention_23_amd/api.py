@@ -38,9 +38,13 @@ class IdxCacheT(C.Structure):
                 ("cap", C.c_int64)]
 
 
+SPLIT_BY_CHUNK, SPLIT_FIXED = 0, 1
+
+
 class AttnParamsT(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("rope_dim", C.c_int32), ("window", C.c_int32), ("m", C.c_int32),
-                ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("rms_eps", C.c_float)]
+                ("rope_base", C.c_float), ("softmax_scale", C.c_float), ("rms_eps", C.c_float),
+                ("split_policy", C.c_int32)]
 
 
 _lib = None
@@ -79,7 +83,7 @@ def lib():
         L.csa_indexer_topk_noalloc.argtypes = [_V, _V, _I32, _V, C.POINTER(IdxCacheT), _V, _I32, _I32, _I32, _I32,
                                                _I32, _V, _V]
         L.csa_attn_workspace_size.restype = _SZ
-        L.csa_attn_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I64, _I32, _I32, _I32]
+        L.csa_attn_workspace_size.argtypes = [_I32, _I32, _I32, _I32, _I64, _I32, _I32, _I32, _I32]
         L.csa_sparse_mqa_attn.restype = C.c_int
         L.csa_sparse_mqa_attn.argtypes = [_V, _I32, _V, _V, _I32, C.POINTER(KVCacheT), C.POINTER(KVCacheT), _V,
                                           _V, C.POINTER(AttnParamsT), _I32, _I32, _I32, _V, _I32, _V, _SZ, _V]
@@ -230,12 +234,12 @@ def indexer_topk_noalloc(q_idx, q_dtype, w_idx, keys, q_pos, m, topk, *, q_scale
     return out
 
 
-def attn_workspace_bytes(B, Tq, H, d, max_comp_entries, window, q_dtype, comp_fmt):
-    return int(lib().csa_attn_workspace_size(B, Tq, H, d, max_comp_entries, window, q_dtype, comp_fmt))
+def attn_workspace_bytes(B, Tq, H, d, max_comp_entries, window, q_dtype, comp_fmt, split_policy=SPLIT_BY_CHUNK):
+    return int(lib().csa_attn_workspace_size(B, Tq, H, d, max_comp_entries, window, q_dtype, comp_fmt, split_policy))
 
 
-def attn_params(d, dr, window, m, base=10000.0, scale=None, eps=1e-6):
-    return AttnParamsT(d, dr, window, m, base, (d ** -0.5) if scale is None else scale, eps)
+def attn_params(d, dr, window, m, base=10000.0, scale=None, eps=1e-6, split_policy=SPLIT_BY_CHUNK):
+    return AttnParamsT(d, dr, window, m, base, (d ** -0.5) if scale is None else scale, eps, split_policy)
 
 
 def _attn(sparse, q, q_pos, comp, win, sink, params, *, topk_idx=None, gamma_q=None, out=None,
@@ -246,7 +250,8 @@ def _attn(sparse, q, q_pos, comp, win, sink, params, *, topk_idx=None, gamma_q=N
         out = torch.empty((B, Tq, H, d), dtype=out_dtype or q.dtype, device=q.device)
     od = torch_dtype_code(out)
     k = topk_idx.shape[-1] if sparse else 0
-    need = attn_workspace_bytes(B, Tq, H, d, k if sparse else comp.cap, params.window, qd, comp.fmt)
+    need = attn_workspace_bytes(B, Tq, H, d, k if sparse else comp.cap, params.window, qd, comp.fmt,
+                                params.split_policy)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()

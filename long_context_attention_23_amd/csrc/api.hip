@@ -74,6 +74,8 @@ csa_status check_attn_common(const void* q, int32_t q_dtype, const int32_t* q_po
     if (dr < 0 || dr > d || dr % 2) return fail(CSA_ERR_INVALID_ARG, "rope_dim %d must be even and <= head_dim", dr);
     if (dr > 128) return fail(CSA_ERR_UNSUPPORTED, "rope_dim %d > 128", dr);
     if (p->window < 0 || p->m < 1) return fail(CSA_ERR_INVALID_ARG, "window %d / m %d", p->window, p->m);
+    if (p->split_policy != CSA_SPLIT_BY_CHUNK && p->split_policy != CSA_SPLIT_FIXED)
+        return fail(CSA_ERR_INVALID_ARG, "split_policy %d", p->split_policy);
     if (!is_act_fmt(q_dtype)) return fail(CSA_ERR_UNSUPPORTED, "q dtype %d", q_dtype);
     if (!is_act_fmt(out_dtype)) return fail(CSA_ERR_UNSUPPORTED, "out dtype %d", out_dtype);
     if (!comp) return fail(CSA_ERR_INVALID_ARG, "comp cache is null");
@@ -105,7 +107,8 @@ csa_status run_attention(const void* q, int32_t q_dtype, const int32_t* q_pos, c
     if (max_entries + p->window > (int64_t)1024 * 256)
         return fail(CSA_ERR_UNSUPPORTED, "entry list of %lld exceeds 262144", (long long)(max_entries + p->window));
     const int64_t rows = (int64_t)B * Tq;
-    const size_t need = csa_attn_workspace_size(B, Tq, H, p->head_dim, max_entries, p->window, q_dtype, comp->fmt);
+    const size_t need =
+        csa_attn_workspace_size(B, Tq, H, p->head_dim, max_entries, p->window, q_dtype, comp->fmt, p->split_policy);
     if (need > 0 && (!workspace || ws_bytes < need))
         return fail(CSA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace ? ws_bytes : (size_t)0, need);
     if (rows == 0) return ok();
@@ -141,6 +144,7 @@ csa_status run_attention(const void* q, int32_t q_dtype, const int32_t* q_pos, c
     a.eps = p->rms_eps;
     csa::fill_rope_table(a.rope, a.dr, a.base);
     a.Tq = Tq;
+    a.split_tq = p->split_policy == CSA_SPLIT_FIXED ? 1 : Tq;
     a.H = H;
     a.rows = (int32_t)rows;
     a.out = out;
@@ -372,12 +376,13 @@ CSA_API csa_status csa_indexer_topk_noalloc(const void* q_idx, const uint8_t* q_
 }
 
 CSA_API size_t csa_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t head_dim, int64_t max_comp_entries,
-                                       int32_t window, int32_t q_dtype, int32_t comp_fmt) {
+                                       int32_t window, int32_t q_dtype, int32_t comp_fmt, int32_t split_policy) {
     const int64_t rows = (int64_t)(B > 0 ? B : 0) * (Tq > 0 ? Tq : 0);
     if (rows == 0 || H < 1 || head_dim < 1) return 0;
     (void)q_dtype;
     (void)comp_fmt;
-    return (size_t)csa::attn_ws_bytes(rows, Tq, H, head_dim, max_comp_entries + (window > 0 ? window : 0));
+    const int32_t split_tq = split_policy == CSA_SPLIT_FIXED ? 1 : Tq;
+    return (size_t)csa::attn_ws_bytes(rows, split_tq, H, head_dim, max_comp_entries + (window > 0 ? window : 0));
 }
 
 CSA_API csa_status csa_sparse_mqa_attn(const void* q, int32_t q_dtype, const int32_t* q_pos, const int32_t* topk_idx,

@@ -124,8 +124,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG) 
     const int64_t t = a.q_pos[row];
     const int64_t nc = comp_slots(a, t);
     const int64_t ne = nc + a.W;
-    const int64_t split = attn_split_len(ne, a.Tq);
-    const int64_t nsplit = attn_nsplit(ne, a.Tq);
+    const int64_t split = attn_split_len(ne, a.split_tq);
+    const int64_t nsplit = attn_nsplit(ne, a.split_tq);
     const int64_t s = blockIdx.x;
     if (s >= nsplit) return;
     const int64_t e0 = s * split, e1 = min(e0 + split, ne);
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     }
     stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
     const int64_t nc = comp_slots(a, t);
-    const int nsplit = (int)attn_nsplit<int64_t>(nc + a.W, a.Tq);
+    const int nsplit = (int)attn_nsplit<int64_t>(nc + a.W, a.split_tq);
     if (nsplit <= 1) return;
     // ---- split weights, one wave (at most 64 splits)
     if (tid < kWave) {
@@ -379,15 +379,15 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     for (int k = tid; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
 }
 
-int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t max_entries) {
-    const int64_t nb = attn_nsplit_bound(max_entries, Tq);
+int64_t attn_ws_bytes(int64_t rows, int32_t split_tq, int32_t H, int32_t d, int64_t max_entries) {
+    const int64_t nb = attn_nsplit_bound(max_entries, split_tq);
     if (nb <= 1) return 0;
     return rows * nb * H * ((int64_t)d + 2) * 4;
 }
 
 hipError_t launch_attention(const AttnArgs& a0, int64_t max_entries, hipStream_t st) {
     if (a0.rows == 0) return hipSuccess;
-    const int64_t nb = attn_nsplit_bound(max_entries, a0.Tq);
+    const int64_t nb = attn_nsplit_bound(max_entries, a0.split_tq);
     AttnArgs a = a0;
     a.nsplit_max = (int32_t)nb;
     // the matrix-core kernel keeps bf16 partials for bf16 outputs (the partial

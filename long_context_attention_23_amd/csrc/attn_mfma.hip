@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const bool sparse = a.topk != nullptr;
     int32_t jf0 = 0, jf1 = 0, jf2 = 0;
     if (sparse && fetcher && a.k > 0) {
-        const int32_t split_s = attn_split_len<int32_t>(a.k + a.W, a.Tq);
+        const int32_t split_s = attn_split_len<int32_t>(a.k + a.W, a.split_tq);
         const int32_t eb = (int32_t)blockIdx.x * split_s + fw + kFetchers * lane;
         const int32_t* top = a.topk + (int64_t)row * a.k;
         jf0 = top[min(eb, a.k - 1)];
@@ -379,8 +379,8 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         c.slot0 = (a.W > 0 && s0 >= 0) ? s0 % (int32_t)a.wcap : s0;
     }
     const int32_t ne = c.nc + a.W;
-    const int32_t split = attn_split_len<int32_t>(ne, a.Tq);
-    const int32_t nsplit = attn_nsplit<int32_t>(ne, a.Tq);
+    const int32_t split = attn_split_len<int32_t>(ne, a.split_tq);
+    const int32_t nsplit = attn_nsplit<int32_t>(ne, a.split_tq);
     const int32_t sp = blockIdx.x;
     if (sp >= nsplit) return;
     const int32_t e0 = sp * split, e1 = min(e0 + split, ne);

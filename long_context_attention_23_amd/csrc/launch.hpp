@@ -114,6 +114,7 @@ struct AttnArgs {
     int32_t d, dr, W, m;
     float base, scale, eps;
     int32_t Tq, H, rows;
+    int32_t split_tq;           // chunk length the split policy sees (1: the decode splits always)
     void* out;                  // [rows][H][d]
     int32_t out_fmt;
     void* ws;
@@ -122,12 +123,13 @@ struct AttnArgs {
     int32_t part_bf16;          // split partials of O stored in bf16 (set by the launcher)
     RopeTable rope;
 };
-int64_t attn_ws_bytes(int64_t rows, int32_t Tq, int32_t H, int32_t d, int64_t max_entries);
+int64_t attn_ws_bytes(int64_t rows, int32_t split_tq, int32_t H, int32_t d, int64_t max_entries);
 
 // Split policy of the attention kernels: entries per split for a query row
 // with n entries.  It depends only on the row's own entry count and on the
 // chunk length Tq, never on the batch size, so a sequence's result does not
-// depend on the batch it is in.  Chunks of >= 64 queries give one split per
+// depend on the batch it is in (the fixed policy passes Tq = 1 for every
+// chunk, so neither does it depend on the chunk length).  Chunks of >= 64 queries give one split per
 // row (enough rows to fill the chip); shorter chunks (decode) cut a row into
 // at most 64 splits of at least 32 entries, a multiple of 32.
 // (templated on the integer type: device code uses 32-bit arithmetic)

@@ -205,6 +205,7 @@ def attn(L, sparse=True, **over):
     (dict(comp=kv(fmt=api.FP4_E2M1)), UNS, "comp fmt"),
     (dict(sink=None), INV, "is null"),
     (dict(p=api.AttnParamsT(512, 63, 128, 4, 1e4, 0.1, 1e-6)), INV, "rope_dim"),
+    (dict(p=api.AttnParamsT(512, 64, 128, 4, 1e4, 0.1, 1e-6, 2)), INV, "split_policy"),
     (dict(), WSP, "workspace"),
 ])
 def test_attention_validation(L, sparse, over, code, frag):
@@ -306,3 +307,14 @@ def test_layer_in_proj_validation(L, over, code, frag):
 def test_layer_in_proj_workspace_size(L):
     assert L.csa_layer_in_proj_workspace_size(4, 4, 64) == 4 * 4 * 64 * 4
     assert L.csa_layer_in_proj_workspace_size(-1, 4, 64) == 0
+
+
+def test_attention_workspace_by_split_policy(L):
+    """A long chunk needs no split workspace by chunk, the decode splits' with
+    the fixed policy; a decode chunk needs the same either way."""
+    by_chunk = L.csa_attn_workspace_size(1, 8192, 64, 512, 1024, 128, api.BF16, api.FP8_E4M3, api.SPLIT_BY_CHUNK)
+    fixed = L.csa_attn_workspace_size(1, 8192, 64, 512, 1024, 128, api.BF16, api.FP8_E4M3, api.SPLIT_FIXED)
+    assert by_chunk == 0
+    assert fixed == 8192 * 36 * 64 * (512 + 2) * 4                 # 1152 entries: 36 splits of 32
+    dec = [L.csa_attn_workspace_size(4, 1, 64, 512, 1024, 128, api.BF16, api.FP8_E4M3, sp) for sp in (0, 1)]
+    assert dec[0] == dec[1] == 4 * 36 * 64 * (512 + 2) * 4
