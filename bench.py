@@ -21,7 +21,14 @@ Profiling helpers (the summaries under profiles/ are made with these):
   --summarize DIR          per-kernel duration summary of a rocprofv3
                            --kernel-trace run written under DIR;
   --summarize-pmc DIR ...  per-call sums of the counters of rocprofv3 --pmc
-                           runs of this benchmark (one counter per run).
+                           runs of this benchmark (one counter per run);
+  --summarize-prefill DIR  per-call kernel durations of the prefill section;
+  --summarize-pmc-kernels DIR ...
+                           per-kernel counter means with MFMA / VALU busy;
+  --summarize-launches DIR ...
+                           per kernel and grid: trace durations and counter
+                           means (tells apart launches of one kernel over
+                           different problem sizes).
 """
 import glob
 import hashlib
@@ -69,6 +76,8 @@ def parse():
     ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+")
     ap.add_argument("--summarize-prefill", metavar="DIR")
     ap.add_argument("--summarize-pmc-kernels", metavar="DIR", nargs="+")
+    ap.add_argument("--summarize-launches", metavar="DIR", nargs="+",
+                    help="per kernel and grid: trace durations and counter means of trace / --pmc runs")
     return ap.parse_args()
 
 
@@ -696,11 +705,11 @@ def cpu_baseline_prefill(target_s, nq=512):
 # profiles/ gives the counts and commands); valid only while the kernels'
 # sources are unchanged (src_hash below).
 TRAFFIC = {
-    "csa_indexer_topk": {"bytes": 45_599_148, "src": "de59d03fe3448def"},
-    "csa_sparse_mqa_attn": {"bytes": 25_898_215, "src": "de59d03fe3448def"},
-    "hca_dense_mqa_attn": {"bytes": 54_348_341, "src": "de59d03fe3448def"},
-    "csa_out_proj": {"bytes": 59_135_074, "src": "de59d03fe3448def"},
-    "hca_out_proj": {"bytes": 59_135_074, "src": "de59d03fe3448def"},
+    "csa_indexer_topk": {"bytes": 38_409_333, "src": "fba07c35355311a0"},
+    "csa_sparse_mqa_attn": {"bytes": 25_898_230, "src": "fba07c35355311a0"},
+    "hca_dense_mqa_attn": {"bytes": 54_348_025, "src": "fba07c35355311a0"},
+    "csa_out_proj": {"bytes": 59_135_068, "src": "fba07c35355311a0"},
+    "hca_out_proj": {"bytes": 59_135_068, "src": "fba07c35355311a0"},
 }
 TRAFFIC_SRC = ["long_context_attention_23_amd/csrc/indexer.hip", "long_context_attention_23_amd/csrc/attn_mfma.hip",
                "long_context_attention_23_amd/csrc/attn.hip", "long_context_attention_23_amd/csrc/proj.hip",
@@ -872,6 +881,7 @@ def summarize_pmc_kernels(dirs, match=("k_idxp_", "k_attn_mfma", "k_proj_mfma"))
       MFMA busy = sum SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE x 1024 SIMDs)
       MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_* x 512
       VALU busy = sum SQ_ACTIVE_INST_VALU / 256 CUs / max GRBM_GUI_ACTIVE
+        (= 4 x the quad-cycles the counter counts per SIMD / 1024 SIMDs)
     (per-dispatch sums over the counter's instances; GRBM_GUI_ACTIVE is taken
     as its largest instance, the busy time of the GPU)."""
     import sqlite3
@@ -910,6 +920,52 @@ def summarize_pmc_kernels(dirs, match=("k_idxp_", "k_attn_mfma", "k_proj_mfma"))
     print(json.dumps(dict(out), indent=1))
 
 
+def summarize_launches(dirs):
+    """Per launch shape (kernel, grid) of the library's kernels in rocprofv3
+    runs of this benchmark: launches and duration from a --kernel-trace run,
+    per-dispatch counter means (summed over the counter's instances; the
+    largest instance for GRBM_GUI_ACTIVE) from --pmc runs, joined on the
+    dispatch id.  Launches of one kernel over different problem sizes (an
+    input and an output projection) fall into different rows."""
+    import sqlite3
+    rows = {}                                        # (kernel, grid) -> {"us": [...], counter: [...]}
+    for d in dirs:
+        db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
+        c = sqlite3.connect(db)
+        have = {r[0] for r in c.execute("select name from sqlite_master where type in ('table','view')")}
+        pmc = "pmc_events" in have and c.execute("select count(*) from pmc_events").fetchone()[0] > 0
+        shape = {}
+        for name, gx, gy, gz, wx, did, a, b in c.execute(
+                "select name, grid_x, grid_y, grid_z, workgroup_x, dispatch_id, start, end from kernels"):
+            if "csa::" not in name:
+                continue
+            key = (_short(name).replace("csa::", ""), f"{gx // max(wx, 1)}x{gy}x{gz} wg of {wx}")
+            shape[did] = key
+            r = rows.setdefault(key, {"us": []})
+            if not pmc:                              # durations from trace runs only (counter runs serialise)
+                r["us"].append((b - a) / 1e3)
+        if not pmc:
+            continue
+        acc = {}
+        for cn, v, did in c.execute("select counter_name, counter_value, dispatch_id from pmc_events"):
+            if did not in shape:
+                continue
+            a = acc.setdefault((did, cn), [0.0, -1e300])
+            a[0] += v
+            a[1] = max(a[1], v)
+        for (did, cn), (sm, mx) in acc.items():
+            rows[shape[did]].setdefault(cn, []).append(mx if cn == "GRBM_GUI_ACTIVE" else sm)
+    cns = sorted({cn for r in rows.values() for cn in r if cn != "us"})
+    out = ["| kernel | grid | launches | avg us | min us | " + " | ".join(cns) + " |",
+           "|---|---|---|---|---|" + "---|" * len(cns)]
+    for (k, g), r in sorted(rows.items()):
+        us = r["us"]
+        t = f"{len(us)} | {np.mean(us):.2f} | {min(us):.2f}" if us else " | | "
+        cells = [f"{np.mean(r[cn]):.6g}" if cn in r else "" for cn in cns]
+        out.append(f"| {k} | {g} | {t} | " + " | ".join(cells) + " |")
+    print("\n".join(out))
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -922,6 +978,8 @@ def main():
         return summarize_prefill(args.summarize_prefill)
     if args.summarize_pmc_kernels:
         return summarize_pmc_kernels(args.summarize_pmc_kernels)
+    if args.summarize_launches:
+        return summarize_launches(args.summarize_launches)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this path runs on a single "
               "MI355X; multi-GPU sharding is not built)", file=sys.stderr)

@@ -85,3 +85,43 @@ def test_prefill_trace_summary(tmp_path, capsys):
     assert rows["csa_sparse_mqa_attn"] == ["4", "3015.0", "3000.0"]
     assert rows["hca_dense_mqa_attn"] == ["4", "17615.0", "17600.0"]
     assert rows["attn_out_proj_grouped"] == ["4", "550.0", "550.0"]
+
+
+def test_launch_summary_by_grid(tmp_path, capsys):
+    """The per-launch summary keeps launches of one kernel over different grid
+    sizes apart, takes durations from the trace run only and joins the
+    counter run's values on the dispatch id (summed over instances; the
+    largest instance for GRBM_GUI_ACTIVE)."""
+    import sqlite3
+    cols = "name text, grid_x integer, grid_y integer, grid_z integer, workgroup_x integer, dispatch_id integer, " \
+           "start integer, end integer"
+
+    def mk(sub, pmc):
+        db = tmp_path / sub / "run_results.db"
+        db.parent.mkdir()
+        c = sqlite3.connect(db)
+        c.execute(f"create table kernels ({cols})")
+        c.execute("create table pmc_events (counter_name text, counter_value real, dispatch_id integer)")
+        did = 0
+        for rep in range(3):
+            for gx, us in ((448 * 256, 55.0 + rep), (112 * 256, 12.0)):
+                did += 1
+                c.execute("insert into kernels values (?,?,?,?,?,?,?,?)",
+                          ("void csa::k_lin8_stream<1, 4>(csa::LinArgs)", gx, 1, 1, 256, did, 0, int(us * 1000)))
+                if pmc:
+                    for inst in range(2):      # two instances of each counter
+                        c.execute("insert into pmc_events values (?,?,?)", ("FETCH_SIZE", gx / 256 + inst, did))
+                        c.execute("insert into pmc_events values (?,?,?)", ("GRBM_GUI_ACTIVE", 100.0 * (inst + 1), did))
+            did += 1
+            c.execute("insert into kernels values (?,?,?,?,?,?,?,?)", ("at::native::fill", 64, 1, 1, 64, did, 0, 5000))
+        c.commit()
+        c.close()
+        return str(db.parent)
+
+    bench.summarize_launches([mk("trace", False), mk("pmc", True)])
+    out = capsys.readouterr().out.splitlines()
+    assert out[0].split("|")[6:8] == [" FETCH_SIZE ", " GRBM_GUI_ACTIVE "]
+    rows = {ln.split("|")[2].strip(): [x.strip() for x in ln.split("|")[3:8]] for ln in out[2:]}
+    assert len(rows) == 2                                  # framework kernels are left out
+    assert rows["448x1x1 wg of 256"] == ["3", "56.00", "55.00", "897", "200"]
+    assert rows["112x1x1 wg of 256"] == ["3", "12.00", "12.00", "225", "200"]
