@@ -1554,13 +1554,13 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
 // FP4 queries and keys (di = 64, Hi = 4) against a large key set (up to 2^18
 // blocks).  Two kernels:
 //   F  the row's keys are split over workgroups of kDfChunk consecutive
-//      blocks.  Every workgroup of a row first scores the same systematic
-//      sample of the row's keys (kDsSampTiles 32-key tiles, every stride-th,
-//      stride and rank from the row's visible count: mostly L2 hits) and
-//      takes the 22-bit prefix T of its rank-th largest score key (low bits
-//      zero, so at least rank samples score at or above T; about 4k keys of
-//      the row do), while its own keys are in flight; every workgroup gets
-//      the same T.  Keys scoring above T go (key, j) to the workgroup's own
+//      blocks.  Every workgroup of a row first scores the same sample of the
+//      row's keys (kDsSampTiles 32-key tiles, one in each window of stride
+//      tiles, stride and rank from the row's visible count: mostly cache
+//      hits), then issues its own keys and, while they are in flight, takes
+//      T, the rank-th largest sample score key itself (at least rank samples
+//      score at or above T; about 4k keys of the row do) by radix passes;
+//      every workgroup gets the same T.  Keys scoring above T go (key, j) to the workgroup's own
 //      segment of the row's candidate area, keys equal to T (j) to its tie
 //      segment, both in ascending j; the counts go to the row header.  No
 //      atomics and nothing to clear: each workgroup writes its own counts.
@@ -1634,11 +1634,15 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint2* 
 // 0), so the values spread over up to 2048 bins wherever the range starts --
 // score keys crowd into a few top-bit bins, and LDS atomics on one address
 // serialise.  add(f) calls f(v, in) for this thread's candidates; the bin
-// holding the need-th largest becomes the new range.  hist (2048 bins) must
-// be zero on entry and is zero again on return.
+// holding the need-th largest becomes the new range.  Passes alternate
+// between two histograms of 2048 bins (hists + 2048 * (pass & 1)), both zero
+// before the first pass: a pass clears its own after the last read of it, and
+// the barriers of the next pass order that clear before the pass after it, so
+// no pass needs a barrier of its own for the clearing.
 template <int NT, typename Add>
-__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* hist,
-                                          uint32_t* wsum, uint32_t* sh) {
+__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* hists,
+                                          int& pass, uint32_t* wsum, uint32_t* sh) {
+    uint32_t* hist = hists + 2048 * (pass & 1);
     const int shift = width > 11 ? width - 11 : 0;
     const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
     add([&](uint32_t v, bool in) {
@@ -1651,8 +1655,8 @@ __device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, u
     base += sh[0] << shift;
     need -= sh[1];
     width = shift;
+    pass++;
     for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0u;
-    __syncthreads();
 }
 
 __device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
@@ -1695,15 +1699,23 @@ __device__ __forceinline__ uint32_t* dec_ties(const IndexerArgs& a, int64_t row,
 }
 
 // A operand of one query row: rows 0..3 its four heads, the rest zero
-__device__ __forceinline__ void pd_load_a(const IndexerArgs& a, int64_t row, int l32, int half, i32x8_t& qa, int& qs) {
-    qa = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    qs = 127;
-    if (l32 < 4) {
-        const int64_t r = row * 4 + l32;
-        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.q) + r * 32 + 16 * half);
-        qa[0] = (int)u.x; qa[1] = (int)u.y; qa[2] = (int)u.z; qa[3] = (int)u.w;
-        qs = a.q_scales[r * 2 + half];
-    }
+// The row's FP4 query as the product's A operand: lanes l32 < 4 hold head
+// l32's row, the others zero rows.  Split in two so that the loads (every
+// lane reads, head l32 & 3) go out before the key loads and the selects come
+// after them: a wait for a load issued after the keys would wait for the keys.
+struct PdQuery {
+    uint4 u;
+    int s;
+};
+__device__ __forceinline__ PdQuery pd_issue_q(const IndexerArgs& a, int64_t row, int l32, int half) {
+    const int64_t r = row * 4 + (l32 & 3);
+    return PdQuery{*reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.q) + r * 32 + 16 * half),
+                   (int)a.q_scales[r * 2 + half]};
+}
+__device__ __forceinline__ void pd_form_a(const PdQuery& p, int l32, i32x8_t& qa, int& qs) {
+    const bool on = l32 < 4;
+    qa = i32x8_t{on ? (int)p.u.x : 0, on ? (int)p.u.y : 0, on ? (int)p.u.z : 0, on ? (int)p.u.w : 0, 0, 0, 0, 0};
+    qs = on ? p.s : 127;
 }
 
 // score of key l32 of a tile for the row's four heads (lanes of the upper
@@ -1717,9 +1729,17 @@ __device__ __forceinline__ float pd_score(const i32x8_t& qa, int qs, const uint4
     return v;
 }
 
+// Sample tile i of a decode row: one tile in each window of `stride` tiles,
+// at an offset that varies with i.  Tiles at a power-of-two stride would all
+// fall into a few cache sets (and every workgroup of the row reads them), so
+// the sample would thrash the caches it is meant to hit.
+__device__ __forceinline__ int64_t dec_sample_tile(int i, int stride) {
+    return (int64_t)i * stride + (int64_t)(((uint32_t)i * 37u + 11u) % (uint32_t)stride);
+}
+
 __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
-    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2 * 2048];
     __shared__ uint32_t sh[2];
     __shared__ uint32_t wcnt[2][kDfWaves];
     __shared__ uint32_t wsum[kDfWaves];
@@ -1729,11 +1749,18 @@ __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     const int b = (int)(row / a.Tq);
     const int seg = (int)blockIdx.x;
     const int64_t t0 = (int64_t)seg * kDfChunk + (int64_t)wv * kDfTiles * 32;    // this wave's first key
+    // loads return in order: the query and head weights (independent of the
+    // position) go first, then the row's sample.  The chunk's keys are issued
+    // once the sample has been scored: issued together, every CU's chunk
+    // competes with the sample for HBM and the sample arrives late; issued
+    // after it, the chunk is in flight while the threshold is formed.
+    const PdQuery pq = pd_issue_q(a, row, l32, half);
+    float w4[4];
+#pragma unroll
+    for (int h = 0; h < 4; h++) w4[h] = a.w[row * 4 + h];
     const int64_t n = visible_blocks(a, row);
     if (n <= a.topk || (int64_t)seg * kDfChunk >= n) return;                     // workgroup-uniform
-    // the row's sample (stride from its visible count), loaded
-    // before the chunk's keys: loads return in order, and the threshold is
-    // formed while the chunk is still in flight
+    // the sample's stride comes from the row's visible count
     const int ntile = (int)((n + 31) / 32);
     const int stride = (ntile + kDsSampTiles - 1) / kDsSampTiles;
     const int nst = (ntile + stride - 1) / stride;                               // sample tiles, <= kDsSampTiles
@@ -1741,26 +1768,25 @@ __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     int ss[kDsSampPerWave];
 #pragma unroll
     for (int i = 0; i < kDsSampPerWave; i++)
-        pf_load_keys(a, b, (int64_t)(wv + kDfWaves * i) * stride * 32, l32, half, sc[i], ss[i]);
-    uint4 kc[kDfTiles];
-    int ks[kDfTiles];
-#pragma unroll
-    for (int i = 0; i < kDfTiles; i++) pf_load_keys(a, b, t0 + 32 * i, l32, half, kc[i], ks[i]);
+        pf_load_keys(a, b, dec_sample_tile(wv + kDfWaves * i, stride) * 32, l32, half, sc[i], ss[i]);
+    for (int i = tid; i < 2 * 2048; i += kDfThreads) hist[i] = 0u;
     i32x8_t qa;
     int qs;
-    pd_load_a(a, row, l32, half, qa, qs);
-    float w4[4];
-#pragma unroll
-    for (int h = 0; h < 4; h++) w4[h] = a.w[row * 4 + h];
-    for (int i = tid; i < 2048; i += kDfThreads) hist[i] = 0u;
+    pd_form_a(pq, l32, qa, qs);
     uint32_t skey[kDsSampPerWave];
 #pragma unroll
     for (int i = 0; i < kDsSampPerWave; i++) {
         const int tile = wv + kDfWaves * i;
-        const int64_t j = (int64_t)tile * stride * 32 + l32;
+        const int64_t j = dec_sample_tile(tile, stride) * 32 + l32;
         const float v = pd_score(qa, qs, sc[i], ss[i], w4);
         skey[i] = (half == 0 && tile < nst && j < n) ? score_key(v) : 0u;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 kc[kDfTiles];
+    int ks[kDfTiles];
+#pragma unroll
+    for (int i = 0; i < kDfTiles; i++) pf_load_keys(a, b, t0 + 32 * i, l32, half, kc[i], ks[i]);
+    __builtin_amdgcn_sched_barrier(0);
     // T: the rank-th largest sample key itself, by range-adaptive radix
     // passes over the samples (key 0 marks no sample).  At least rank samples
     // score at or above T; an exact sample value (not a bin edge) keeps a
@@ -1781,12 +1807,12 @@ __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     if (valid > 0) {
         uint32_t need = (uint32_t)min<int64_t>(max<int64_t>(((int64_t)4 * a.topk * valid + n - 1) / n, 1), valid);
         uint32_t base = mn;
-        int width = bit_width(mx - mn);
+        int width = bit_width(mx - mn), pass = 0;
         while (width > 0)                                                        // workgroup-uniform
             span_pass<kDfThreads>([&](auto f) {
 #pragma unroll
                 for (int i = 0; i < kDsSampPerWave; i++) f(skey[i], half == 0 && skey[i] != 0u);
-            }, base, width, need, hist, wsum, sh);
+            }, base, width, need, hist, pass, wsum, sh);
         T = base;
     }
     __syncthreads();                                   // wcnt is reused below
@@ -1842,9 +1868,10 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
     __shared__ uint4 bmA4[kDsWords / 4];                             // members (also the exact path's bitmap)
     __shared__ uint4 bmT4[kDsWords / 4];                             // ties to choose from
     __shared__ uint2 cl[kIdxPfCands];                                // compacted above-threshold candidates
-    __shared__ __attribute__((aligned(16))) uint32_t hist[2048];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[2 * 2048];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t segoff[2][kDecMaxSeg];
+    __shared__ uint32_t segcnt[kDecMaxSeg];                          // stored above-threshold entries
     __shared__ uint2 mm[kDsThreads / kWave];
     __shared__ uint32_t wsum[2][kDsThreads / kWave];
     uint32_t* bmA = reinterpret_cast<uint32_t*>(bmA4);
@@ -1868,7 +1895,11 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
         if (lane >= nseg) { ca = 0; ct = 0; }
         const bool over = __ballot(ca > (uint32_t)kDfSegCands) != 0;
         const uint32_t ia = wave_incl_scan_dpp(ca), it = wave_incl_scan_dpp(ct);
-        if (lane < kDecMaxSeg) { segoff[0][lane] = ia - ca; segoff[1][lane] = it - ct; }
+        if (lane < kDecMaxSeg) {
+            segoff[0][lane] = ia - ca;
+            segoff[1][lane] = it - ct;
+            segcnt[lane] = min(ca, (uint32_t)kDfSegCands);
+        }
         if (lane == kWave - 1) { sh[0] = ia; sh[1] = it; sh[2] = over ? 1u : 0u; }
     }
     __syncthreads();
@@ -1878,19 +1909,18 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
         return;
     }
     // compaction: kDsThreads / kDecMaxSeg threads per segment, each copying
-    // every (that many)-th entry, loads batched four deep
+    // every (that many)-th entry, four loads in flight (clamped to the
+    // segment's last entry, so none is conditional) before the first store
     {
         constexpr int kTps = kDsThreads / kDecMaxSeg;
         const int sg = tid / kTps, sub = tid % kTps;
-        const uint32_t c = sg < nseg ? min(hd[2 + sg], (uint32_t)kDfSegCands) : 0u, o = segoff[0][sg];
+        const uint32_t c = segcnt[sg], o = segoff[0][sg];           // zero past the row's segments
         const uint2* src = dec_cand(a, row, sg);
         for (uint32_t e0 = sub; e0 < c; e0 += 4 * kTps) {
             uint2 v[4];
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const uint32_t e = e0 + u * kTps;
-                v[u] = e < c ? src[e] : make_uint2(0u, 0u);
-            }
+            for (int u = 0; u < 4; u++) v[u] = src[min(e0 + u * kTps, c - 1)];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < 4; u++)
                 if (e0 + u * kTps < c) cl[o + e0 + u * kTps] = v[u];
@@ -1902,7 +1932,7 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
         bmA4[i] = make_uint4(0u, 0u, 0u, 0u);
         bmT4[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    for (int i = tid; i < 2048; i += kDsThreads) hist[i] = 0u;
+    for (int i = tid; i < 2 * 2048; i += kDsThreads) hist[i] = 0u;
     __syncthreads();
     uint2 cv[kDsCPT];
 #pragma unroll
@@ -1920,12 +1950,12 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
             if (tid + q * kDsThreads < (int)tot) { mn = min(mn, cv[q].x); mx = max(mx, cv[q].x); }
         block_minmax(mn, mx, mm);
         uint32_t need = k, prefix = mn;
-        int width = bit_width(mx - mn);
+        int width = bit_width(mx - mn), pass = 0;
         while (width > 0)                                            // workgroup-uniform
             span_pass<kDsThreads>([&](auto f) {
 #pragma unroll
                 for (int q = 0; q < kDsCPT; q++) f(cv[q].x, tid + q * kDsThreads < (int)tot);
-            }, prefix, width, need, hist, wsum[0], sh);
+            }, prefix, width, need, hist, pass, wsum[0], sh);
         const uint32_t T1 = prefix;
         needT = need;
 #pragma unroll

@@ -340,9 +340,12 @@ def test_indexer_prefill_fallback_rows_exact():
 def test_indexer_decode_fallback_rows_exact():
     """Decode rows (a few queries per sequence, FP4) that a sampled threshold
     cannot serve, recomputed exactly: all weights zero (every key ties: more
-    ties than the lists hold), and keys of every 32-key tile whose index is a
-    multiple of ceil(tiles / 128) made to outrank the rest (a systematic
-    sample of such tiles ranks its threshold too high: too few candidates)."""
+    ties than the lists hold), and, for a query with positive codes and
+    weights, the first four keys of every tile the decode filter samples
+    (one per window of ceil(tiles / 64) tiles, at offset (37 i + 11) mod
+    window in window i) made to outrank the rest: the sample's threshold is
+    then the top score, which fewer than k keys of the row reach (too few
+    candidates)."""
     g = synth.rng(571)
     B, Tq, Hi, di, m, k, cap = 2, 3, 4, 64, 4, 1024, 90000
     kc, ks = synth.fp4_rows(g, (B, cap), di, -2, 0)
@@ -352,10 +355,12 @@ def test_indexer_decode_fallback_rows_exact():
     qc[1, 2] = 0x22                                          # +1.0 in both nibbles
     qs[1, 2] = 127
     w[1, 2] = 1.0
-    stride = max(1, -(-(-(-cap // 32)) // 128))
-    for t0 in range(0, cap, stride * 32):
-        kc[1, t0:t0 + 32] = 0x77
-        ks[1, t0:t0 + 32] = 127
+    ntile = -(-cap // 32)                                    # query (1, 2) sees every block
+    stride = -(-ntile // 64)
+    for i in range(-(-ntile // stride)):
+        t0 = 32 * (i * stride + (i * 37 + 11) % stride)
+        kc[1, t0:t0 + 4] = 0x77
+        ks[1, t0:t0 + 4] = 127
     pos = np.array([[4 * cap - 1, 4 * cap - 1, 4 * 30000 + 1], [4 * 60000, 4 * cap - 1, 4 * cap - 1]], np.int32)
     got, ref = run_indexer(qc, qs, O.FP4_E2M1, w, pos, kc, ks, O.FP4_E2M1, m, k, di)
     assert np.array_equal(got, ref)
