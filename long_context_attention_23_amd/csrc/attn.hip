@@ -359,24 +359,34 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     }
     part[tid] = acc;
     __syncthreads();
-    const float den = den_s;
+    // ---- thread c < d / 4 adds the groups in order, normalises its four
+    // dims, rotates the RoPE pairs among them (pairs start at even dims and
+    // d - dr is even, so a pair never straddles two threads) and stores them
     if (tid < nc4) {
+        const float den = den_s;
         float4 r = part[tid];
         for (int q = 1; q < G; q++) {
             const float4 y = part[q * nc4 + tid];
             r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
         }
         const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-        v[4 * tid] = den > 0.0f ? r.x * inv : 0.0f;
-        v[4 * tid + 1] = den > 0.0f ? r.y * inv : 0.0f;
-        v[4 * tid + 2] = den > 0.0f ? r.z * inv : 0.0f;
-        v[4 * tid + 3] = den > 0.0f ? r.w * inv : 0.0f;
+        float o[4] = {den > 0.0f ? r.x * inv : 0.0f, den > 0.0f ? r.y * inv : 0.0f,
+                      den > 0.0f ? r.z * inv : 0.0f, den > 0.0f ? r.w * inv : 0.0f};
+        const int k0 = 4 * tid, off = d - a.dr;
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            if (k0 + 2 * u >= off) {
+                float sn, cs;
+                rope_sincos(-(double)t, rf[(k0 + 2 * u - off) / 2], sn, cs);
+                const float x0 = o[2 * u], x1 = o[2 * u + 1];
+                o[2 * u] = x0 * cs - x1 * sn;
+                o[2 * u + 1] = x0 * sn + x1 * cs;
+            }
+        }
+        OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
+#pragma unroll
+        for (int u = 0; u < 4; u++) st_scalar<OT>(out, k0 + u, o[u]);
     }
-    __syncthreads();
-    rotate_out(a, t, v, tid, blockDim.x, rf);
-    __syncthreads();
-    OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
-    for (int k = tid; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
 }
 
 int64_t attn_ws_bytes(int64_t rows, int32_t split_tq, int32_t H, int32_t d, int64_t max_entries) {

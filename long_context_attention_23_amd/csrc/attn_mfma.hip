@@ -327,7 +327,26 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const int MT = min(4, (a.H - h0) / 16);           // 16-head groups in this workgroup
     const int dbase = qd * DQ;                         // first dim of this wave's quarter
 
-    // ---- the query loads go out first (they do not depend on the position).
+    // ---- sparse rows: the entry layout (k top-k entries, then the window)
+    // does not depend on the position, so the fetching waves read the first
+    // tiles' top-k indices first of all.  Loads return in order: issued after
+    // the query, the wait for an index would wait for the whole query, and
+    // the first records would go out only once the query had arrived.
+    const int fw = w - (kNW - kFetchers);              // fetching wave index (>= 0 for waves 4..7)
+    const bool fetcher = fw >= 0;
+    const bool sparse = a.topk != nullptr;
+    int32_t jf0 = 0, jf1 = 0, jf2 = 0;
+    if (sparse && fetcher && a.k > 0) {
+        const int32_t split_s = attn_split_len<int32_t>(a.k + a.W, a.split_tq);
+        const int32_t eb = (int32_t)blockIdx.x * split_s + fw + kFetchers * lane;
+        const int32_t* top = a.topk + (int64_t)row * a.k;
+        jf0 = top[min(eb, a.k - 1)];
+        jf1 = top[min(eb + kMTE, a.k - 1)];
+        jf2 = top[min(eb + 2 * kMTE, a.k - 1)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- then the query loads (they do not depend on the position either).
     // No load sits under a branch: a head group beyond MT reads group 0 (its
     // results are never stored), and without gamma the loads read the query
     // and are replaced by ones.
@@ -351,21 +370,6 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     }
 
     const int b = row / a.Tq;
-    // sparse rows: the entry layout (k top-k entries, then the window) does
-    // not depend on the position, so the fetching waves read the first tiles'
-    // top-k indices before it arrives
-    const int fw = w - (kNW - kFetchers);              // fetching wave index (>= 0 for waves 4..7)
-    const bool fetcher = fw >= 0;
-    const bool sparse = a.topk != nullptr;
-    int32_t jf0 = 0, jf1 = 0, jf2 = 0;
-    if (sparse && fetcher && a.k > 0) {
-        const int32_t split_s = attn_split_len<int32_t>(a.k + a.W, a.split_tq);
-        const int32_t eb = (int32_t)blockIdx.x * split_s + fw + kFetchers * lane;
-        const int32_t* top = a.topk + (int64_t)row * a.k;
-        jf0 = top[min(eb, a.k - 1)];
-        jf1 = top[min(eb + kMTE, a.k - 1)];
-        jf2 = top[min(eb + 2 * kMTE, a.k - 1)];
-    }
     const int t = load_uniform_i32(a.q_pos + row);
     RowCtx c;
     c.vis = t < 0 ? 0 : (t + 1) / a.m;

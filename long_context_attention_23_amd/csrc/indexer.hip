@@ -1580,8 +1580,9 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
 // above it, found by the whole workgroup: thread t sums the BPT bins
 // [nb - BPT (t + 1), nb - BPT t) with one vector read (consecutive threads,
 // consecutive bins: no bank conflicts), a workgroup scan orders the sums from
-// the top, and the thread holding the need-th count writes (digit, above) to
-// sh[0..1].  Every thread calls it; read sh after a barrier.
+// the top, and the thread holding the need-th count writes (digit, above,
+// count in the digit's bin) to sh[0..2].  Every thread calls it; read sh after
+// a barrier.
 template <int BPT>
 __device__ __forceinline__ void block_pick(const uint32_t* hist, uint32_t need, uint32_t* wsum, uint32_t* sh) {
     static_assert(BPT == 1 || BPT == 2 || BPT == 4, "bins per thread");
@@ -1605,7 +1606,7 @@ __device__ __forceinline__ void block_pick(const uint32_t* hist, uint32_t need, 
         uint32_t c = ex;
 #pragma unroll
         for (int q = 0; q < BPT; q++) {
-            if (c + h[q] >= need) { sh[0] = (uint32_t)(lo + BPT - 1 - q); sh[1] = c; break; }
+            if (c + h[q] >= need) { sh[0] = (uint32_t)(lo + BPT - 1 - q); sh[1] = c; sh[2] = h[q]; break; }
             c += h[q];
         }
     }
@@ -1640,8 +1641,8 @@ __device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint2* 
 // the barriers of the next pass order that clear before the pass after it, so
 // no pass needs a barrier of its own for the clearing.
 template <int NT, typename Add>
-__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* hists,
-                                          int& pass, uint32_t* wsum, uint32_t* sh) {
+__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t& inbin,
+                                          uint32_t* hists, int& pass, uint32_t* wsum, uint32_t* sh) {
     uint32_t* hist = hists + 2048 * (pass & 1);
     const int shift = width > 11 ? width - 11 : 0;
     const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
@@ -1654,9 +1655,46 @@ __device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, u
     __syncthreads();
     base += sh[0] << shift;
     need -= sh[1];
+    inbin = sh[2];
     width = shift;
     pass++;
     for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0u;
+}
+
+// A range [base, base + 2^width) left by span_pass that holds few values
+// (inbin <= 64) is finished by one wave instead of further passes: the
+// values in it go to fin[0..63] (fin[64] counts them, zero on entry), and
+// lane i of wave 0 counts the listed values above and equal to its own; the
+// lane whose value is the need-th largest gives base = that value and
+// need -= the count above it, as the remaining passes would (width becomes
+// 0).  Lanes holding equal values write equal results.  Two barriers.
+template <typename Add>
+__device__ __forceinline__ void span_finish(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* fin,
+                                            uint32_t* sh) {
+    const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
+    add([&](uint32_t v, bool in) {
+        if (in && v - base <= lim) {
+            const uint32_t i = atomicAdd(&fin[64], 1u);
+            if (i < 64u) fin[i] = v;
+        }
+    });
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const uint32_t n = min(fin[64], 64u);
+        const uint32_t lane = threadIdx.x;
+        const uint32_t x = lane < n ? fin[lane] : 0u;
+        uint32_t g = 0, e = 0;
+        for (uint32_t j = 0; j < n; j++) {
+            const uint32_t y = fin[j];
+            g += y > x ? 1u : 0u;
+            e += y == x ? 1u : 0u;
+        }
+        if (lane < n && g < need && need <= g + e) { sh[0] = x; sh[1] = g; }
+    }
+    __syncthreads();
+    base = sh[0];
+    need -= sh[1];
+    width = 0;
 }
 
 __device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
@@ -1730,21 +1768,23 @@ __device__ __forceinline__ float pd_score(const i32x8_t& qa, int qs, const uint4
 }
 
 // Sample tile i of a decode row: one tile in each window of `stride` tiles,
-// at an offset that varies with i.  Tiles at a power-of-two stride would all
-// fall into a few cache sets (and every workgroup of the row reads them), so
-// the sample would thrash the caches it is meant to hit.
+// at an offset that varies with i (((37 i + 11) mod 64) / 64 of the window,
+// no division).  Tiles at a power-of-two stride would all fall into a few
+// cache sets (and every workgroup of the row reads them).
 __device__ __forceinline__ int64_t dec_sample_tile(int i, int stride) {
-    return (int64_t)i * stride + (int64_t)(((uint32_t)i * 37u + 11u) % (uint32_t)stride);
+    return (int64_t)i * stride + (int64_t)((((uint32_t)i * 37u + 11u) & 63u) * (uint32_t)stride >> 6);
 }
 
 __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
     __shared__ __attribute__((aligned(16))) uint32_t hist[2 * 2048];
-    __shared__ uint32_t sh[2];
+    __shared__ uint32_t fin[65];
+    __shared__ uint32_t sh[4];
     __shared__ uint32_t wcnt[2][kDfWaves];
     __shared__ uint32_t wsum[kDfWaves];
     __shared__ uint2 mm[kDfWaves];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, half = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);           // uniform: tile math on the scalar unit
     const int64_t row = blockIdx.y;
     const int b = (int)(row / a.Tq);
     const int seg = (int)blockIdx.x;
@@ -1770,6 +1810,7 @@ __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     for (int i = 0; i < kDsSampPerWave; i++)
         pf_load_keys(a, b, dec_sample_tile(wv + kDfWaves * i, stride) * 32, l32, half, sc[i], ss[i]);
     for (int i = tid; i < 2 * 2048; i += kDfThreads) hist[i] = 0u;
+    if (tid == 0) fin[64] = 0u;
     i32x8_t qa;
     int qs;
     pd_form_a(pq, l32, qa, qs);
@@ -1806,13 +1847,16 @@ __global__ __launch_bounds__(kDfThreads) void k_idxd_filter(IndexerArgs a) {
     uint32_t T = score_key(-__builtin_huge_valf());    // no sample: every non-NaN score is above it
     if (valid > 0) {
         uint32_t need = (uint32_t)min<int64_t>(max<int64_t>(((int64_t)4 * a.topk * valid + n - 1) / n, 1), valid);
-        uint32_t base = mn;
+        uint32_t base = mn, inbin = 0;
         int width = bit_width(mx - mn), pass = 0;
-        while (width > 0)                                                        // workgroup-uniform
-            span_pass<kDfThreads>([&](auto f) {
+        auto samples = [&](auto f) {
 #pragma unroll
-                for (int i = 0; i < kDsSampPerWave; i++) f(skey[i], half == 0 && skey[i] != 0u);
-            }, base, width, need, hist, pass, wsum, sh);
+            for (int i = 0; i < kDsSampPerWave; i++) f(skey[i], half == 0 && skey[i] != 0u);
+        };
+        while (width > 0) {                                                      // workgroup-uniform
+            span_pass<kDfThreads>(samples, base, width, need, inbin, hist, pass, wsum, sh);
+            if (width > 0 && inbin <= 64u) span_finish(samples, base, width, need, fin, sh);
+        }
         T = base;
     }
     __syncthreads();                                   // wcnt is reused below
@@ -1869,6 +1913,7 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
     __shared__ uint4 bmT4[kDsWords / 4];                             // ties to choose from
     __shared__ uint2 cl[kIdxPfCands];                                // compacted above-threshold candidates
     __shared__ __attribute__((aligned(16))) uint32_t hist[2 * 2048];
+    __shared__ uint32_t fin[65];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t segoff[2][kDecMaxSeg];
     __shared__ uint32_t segcnt[kDecMaxSeg];                          // stored above-threshold entries
@@ -1933,6 +1978,7 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
         bmT4[i] = make_uint4(0u, 0u, 0u, 0u);
     }
     for (int i = tid; i < 2 * 2048; i += kDsThreads) hist[i] = 0u;
+    if (tid == 0) fin[64] = 0u;
     __syncthreads();
     uint2 cv[kDsCPT];
 #pragma unroll
@@ -1949,13 +1995,16 @@ __global__ __launch_bounds__(kDsThreads) void k_idxd_select(IndexerArgs a) {
         for (int q = 0; q < kDsCPT; q++)
             if (tid + q * kDsThreads < (int)tot) { mn = min(mn, cv[q].x); mx = max(mx, cv[q].x); }
         block_minmax(mn, mx, mm);
-        uint32_t need = k, prefix = mn;
+        uint32_t need = k, prefix = mn, inbin = 0;
         int width = bit_width(mx - mn), pass = 0;
-        while (width > 0)                                            // workgroup-uniform
-            span_pass<kDsThreads>([&](auto f) {
+        auto cands = [&](auto f) {
 #pragma unroll
-                for (int q = 0; q < kDsCPT; q++) f(cv[q].x, tid + q * kDsThreads < (int)tot);
-            }, prefix, width, need, hist, pass, wsum[0], sh);
+            for (int q = 0; q < kDsCPT; q++) f(cv[q].x, tid + q * kDsThreads < (int)tot);
+        };
+        while (width > 0) {                                          // workgroup-uniform
+            span_pass<kDsThreads>(cands, prefix, width, need, inbin, hist, pass, wsum[0], sh);
+            if (width > 0 && inbin <= 64u) span_finish(cands, prefix, width, need, fin, sh);
+        }
         const uint32_t T1 = prefix;
         needT = need;
 #pragma unroll

@@ -342,8 +342,9 @@ def test_indexer_decode_fallback_rows_exact():
     cannot serve, recomputed exactly: all weights zero (every key ties: more
     ties than the lists hold), and, for a query with positive codes and
     weights, the first four keys of every tile the decode filter samples
-    (one per window of ceil(tiles / 64) tiles, at offset (37 i + 11) mod
-    window in window i) made to outrank the rest: the sample's threshold is
+    (one per window of ceil(tiles / 64) tiles, at offset
+    floor(((37 i + 11) mod 64) window / 64) in window i) made to outrank the
+    rest: the sample's threshold is
     then the top score, which fewer than k keys of the row reach (too few
     candidates)."""
     g = synth.rng(571)
@@ -358,7 +359,7 @@ def test_indexer_decode_fallback_rows_exact():
     ntile = -(-cap // 32)                                    # query (1, 2) sees every block
     stride = -(-ntile // 64)
     for i in range(-(-ntile // stride)):
-        t0 = 32 * (i * stride + (i * 37 + 11) % stride)
+        t0 = 32 * (i * stride + (((i * 37 + 11) & 63) * stride >> 6))
         kc[1, t0:t0 + 4] = 0x77
         ks[1, t0:t0 + 4] = 127
     pos = np.array([[4 * cap - 1, 4 * cap - 1, 4 * 30000 + 1], [4 * 60000, 4 * cap - 1, 4 * cap - 1]], np.int32)
