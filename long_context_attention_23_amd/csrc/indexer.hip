@@ -913,8 +913,9 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
 // 32x32x64 product scores 32 keys for 8 queries (the per-row path pads the
 // four heads to 32 rows).  Kernels:
 //   T  per query, the r-th largest score key of a systematic sample (every
-//      stride-th 32-key tile); r * stride ~ 4k, so about 4k keys of the row
-//      score at or above it;
+//      stride-th 32-key tile); r * stride ~ 3k, so about 3k keys of the row
+//      score at or above it (fewer than k only far in the sample's tail: the
+//      row then goes to the exact kernel);
 //   F  16 queries per workgroup stream every key tile once; keys scoring
 //      above their query's threshold are appended (key, j) to per-(query,
 //      wave) segments, keys tying with it (j) to per-(query, wave) tie
@@ -2086,7 +2087,7 @@ static hipError_t launch_tpl(IndexerArgs a, int64_t total_rows, int64_t ws_bytes
             const unsigned B = (unsigned)(total_rows / a.Tq);
             const int64_t ntile = (a.cap + 31) / 32;
             const int64_t stride = std::max<int64_t>(64, (ntile + kPfMaxSampTiles - 1) / kPfMaxSampTiles);
-            const int32_t rank = (int32_t)((4 * (int64_t)a.topk + stride - 1) / stride);
+            const int32_t rank = (int32_t)((3 * (int64_t)a.topk + stride - 1) / stride);
             a.row0 = 0;
             a.rows = (int32_t)total_rows;
             a.ws_row_bytes = idx_prefill_row_bytes();
