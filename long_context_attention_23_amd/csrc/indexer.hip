@@ -917,7 +917,7 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
 //      score at or above it (fewer than k only far in the sample's tail: the
 //      row then goes to the exact kernel);
 //   F  16 queries per workgroup stream every key tile once; keys scoring
-//      above their query's threshold are appended (key, j) to per-(query,
+//      above their query's threshold are appended (score bits, j) to per-(query,
 //      wave) segments, keys tying with it (j) to per-(query, wave) tie
 //      segments that keep each wave's first ties in ascending j (no atomics:
 //      each wave counts its own);
@@ -949,8 +949,8 @@ static_assert(idx_prefill_row_bytes() == kPfHdr + (int64_t)kIdxPfCands * 8 + (in
               "prefill row layout");
 
 // row layout: header words [0] threshold key, [1] flag, [2..10) above counts
-// per wave, [10..18) tie counts per wave; then the above-threshold (key, j)
-// segments, then the tie j segments (each wave's first kPfTieSeg ties, in
+// per wave, [10..18) tie counts per wave; then the above-threshold (score
+// bits, j) segments, then the tie j segments (each wave's first kPfTieSeg ties, in
 // ascending j)
 __device__ __forceinline__ uint32_t* pf_hdr(const IndexerArgs& a, int64_t row) {
     return reinterpret_cast<uint32_t*>(a.ws + row * a.ws_row_bytes);
@@ -1161,7 +1161,14 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                     bt &= vm;
                 }
                 if (bal | bt) {
-                    const bool above = (bal >> lane) & 1u, tie = (bt >> lane) & 1u;
+                    // this lane's own tests as vector compares (exec masks
+                    // straight from them, no bit extraction from the ballots)
+                    bool above = sc > thr[rb][s], tie = sc == thr[rb][s];
+                    if constexpr (kVis) {
+                        const bool vis = j < nq[rb][s];
+                        above = above && vis;
+                        tie = tie && vis;
+                    }
                     // rank among this half's hits: mbcnt over the whole wave,
                     // less the lower half's count for the upper half
                     const uint32_t alo = (uint32_t)bal, ahi = (uint32_t)(bal >> 32);
@@ -1170,8 +1177,8 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                     if (above) {
                         const uint32_t r = __builtin_amdgcn_mbcnt_hi(ahi, __builtin_amdgcn_mbcnt_lo(alo, 0u));
                         const uint32_t pos = r + (half ? cnt[rb][s][1] - __popc(alo) : cnt[rb][s][0]);
-                        if (pos < (uint32_t)kPfSeg)
-                            reinterpret_cast<uint2*>(rp + kPfHdr)[wv * kPfSeg + pos] = make_uint2(score_key(sc), (uint32_t)j);
+                        if (pos < (uint32_t)kPfSeg)                      // the select forms the key
+                            reinterpret_cast<uint2*>(rp + kPfHdr)[wv * kPfSeg + pos] = make_uint2(__float_as_uint(sc), (uint32_t)j);
                     }
                     if (tie) {
                         const uint32_t r = __builtin_amdgcn_mbcnt_hi(thi, __builtin_amdgcn_mbcnt_lo(tlo, 0u));
@@ -1372,6 +1379,8 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
         cv[q] = make_uint2(0u, 0u);
         if (i < tot) cv[q] = cand[pf_slot(i, segc, kPfSeg)];
     }
+#pragma unroll
+    for (int q = 0; q < kCPT; q++) cv[q].x = score_key(__uint_as_float(cv[q].x));   // the filter stores score bits
     for (int i = tid; i < nw4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tot >= k) {
         // the top k lie among the keys above the threshold: three digit passes
