@@ -936,6 +936,7 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
 // are among the stored ones (a wave's ties arrive in ascending j).
 constexpr int kPfQ = 8;                  // queries per MFMA row block
 constexpr int kPfRB = 2;                 // row blocks per filter workgroup
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kPfQB = kPfQ * kPfRB;      // queries per filter workgroup
 constexpr int kPfThreads = 512;          // threshold, filter and exact workgroups
 constexpr int kPfWaves = kPfThreads / kWave;
@@ -1122,13 +1123,18 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
         for (int s = 0; s < 4; s++) { cnt[rb][s][0] = cnt[rb][s][1] = tcnt[rb][s][0] = tcnt[rb][s][1] = 0u; }
     const int64_t rowb = a.ws_row_bytes;
     uint8_t* wbase = a.ws + ((int64_t)b * a.Tq + t0) * rowb;   // this workgroup's first query row
+    // appends go through a buffer resource over the workgroup's query rows:
+    // 32-bit offsets (the uniform part on the scalar unit), no 64-bit
+    // address arithmetic per append
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        wbase, (short)0, (int)(min(kPfQB, a.Tq - t0) * rowb), 0x00020000);
+    const int wvs = __builtin_amdgcn_readfirstlane(wv);
     uint4 kc;
     int ks;
     if (wv < ntile) pf_load_keys(a, b, (int64_t)wv * 32, l32, half, kc, ks);
     for (int tile = wv; tile < ntile; tile += kPfWaves) {
-        // odd queries of a slot pair, re-derived every tile (the empty asm
-        // keeps the compiler from hoisting eight 64-bit row addresses out of
-        // the loop, which would not fit in four waves' registers)
+        // odd queries of a slot pair: one row further (re-derived every tile,
+        // so that no per-slot offsets are kept in registers across the loop)
         uint32_t hoff = half ? (uint32_t)rowb : 0u;
         asm volatile("" : "+v"(hoff));
         const uint4 kcur = kc;
@@ -1173,18 +1179,22 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                     // less the lower half's count for the upper half
                     const uint32_t alo = (uint32_t)bal, ahi = (uint32_t)(bal >> 32);
                     const uint32_t tlo = (uint32_t)bt, thi = (uint32_t)(bt >> 32);
-                    uint8_t* rp = wbase + (int64_t)(kPfQ * rb + 2 * s) * rowb + (int64_t)hoff;
+                    const int slot = (kPfQ * rb + 2 * s) * (int)rowb;   // the pair's even query row
                     if (above) {
                         const uint32_t r = __builtin_amdgcn_mbcnt_hi(ahi, __builtin_amdgcn_mbcnt_lo(alo, 0u));
                         const uint32_t pos = r + (half ? cnt[rb][s][1] - __popc(alo) : cnt[rb][s][0]);
-                        if (pos < (uint32_t)kPfSeg)                      // the select forms the key
-                            reinterpret_cast<uint2*>(rp + kPfHdr)[wv * kPfSeg + pos] = make_uint2(__float_as_uint(sc), (uint32_t)j);
+                        if (pos < (uint32_t)kPfSeg) {                    // the select forms the key
+                            const u32x2_t v = {__float_as_uint(sc), (uint32_t)j};
+                            __builtin_amdgcn_raw_buffer_store_b64(v, wres, (int)(hoff + 8 * pos),
+                                                                  slot + kPfHdr + 8 * kPfSeg * wvs, 0);
+                        }
                     }
                     if (tie) {
                         const uint32_t r = __builtin_amdgcn_mbcnt_hi(thi, __builtin_amdgcn_mbcnt_lo(tlo, 0u));
                         const uint32_t pos = r + (half ? tcnt[rb][s][1] - __popc(tlo) : tcnt[rb][s][0]);
                         if (pos < (uint32_t)kPfTieSeg)
-                            reinterpret_cast<uint32_t*>(rp + kPfHdr + (int64_t)kIdxPfCands * 8)[wv * kPfTieSeg + pos] = (uint32_t)j;
+                            __builtin_amdgcn_raw_buffer_store_b32((uint32_t)j, wres, (int)(hoff + 4 * pos),
+                                                                  slot + kPfHdr + kIdxPfCands * 8 + 4 * kPfTieSeg * wvs, 0);
                     }
                     cnt[rb][s][0] += __popc(alo);
                     cnt[rb][s][1] += __popc(ahi);
