@@ -907,6 +907,133 @@ __global__ __launch_bounds__(kIdxFinalThreads) void k_idx_final(IndexerArgs a) {
     for (int i = threadIdx.x; i < a.topk; i += blockDim.x) out[i] = arr[i];
 }
 
+// ------------------------------------------------------------------ radix helpers
+// In an nb-bin histogram (nb = BPT x the workgroup's threads), the digit whose
+// cumulative count from the top first reaches need, and the count strictly
+// above it, found by the whole workgroup: thread t sums the BPT bins
+// [nb - BPT (t + 1), nb - BPT t) with one vector read (consecutive threads,
+// consecutive bins: no bank conflicts), a workgroup scan orders the sums from
+// the top, and the thread holding the need-th count writes (digit, above,
+// count in the digit's bin) to sh[0..2].  Every thread calls it; read sh after
+// a barrier.
+template <int BPT>
+__device__ __forceinline__ void block_pick(const uint32_t* hist, uint32_t need, uint32_t* wsum, uint32_t* sh) {
+    static_assert(BPT == 1 || BPT == 2 || BPT == 4, "bins per thread");
+    const int nb = BPT * (int)blockDim.x;
+    const int lo = nb - BPT * ((int)threadIdx.x + 1);            // lowest bin of this thread's range
+    uint32_t h[BPT];
+    if constexpr (BPT == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(hist + lo);
+        h[0] = v.w; h[1] = v.z; h[2] = v.y; h[3] = v.x;            // highest bin first
+    } else if constexpr (BPT == 2) {
+        const uint2 v = *reinterpret_cast<const uint2*>(hist + lo);
+        h[0] = v.y; h[1] = v.x;
+    } else {
+        h[0] = hist[lo];
+    }
+    uint32_t s = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; q++) s += h[q];
+    const uint32_t ex = block_exclusive_scan(s, wsum);            // counts in the bins above mine
+    if (ex < need && ex + s >= need) {
+        uint32_t c = ex;
+#pragma unroll
+        for (int q = 0; q < BPT; q++) {
+            if (c + h[q] >= need) { sh[0] = (uint32_t)(lo + BPT - 1 - q); sh[1] = c; sh[2] = h[q]; break; }
+            c += h[q];
+        }
+    }
+}
+
+// smallest and largest of v over the workgroup (all threads call; wv is the
+// caller's scratch of one word pair per wave; a barrier inside)
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint2* wv) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
+    }
+    if ((threadIdx.x & (kWave - 1)) == 0) wv[threadIdx.x / kWave] = make_uint2(mn, mx);
+    __syncthreads();
+    const int nw = (int)(blockDim.x / kWave);
+    for (int q = 0; q < nw; q++) {
+        const uint2 x = wv[q];
+        mn = min(mn, x.x);
+        mx = max(mx, x.y);
+    }
+}
+
+// One pass of a radix select over values known to lie in [base, base + 2^width)
+// (width <= 32): the digit is (v - base) >> shift with shift = width - 11 (or
+// 0), so the values spread over up to 2048 bins wherever the range starts --
+// score keys crowd into a few top-bit bins, and LDS atomics on one address
+// serialise.  add(f) calls f(v, in) for this thread's candidates; the bin
+// holding the need-th largest becomes the new range.  With kTwo, passes
+// alternate between two histograms of 2048 bins (hists + 2048 * (pass & 1)),
+// both zero before the first pass: a pass clears its own after the last read
+// of it, and the barriers of the next pass order that clear before the pass
+// after it, so no pass needs a barrier of its own for the clearing.  Without
+// kTwo (one histogram, where LDS is short) the clearing takes a barrier.
+template <int NT, bool kTwo = true, typename Add>
+__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t& inbin,
+                                          uint32_t* hists, int& pass, uint32_t* wsum, uint32_t* sh) {
+    uint32_t* hist = kTwo ? hists + 2048 * (pass & 1) : hists;
+    const int shift = width > 11 ? width - 11 : 0;
+    const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
+    add([&](uint32_t v, bool in) {
+        const uint32_t d = v - base;                   // wraps past lim for v below base
+        if (in && d <= lim) atomicAdd(&hist[d >> shift], 1u);
+    });
+    __syncthreads();
+    block_pick<2048 / NT>(hist, need, wsum, sh);
+    __syncthreads();
+    base += sh[0] << shift;
+    need -= sh[1];
+    inbin = sh[2];
+    width = shift;
+    pass++;
+    for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0u;
+    if constexpr (!kTwo) __syncthreads();
+}
+
+// A range [base, base + 2^width) left by span_pass that holds few values
+// (inbin <= 64) is finished by one wave instead of further passes: the
+// values in it go to fin[0..63] (fin[64] counts them, zero on entry), and
+// lane i of wave 0 counts the listed values above and equal to its own; the
+// lane whose value is the need-th largest gives base = that value and
+// need -= the count above it, as the remaining passes would (width becomes
+// 0).  Lanes holding equal values write equal results.  Two barriers.
+template <typename Add>
+__device__ __forceinline__ void span_finish(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* fin,
+                                            uint32_t* sh) {
+    const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
+    add([&](uint32_t v, bool in) {
+        if (in && v - base <= lim) {
+            const uint32_t i = atomicAdd(&fin[64], 1u);
+            if (i < 64u) fin[i] = v;
+        }
+    });
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const uint32_t n = min(fin[64], 64u);
+        const uint32_t lane = threadIdx.x;
+        const uint32_t x = lane < n ? fin[lane] : 0u;
+        uint32_t g = 0, e = 0;
+        for (uint32_t j = 0; j < n; j++) {
+            const uint32_t y = fin[j];
+            g += y > x ? 1u : 0u;
+            e += y == x ? 1u : 0u;
+        }
+        if (lane < n && g < need && need <= g + e) { sh[0] = x; sh[1] = g; }
+    }
+    __syncthreads();
+    base = sh[0];
+    need -= sh[1];
+    width = 0;
+}
+
+__device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
+
 // ------------------------------------------------------------------ prefill path
 // A chunk of many query rows with FP4 queries and keys (di = 64, Hi = 4):
 // eight queries x four heads fill the 32 rows of one FP4 MFMA, so one
@@ -1350,6 +1477,8 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
     constexpr int kCPT = kIdxPfCands / kPfSelThreads;          // candidates per thread
     __shared__ uint4 bm4[kPfWords / 4];
     __shared__ uint32_t hist[2048];
+    __shared__ uint32_t fin[65];
+    __shared__ uint2 mm[kPfSelThreads / kWave];
     __shared__ uint32_t sh[4];
     __shared__ uint32_t wsum[kPfSelThreads / kWave];
     uint32_t* bm = reinterpret_cast<uint32_t*>(bm4);
@@ -1393,33 +1522,26 @@ __global__ __launch_bounds__(kPfSelThreads) void k_idxp_select(IndexerArgs a) {
     for (int q = 0; q < kCPT; q++) cv[q].x = score_key(__uint_as_float(cv[q].x));   // the filter stores score bits
     for (int i = tid; i < nw4; i += blockDim.x) bm4[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tot >= k) {
-        // the top k lie among the keys above the threshold: three digit passes
-        // over the 32-bit score key (11, 11, 10 bits), then the smallest j of
-        // the ties at the k-th largest key
-        uint32_t need = k, prefix = 0, pmask = 0;
-        const int shifts[3] = {21, 10, 0};
-        const uint32_t masks[3] = {2047u, 2047u, 1023u};
-        for (int p = 0; p < 3; p++) {
-            for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;
-            __syncthreads();
+        // the top k lie among the keys above the threshold: range-adaptive
+        // radix passes over their score keys, finished in one wave once the
+        // range holds at most 64 of them, give the k-th largest key; then the
+        // smallest j of the ties at it
+        for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;
+        if (tid == 0) fin[64] = 0u;
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
-            for (int q = 0; q < kCPT; q++) {
-                if (q * kPfSelThreads >= tot) break;              // block-uniform
-                const bool in = tid + q * kPfSelThreads < tot && (cv[q].x & pmask) == prefix;
-                pf_hist_round(cv[q].x, in, shifts[p], masks[p], hist);
-            }
-            __syncthreads();
-            if (tid < kWave) {
-                uint32_t dg, ab;
-                if (p < 2) pf_pick<2048>(hist, need, dg, ab);
-                else pf_pick<1024>(hist, need, dg, ab);
-                if (tid == 0) { sh[0] = dg; sh[1] = ab; }
-            }
-            __syncthreads();
-            prefix |= sh[0] << shifts[p];
-            pmask |= masks[p] << shifts[p];
-            need -= sh[1];
-            __syncthreads();
+        for (int q = 0; q < kCPT; q++)
+            if (tid + q * kPfSelThreads < (int)tot) { mn = min(mn, cv[q].x); mx = max(mx, cv[q].x); }
+        block_minmax(mn, mx, mm);                                // barrier inside: hist and fin cleared
+        uint32_t need = k, prefix = mn, inbin = 0;
+        int width = bit_width(mx - mn), pass = 0;
+        auto cands = [&](auto f) {
+#pragma unroll
+            for (int q = 0; q < kCPT; q++) f(cv[q].x, tid + q * kPfSelThreads < (int)tot);
+        };
+        while (width > 0) {                                      // workgroup-uniform
+            span_pass<kPfSelThreads, false>(cands, prefix, width, need, inbin, hist, pass, wsum, sh);
+            if (width > 0 && inbin <= 64u) span_finish(cands, prefix, width, need, fin, sh);
         }
         const uint32_t T1 = prefix;
         uint32_t jv[kCPT];
@@ -1595,129 +1717,6 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_exact(IndexerArgs a) {
 //      above T (a sample ranked too high), is recomputed exactly in place.
 // Every kernel forms a key's score from the same MFMA result and the same
 // fp32 operations, so the score is the same number in all of them.
-// In an nb-bin histogram (nb = BPT x the workgroup's threads), the digit whose
-// cumulative count from the top first reaches need, and the count strictly
-// above it, found by the whole workgroup: thread t sums the BPT bins
-// [nb - BPT (t + 1), nb - BPT t) with one vector read (consecutive threads,
-// consecutive bins: no bank conflicts), a workgroup scan orders the sums from
-// the top, and the thread holding the need-th count writes (digit, above,
-// count in the digit's bin) to sh[0..2].  Every thread calls it; read sh after
-// a barrier.
-template <int BPT>
-__device__ __forceinline__ void block_pick(const uint32_t* hist, uint32_t need, uint32_t* wsum, uint32_t* sh) {
-    static_assert(BPT == 1 || BPT == 2 || BPT == 4, "bins per thread");
-    const int nb = BPT * (int)blockDim.x;
-    const int lo = nb - BPT * ((int)threadIdx.x + 1);            // lowest bin of this thread's range
-    uint32_t h[BPT];
-    if constexpr (BPT == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(hist + lo);
-        h[0] = v.w; h[1] = v.z; h[2] = v.y; h[3] = v.x;            // highest bin first
-    } else if constexpr (BPT == 2) {
-        const uint2 v = *reinterpret_cast<const uint2*>(hist + lo);
-        h[0] = v.y; h[1] = v.x;
-    } else {
-        h[0] = hist[lo];
-    }
-    uint32_t s = 0;
-#pragma unroll
-    for (int q = 0; q < BPT; q++) s += h[q];
-    const uint32_t ex = block_exclusive_scan(s, wsum);            // counts in the bins above mine
-    if (ex < need && ex + s >= need) {
-        uint32_t c = ex;
-#pragma unroll
-        for (int q = 0; q < BPT; q++) {
-            if (c + h[q] >= need) { sh[0] = (uint32_t)(lo + BPT - 1 - q); sh[1] = c; sh[2] = h[q]; break; }
-            c += h[q];
-        }
-    }
-}
-
-// smallest and largest of v over the workgroup (all threads call; wv is the
-// caller's scratch of one word pair per wave; a barrier inside)
-__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint2* wv) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, kWave));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, kWave));
-    }
-    if ((threadIdx.x & (kWave - 1)) == 0) wv[threadIdx.x / kWave] = make_uint2(mn, mx);
-    __syncthreads();
-    const int nw = (int)(blockDim.x / kWave);
-    for (int q = 0; q < nw; q++) {
-        const uint2 x = wv[q];
-        mn = min(mn, x.x);
-        mx = max(mx, x.y);
-    }
-}
-
-// One pass of a radix select over values known to lie in [base, base + 2^width)
-// (width <= 32): the digit is (v - base) >> shift with shift = width - 11 (or
-// 0), so the values spread over up to 2048 bins wherever the range starts --
-// score keys crowd into a few top-bit bins, and LDS atomics on one address
-// serialise.  add(f) calls f(v, in) for this thread's candidates; the bin
-// holding the need-th largest becomes the new range.  Passes alternate
-// between two histograms of 2048 bins (hists + 2048 * (pass & 1)), both zero
-// before the first pass: a pass clears its own after the last read of it, and
-// the barriers of the next pass order that clear before the pass after it, so
-// no pass needs a barrier of its own for the clearing.
-template <int NT, typename Add>
-__device__ __forceinline__ void span_pass(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t& inbin,
-                                          uint32_t* hists, int& pass, uint32_t* wsum, uint32_t* sh) {
-    uint32_t* hist = hists + 2048 * (pass & 1);
-    const int shift = width > 11 ? width - 11 : 0;
-    const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
-    add([&](uint32_t v, bool in) {
-        const uint32_t d = v - base;                   // wraps past lim for v below base
-        if (in && d <= lim) atomicAdd(&hist[d >> shift], 1u);
-    });
-    __syncthreads();
-    block_pick<2048 / NT>(hist, need, wsum, sh);
-    __syncthreads();
-    base += sh[0] << shift;
-    need -= sh[1];
-    inbin = sh[2];
-    width = shift;
-    pass++;
-    for (int i = threadIdx.x; i < 2048; i += NT) hist[i] = 0u;
-}
-
-// A range [base, base + 2^width) left by span_pass that holds few values
-// (inbin <= 64) is finished by one wave instead of further passes: the
-// values in it go to fin[0..63] (fin[64] counts them, zero on entry), and
-// lane i of wave 0 counts the listed values above and equal to its own; the
-// lane whose value is the need-th largest gives base = that value and
-// need -= the count above it, as the remaining passes would (width becomes
-// 0).  Lanes holding equal values write equal results.  Two barriers.
-template <typename Add>
-__device__ __forceinline__ void span_finish(Add add, uint32_t& base, int& width, uint32_t& need, uint32_t* fin,
-                                            uint32_t* sh) {
-    const uint32_t lim = width >= 32 ? 0xFFFFFFFFu : (1u << width) - 1u;
-    add([&](uint32_t v, bool in) {
-        if (in && v - base <= lim) {
-            const uint32_t i = atomicAdd(&fin[64], 1u);
-            if (i < 64u) fin[i] = v;
-        }
-    });
-    __syncthreads();
-    if (threadIdx.x < kWave) {
-        const uint32_t n = min(fin[64], 64u);
-        const uint32_t lane = threadIdx.x;
-        const uint32_t x = lane < n ? fin[lane] : 0u;
-        uint32_t g = 0, e = 0;
-        for (uint32_t j = 0; j < n; j++) {
-            const uint32_t y = fin[j];
-            g += y > x ? 1u : 0u;
-            e += y == x ? 1u : 0u;
-        }
-        if (lane < n && g < need && need <= g + e) { sh[0] = x; sh[1] = g; }
-    }
-    __syncthreads();
-    base = sh[0];
-    need -= sh[1];
-    width = 0;
-}
-
-__device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __builtin_clz(x) : 0; }
 
 constexpr int kDfThreads = 512;
 constexpr int kDfWaves = kDfThreads / kWave;
