@@ -90,7 +90,8 @@ struct MfmaSmem : MfmaTiles<D, DR, F8> {
     float fin[64];                        // per-head final factor (single-split rows)
     float ssq[4][64];                     // per-quarter sums of squares of the queries
     alignas(8) int moved[4];              // per head group: accumulators need rescaling
-    double rf[64];                        // RoPE inverse frequencies
+    float2 qsc[DR / 2];                   // (sin, cos) of t * freq, per RoPE pair (query)
+    float2 osc[DR / 2];                   // (sin, cos) of -t * freq (output)
 };
 
 // ---- per-row entry enumeration (wave-uniform)
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     constexpr int KS = DQ / 32;            // Q K^T K-steps per wave
     constexpr int NT = DQ / 16;            // P V N-tiles per wave
     constexpr int dn = D - DR;             // non-RoPE dims (multiple of 32)
+    static_assert(DR / 2 <= 32, "one RoPE pair per lane of half a wave");
     constexpr int RS = D * 2 + 16;         // bf16 tile row stride in bytes
     constexpr int REC = fp8_rec_bytes<D, DR>();   // FP8 ring row stride in bytes
     constexpr uint32_t kAll = (1u << kEntPerWave) - 1;
@@ -360,17 +362,28 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             qraw[mt][ks] = *reinterpret_cast<const uint4*>(qb + (hg + l16) * D + dbase + 32 * ks + 8 * g4);
     }
     float4 gam[KS][2];
+    const bool hasg = a.gamma_q != nullptr;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
-        const float* gsrc = a.gamma_q ? a.gamma_q + dbase + 32 * ks + 8 * g4 : reinterpret_cast<const float*>(a.q);
+        const float* gsrc = hasg ? a.gamma_q + dbase + 32 * ks + 8 * g4 : reinterpret_cast<const float*>(a.q);
         const float4 g0 = reinterpret_cast<const float4*>(gsrc)[0], g1 = reinterpret_cast<const float4*>(gsrc)[1];
-        const float4 one = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-        gam[ks][0] = a.gamma_q ? g0 : one;
-        gam[ks][1] = a.gamma_q ? g1 : one;
+        // component selects (a select of whole vectors became a private-array lookup)
+        gam[ks][0] = make_float4(hasg ? g0.x : 1.0f, hasg ? g0.y : 1.0f, hasg ? g0.z : 1.0f, hasg ? g0.w : 1.0f);
+        gam[ks][1] = make_float4(hasg ? g1.x : 1.0f, hasg ? g1.y : 1.0f, hasg ? g1.z : 1.0f, hasg ? g1.w : 1.0f);
     }
 
     const int b = row / a.Tq;
     const int t = load_uniform_i32(a.q_pos + row);
+    // the RoPE factors of the position, for the query (t) and the output
+    // (-t), one pair per lane of wave 0, computed while the query loads are
+    // in flight (read after the prologue's barrier)
+    if (w == 0 && (lane & 31) < DR / 2) {
+        const double* rfa = (const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(AttnArgs, rope));
+        const int p = lane & 31;
+        float sn, cs;
+        rope_sincos(lane < 32 ? (double)t : -(double)t, rfa[p], sn, cs);
+        (lane < 32 ? sm.qsc : sm.osc)[p] = make_float2(sn, cs);
+    }
     RowCtx c;
     c.vis = t < 0 ? 0 : (t + 1) / a.m;
     if (c.vis > a.ccap) c.vis = (int32_t)a.ccap;
@@ -428,7 +441,6 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
         }
     }
-    stage_rope_arg(offsetof(AttnArgs, rope), sm.rf, a.dr / 2);
 
     // ---- query prologue: q^ = RoPE_t(RMSNorm(q)), this wave's 32 heads and quarter
 #pragma unroll
@@ -468,8 +480,11 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         }
         if (ks >= nks) {
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-                rope_sincos((double)t, sm.rf[(dbase + 32 * ks + 8 * g4 + 2 * j - dn) / 2], sn[j], cs[j]);
+            for (int j = 0; j < 4; j++) {
+                const float2 v = sm.qsc[(dbase + 32 * ks + 8 * g4 + 2 * j - dn) / 2];
+                sn[j] = v.x;
+                cs[j] = v.y;
+            }
         }
 #pragma unroll
         for (int mt = 0; mt < 2; mt++) {
@@ -777,7 +792,11 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             const int dim = dbase + 16 * nd + l16;
             const bool rope = nd >= nnt;
             float sn = 0.0f, cs = 1.0f;
-            if (rope) rope_sincos(-(double)t, sm.rf[(dim - dn) / 2], sn, cs);
+            if (rope) {
+                const float2 v = sm.osc[(dim - dn) / 2];
+                sn = v.x;
+                cs = v.y;
+            }
 #pragma unroll
             for (int mt = 0; mt < 2; mt++) {
                 const int g = 2 * hp + mt;
