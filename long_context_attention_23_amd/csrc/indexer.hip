@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kIdxScoreThreads) void k_idx_score_mfma(IndexerArgs
     constexpr int DI = 64;
     constexpr int NKS = KF == CSA_FP4_E2M1 ? 1 : 4;            // K steps per 32-key group
     // 32-key groups whose loads a wave issues before computing them
-    constexpr int kIdxMfmaBatch = KF == CSA_FP4_E2M1 ? kIdxChunk / kIdxScoreThreads : 4;
+    constexpr int kIdxMfmaBatch = KF == CSA_FP4_E2M1 ? kIdxChunk / kIdxScoreThreads : 3;   // bf16: 4 would spill
     constexpr int KROW = KF == CSA_FP4_E2M1 ? DI / 2 : 2 * DI;  // key row bytes
     __shared__ uint32_t lh[kIdxHistBins];
     const int64_t r = blockIdx.y, row = a.row0 + r;
