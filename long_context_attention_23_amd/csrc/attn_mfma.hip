@@ -307,7 +307,10 @@ __device__ __forceinline__ uint2 lds_read_tr8(const void* p) {
 // (row pitch = 4 banks mod 32: offsets 0, 8, 16, 24 banks)
 __device__ __forceinline__ int pv_k_of_entry(int e) { return (e & ~7) + 4 * (e & 1) + ((e & 7) >> 1); }
 
-template <int D, int DR, bool F8, typename OT>
+// MTW: 16-head groups per wave.  2: wave w takes the 32 heads of half w / 4
+// (64 heads per workgroup); 1: wave w takes the 16 heads of group w / 4 (a
+// workgroup of at most 32 heads keeps all eight waves busy in the products).
+template <int D, int DR, bool F8, typename OT, int MTW>
 __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     warm_kernargs(offsetof(AttnArgs, rope));
     constexpr int DQ = D / 4;              // dims per quarter
@@ -323,6 +326,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qd = w & 3, hp = w >> 2;                 // dim quarter, head half
+    const int g0 = MTW * hp;                           // this wave's first 16-head group
     const int l16 = lane & 15, g4 = lane >> 4;
     const int row = blockIdx.y;
     const int h0 = blockIdx.z * 64;
@@ -353,10 +357,10 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     // results are never stored), and without gamma the loads read the query
     // and are replaced by ones.
     const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)row * a.H + h0) * D;
-    uint4 qraw[2][KS];
+    uint4 qraw[MTW][KS];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-        const int hg = (2 * hp + mt < MT) ? 32 * hp + 16 * mt : 0;
+    for (int mt = 0; mt < MTW; mt++) {
+        const int hg = (g0 + mt < MT) ? 16 * (g0 + mt) : 0;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++)
             qraw[mt][ks] = *reinterpret_cast<const uint4*>(qb + (hg + l16) * D + dbase + 32 * ks + 8 * g4);
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const int32_t sp = blockIdx.x;
     if (sp >= nsplit) return;
     const int32_t e0 = sp * split, e1 = min(e0 + split, ne);
-    const bool active = 2 * hp < MT;                   // this wave's head half exists
+    const bool active = g0 < MT;                       // this wave's first head group exists
     const bool owner = w < MT;                         // wave w runs the softmax of head group w
     // non-RoPE K-steps / N-tiles of this quarter
     const int nks = max(0, min(KS, (dn - dbase) / 32));
@@ -444,7 +448,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
 
     // ---- query prologue: q^ = RoPE_t(RMSNorm(q)), this wave's 32 heads and quarter
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
+    for (int mt = 0; mt < MTW; mt++) {
         float ss = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
@@ -457,17 +461,17 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         }
         ss += __shfl_xor(ss, 16, kWave);
         ss += __shfl_xor(ss, 32, kWave);
-        if (g4 == 0) sm.ssq[qd][32 * hp + 16 * mt + l16] = ss;
+        if (g4 == 0) sm.ssq[qd][16 * (g0 + mt) + l16] = ss;
     }
     lds_barrier();
-    float inv[2];
+    float inv[MTW];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++) {
-        const int hl = 32 * hp + 16 * mt + l16;
+    for (int mt = 0; mt < MTW; mt++) {
+        const int hl = 16 * (g0 + mt) + l16;
         const float ss = ((sm.ssq[0][hl] + sm.ssq[1][hl]) + sm.ssq[2][hl]) + sm.ssq[3][hl];
         inv[mt] = 1.0f / sqrtf(ss / (float)D + a.eps);
     }
-    bf16x8_t qf[2][KS];
+    bf16x8_t qf[MTW][KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
         const float gv[8] = {gam[ks][0].x, gam[ks][0].y, gam[ks][0].z, gam[ks][0].w,
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             }
         }
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
+        for (int mt = 0; mt < MTW; mt++) {
             const uint32_t wd[4] = {qraw[mt][ks].x, qraw[mt][ks].y, qraw[mt][ks].z, qraw[mt][ks].w};
 #pragma unroll
             for (int j = 0; j < 4; j++) {
@@ -501,9 +505,9 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
 
     // P rows of a head group beyond MT are never written: its accumulators
     // collect garbage and are never stored
-    f32x4_t o[2][NT];
+    f32x4_t o[MTW][NT];
 #pragma unroll
-    for (int mt = 0; mt < 2; mt++)
+    for (int mt = 0; mt < MTW; mt++)
 #pragma unroll
         for (int nd = 0; nd < NT; nd++) o[mt][nd] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     // running max (base 2) of the owned heads 16w + 4*g4 + i, and this lane's
@@ -571,25 +575,25 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         }
 #pragma unroll
         for (int n = 0; n < 2; n++) {
-            f32x4_t acc[2];
+            f32x4_t acc[MTW];
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int mt = 0; mt < MTW; mt++) acc[mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) {
                 if (ks == NKS && ks > 0) {
 #pragma unroll
-                    for (int mt = 0; mt < 2; mt++) acc[mt] *= esc[n];
+                    for (int mt = 0; mt < MTW; mt++) acc[mt] *= esc[n];
                 }
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++)
+                for (int mt = 0; mt < MTW; mt++)
                     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[mt][ks], kb[n][ks], acc[mt], 0, 0, 0);
             }
             if (NKS == KS) {
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++) acc[mt] *= esc[n];
+                for (int mt = 0; mt < MTW; mt++) acc[mt] *= esc[n];
             }
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
+            for (int mt = 0; mt < MTW; mt++)
                 *reinterpret_cast<f32x4_t*>(&sm.zx[w][mt][n][lane][0]) = acc[mt];
         }
     };
@@ -603,7 +607,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             else esc[n] = sm.scale[bq][16 * n + l16];
             eok[n] = sm.valid[bq][16 * n + l16] != 0;
         }
-        const int src = 4 * (w >> 1), lg = w & 1;        // waves holding this group's quarters
+        const int src = 4 * (w / MTW), lg = w % MTW;    // waves holding this group's quarters
         f32x4_t z[2];
 #pragma unroll
         for (int n = 0; n < 2; n++) {
@@ -662,7 +666,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     // per-lane LDS coordinates of the transposing reads
     const int v_row = 8 * g4 + 2 * (l16 >> 2);
     const int p_row = 8 * g4 + (l16 >> 2);
-    const int p_col = 32 * hp + 4 * (l16 & 3);
+    const int p_col = 16 * g0 + 4 * (l16 & 3);
     // rescale O of the head groups whose max moved at tile tt (rare), then
     // O += P V.  The quarter is a template constant: the FP8/RoPE split of its
     // N-tiles is static, and the flags, P fragments and V fragments are all
@@ -670,11 +674,13 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     auto pv_step = [&](auto qdc, int bq) {
         constexpr int DB = decltype(qdc)::value * DQ;
         constexpr int NNT = (dn - DB) / 16 < 0 ? 0 : ((dn - DB) / 16 > NT ? NT : (dn - DB) / 16);
-        const int2 mv = *reinterpret_cast<const int2*>(&sm.moved[2 * hp]);
-        // P A-fragments: scaled P for the non-RoPE dims, plain P for the RoPE dims
-        bf16x8_t pfs[2], pfp[2];
+        int mv[MTW];
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
+        for (int mt = 0; mt < MTW; mt++) mv[mt] = sm.moved[g0 + mt];      // g0 + mt <= 3
+        // P A-fragments: scaled P for the non-RoPE dims, plain P for the RoPE dims
+        bf16x8_t pfs[MTW], pfp[MTW];
+#pragma unroll
+        for (int mt = 0; mt < MTW; mt++) {
             if (NNT > 0) pfs[mt] = tr_pair(&sm.pt[0][p_row][16 * mt + p_col], &sm.pt[0][p_row + 4][16 * mt + p_col]);
             if (NNT < NT) pfp[mt] = tr_pair(&sm.pt[1][p_row][16 * mt + p_col], &sm.pt[1][p_row + 4][16 * mt + p_col]);
         }
@@ -702,9 +708,9 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             for (int nd = 0; nd < NT; nd++) vb[nd] = tr_pair(vp + 32 * nd, vp + RS + 32 * nd);
         }
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
-            const int g = 2 * hp + mt;
-            if (g < MT && (mt ? mv.y : mv.x)) {
+        for (int mt = 0; mt < MTW; mt++) {
+            const int g = g0 + mt;
+            if (g < MT && mv[mt]) {
                 const float4 al = *reinterpret_cast<const float4*>(&sm.alpha[16 * g + 4 * g4]);
 #pragma unroll
                 for (int nd = 0; nd < NT; nd++) {
@@ -718,7 +724,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
         for (int nd = 0; nd < NT; nd++)
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
+            for (int mt = 0; mt < MTW; mt++)
                 o[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nd < NNT ? pfs[mt] : pfp[mt], vb[nd], o[mt][nd], 0, 0, 0);
     };
     // the steps for this wave's quarter (wave-uniform dispatch)
@@ -798,8 +804,8 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
                 cs = v.y;
             }
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++) {
-                const int g = 2 * hp + mt;
+            for (int mt = 0; mt < MTW; mt++) {
+                const int g = g0 + mt;
                 if (g < MT) {
                     const float4 f = *reinterpret_cast<const float4*>(&sm.fin[16 * g + 4 * g4]);
                     const float fv[4] = {f.x, f.y, f.z, f.w};
@@ -834,12 +840,12 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         __syncthreads();
         if (active) {
 #pragma unroll
-            for (int mt = 0; mt < 2; mt++)
+            for (int mt = 0; mt < MTW; mt++)
 #pragma unroll
                 for (int nd = 0; nd < NT; nd++)
 #pragma unroll
                     for (int i = 0; i < 4; i++)
-                        ost[(32 * hp + 16 * mt + 4 * g4 + i) * (D + 8) + dbase + 16 * nd + l16] =
+                        ost[(16 * (g0 + mt) + 4 * g4 + i) * (D + 8) + dbase + 16 * nd + l16] =
                             f32_to_bf16(o[mt][nd][i]);
         }
         __syncthreads();
@@ -855,14 +861,16 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         for (int half = 0; half < 2; half++) {
             if (2 * half >= MT) break;
             __syncthreads();
-            if (hp == half) {
 #pragma unroll
-                for (int mt = 0; mt < 2; mt++)
+            for (int mt = 0; mt < MTW; mt++) {
+                const int g = g0 + mt;                       // head group; half g / 2
+                if ((g >> 1) == half) {
 #pragma unroll
                     for (int nd = 0; nd < NT; nd++)
 #pragma unroll
                         for (int i = 0; i < 4; i++)
-                            ost[(16 * mt + 4 * g4 + i) * (D + 4) + dbase + 16 * nd + l16] = o[mt][nd][i];
+                            ost[(16 * (g & 1) + 4 * g4 + i) * (D + 4) + dbase + 16 * nd + l16] = o[mt][nd][i];
+                }
             }
             __syncthreads();
             const int nv = min(32, 16 * MT - 32 * half) * (D / 4);      // float4s of the valid heads
@@ -898,11 +906,13 @@ static void launch_d(const AttnArgs& a0, int nsplit, hipStream_t st) {
     a.nsplit_max = nsplit;                              // part_bf16: set by launch_attention
     const int groups = (a.H + 63) / 64;
     dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)groups);
-    // eight waves per workgroup always (head halves x dim quarters); a
-    // workgroup covers up to 64 heads
-    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a);
-    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT>), grid, dim3(kNW * 64), 0, st, a);
+    // eight waves per workgroup always (head groups x dim quarters); a
+    // workgroup covers up to 64 heads, or with at most 32 heads (d 512) one
+    // 16-head group per wave, so that all eight waves multiply
+    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, F8, OT, 2>), grid, dim3(kNW * 64), 0, st, a);
+    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, F8, OT, 2>), grid, dim3(kNW * 64), 0, st, a);
+    else if (a.H <= 32) hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT, 1>), grid, dim3(kNW * 64), 0, st, a);
+    else hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT, 2>), grid, dim3(kNW * 64), 0, st, a);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, int64_t nsplit_bound, hipStream_t st) {
