@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     int32_t jn = 0;
     // FP8 ring: plan and send tile tt into ring buffer rb; record validity, and
     // zero the rows of missing entries (no stale codes reach P V)
-    auto ring_issue = [&](int tt, int rb, int32_t j) {
+    auto ring_issue = [&](int tt, int rb, int32_t j) __attribute__((always_inline)) {
         if constexpr (F8) {
             const Fetch f = fetch_plan(a, c, e0 + tt * kMTE, e1, fw, lane, j);
             fetch_issue<D, DR>(&sm.ring[rb][0][0], REC, fw, lane, f);
@@ -516,10 +516,9 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; i++) { mrun[i] = -INFINITY; lrun[i] = 0.0f; }
 
-    // expand tile tt into buffer tt % 2 and send the fetch of tile tt + 1
     // (any formats) expand tile tt into buffer tt % 2, send the fetch of tile tt + 1;
     // (FP8 ring) wait for tile tt, send the fetch of tile tt + 1 into ring (tt + 1) % 3
-    auto fetch_step = [&](int tt, int rb_next) {
+    auto fetch_step = [&](int tt, int rb_next) __attribute__((always_inline)) {
         if (!fetcher || tt >= ntiles) return;
         const int32_t et = e0 + tt * kMTE;
         wait_vm();
@@ -542,9 +541,9 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     // groups: scale * <q, code>_non-RoPE + <q, k>_RoPE, to LDS.  The quarter is
     // a template constant (QD), so the FP8/RoPE split of its K-steps is known at
     // compile time and every K fragment is read before the first product.
-    auto qk_step = [&](auto qdc, int bq) {
-        constexpr int DB = decltype(qdc)::value * DQ;
-        constexpr int NKS = (dn - DB) / 32 < 0 ? 0 : ((dn - DB) / 32 > KS ? KS : (dn - DB) / 32);
+    auto qk_step = [&](auto qdc, int bq) __attribute__((always_inline)) {
+        constexpr int DC = decltype(qdc)::value * DQ;
+        constexpr int NKS = (dn - DC) / 32 < 0 ? 0 : ((dn - DC) / 32 > KS ? KS : (dn - DC) / 32);
         float esc[2];
         bf16x8_t kb[2][KS];
         if constexpr (F8) {
@@ -555,7 +554,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
                 esc[n] = *reinterpret_cast<const float*>(kr + dn + 2 * DR);
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) {
-                    const int dim = DB + 32 * ks + 8 * g4;
+                    const int dim = dbase + 32 * ks + 8 * g4;
                     if (ks < NKS) kc[n][ks] = *reinterpret_cast<const uint2*>(kr + dim);
                     else kb[n][ks] = *reinterpret_cast<const bf16x8_t*>(kr + dn + 2 * (dim - dn));
                 }
@@ -567,7 +566,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         } else {
 #pragma unroll
             for (int n = 0; n < 2; n++) {
-                const uint8_t* kr = &sm.tile[bq][16 * n + l16][2 * DB + 16 * g4];
+                const uint8_t* kr = &sm.tile[bq][16 * n + l16][2 * dbase + 16 * g4];
                 esc[n] = sm.scale[bq][16 * n + l16];
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++) kb[n][ks] = *reinterpret_cast<const bf16x8_t*>(kr + 64 * ks);
@@ -598,7 +597,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         }
     };
     // owner waves: add the quarters of tile tt in order, online softmax, publish P
-    auto softmax_step = [&](int bq) {
+    auto softmax_step = [&](int bq) __attribute__((always_inline)) {
         float esc[2];
         bool eok[2];
 #pragma unroll
@@ -671,9 +670,9 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     // O += P V.  The quarter is a template constant: the FP8/RoPE split of its
     // N-tiles is static, and the flags, P fragments and V fragments are all
     // read before the first product.
-    auto pv_step = [&](auto qdc, int bq) {
-        constexpr int DB = decltype(qdc)::value * DQ;
-        constexpr int NNT = (dn - DB) / 16 < 0 ? 0 : ((dn - DB) / 16 > NT ? NT : (dn - DB) / 16);
+    auto pv_step = [&](auto qdc, int bq) __attribute__((always_inline)) {
+        constexpr int DC = decltype(qdc)::value * DQ;
+        constexpr int NNT = (dn - DC) / 16 < 0 ? 0 : ((dn - DC) / 16 > NT ? NT : (dn - DC) / 16);
         int mv[MTW];
 #pragma unroll
         for (int mt = 0; mt < MTW; mt++) mv[mt] = sm.moved[g0 + mt];      // g0 + mt <= 3
@@ -694,16 +693,16 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             for (int nd = 0; nd < NT; nd++) {
                 if (nd < NNT) {
                     const int r = 8 * g4 + (l16 >> 3) + 2 * ((l16 >> 1) & 3);
-                    vc[nd] = lds_read_tr8(rb + r * REC + DB + 16 * nd + 8 * (l16 & 1));
+                    vc[nd] = lds_read_tr8(rb + r * REC + dbase + 16 * nd + 8 * (l16 & 1));
                 } else {
-                    const int cb = dn + 2 * (DB + 16 * nd - dn + 4 * (l16 & 3));
+                    const int cb = dn + 2 * (dbase + 16 * nd - dn + 4 * (l16 & 3));
                     vb[nd] = tr_pair(rb + v_row * REC + cb, rb + (v_row + 1) * REC + cb);
                 }
             }
 #pragma unroll
             for (int nd = 0; nd < NNT; nd++) vb[nd] = fp8x8_to_bf16(vc[nd]);
         } else {
-            const uint8_t* vp = &sm.tile[bq][v_row][2 * (DB + 4 * (l16 & 3))];
+            const uint8_t* vp = &sm.tile[bq][v_row][2 * (dbase + 4 * (l16 & 3))];
 #pragma unroll
             for (int nd = 0; nd < NT; nd++) vb[nd] = tr_pair(vp + 32 * nd, vp + RS + 32 * nd);
         }
@@ -727,14 +726,20 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             for (int mt = 0; mt < MTW; mt++)
                 o[mt][nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(nd < NNT ? pfs[mt] : pfp[mt], vb[nd], o[mt][nd], 0, 0, 0);
     };
-    // the steps for this wave's quarter (wave-uniform dispatch)
+    // the tile loop for this wave's quarter (wave-uniform dispatch, outside
+    // the loop).  Quarters with the same split into non-RoPE and RoPE dims
+    // share one instantiation (the quarter's base dim is a runtime value):
+    // quarters 0 .. QF-1 hold only non-RoPE dims, quarter QF holds the
+    // boundary (or only RoPE dims, as do the ones after it).  Dispatching per
+    // tile instead made the register allocator move the output accumulators
+    // between the instantiations' registers on every tile.
+    constexpr int QF = dn / DQ;
+    static_assert(QF < 4, "the RoPE dims take part of the last quarter");
+    constexpr bool kMixed = dn % DQ != 0;
     auto with_quarter = [&](auto&& f) {
-        switch (qd) {
-            case 0: f(std::integral_constant<int, 0>{}); break;
-            case 1: f(std::integral_constant<int, 1>{}); break;
-            case 2: f(std::integral_constant<int, 2>{}); break;
-            default: f(std::integral_constant<int, 3>{}); break;
-        }
+        if (qd < QF) f(std::integral_constant<int, 0>{});
+        else if (!kMixed || qd == QF) f(std::integral_constant<int, QF>{});
+        else f(std::integral_constant<int, 3>{});
     };
 
     // ---- software pipeline over the tiles; per tile two barriers:
@@ -749,28 +754,28 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
         fetch_step(0, 0);
     }
     __syncthreads();
-    int bcur = 0, bprev = NB - 1;
-    for (int tt = 0; tt < ntiles; tt++) {
-        if (active) {
-            with_quarter([&](auto qdc) {
+    with_quarter([&](auto qdc) {
+        int bcur = 0, bprev = NB - 1;
+        for (int tt = 0; tt < ntiles; tt++) {
+            if (active) {
                 if (tt > 0) pv_step(qdc, bprev);
                 qk_step(qdc, bcur);
-            });
+            }
+            __syncthreads();
+            if (owner) softmax_step(bcur);
+            if constexpr (F8) {
+                int bn2 = bcur + 2;
+                if (bn2 >= NB) bn2 -= NB;
+                fetch_step(tt + 1, bn2);      // waits for tile tt+1, sends tile tt+2
+            } else {
+                fetch_step(tt + 1, 0);
+            }
+            __syncthreads();
+            bprev = bcur;
+            bcur = bcur + 1 == NB ? 0 : bcur + 1;
         }
-        __syncthreads();
-        if (owner) softmax_step(bcur);
-        if constexpr (F8) {
-            int bn2 = bcur + 2;
-            if (bn2 >= NB) bn2 -= NB;
-            fetch_step(tt + 1, bn2);      // waits for tile tt+1, sends tile tt+2
-        } else {
-            fetch_step(tt + 1, 0);
-        }
-        __syncthreads();
-        bprev = bcur;
-        bcur = bcur + 1 == NB ? 0 : bcur + 1;
-    }
-    if (active && ntiles > 0) with_quarter([&](auto qdc) { pv_step(qdc, bprev); });
+        if (active && ntiles > 0) pv_step(qdc, bprev);
+    });
 
     // ---- epilogue
 #pragma unroll
