@@ -761,7 +761,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
                 if (tt > 0) pv_step(qdc, bprev);
                 qk_step(qdc, bcur);
             }
-            __syncthreads();
+            lds_barrier();
             if (owner) softmax_step(bcur);
             if constexpr (F8) {
                 int bn2 = bcur + 2;
@@ -770,7 +770,9 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             } else {
                 fetch_step(tt + 1, 0);
             }
-            __syncthreads();
+            // LDS-only barriers: the copies of the tile just sent stay in
+            // flight through the next step (fetch_step waits for them)
+            lds_barrier();
             bprev = bcur;
             bcur = bcur + 1 == NB ? 0 : bcur + 1;
         }
