@@ -1191,7 +1191,7 @@ __global__ __launch_bounds__(kPfThreads) void k_idxp_thresh(IndexerArgs a, int32
 }
 
 // compare predicates of the lane-mask compare builtin (LLVM's numbering)
-constexpr int kFcmpOeq = 1, kFcmpOgt = 2;
+constexpr int kFcmpOeq = 1, kFcmpOgt = 2, kFcmpOge = 3;
 
 __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
     warm_kernargs(sizeof(IndexerArgs));
@@ -1284,16 +1284,12 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                 const float4 w4 = wl[rb][s][half];
                 const float wv4[4] = {w4.x, w4.y, w4.z, w4.w};
                 const float sc = pf_score(acc, s, wv4);
-                // lane masks straight from the compares (ordered: a NaN score
-                // is neither above nor at the threshold)
-                uint64_t bal = __builtin_amdgcn_fcmpf(sc, thr[rb][s], kFcmpOgt);
-                uint64_t bt = __builtin_amdgcn_fcmpf(sc, thr[rb][s], kFcmpOeq);
-                if constexpr (kVis) {
-                    const uint64_t vm = ballot64(j < nq[rb][s]);
-                    bal &= vm;
-                    bt &= vm;
-                }
-                if (bal | bt) {
+                // one compare decides whether any lane appends (ordered: a NaN
+                // score is neither above nor at the threshold); above and at
+                // are told apart only on that rarer path
+                uint64_t bge = __builtin_amdgcn_fcmpf(sc, thr[rb][s], kFcmpOge);
+                if constexpr (kVis) bge &= ballot64(j < nq[rb][s]);
+                if (bge) {
                     // this lane's own tests as vector compares (exec masks
                     // straight from them, no bit extraction from the ballots)
                     bool above = sc > thr[rb][s], tie = sc == thr[rb][s];
@@ -1302,6 +1298,7 @@ __global__ __launch_bounds__(kPfThreads, 4) void k_idxp_filter(IndexerArgs a) {
                         above = above && vis;
                         tie = tie && vis;
                     }
+                    const uint64_t bal = ballot64(above), bt = ballot64(tie);
                     // rank among this half's hits: mbcnt over the whole wave,
                     // less the lower half's count for the upper half
                     const uint32_t alo = (uint32_t)bal, ahi = (uint32_t)(bal >> 32);
