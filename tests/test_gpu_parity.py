@@ -467,6 +467,12 @@ ATTN_CASES = [
     (True, 2, 2, 8, 512, 64, 128, 4, 64, 1000, O.BF16, O.BF16, O.BF16),     # H 8: generic kernel, bf16 q
     (False, 2, 2, 32, 512, 64, 128, 4, 0, 900, (O.BF16, O.FP8_E4M3), O.BF16, O.BF16),  # mixed cache formats
     (True, 3, 4, 64, 512, 64, 128, 4, 1024, 8000, O.FP8_E4M3, O.BF16, O.F32),  # prefill-like rows, f32 out
+    # FP8 records with one 16-head group per wave, and the dim-quarter classes
+    # of d = 128 (quarters 2 and 3 all RoPE) and d = 256 (quarter 3 all RoPE)
+    (True, 2, 2, 32, 512, 64, 128, 4, 256, 2000, O.FP8_E4M3, O.BF16, O.BF16),   # 32 heads, sparse
+    (False, 1, 3, 16, 512, 64, 64, 16, 0, 300, O.FP8_E4M3, O.BF16, O.F32),      # 16 heads: half the waves idle
+    (True, 2, 3, 16, 128, 64, 40, 4, 50, 400, O.FP8_E4M3, O.BF16, O.BF16),      # d 128
+    (False, 1, 2, 32, 256, 64, 128, 8, 0, 600, O.FP8_E4M3, O.BF16, O.BF16),     # d 256, 32 heads
 ]
 
 
