@@ -6,10 +6,11 @@
 // RoPE with the -i output RoPE, sink logit in the denominator), arranged for
 // the matrix cores of one CU:
 //   - one query row (up to 64 heads) per workgroup and split, eight waves
-//     (two per SIMD): wave w takes the 32 heads of half w/4 and the quarter
-//     w%4 of the head dimension D.  It holds those queries as MFMA
-//     A-fragments and that block of the output as accumulators (64 fp32
-//     per lane at D = 512, so everything stays in plain VGPRs);
+//     (two per SIMD): wave w takes the 32 heads of half w/4 (with at most 32
+//     heads, the 16 heads of group w/4) and the quarter w%4 of the head
+//     dimension D.  It holds those queries as MFMA A-fragments and that
+//     block of the output as accumulators (64 fp32 per lane at D = 512, so
+//     everything stays in plain VGPRs);
 //   - a tile of 32 entries is shared by all heads (MQA: one KV vector per
 //     entry serves every head).  FP8 records are expanded exactly to bf16
 //     codes with the hardware OCP-E4M3 conversion; the row scale multiplies
@@ -32,10 +33,12 @@
 //     are converted on the way out of LDS: K rows with 64-bit reads, V
 //     columns with the byte-transposing read (ds_read_b64_tr_b8).  Other
 //     formats go through a staging area and are expanded to bf16 rows;
-//   - software pipeline, two barriers per tile: phase 1 (all waves) runs
-//     P V of tile t-1 and Q K^T of tile t back to back on the matrix cores;
-//     phase 2 runs the softmax of tile t (waves 0..3) beside the fetch work
-//     (waves 4..7).
+//   - software pipeline, two LDS-only barriers per tile: phase 1 (all waves)
+//     runs P V of tile t-1 and Q K^T of tile t back to back on the matrix
+//     cores; phase 2 runs the softmax of tile t (waves 0..3) beside the fetch
+//     work (waves 4..7), whose copies stay in flight through the next phase 1.
+//     The dispatch on the dim quarter (which K-steps and N-tiles are FP8
+//     codes, which RoPE dims) sits outside the tile loop.
 #include <stddef.h>
 
 #include <type_traits>
