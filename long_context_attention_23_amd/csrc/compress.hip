@@ -218,6 +218,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
 // in DPP row order instead of a butterfly, so the last bits may differ.
 struct CompFastSmem {
     float part[kCompThreads * 8];
+    float pw[kMaxM];                      // pooling weight of each token row of the block
     float red_ss[kCompThreads / kWave];
     float red_mx[kCompThreads / kWave];
     int se[kMaxD / 32];
@@ -242,20 +243,18 @@ __device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t
     const int c = tid % nch, tg = tid / nch;
     const int off = d - a.dr;
 
-    // ---- every load first: token rows and their biases, the lane's share of
-    // all biases, gamma and the RoPE frequencies of this thread's elements
-    uint4 u[QR];
-    float br[QR];
-#pragma unroll
-    for (int q = 0; q < QR; q++) {
-        const int r = tg + q * TG;
-        const bool ok = tg < TG && r < m;
-        u[q] = ok ? *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC) : make_uint4(0u, 0u, 0u, 0u);
-        br[q] = ok ? a.sbias[r] : 0.0f;
-    }
+    // ---- every load first: the biases (the lane's share of all of them, and
+    // those of the rows whose pooling weight this thread forms), gamma, the
+    // RoPE frequencies of this thread's elements, then the token rows (one
+    // load per row slot, clamped to a valid row: the softmax below waits for
+    // the biases only, with the rows still in flight)
     float sb[SB];
 #pragma unroll
     for (int s = 0; s < SB; s++) sb[s] = lane + s * kWave < m ? a.sbias[lane + s * kWave] : -INFINITY;
+    constexpr int PR = kMaxM / kCompThreads;             // pooling weights formed per thread
+    float bo[PR];
+#pragma unroll
+    for (int t = 0; t < PR; t++) bo[t] = tid + t * kCompThreads < m ? a.sbias[tid + t * kCompThreads] : 0.0f;
     float gk[KT];
     double fk[KT];
 #pragma unroll
@@ -264,9 +263,15 @@ __device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t
         gk[t] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
         fk[t] = (k < d && k >= off) ? rope_freq_arg(rope_off, (k - off) >> 1) : 0.0;
     }
-    const int64_t j = (int64_t)(a.tok_start[b] / m) + i;
-    if (!a.ring && j >= a.cap) return;
-    const int64_t slot = a.ring ? j % a.cap : j;
+    const int64_t tok0 = a.tok_start[b];
+    uint4 u[QR];
+#pragma unroll
+    for (int q = 0; q < QR; q++) {
+        const int r = min(tg + q * TG, m - 1);
+        u[q] = *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC);
+    }
+    __builtin_amdgcn_sched_barrier(0);                   // the rows go out before the softmax waits for the biases
+    const int64_t j = (int64_t)(tok0 / m) + i;
 
     // ---- softmax of the biases: every wave reduces the same values itself
     float zmax = -INFINITY;
@@ -278,6 +283,11 @@ __device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t
     for (int s = 0; s < SB; s++)
         if (lane + s * kWave < m) zsum += expf(sb[s] - zmax);
     zsum = wave_sum_dpp(zsum);
+    // the pooling weight of each row, formed once (row r by thread r % threads)
+#pragma unroll
+    for (int t = 0; t < PR; t++)
+        if (tid + t * kCompThreads < m) sm.pw[tid + t * kCompThreads] = expf(bo[t] - zmax) / zsum;
+    __syncthreads();                                      // barrier 0: pooling weights
 
     // ---- pooled partial sums of this thread's token group
     if (tg < TG) {
@@ -287,7 +297,7 @@ __device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t
 #pragma unroll
         for (int q = 0; q < QR; q++) {
             if (tg + q * TG >= m) break;
-            const float p = expf(br[q] - zmax) / zsum;
+            const float p = sm.pw[tg + q * TG];
             if constexpr (sizeof(XT) == 2) {
                 const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
 #pragma unroll
@@ -342,7 +352,11 @@ __device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t
         }
     }
 
-    // ---- quantise into the output record
+    // ---- quantise into the output record (a block beyond a linear cache's
+    // capacity is not stored; the test sits here, after every load, so that
+    // no load waits for the block index)
+    if (!a.ring && j >= a.cap) return;                   // the whole workgroup
+    const int64_t slot = a.ring ? j % a.cap : j;
     const size_t rrow = (size_t)b * a.cap + slot;
     uint8_t* rec = a.out + rrow * a.rec_bytes;
     if (a.fmt == CSA_F32) {
