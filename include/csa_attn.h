@@ -205,6 +205,50 @@ typedef struct {
 csa_status csa_compress_kv_batch(const csa_compress_job* jobs, int32_t njobs, int32_t x_dtype, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * csa_compress_kv_step -- the compression of csa_compress_kv fed one token
+ * per sequence per call (decode; peacm 3.2 CSA step 1: every m tokens become
+ * one compressed entry, 128:1 for HCA).  For job k and sequence b the token
+ * x[b] (row of d values, x_dtype) sits at position t = tok_pos[b] (device
+ * int32 [B]; a negative t writes nothing), token r = t mod m of block
+ * j = t / m, with score z = score_bias[r] + <score_proj, x[b]>.
+ * The pooling softmax over the block's m scores runs as an online softmax
+ * over its tokens, in the caller's state: device f32 [B][d + 2] per job
+ * (m > 1; NULL for m == 1) holding the running sum of weighted tokens, the
+ * running maximum score and the running sum of exp(score - maximum):
+ *   r == 0       the state starts from the token (its contents are not read);
+ *   0 < r        max' = max(max, z); both sums are scaled by exp(max - max')
+ *                and the token added with weight exp(z - max');
+ *   r == m - 1   the block is finished from (weighted sum / sum) exactly as
+ *                csa_compress_kv finishes a block (RMSNorm, RoPE at j*m,
+ *                quantiser into slot j of the one output), and the state is
+ *                left as it was before this token (the call can be repeated).
+ * The tokens of a block must come in order, one call per token, starting at
+ * r == 0.  The entry equals csa_compress_kv's over the same m tokens up to
+ * the rounding of the pooling sums (the same terms, added in another form);
+ * m == 1 entries (window entries) are the same bits.  Jobs run concurrently
+ * (outputs and states must not overlap); up to 4 share a launch.
+ * Errors: those of csa_compress_kv for a call over one block of m tokens, and
+ * INVALID_ARG (njobs < 0, jobs NULL with njobs > 0, m > 1 without a state).
+ * ------------------------------------------------------------------------- */
+typedef struct {
+    const void* x;
+    int32_t B;
+    int32_t d;
+    const int32_t* tok_pos;
+    int32_t m;
+    const float* score_bias;
+    const float* score_proj;
+    const float* gamma;
+    float eps;
+    int32_t rope_dim;
+    float rope_base;
+    float* state;
+    const csa_kv_cache* kv_out;
+    const csa_idx_cache* idx_out;
+} csa_compress_step_job;
+csa_status csa_compress_kv_step(const csa_compress_step_job* jobs, int32_t njobs, int32_t x_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------
  * csa_indexer_topk -- CSA step 2 (peacm 3.2: the lightning indexer scores
  * each query against the compressed blocks and keeps the most relevant
  * top-k; digest 3.2: the QK path in FP4).

@@ -16,7 +16,8 @@ F32, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3
 CSA_OK, CSA_ERR_INVALID_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_CAPACITY, CSA_ERR_WORKSPACE, CSA_ERR_HIP = 0, -1, -2, -3, -4, -5
 STATUS = {CSA_OK: "CSA_OK", CSA_ERR_INVALID_ARG: "CSA_ERR_INVALID_ARG", CSA_ERR_UNSUPPORTED: "CSA_ERR_UNSUPPORTED",
           CSA_ERR_CAPACITY: "CSA_ERR_CAPACITY", CSA_ERR_WORKSPACE: "CSA_ERR_WORKSPACE", CSA_ERR_HIP: "CSA_ERR_HIP"}
-EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_compress_kv_batch", "csa_indexer_topk_workspace_size", "csa_indexer_topk",
+EXPORTS = ["csa_kv_record_bytes", "csa_compress_kv", "csa_compress_kv_batch", "csa_compress_kv_step",
+           "csa_indexer_topk_workspace_size", "csa_indexer_topk",
            "csa_indexer_topk_noalloc",
            "csa_attn_workspace_size", "csa_sparse_mqa_attn", "hca_dense_mqa_attn", "attn_out_proj_grouped",
            "csa_linear_fp8", "csa_layer_in_proj_workspace_size", "csa_layer_in_proj", "csa_last_error"]
@@ -57,6 +58,12 @@ class CompressJobT(C.Structure):
                 ("rope_base", _F), ("kv_out", C.POINTER(KVCacheT)), ("idx_out", C.POINTER(IdxCacheT))]
 
 
+class CompressStepJobT(C.Structure):
+    _fields_ = [("x", _V), ("B", _I32), ("d", _I32), ("tok_pos", _V), ("m", _I32),
+                ("score_bias", _V), ("score_proj", _V), ("gamma", _V), ("eps", _F), ("rope_dim", _I32),
+                ("rope_base", _F), ("state", _V), ("kv_out", C.POINTER(KVCacheT)), ("idx_out", C.POINTER(IdxCacheT))]
+
+
 def lib():
     """Load the HIP library (raises if it has not been built)."""
     global _lib
@@ -74,6 +81,8 @@ def lib():
                                       C.POINTER(KVCacheT), C.POINTER(IdxCacheT), _V]
         L.csa_compress_kv_batch.restype = C.c_int
         L.csa_compress_kv_batch.argtypes = [C.POINTER(CompressJobT), _I32, _I32, _V]
+        L.csa_compress_kv_step.restype = C.c_int
+        L.csa_compress_kv_step.argtypes = [C.POINTER(CompressStepJobT), _I32, _I32, _V]
         L.csa_indexer_topk_workspace_size.restype = _SZ
         L.csa_indexer_topk_workspace_size.argtypes = [_I32, _I32, _I64, _I32]
         L.csa_indexer_topk.restype = C.c_int
@@ -201,6 +210,43 @@ def compress_kv_batch(jobs, stream=None):
             if not t.is_contiguous():
                 raise ValueError("tensors passed to the C ABI must be contiguous")
     _check(lib().csa_compress_kv_batch(arr, n, dt, _stream(stream)))
+
+
+def compress_state(B, d, device="cuda"):
+    """A zeroed running state for csa_compress_kv_step: float32 [B, d + 2] (its first token sets it)."""
+    return torch.zeros((B, d + 2), dtype=torch.float32, device=device)
+
+
+def compress_kv_step(jobs, stream=None):
+    """csa_compress_kv_step.  jobs: dicts with x ([B, d] float32 / bfloat16: the step's token of each
+    sequence), tok_pos (int32 [B]: its position), m, score_bias, state (float32 [B, d + 2]; None for
+    m == 1) and compress_kv's keywords; every x has the same dtype."""
+    n = len(jobs)
+    arr = (CompressStepJobT * max(n, 1))()
+    keep = []                                   # cache structs referenced by the descriptors
+    dt = torch_dtype_code(jobs[0]["x"]) if n else F32
+    for k, j in enumerate(jobs):
+        x = j["x"]
+        if torch_dtype_code(x) != dt:
+            raise TypeError("every job of a step needs the same x dtype")
+        B, d = x.shape
+        st = j.get("state")
+        if st is not None and (st.dtype != torch.float32 or tuple(st.shape) != (B, d + 2) or not st.is_contiguous()):
+            raise ValueError("state must be a contiguous float32 [B, d + 2] tensor")
+        kv = j.get("kv_out")
+        ix = j.get("idx_out")
+        kvs = kv.struct() if kv is not None else None
+        ixs = ix.struct() if ix is not None else None
+        keep += [kvs, ixs]
+        arr[k] = CompressStepJobT(x.data_ptr(), B, d, j["tok_pos"].data_ptr(), j["m"], j["score_bias"].data_ptr(),
+                                  _ptr(j.get("score_proj")), _ptr(j.get("gamma")), j.get("eps", 1e-6),
+                                  j.get("rope_dim", 0), j.get("rope_base", 10000.0), _ptr(st),
+                                  C.pointer(kvs) if kvs is not None else None,
+                                  C.pointer(ixs) if ixs is not None else None)
+        for t in (x, j["tok_pos"], j["score_bias"]):
+            if not t.is_contiguous():
+                raise ValueError("tensors passed to the C ABI must be contiguous")
+    _check(lib().csa_compress_kv_step(arr, n, dt, _stream(stream)))
 
 
 def indexer_workspace_bytes(B, Tq, key_cap, topk):

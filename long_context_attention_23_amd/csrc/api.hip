@@ -262,6 +262,26 @@ CSA_API csa_status csa_compress_kv_batch(const csa_compress_job* jobs, int32_t n
                       "compress batch launch");
 }
 
+CSA_API csa_status csa_compress_kv_step(const csa_compress_step_job* jobs, int32_t njobs, int32_t x_dtype,
+                                        void* stream) {
+    if (njobs < 0 || (njobs > 0 && !jobs))
+        return fail(CSA_ERR_INVALID_ARG, "njobs %d with jobs %p", njobs, (const void*)jobs);
+    std::vector<csa::CompressArgs> args((size_t)njobs);
+    for (int k = 0; k < njobs; k++) {
+        const csa_compress_step_job& j = jobs[k];
+        // the checks of a call over one block of m tokens
+        const csa_status st = compress_args(j.x, x_dtype, j.B, j.m, j.d, j.tok_pos, j.m, j.score_bias, j.score_proj,
+                                            j.gamma, j.eps, j.rope_dim, j.rope_base, j.kv_out, j.idx_out, args[k]);
+        if (st != CSA_OK) return st;
+        if (j.m > 1 && j.B > 0 && !j.state) return fail(CSA_ERR_INVALID_ARG, "job %d: m %d needs a state", k, j.m);
+        args[k].T = 1;
+        args[k].state = j.m > 1 ? j.state : nullptr;
+    }
+    if (njobs == 0) return CSA_OK;
+    return hip_status(csa::launch_compress_step(args.data(), njobs, x_dtype, static_cast<hipStream_t>(stream)),
+                      "compress step launch");
+}
+
 CSA_API size_t csa_indexer_topk_workspace_size(int32_t B, int32_t Tq, int64_t key_cap, int32_t topk) {
     const int64_t rows = (int64_t)(B > 0 ? B : 0) * (Tq > 0 ? Tq : 0);
     if (rows == 0 || key_cap <= csa::kIdxSmallMaxKeys || topk < 1) return 0;

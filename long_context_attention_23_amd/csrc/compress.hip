@@ -219,6 +219,7 @@ __global__ __launch_bounds__(kCompThreads) void k_compress(CompressArgs a) {
 struct CompFastSmem {
     float part[kCompThreads * 8];
     float pw[kMaxM];                      // pooling weight of each token row of the block
+    float red_z[kCompThreads / kWave];    // per-wave partials of a token's content score
     float red_ss[kCompThreads / kWave];
     float red_mx[kCompThreads / kWave];
     int se[kMaxD / 32];
@@ -226,107 +227,25 @@ struct CompFastSmem {
 
 // block i of sequence b; `a` lives in the argument segment with its RoPE table
 // at byte rope_off of the segment
-template <typename XT, int QR>
-__device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t rope_off, CompFastSmem& sm, int b,
-                                                   int i) {
-    float* part = sm.part;
+// The tail of a block's compression, shared by the block and the per-token
+// kernels: RMSNorm, RoPE at j*m on the last dr dims, the quantiser into slot
+// j of the output (a block beyond a linear cache's capacity is not stored).
+// v: the pooled vector, element tid + t * threads in v[t]; gk, fk: gamma and
+// the RoPE frequency of those elements.  Every thread of the workgroup calls it.
+template <int KT>
+__device__ __forceinline__ void finish_block(const CompressArgs& a, size_t rope_off, CompFastSmem& sm, float (&v)[KT],
+                                             const float (&gk)[KT], const double (&fk)[KT], int64_t j, int b) {
     float* red_ss = sm.red_ss;
     float* red_mx = sm.red_mx;
     int* se = sm.se;
-    constexpr int EPC = 16 / (int)sizeof(XT);
-    constexpr int KT = kMaxD / kCompThreads;              // elements per thread
-    constexpr int SB = 2 * QR < 16 ? 2 * QR : 16;        // pooling biases per lane (m <= 64 SB)
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
     const int d = a.d, m = a.m;
-    const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + (int64_t)i * m) * d;
-    const int nch = d / EPC, TG = kCompThreads / nch;
-    const int c = tid % nch, tg = tid / nch;
     const int off = d - a.dr;
-
-    // ---- every load first: the biases (the lane's share of all of them, and
-    // those of the rows whose pooling weight this thread forms), gamma, the
-    // RoPE frequencies of this thread's elements, then the token rows (one
-    // load per row slot, clamped to a valid row: the softmax below waits for
-    // the biases only, with the rows still in flight)
-    float sb[SB];
-#pragma unroll
-    for (int s = 0; s < SB; s++) sb[s] = lane + s * kWave < m ? a.sbias[lane + s * kWave] : -INFINITY;
-    constexpr int PR = kMaxM / kCompThreads;             // pooling weights formed per thread
-    float bo[PR];
-#pragma unroll
-    for (int t = 0; t < PR; t++) bo[t] = tid + t * kCompThreads < m ? a.sbias[tid + t * kCompThreads] : 0.0f;
-    float gk[KT];
-    double fk[KT];
-#pragma unroll
-    for (int t = 0; t < KT; t++) {
-        const int k = tid + t * kCompThreads;
-        gk[t] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
-        fk[t] = (k < d && k >= off) ? rope_freq_arg(rope_off, (k - off) >> 1) : 0.0;
-    }
-    const int64_t tok0 = a.tok_start[b];
-    uint4 u[QR];
-#pragma unroll
-    for (int q = 0; q < QR; q++) {
-        const int r = min(tg + q * TG, m - 1);
-        u[q] = *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC);
-    }
-    __builtin_amdgcn_sched_barrier(0);                   // the rows go out before the softmax waits for the biases
-    const int64_t j = (int64_t)(tok0 / m) + i;
-
-    // ---- softmax of the biases: every wave reduces the same values itself
-    float zmax = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < SB; s++) zmax = fmaxf(zmax, sb[s]);
-    zmax = wave_max_dpp(zmax);
-    float zsum = 0.0f;
-#pragma unroll
-    for (int s = 0; s < SB; s++)
-        if (lane + s * kWave < m) zsum += expf(sb[s] - zmax);
-    zsum = wave_sum_dpp(zsum);
-    // the pooling weight of each row, formed once (row r by thread r % threads)
-#pragma unroll
-    for (int t = 0; t < PR; t++)
-        if (tid + t * kCompThreads < m) sm.pw[tid + t * kCompThreads] = expf(bo[t] - zmax) / zsum;
-    __syncthreads();                                      // barrier 0: pooling weights
-
-    // ---- pooled partial sums of this thread's token group
-    if (tg < TG) {
-        float acc[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; e++) acc[e] = 0.0f;
-#pragma unroll
-        for (int q = 0; q < QR; q++) {
-            if (tg + q * TG >= m) break;
-            const float p = sm.pw[tg + q * TG];
-            if constexpr (sizeof(XT) == 2) {
-                const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    acc[2 * e] = fmaf(p, __uint_as_float(wd[e] << 16), acc[2 * e]);
-                    acc[2 * e + 1] = fmaf(p, __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
-                }
-            } else {
-                acc[0] = fmaf(p, __uint_as_float(u[q].x), acc[0]);
-                acc[1] = fmaf(p, __uint_as_float(u[q].y), acc[1]);
-                acc[2] = fmaf(p, __uint_as_float(u[q].z), acc[2]);
-                acc[3] = fmaf(p, __uint_as_float(u[q].w), acc[3]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < EPC; e++) part[tg * d + c * EPC + e] = acc[e];
-    }
-    __syncthreads();                                      // barrier 1: partials
-    const int tgu = m < TG ? m : TG;                      // token groups that hold rows
-    float v[KT];
     float ss = 0.0f;
 #pragma unroll
     for (int t = 0; t < KT; t++) {
         const int k = tid + t * kCompThreads;
-        v[t] = 0.0f;
-        if (k < d) {
-            for (int q = 0; q < tgu; q++) v[t] += part[q * d + k];
-            ss += v[t] * v[t];
-        }
+        if (k < d) ss += v[t] * v[t];
     }
     if (a.gamma) {                                        // RMSNorm
         ss = wave_sum_dpp(ss);
@@ -434,6 +353,105 @@ __device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t
 }
 
 template <typename XT, int QR>
+__device__ __forceinline__ void compress_fast_body(const CompressArgs& a, size_t rope_off, CompFastSmem& sm, int b,
+                                                   int i) {
+    float* part = sm.part;
+    constexpr int EPC = 16 / (int)sizeof(XT);
+    constexpr int KT = kMaxD / kCompThreads;              // elements per thread
+    constexpr int SB = 2 * QR < 16 ? 2 * QR : 16;        // pooling biases per lane (m <= 64 SB)
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int d = a.d, m = a.m;
+    const XT* xb = reinterpret_cast<const XT*>(a.x) + ((int64_t)b * a.T + (int64_t)i * m) * d;
+    const int nch = d / EPC, TG = kCompThreads / nch;
+    const int c = tid % nch, tg = tid / nch;
+    const int off = d - a.dr;
+
+    // ---- every load first: the biases (the lane's share of all of them, and
+    // those of the rows whose pooling weight this thread forms), gamma, the
+    // RoPE frequencies of this thread's elements, then the token rows (one
+    // load per row slot, clamped to a valid row: the softmax below waits for
+    // the biases only, with the rows still in flight)
+    float sb[SB];
+#pragma unroll
+    for (int s = 0; s < SB; s++) sb[s] = lane + s * kWave < m ? a.sbias[lane + s * kWave] : -INFINITY;
+    constexpr int PR = kMaxM / kCompThreads;             // pooling weights formed per thread
+    float bo[PR];
+#pragma unroll
+    for (int t = 0; t < PR; t++) bo[t] = tid + t * kCompThreads < m ? a.sbias[tid + t * kCompThreads] : 0.0f;
+    float gk[KT];
+    double fk[KT];
+#pragma unroll
+    for (int t = 0; t < KT; t++) {
+        const int k = tid + t * kCompThreads;
+        gk[t] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
+        fk[t] = (k < d && k >= off) ? rope_freq_arg(rope_off, (k - off) >> 1) : 0.0;
+    }
+    const int64_t tok0 = a.tok_start[b];
+    uint4 u[QR];
+#pragma unroll
+    for (int q = 0; q < QR; q++) {
+        const int r = min(tg + q * TG, m - 1);
+        u[q] = *reinterpret_cast<const uint4*>(xb + (size_t)r * d + (size_t)c * EPC);
+    }
+    __builtin_amdgcn_sched_barrier(0);                   // the rows go out before the softmax waits for the biases
+    const int64_t j = (int64_t)(tok0 / m) + i;
+
+    // ---- softmax of the biases: every wave reduces the same values itself
+    float zmax = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < SB; s++) zmax = fmaxf(zmax, sb[s]);
+    zmax = wave_max_dpp(zmax);
+    float zsum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SB; s++)
+        if (lane + s * kWave < m) zsum += expf(sb[s] - zmax);
+    zsum = wave_sum_dpp(zsum);
+    // the pooling weight of each row, formed once (row r by thread r % threads)
+#pragma unroll
+    for (int t = 0; t < PR; t++)
+        if (tid + t * kCompThreads < m) sm.pw[tid + t * kCompThreads] = expf(bo[t] - zmax) / zsum;
+    __syncthreads();                                      // barrier 0: pooling weights
+
+    // ---- pooled partial sums of this thread's token group
+    if (tg < TG) {
+        float acc[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; e++) acc[e] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < QR; q++) {
+            if (tg + q * TG >= m) break;
+            const float p = sm.pw[tg + q * TG];
+            if constexpr (sizeof(XT) == 2) {
+                const uint32_t wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    acc[2 * e] = fmaf(p, __uint_as_float(wd[e] << 16), acc[2 * e]);
+                    acc[2 * e + 1] = fmaf(p, __uint_as_float(wd[e] & 0xFFFF0000u), acc[2 * e + 1]);
+                }
+            } else {
+                acc[0] = fmaf(p, __uint_as_float(u[q].x), acc[0]);
+                acc[1] = fmaf(p, __uint_as_float(u[q].y), acc[1]);
+                acc[2] = fmaf(p, __uint_as_float(u[q].z), acc[2]);
+                acc[3] = fmaf(p, __uint_as_float(u[q].w), acc[3]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; e++) part[tg * d + c * EPC + e] = acc[e];
+    }
+    __syncthreads();                                      // barrier 1: partials
+    const int tgu = m < TG ? m : TG;                      // token groups that hold rows
+    float v[KT];
+#pragma unroll
+    for (int t = 0; t < KT; t++) {
+        const int k = tid + t * kCompThreads;
+        v[t] = 0.0f;
+        if (k < d)
+            for (int q = 0; q < tgu; q++) v[t] += part[q * d + k];
+    }
+    finish_block<KT>(a, rope_off, sm, v, gk, fk, j, b);
+}
+
+template <typename XT, int QR>
 __global__ __launch_bounds__(kCompThreads) void k_compress_fast(CompressArgs a) {
     warm_kernargs(offsetof(CompressArgs, rope));
     __shared__ CompFastSmem sm;
@@ -456,6 +474,112 @@ __global__ __launch_bounds__(kCompThreads) void k_compress_batch(CompressBatch b
     const int TG = kCompThreads / (a.d / EPC);
     if (a.m <= TG) compress_fast_body<XT, 1>(a, off + offsetof(CompressArgs, rope), sm, blockIdx.y, blockIdx.x);
     else compress_fast_body<XT, QRB>(a, off + offsetof(CompressArgs, rope), sm, blockIdx.y, blockIdx.x);
+}
+
+// One token of each sequence per call (decode): the block compression in
+// its incremental form.  The pooling softmax over a block's m scores is an
+// online softmax over its tokens (peacm.com section 3.2, CSA step 1: every
+// m tokens become one entry), kept per sequence in a state of d + 2 floats:
+// the running weighted sum of the tokens, the running maximum score and the
+// running sum of exp(score - maximum).  Token r = t % m of block j = t / m:
+//   r == 0     the state starts from the token (weight 1);
+//   r > 0      max' = max(max, z); sum and the weighted sum are rescaled by
+//              exp(max - max') and the token added with exp(z - max');
+//   r == m - 1 the block is finished like a whole block (RMSNorm, RoPE at
+//              j * m, quantiser into slot j) from weighted sum / sum; the
+//              state is not written back (the next block starts afresh).
+// m == 1 (window entries) needs no state: the token is the entry.  The
+// result equals the block kernel's up to rounding in the pooling (the two
+// forms add the same terms with other roundings); m == 1 entries are the
+// same bits.  One workgroup per (sequence, job); a.tok_start holds each
+// sequence's token position t.
+template <typename XT>
+__device__ __forceinline__ void compress_step_body(const CompressArgs& a, size_t rope_off, CompFastSmem& sm, int b) {
+    constexpr int KT = kMaxD / kCompThreads;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+    const int d = a.d, m = a.m;
+    const int off = d - a.dr;
+    // ---- every load first: the position, the token, gamma, the RoPE
+    // frequencies, the content-score weights and the state
+    const int64_t t = a.tok_start[b];
+    if (t < 0) return;                                    // no position, no entry (the whole workgroup)
+    const XT* xr = reinterpret_cast<const XT*>(a.x) + (size_t)b * d;
+    float xv[KT], gk[KT], uk[KT], acc[KT];
+    double fk[KT];
+#pragma unroll
+    for (int q = 0; q < KT; q++) {
+        const int k = tid + q * kCompThreads;
+        if constexpr (sizeof(XT) == 2) xv[q] = k < d ? __uint_as_float((uint32_t)xr[k] << 16) : 0.0f;
+        else xv[q] = k < d ? xr[k] : 0.0f;
+        gk[q] = (a.gamma && k < d) ? a.gamma[k] : 1.0f;
+        fk[q] = (k < d && k >= off) ? rope_freq_arg(rope_off, (k - off) >> 1) : 0.0;
+        uk[q] = (a.sproj && k < d) ? a.sproj[k] : 0.0f;
+        acc[q] = (a.state && k < d) ? a.state[(size_t)b * (d + 2) + k] : 0.0f;
+    }
+    const float smax = a.state ? a.state[(size_t)b * (d + 2) + d] : 0.0f;
+    const float ssum = a.state ? a.state[(size_t)b * (d + 2) + d + 1] : 0.0f;
+    const int64_t j = t / m;
+    const int r = (int)(t - j * m);
+    float z = a.sbias[r];
+    if (a.sproj) {                                        // z += <u, x>: fixed-order block sum
+        float pz = 0.0f;
+#pragma unroll
+        for (int q = 0; q < KT; q++) pz = fmaf(uk[q], xv[q], pz);
+        pz = wave_sum_dpp(pz);
+        if (lane == 0) sm.red_z[wv] = pz;
+        __syncthreads();
+        float tot = 0.0f;
+        for (int w = 0; w < kCompThreads / kWave; w++) tot += sm.red_z[w];
+        z += tot;
+    }
+    float v[KT];
+    if (m == 1) {
+#pragma unroll
+        for (int q = 0; q < KT; q++) v[q] = xv[q];
+    } else {
+        float mx, sw;
+        if (r == 0) {
+            mx = z;
+            sw = 1.0f;
+#pragma unroll
+            for (int q = 0; q < KT; q++) acc[q] = xv[q];
+        } else {
+            mx = fmaxf(smax, z);
+            const float a1 = expf(smax - mx), a2 = expf(z - mx);
+            sw = fmaf(ssum, a1, a2);
+#pragma unroll
+            for (int q = 0; q < KT; q++) acc[q] = fmaf(a2, xv[q], acc[q] * a1);
+        }
+        if (r < m - 1) {                                  // the block goes on: keep the state
+            float* st = a.state + (size_t)b * (d + 2);
+#pragma unroll
+            for (int q = 0; q < KT; q++) {
+                const int k = tid + q * kCompThreads;
+                if (k < d) st[k] = acc[q];
+            }
+            if (tid == 0) {
+                st[d] = mx;
+                st[d + 1] = sw;
+            }
+            return;                                       // the whole workgroup
+        }
+#pragma unroll
+        for (int q = 0; q < KT; q++) v[q] = acc[q] / sw;
+    }
+    finish_block<KT>(a, rope_off, sm, v, gk, fk, j, b);
+}
+
+// a decode step's per-token compressions (blockIdx.y = job), one workgroup
+// per sequence
+template <typename XT>
+__global__ __launch_bounds__(kCompThreads) void k_compress_step(CompressBatch bt) {
+    __shared__ CompFastSmem sm;
+    const int z = blockIdx.y;
+    const CompressArgs& a = bt.job[z];
+    const size_t off = (size_t)z * sizeof(CompressArgs);
+    warm_kernargs_at<offsetof(CompressArgs, rope)>(off);
+    if ((int)blockIdx.x >= a.B) return;
+    compress_step_body<XT>(a, off + offsetof(CompressArgs, rope), sm, blockIdx.x);
 }
 
 // token rows per thread of the fast kernel for this job, or 0 when the job
@@ -529,6 +653,29 @@ static hipError_t launch_compress_batch_t(const CompressArgs* jobs, int n, hipSt
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, int x_dtype, hipStream_t st) {
     if (x_dtype == CSA_F32) return launch_compress_batch_t<float>(jobs, n, st);
     return launch_compress_batch_t<uint16_t>(jobs, n, st);
+}
+
+template <typename XT>
+static hipError_t launch_compress_step_t(const CompressArgs* jobs, int n, hipStream_t st) {
+    for (int k0 = 0; k0 < n; k0 += kCompBatchMax) {
+        const int nk = n - k0 < kCompBatchMax ? n - k0 : kCompBatchMax;
+        CompressBatch bt{};
+        int64_t gx = 0;
+        for (int k = 0; k < nk; k++) {
+            bt.job[k] = jobs[k0 + k];
+            gx = std::max(gx, (int64_t)jobs[k0 + k].B);
+        }
+        if (gx == 0) continue;
+        hipLaunchKernelGGL(k_compress_step<XT>, dim3((unsigned)gx, (unsigned)nk), dim3(kCompThreads), 0, st, bt);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_compress_step(const CompressArgs* jobs, int n, int x_dtype, hipStream_t st) {
+    if (x_dtype == CSA_F32) return launch_compress_step_t<float>(jobs, n, st);
+    return launch_compress_step_t<uint16_t>(jobs, n, st);
 }
 
 }  // namespace csa

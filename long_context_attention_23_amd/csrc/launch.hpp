@@ -33,6 +33,7 @@ struct CompressArgs {
     int64_t cap;
     int32_t ring;
     int32_t rec_bytes;
+    float* state;       // per-token compression: [B][d + 2] running pooled state (null: m == 1 or block kernels)
     RopeTable rope;
 };
 hipError_t launch_compress(const CompressArgs& a, int x_dtype, hipStream_t st);
@@ -42,6 +43,9 @@ struct CompressBatch {
     CompressArgs job[kCompBatchMax];
 };
 hipError_t launch_compress_batch(const CompressArgs* jobs, int n, int x_dtype, hipStream_t st);
+// one token per sequence of each job (tok_start: the token's position), the
+// per-token form of the block compression with a running state per sequence
+hipError_t launch_compress_step(const CompressArgs* jobs, int n, int x_dtype, hipStream_t st);
 
 // ---- indexer + top-k
 constexpr int kIdxSmallMaxKeys = 4096;   // one workgroup per query row up to this key count

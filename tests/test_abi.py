@@ -28,7 +28,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     assert sorted(names) == sorted(api.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -135,6 +135,39 @@ def test_compress_batch_validation(L):
     arr = (api.CompressJobT * 2)(empty, empty)
     st, msg = status_and_msg(L, L.csa_compress_kv_batch(arr, 2, api.BF16, None))
     assert st == 0
+
+
+def step_job(**over):
+    kvs = over.pop("kv_struct", kv())
+    a = dict(x=FAKE.value, B=2, d=512, tok_pos=FAKE.value, m=4, score_bias=FAKE.value, score_proj=None,
+             gamma=None, eps=1e-6, rope_dim=64, rope_base=10000.0, state=FAKE.value, kv_out=C.pointer(kvs),
+             idx_out=None)
+    a.update(over)
+    return api.CompressStepJobT(**a), kvs
+
+
+def test_compress_step_validation(L):
+    st, msg = status_and_msg(L, L.csa_compress_kv_step(None, 1, api.BF16, None))
+    assert st == INV and "njobs" in msg
+    st, msg = status_and_msg(L, L.csa_compress_kv_step(None, 0, api.BF16, None))
+    assert st == 0
+    # a pooled job needs its running state; a window entry (m = 1) needs none
+    good, k0 = step_job()
+    nostate, k1 = step_job(state=None)
+    arr = (api.CompressStepJobT * 2)(good, nostate)
+    st, msg = status_and_msg(L, L.csa_compress_kv_step(arr, 2, api.BF16, None))
+    assert st == INV and "state" in msg
+    bad, k2 = step_job(d=513, kv_struct=kv(d=513))
+    arr = (api.CompressStepJobT * 2)(good, bad)
+    st, msg = status_and_msg(L, L.csa_compress_kv_step(arr, 2, api.BF16, None))
+    assert st == INV and "even" in msg
+    nopos, k3 = step_job(tok_pos=None)
+    arr = (api.CompressStepJobT * 1)(nopos)
+    st, msg = status_and_msg(L, L.csa_compress_kv_step(arr, 1, api.BF16, None))
+    assert st == INV and "null" in msg
+    arr = (api.CompressStepJobT * 1)(good)
+    st, msg = status_and_msg(L, L.csa_compress_kv_step(arr, 1, api.FP8_E4M3, None))
+    assert st == UNS and "x dtype" in msg
 
 
 def indexer(L, **over):

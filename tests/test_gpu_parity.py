@@ -121,6 +121,59 @@ def check_pooled(kind, fmt, d, dr, codes, scales, gc, gs):
         assert np.all(np.abs(q - r) <= step)
 
 
+@pytest.mark.parametrize("kind,fmt,m,dr,xfmt,ring,content", [
+    (0, O.FP8_E4M3, 4, 64, O.BF16, False, False), (0, O.FP8_E4M3, 128, 64, O.BF16, False, False),
+    (1, O.FP4_E2M1, 4, 0, O.BF16, False, False), (0, O.BF16, 16, 64, O.F32, False, True),
+    (1, O.F32, 4, 0, O.F32, False, True), (0, O.FP8_E4M3, 1, 64, O.BF16, True, False)])
+def test_compress_step_matches_oracle(kind, fmt, m, dr, xfmt, ring, content):
+    """csa_compress_kv_step fed one token per call: every entry against the
+    oracle's pooling of the same tokens (within one code, as the block kernel;
+    m = 1 entries bit for bit against csa_compress_kv); a block's last token
+    writes one entry per sequence, leaves the state alone, and repeating it
+    changes nothing."""
+    g = synth.rng(4400 + m + fmt + 7 * kind + 1000 * content)
+    d = 512 if kind == 0 and fmt != O.F32 else (64 if kind == 1 else 128)
+    B = 3
+    T = 3 * m if m > 1 else 4
+    x = synth.normal(g, (B, T, d))
+    b = synth.normal(g, m)
+    u = synth.normal(g, d) * np.float32(0.05) if content else None
+    gamma = (1 + 0.2 * synth.normal(g, d)).astype(np.float32) if kind == 0 else None
+    tok = [0, m * 3, m * 1000]
+    cap = 7 if ring else 1010
+    codes, scales, gc_blk, _ = run_compress_both(x, xfmt, tok, m, b, u, gamma, dr, kind, fmt, cap, ring, 0)
+    say(f"compress step kind={kind} fmt={fmt} xfmt={xfmt} m={m} d={d} T={T}")
+    xdev = dev_bf16((x.view(np.uint32) >> 16).astype(np.uint16)) if xfmt == O.BF16 else dev(x)
+    out = api.KVCache(B, cap, d, dr, fmt, ring=ring) if kind == 0 else api.IdxCache(B, cap, d, fmt)
+    state = api.compress_state(B, d) if m > 1 else None
+    job = dict(m=m, score_bias=dev(np.asarray(b, np.float32)), score_proj=None if u is None else dev(u),
+               gamma=None if gamma is None else dev(gamma), rope_dim=dr, state=state)
+    job["kv_out" if kind == 0 else "idx_out"] = out
+
+    def step(i):
+        pos = dev(np.array([t0 + i for t0 in tok], np.int32))
+        api.compress_kv_step([dict(job, x=xdev[:, i].contiguous(), tok_pos=pos)])
+        torch.cuda.synchronize()
+        if kind == 0:
+            return out.rec.cpu().numpy(), None
+        return out.codes.cpu().numpy(), None if out.scales is None else out.scales.cpu().numpy()
+
+    for i in range(T - 1):
+        c1, _ = step(i)
+    st1 = None if state is None else state.clone()
+    gc, gs = step(T - 1)
+    assert np.sum(np.any(c1 != gc, axis=-1)) == B          # one new entry per sequence
+    if m == 1:
+        assert np.array_equal(gc, gc_blk)
+    else:
+        check_pooled(kind, fmt, d, dr, codes, scales, gc, gs)
+        assert torch.equal(state, st1)
+    again, _ = step(T - 1)
+    assert np.array_equal(again, gc)
+    if state is not None:
+        assert torch.equal(state, st1)
+
+
 @pytest.mark.parametrize("case", ["decode_step", "multi_block", "five_jobs", "content_score"])
 def test_compress_batch_matches_single_calls(case):
     """csa_compress_kv_batch: every job's output equals that of its own
