@@ -2,12 +2,18 @@
 1,048,576-token context (DeepSeek-V4-Pro shape), batch 4, on one MI355X.
 
 A step is the whole hot path for one new token per sequence:
-  CSA layer: window append (m=1) + compress the completed 4-token block +
-             compress its indexer key (FP4) + indexer top-1024 over 262,144
-             blocks + sparse MQA (64 heads x 512, 1024 blocks + 128 window,
-             FP8 cache) + grouped output projection 32768 -> 7168 (8 groups)
-  HCA layer: window append + compress the completed 128-token block + dense
-             MQA over 8,192 entries + window + grouped output projection.
+  CSA layer: window append (m=1) + the new token folded into its 4-token
+             block's pooling state, which completes the block (FP8 entry),
+             and likewise into its indexer key (FP4) + indexer top-1024 over
+             262,144 blocks + sparse MQA (64 heads x 512, 1024 blocks + 128
+             window, FP8 cache) + grouped output projection 32768 -> 7168
+             (8 groups)
+  HCA layer: window append + the new token completing its 128-token block
+             from the pooling state + dense MQA over 8,192 entries + window +
+             grouped output projection.
+The timed step is the one whose token completes a block in both layers (the
+position L - 1); the pooling states hold the blocks' earlier tokens, folded
+in by the per-token compression call before timing.
 Inputs are resident in HBM before timing; R copies of every cache, weight and
 workspace are rotated so that consecutive reuse of a buffer is separated by
 more traffic than the 256 MB last-level cache holds.
@@ -88,11 +94,12 @@ def algorithmic_bytes():
     o = B * H * D_HEAD * 2
     win = B * W * REC_ALGO
     return {
-        "csa_compress_kv": B * (1 + M_CSA) * D_HEAD * 2 + B * M_CSA * DI * 2 + 2 * B * REC_ALGO + B * (DI // 2 + DI // 32),
+        "csa_compress_kv": B * (D_HEAD * 2 + (D_HEAD + 2) * 4 + DI * 2 + (DI + 2) * 4) + 2 * B * REC_ALGO
+                           + B * (DI // 2 + DI // 32),
         "csa_indexer_topk": B * N_CSA * (DI // 2 + DI // 32) + B * HI * (DI // 2 + DI // 32 + 4) + B * K_CSA * 4,
         "csa_sparse_mqa_attn": q + B * K_CSA * REC_ALGO + win + o + B * K_CSA * 4,
         "csa_out_proj": G * (HIDDEN // G) * (H * D_HEAD // G) * 2 + B * H * D_HEAD * 2 + B * HIDDEN * 2,
-        "hca_compress_kv": B * (1 + M_HCA) * D_HEAD * 2 + 2 * B * REC_ALGO,
+        "hca_compress_kv": B * (D_HEAD * 2 + (D_HEAD + 2) * 4) + 2 * B * REC_ALGO,
         "hca_dense_mqa_attn": q + B * N_HCA * REC_ALGO + win + o,
         "hca_out_proj": G * (HIDDEN // G) * (H * D_HEAD // G) * 2 + B * H * D_HEAD * 2 + B * HIDDEN * 2,
     }
@@ -149,8 +156,24 @@ def build_state(torch, api, copies, seed=4004):
         s["x_csa"] = randn(B, M_CSA, D_HEAD)
         s["xi_csa"] = randn(B, M_CSA, DI)
         s["x_hca"] = randn(B, M_HCA, D_HEAD)
-        s["x_new_csa"] = s["x_csa"][:, M_CSA - 1:].contiguous()
-        s["x_new_hca"] = s["x_hca"][:, M_HCA - 1:].contiguous()
+        s["x_new_csa"] = s["x_csa"][:, M_CSA - 1].contiguous()
+        s["xi_new_csa"] = s["xi_csa"][:, M_CSA - 1].contiguous()
+        s["x_new_hca"] = s["x_hca"][:, M_HCA - 1].contiguous()
+        # online pooling states of the blocks the step completes, holding the
+        # blocks' earlier tokens (folded in below, one call per token)
+        s["st_csa"] = torch.empty((B, D_HEAD + 2), dtype=torch.float32, device=dev)
+        s["st_idx"] = torch.empty((B, DI + 2), dtype=torch.float32, device=dev)
+        s["st_hca"] = torch.empty((B, D_HEAD + 2), dtype=torch.float32, device=dev)
+        for r_ in range(M_HCA - 1):
+            pos_r = lambda m: torch.full((B,), t + 1 - m + r_, dtype=torch.int32, device=dev)
+            jobs = [dict(x=s["x_hca"][:, r_].contiguous(), tok_pos=pos_r(M_HCA), m=M_HCA, score_bias=b_hca,
+                         state=s["st_hca"], gamma=gam, rope_dim=DR, kv_out=s["hca_c"])]
+            if r_ < M_CSA - 1:
+                jobs += [dict(x=s["x_csa"][:, r_].contiguous(), tok_pos=pos_r(M_CSA), m=M_CSA, score_bias=b_csa,
+                              state=s["st_csa"], gamma=gam, rope_dim=DR, kv_out=s["csa_c"]),
+                         dict(x=s["xi_csa"][:, r_].contiguous(), tok_pos=pos_r(M_CSA), m=M_CSA, score_bias=b_idx,
+                              state=s["st_idx"], idx_out=s["keys"])]
+            api.compress_kv_step(jobs)
         s["q_csa"] = randn(B, 1, H, D_HEAD)
         s["q_hca"] = randn(B, 1, H, D_HEAD)
         qc = torch.randint(0, 256, (B, 1, HI, DI // 2), generator=gen, device=dev, dtype=torch.int32).to(torch.uint8)
@@ -174,8 +197,6 @@ def build_state(torch, api, copies, seed=4004):
         b_csa=b_csa, b_idx=b_idx, b_hca=b_hca, gam=gam, zero1=torch.zeros(1, device=dev),
         pos=torch.full((B, 1), t, dtype=torch.int32, device=dev),
         tok_new=torch.full((B,), t, dtype=torch.int32, device=dev),
-        tok_csa=torch.full((B,), t + 1 - M_CSA, dtype=torch.int32, device=dev),
-        tok_hca=torch.full((B,), t + 1 - M_HCA, dtype=torch.int32, device=dev),
         p_csa=api.attn_params(D_HEAD, DR, W, M_CSA), p_hca=api.attn_params(D_HEAD, DR, W, M_HCA))
     torch.cuda.synchronize()
     return sets, shared
@@ -186,11 +207,11 @@ CALLS = ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_mqa_attn", "csa_out_
 
 # the kernels each call launches, in launch order (for matching rocprof traces)
 CALL_KERNELS = {
-    "csa_compress_kv": ["k_compress"],
+    "csa_compress_kv": ["k_compress_step"],
     "csa_indexer_topk": ["k_idxd_filter", "k_idxd_select"],
     "csa_sparse_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "csa_out_proj": ["k_proj_gemv"],
-    "hca_compress_kv": ["k_compress"],
+    "hca_compress_kv": ["k_compress_step"],
     "hca_dense_mqa_attn": ["k_attn_mfma", "k_attn_combine"],
     "hca_out_proj": ["k_proj_gemv"],
 }
@@ -198,15 +219,16 @@ CALL_KERNELS = {
 
 def call_fns(api):
     """One function per call of the decode step (each launches that call's kernels)."""
-    # the step's three CSA compressions (window entry, block, indexer key) and
-    # two HCA ones are each one batched call
+    # the step's three CSA compressions (window entry, the block's last token,
+    # the indexer key's last token) and two HCA ones are each one per-token call
     def c0(s, sh):
-        api.compress_kv_batch([
-            dict(x=s["x_new_csa"], tok_start=sh["tok_new"], m=1, score_bias=sh["zero1"], gamma=sh["gam"],
+        api.compress_kv_step([
+            dict(x=s["x_new_csa"], tok_pos=sh["tok_new"], m=1, score_bias=sh["zero1"], gamma=sh["gam"],
                  rope_dim=DR, kv_out=s["win_csa"]),
-            dict(x=s["x_csa"], tok_start=sh["tok_csa"], m=M_CSA, score_bias=sh["b_csa"], gamma=sh["gam"],
-                 rope_dim=DR, kv_out=s["csa_c"]),
-            dict(x=s["xi_csa"], tok_start=sh["tok_csa"], m=M_CSA, score_bias=sh["b_idx"], idx_out=s["keys"])])
+            dict(x=s["x_new_csa"], tok_pos=sh["tok_new"], m=M_CSA, score_bias=sh["b_csa"], state=s["st_csa"],
+                 gamma=sh["gam"], rope_dim=DR, kv_out=s["csa_c"]),
+            dict(x=s["xi_new_csa"], tok_pos=sh["tok_new"], m=M_CSA, score_bias=sh["b_idx"], state=s["st_idx"],
+                 idx_out=s["keys"])])
 
     def c1(s, sh):
         api.indexer_topk(s["qI"], api.FP4_E2M1, s["w_idx"], s["keys"], sh["pos"], M_CSA, K_CSA, q_scales=s["qI_s"],
@@ -220,11 +242,11 @@ def call_fns(api):
         api.out_proj_grouped(s["o_csa"].view(B, H * D_HEAD), s["Wo_csa"], y=s["y_csa"])
 
     def c4(s, sh):
-        api.compress_kv_batch([
-            dict(x=s["x_new_hca"], tok_start=sh["tok_new"], m=1, score_bias=sh["zero1"], gamma=sh["gam"],
+        api.compress_kv_step([
+            dict(x=s["x_new_hca"], tok_pos=sh["tok_new"], m=1, score_bias=sh["zero1"], gamma=sh["gam"],
                  rope_dim=DR, kv_out=s["win_hca"]),
-            dict(x=s["x_hca"], tok_start=sh["tok_hca"], m=M_HCA, score_bias=sh["b_hca"], gamma=sh["gam"],
-                 rope_dim=DR, kv_out=s["hca_c"])])
+            dict(x=s["x_new_hca"], tok_pos=sh["tok_new"], m=M_HCA, score_bias=sh["b_hca"], state=s["st_hca"],
+                 gamma=sh["gam"], rope_dim=DR, kv_out=s["hca_c"])])
 
     def c5(s, sh):
         api.hca_dense_mqa_attn(s["q_hca"], sh["pos"], s["hca_c"], s["win_hca"], s["sink_hca"], sh["p_hca"],
@@ -397,11 +419,11 @@ def prefill_flops():
 def decode_configs_measure(torch, api, reps=20, seed=6006):
     """The two other decode workloads, each one step per rep with L2 and the
     last-level cache evicted before it (a 1 GiB write outside the events):
-      HCA decode, bf16, batch 16 at 65,536 tokens: window append + 128-token
-        block compress, dense attention over 512 entries + window (32 heads x
+      HCA decode, bf16, batch 16 at 65,536 tokens: window append + the token
+        completing its 128-token block (per-token compression), dense attention over 512 entries + window (32 heads x
         512), grouped projection 16384 -> 4096 (8 groups);
-      CSA decode, bf16, batch 32 at 131,072 tokens: window append + block +
-        indexer-key compress, indexer top-1024 over 32,768 bf16 keys, sparse
+      CSA decode, bf16, batch 32 at 131,072 tokens: window append + the token
+        completing its block and its indexer key, indexer top-1024 over 32,768 bf16 keys, sparse
         attention over 1,024 entries + window (32 heads x 512), grouped
         projection 16384 -> 4096.
     Caches are the library's compression of seeded N(0,1) raw tokens.
@@ -439,10 +461,22 @@ def decode_configs_measure(torch, api, reps=20, seed=6006):
                         rope_dim=DR, kv_out=win)
         pos = torch.full((Bc, 1), t, dtype=torch.int32, device=dev)
         x_blk = torch.randn(Bc, m, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
-        x_new = x_blk[:, m - 1:].contiguous()
+        x_new = x_blk[:, m - 1].contiguous()
         xi_blk = torch.randn(Bc, m, DI, generator=gen, device=dev).to(torch.bfloat16)
+        xi_new = xi_blk[:, m - 1].contiguous()
         tok_new = torch.full((Bc,), t, dtype=torch.int32, device=dev)
-        tok_blk = torch.full((Bc,), t + 1 - m, dtype=torch.int32, device=dev)
+        # pooling states of the block the timed step completes, holding its
+        # earlier tokens
+        st_kv = torch.empty((Bc, D_HEAD + 2), dtype=torch.float32, device=dev)
+        st_ix = torch.empty((Bc, DI + 2), dtype=torch.float32, device=dev)
+        for r_ in range(m - 1):
+            pr = torch.full((Bc,), t + 1 - m + r_, dtype=torch.int32, device=dev)
+            jobs = [dict(x=x_blk[:, r_].contiguous(), tok_pos=pr, m=m, score_bias=bias, state=st_kv, gamma=gam,
+                         rope_dim=DR, kv_out=comp)]
+            if sparse:
+                jobs.append(dict(x=xi_blk[:, r_].contiguous(), tok_pos=pr, m=m, score_bias=caches[1][2], state=st_ix,
+                                 idx_out=keys))
+            api.compress_kv_step(jobs)
         q = torch.randn(Bc, 1, Hq, D_HEAD, generator=gen, device=dev).to(torch.bfloat16)
         qI = torch.randn(Bc, 1, HI, DI, generator=gen, device=dev).to(torch.bfloat16)
         wI = torch.randn(Bc, 1, HI, generator=gen, device=dev)
@@ -457,11 +491,13 @@ def decode_configs_measure(torch, api, reps=20, seed=6006):
         iws = torch.empty(max(1, api.indexer_workspace_bytes(Bc, 1, n, K_CSA)), dtype=torch.uint8, device=dev)
 
         def comp_call():
-            jobs = [dict(x=x_new, tok_start=tok_new, m=1, score_bias=zero1, gamma=gam, rope_dim=DR, kv_out=win),
-                    dict(x=x_blk, tok_start=tok_blk, m=m, score_bias=bias, gamma=gam, rope_dim=DR, kv_out=comp)]
+            jobs = [dict(x=x_new, tok_pos=tok_new, m=1, score_bias=zero1, gamma=gam, rope_dim=DR, kv_out=win),
+                    dict(x=x_new, tok_pos=tok_new, m=m, score_bias=bias, state=st_kv, gamma=gam, rope_dim=DR,
+                         kv_out=comp)]
             if sparse:
-                jobs.append(dict(x=xi_blk, tok_start=tok_blk, m=m, score_bias=caches[1][2], idx_out=keys))
-            api.compress_kv_batch(jobs)
+                jobs.append(dict(x=xi_new, tok_pos=tok_new, m=m, score_bias=caches[1][2], state=st_ix,
+                                 idx_out=keys))
+            api.compress_kv_step(jobs)
 
         def idx_call():
             api.indexer_topk(qI, api.BF16, wI, keys, pos, m, K_CSA, out=top, workspace=iws)
@@ -486,7 +522,8 @@ def decode_configs_measure(torch, api, reps=20, seed=6006):
         ms = float(np.median(st))
         qo = Bc * Hq * D_HEAD * 2
         ne = (K_CSA if sparse else n) + W
-        algo = {"compress_kv": Bc * (1 + m) * D_HEAD * 2 + 2 * Bc * 2 * D_HEAD + (Bc * m * DI * 2 + Bc * DI * 2 if sparse else 0),
+        algo = {"compress_kv": Bc * (D_HEAD * 2 + (D_HEAD + 2) * 4) + 2 * Bc * 2 * D_HEAD
+                               + (Bc * (DI * 2 + (DI + 2) * 4) + Bc * DI * 2 if sparse else 0),
                 "attention": 2 * qo + Bc * ne * 2 * D_HEAD + (Bc * K_CSA * 4 if sparse else 0),
                 "out_proj": G * (hid // G) * (Hq * D_HEAD // G) * 2 + qo + Bc * hid * 2}
         if sparse:
@@ -705,11 +742,11 @@ def cpu_baseline_prefill(target_s, nq=512):
 # profiles/ gives the counts and commands); valid only while the kernels'
 # sources are unchanged (src_hash below).
 TRAFFIC = {
-    "csa_indexer_topk": {"bytes": 38_515_914, "src": "11826d2d82e0a7ae"},
-    "csa_sparse_mqa_attn": {"bytes": 25_819_603, "src": "11826d2d82e0a7ae"},
-    "hca_dense_mqa_attn": {"bytes": 54_434_710, "src": "11826d2d82e0a7ae"},
-    "csa_out_proj": {"bytes": 59_134_999, "src": "11826d2d82e0a7ae"},
-    "hca_out_proj": {"bytes": 59_134_999, "src": "11826d2d82e0a7ae"},
+    "csa_indexer_topk": {"bytes": 38_521_188, "src": "14646f085a62e30a"},
+    "csa_sparse_mqa_attn": {"bytes": 25_819_245, "src": "14646f085a62e30a"},
+    "hca_dense_mqa_attn": {"bytes": 54_433_968, "src": "14646f085a62e30a"},
+    "csa_out_proj": {"bytes": 59_134_999, "src": "14646f085a62e30a"},
+    "hca_out_proj": {"bytes": 59_134_999, "src": "14646f085a62e30a"},
 }
 TRAFFIC_SRC = ["long_context_attention_23_amd/csrc/indexer.hip", "long_context_attention_23_amd/csrc/attn_mfma.hip",
                "long_context_attention_23_amd/csrc/attn.hip", "long_context_attention_23_amd/csrc/proj.hip",

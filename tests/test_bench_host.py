@@ -31,7 +31,11 @@ def test_algorithmic_bytes_of_the_layer_pair():
     assert a["hca_dense_mqa_attn"] == 2 * 4 * 64 * 512 * 2 + 4 * n_hca * 580 + 4 * 128 * 580
     # the projection streams its weights once: 8 x 896 x 4096 bf16
     assert a["csa_out_proj"] == 8 * 896 * 4096 * 2 + 4 * 32768 * 2 + 4 * 7168 * 2
-    assert round(sum(a.values()) / 1e6, 2) == 177.35
+    # per-token compression: the new token (bf16) and the block's pooling
+    # state (d + 2 floats) in, the window entry and the finished block out
+    assert a["hca_compress_kv"] == 4 * (512 * 2 + 514 * 4) + 2 * 4 * 580
+    assert a["csa_compress_kv"] == 4 * (512 * 2 + 514 * 4 + 64 * 2 + 66 * 4) + 2 * 4 * 580 + 4 * 34
+    assert round(sum(a.values()) / 1e6, 2) == 176.82
 
 
 def test_traffic_sources_exist_and_hash():
