@@ -39,6 +39,8 @@
 //     work (waves 4..7), whose copies stay in flight through the next phase 1.
 //     The dispatch on the dim quarter (which K-steps and N-tiles are FP8
 //     codes, which RoPE dims) sits outside the tile loop.
+#include <map>
+#include <mutex>
 #include <stddef.h>
 
 #include <type_traits>
@@ -313,7 +315,11 @@ __device__ __forceinline__ int pv_k_of_entry(int e) { return (e & ~7) + 4 * (e &
 // MTW: 16-head groups per wave.  2: wave w takes the 32 heads of half w / 4
 // (64 heads per workgroup); 1: wave w takes the 16 heads of group w / 4 (a
 // workgroup of at most 32 heads keeps all eight waves busy in the products).
-template <int D, int DR, bool F8, typename OT, int MTW>
+// LOOP: the workgroup runs splits blockIdx.x, blockIdx.x + gridDim.x, ...
+// of its row (instantiated for d = 512 and launched only when a row's splits
+// outnumber its workgroups: the loop keeps the query fragments live through
+// the epilogue, more registers than a single split needs).
+template <int D, int DR, bool F8, typename OT, int MTW, bool LOOP>
 __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     warm_kernargs(offsetof(AttnArgs, rope));
     constexpr int DQ = D / 4;              // dims per quarter
@@ -405,9 +411,12 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const int32_t ne = c.nc + a.W;
     const int32_t split = attn_split_len<int32_t>(ne, a.split_tq);
     const int32_t nsplit = attn_nsplit<int32_t>(ne, a.split_tq);
-    const int32_t sp = blockIdx.x;
+    // with LOOP the workgroup runs splits blockIdx.x, blockIdx.x + gridDim.x,
+    // ... of its row one after another (the query prologue once); each split
+    // is computed and stored exactly as by a workgroup of its own
+    int32_t sp = blockIdx.x;
     if (sp >= nsplit) return;
-    const int32_t e0 = sp * split, e1 = min(e0 + split, ne);
+    int32_t e0 = sp * split, e1 = min(e0 + split, ne);
     const bool active = g0 < MT;                       // this wave's first head group exists
     const bool owner = w < MT;                         // wave w runs the softmax of head group w
     // non-RoPE K-steps / N-tiles of this quarter
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     const int nnt = max(0, min(NT, (dn - dbase) / 16));
     const float zscale = a.scale * kLog2e;             // logits in base-2 units
 
-    const int ntiles = (e1 - e0 + kMTE - 1) / kMTE;
+    int ntiles = (e1 - e0 + kMTE - 1) / kMTE;
     // the first tile's records go out before the query prologue; the top-k
     // indices are read two tiles ahead of their records
     Fetch fr;
@@ -437,17 +446,35 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     };
     // the first tiles' records go out as soon as their addresses are known:
     // the barrier after the query's square sums does not wait for them
-    if (fetcher) {
-        if constexpr (F8) {
-            jn = jf2;
-            ring_issue(0, 0, jf0);
-            if (ntiles > 1) ring_issue(1, 1, jf1);
-        } else {
-            jn = jf1;
-            fr = fetch_plan(a, c, e0, e1, fw, lane, jf0);
-            fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
+    auto first_tiles = [&]() __attribute__((always_inline)) {
+        if (fetcher) {
+            if constexpr (F8) {
+                jn = jf2;
+                ring_issue(0, 0, jf0);
+                if (ntiles > 1) ring_issue(1, 1, jf1);
+            } else {
+                jn = jf1;
+                fr = fetch_plan(a, c, e0, e1, fw, lane, jf0);
+                fetch_issue<D, DR>(&sm.raw[0][0], D * 2, fw, lane, fr);
+            }
         }
-    }
+    };
+    first_tiles();
+    // (LOOP) the next split's first top-k indices, read while this split runs
+    int32_t nj0 = 0, nj1 = 0, nj2 = 0;
+    auto next_indices = [&]() __attribute__((always_inline)) {
+        if constexpr (LOOP) {
+            const int32_t sn = sp + (int32_t)gridDim.x;
+            if (sparse && fetcher && a.k > 0 && sn < nsplit) {
+                const int32_t eb = sn * split + fw + kFetchers * lane;
+                const int32_t* top = a.topk + (int64_t)row * a.k;
+                nj0 = top[min(eb, a.k - 1)];
+                nj1 = top[min(eb + kMTE, a.k - 1)];
+                nj2 = top[min(eb + 2 * kMTE, a.k - 1)];
+            }
+        }
+    };
+    next_indices();
 
     // ---- query prologue: q^ = RoPE_t(RMSNorm(q)), this wave's 32 heads and quarter
 #pragma unroll
@@ -751,13 +778,18 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     //            expand tile t+1 and send the fetch of tile t+2
     // buffers: any formats, tile t in bf16 buffer t % 2; FP8 ring, tile t in ring t % 3
     constexpr int NB = MfmaTiles<D, DR, F8>::kBufs;
+    // the quarter dispatch sits outside the split loop too, so that the
+    // output accumulators keep one register set (the epilogue's returns end
+    // the kernel)
+    with_quarter([&](auto qdc) {
+    for (;;) {                                          // this workgroup's splits
     if constexpr (F8) {
         if (fetcher) wait_vm();
     } else {
         fetch_step(0, 0);
     }
     __syncthreads();
-    with_quarter([&](auto qdc) {
+    {
         int bcur = 0, bprev = NB - 1;
         for (int tt = 0; tt < ntiles; tt++) {
             if (active) {
@@ -780,7 +812,7 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             bcur = bcur + 1 == NB ? 0 : bcur + 1;
         }
         if (active && ntiles > 0) pv_step(qdc, bprev);
-    });
+    }
 
     // ---- epilogue
 #pragma unroll
@@ -899,6 +931,28 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
             wml[hr * 2 + 1] = lrun[i];
         }
     }
+    // ---- the next split of this workgroup: its entries, top-k indices and
+    // first records (once every wave has read the staged partial out of
+    // LDS), then fresh accumulators
+    sp += (int32_t)gridDim.x;
+    if (!LOOP || sp >= nsplit) return;                  // workgroup-uniform
+    e0 = sp * split;
+    e1 = min(e0 + split, ne);
+    ntiles = (e1 - e0 + kMTE - 1) / kMTE;
+    __syncthreads();
+    jf0 = nj0;
+    jf1 = nj1;
+    jf2 = nj2;
+    first_tiles();
+    next_indices();
+#pragma unroll
+    for (int mt = 0; mt < MTW; mt++)
+#pragma unroll
+        for (int nd = 0; nd < NT; nd++) o[mt][nd] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < 4; i++) { mrun[i] = -INFINITY; lrun[i] = 0.0f; }
+    }
+    });
 }
 
 bool attn_mfma_supported(const AttnArgs& a) {
@@ -910,19 +964,53 @@ bool attn_mfma_supported(const AttnArgs& a) {
     return true;
 }
 
+// Workgroups of kernel k resident on the whole current device at once (CUs
+// times the workgroups one CU holds), cached per (device, kernel); 0 when
+// the runtime cannot say.
+static int resident_wgs(const void* k) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    const auto key = std::make_pair(dev, k);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, kNW * 64, 0) != hipSuccess)
+        return 0;
+    const int v = cus * (per > 0 ? per : 1);
+    cache[key] = v;
+    return v;
+}
+
 template <bool F8, typename OT>
 static void launch_d(const AttnArgs& a0, int nsplit, hipStream_t st) {
     AttnArgs a = a0;
     a.nsplit_max = nsplit;                              // part_bf16: set by launch_attention
     const int groups = (a.H + 63) / 64;
-    dim3 grid((unsigned)nsplit, (unsigned)a.rows, (unsigned)groups);
     // eight waves per workgroup always (head groups x dim quarters); a
     // workgroup covers up to 64 heads, or with at most 32 heads (d 512) one
     // 16-head group per wave, so that all eight waves multiply
-    if (a.d == 128) hipLaunchKernelGGL((k_attn_mfma<128, 64, F8, OT, 2>), grid, dim3(kNW * 64), 0, st, a);
-    else if (a.d == 256) hipLaunchKernelGGL((k_attn_mfma<256, 64, F8, OT, 2>), grid, dim3(kNW * 64), 0, st, a);
-    else if (a.H <= 32) hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT, 1>), grid, dim3(kNW * 64), 0, st, a);
-    else hipLaunchKernelGGL((k_attn_mfma<512, 64, F8, OT, 2>), grid, dim3(kNW * 64), 0, st, a);
+    void (*k)(AttnArgs) = a.d == 128 ? k_attn_mfma<128, 64, F8, OT, 2, false>
+                        : a.d == 256 ? k_attn_mfma<256, 64, F8, OT, 2, false>
+                        : a.H <= 32  ? k_attn_mfma<512, 64, F8, OT, 1, false>
+                                     : k_attn_mfma<512, 64, F8, OT, 2, false>;
+    // split slots per row: every split its own workgroup while they all fit
+    // on the chip at once; beyond that (d = 512) as many slots as fit, each
+    // workgroup running several splits of its row in turn (the query
+    // prologue is paid once per workgroup, not once per split).  A split's
+    // result does not depend on the workgroup that runs it, so neither does
+    // any output bit.
+    int gx = nsplit;
+    const int64_t per_slot = (int64_t)a.rows * groups;
+    const int slots = a.d == 512 ? resident_wgs(reinterpret_cast<const void*>(k)) : 0;
+    if (slots > 0 && per_slot * nsplit > slots) {
+        gx = (int)std::max<int64_t>(1, slots / per_slot);
+        k = a.H <= 32 ? k_attn_mfma<512, 64, F8, OT, 1, true> : k_attn_mfma<512, 64, F8, OT, 2, true>;
+    }
+    hipLaunchKernelGGL(k, dim3((unsigned)gx, (unsigned)a.rows, (unsigned)groups), dim3(kNW * 64), 0, st, a);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, int64_t nsplit_bound, hipStream_t st) {

@@ -640,6 +640,44 @@ def test_sparse_attention_deterministic_and_batch_invariant():
         assert torch.equal(c[0].view(torch.int16), a[i].view(torch.int16))
 
 
+def test_attention_workgroups_running_several_splits_are_bit_exact():
+    """At 32 sequences the decode splits outnumber the workgroups the chip
+    holds (32 rows x 36 splits of the 1,152 entries), so each workgroup runs
+    several splits of its row in turn; every row must equal, bit for bit, the
+    same row computed alone (36 workgroups, one split each), for the sparse
+    and the dense path."""
+    g = synth.rng(663)
+    B, H, d, dr, W, m, ccap, k = 32, 64, 512, 64, 128, 4, 2048, 1024
+    comp, win = build_caches(g, B, ccap, W + 8, d, dr, O.FP8_E4M3, O.FP8_E4M3)
+    q = synth.normal(g, (B, 1, H, d))
+    qb = dev_bf16((q.view(np.uint32) >> 16).astype(np.uint16))
+    pos = (m * ccap - 1 - 3 * np.arange(B, dtype=np.int32)).reshape(B, 1)
+    vis = np.minimum((pos.reshape(-1) + 1) // m, ccap)
+    topk = synth.topk_lists(g, vis, k, B).reshape(B, 1, k)
+    sink = synth.normal(g, H)
+    cc = api.KVCache(B, ccap, d, dr, O.FP8_E4M3, rec=dev(comp))
+    wc = api.KVCache(B, W + 8, d, dr, O.FP8_E4M3, ring=True, rec=dev(win))
+    # dense rows: m = 128 over the same 2,048-record caches (~2,176 entries, 34 splits)
+    pos_d = (128 * ccap - 1 - 3 * np.arange(B, dtype=np.int32)).reshape(B, 1)
+    for dense in (False, True):
+        p = api.attn_params(d, dr, W, 128 if dense else m)
+        if dense:
+            pos = pos_d
+        say(f"several splits per workgroup, dense={dense}")
+        if dense:
+            a = api.hca_dense_mqa_attn(qb, dev(pos), cc, wc, dev(sink), p)
+        else:
+            a = api.sparse_mqa_attn(qb, dev(pos), dev(topk), cc, wc, dev(sink), p)
+        for i in (0, 1, 13, 31):
+            c1 = api.KVCache(1, ccap, d, dr, O.FP8_E4M3, rec=dev(comp[i:i + 1]))
+            w1 = api.KVCache(1, W + 8, d, dr, O.FP8_E4M3, ring=True, rec=dev(win[i:i + 1]))
+            if dense:
+                c = api.hca_dense_mqa_attn(qb[i:i + 1], dev(pos[i:i + 1]), c1, w1, dev(sink), p)
+            else:
+                c = api.sparse_mqa_attn(qb[i:i + 1], dev(pos[i:i + 1]), dev(topk[i:i + 1]), c1, w1, dev(sink), p)
+            assert torch.equal(c[0].view(torch.int16), a[i].view(torch.int16)), (dense, i)
+
+
 @pytest.mark.parametrize("fmt", [O.F32, O.BF16, O.FP8_E4M3])
 def test_sparse_with_every_block_equals_dense(fmt):
     """CSA with a top-k list holding every visible block, in ascending order,
