@@ -949,8 +949,8 @@ __global__ __launch_bounds__(kNW * 64) void k_attn_mfma(AttnArgs a) {
     for (int mt = 0; mt < MTW; mt++)
 #pragma unroll
         for (int nd = 0; nd < NT; nd++) o[mt][nd] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int i = 0; i < 4; i++) { mrun[i] = -INFINITY; lrun[i] = 0.0f; }
+    mrun[0] = mrun[1] = mrun[2] = mrun[3] = -INFINITY;
+    lrun[0] = lrun[1] = lrun[2] = lrun[3] = 0.0f;
     }
     });
 }
