@@ -246,9 +246,10 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG) 
 
 // merge the splits of (row, head): weights exp(m_s - M) with M over the split
 // maxima and the sink.  Thread t sums float4 column t % (d/4) over the splits
-// of group t / (d/4) (splits g, g + G, ... in order); every partial load is
-// issued before the weights are known, so the workgroup waits for memory
-// once; the groups are then added in group order.
+// of group t / (d/4) (splits g, g + G, ... in order); the groups are then
+// added in group order.  Loads return in order: the position and the split
+// maxima and sums go out first, then every partial, so the split weights and
+// the output's RoPE factors are formed while the partials are in flight.
 template <typename OT>
 __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     warm_kernargs(offsetof(AttnArgs, rope));
@@ -265,9 +266,17 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     const float* wo = reinterpret_cast<const float*>(a.ws);
     const float* wml = wo + (size_t)a.rows * NS * a.H * d;
     const size_t mbase = (size_t)row * NS * a.H + h;           // split s at mbase + s * H
-    // ---- every load first: this thread's partial columns of its splits
-    // (addresses clamped to the buffer; splits past the row's count get weight
-    // 0 and are skipped), the position, the split maxima and sums
+    const int lane = tid & (kWave - 1);
+    const int64_t t = a.q_pos[row];
+    float ms = -INFINITY, ls = 0.0f;
+    if (tid < kWave) {
+        const size_t i = (mbase + (size_t)min(lane, NS - 1) * a.H) * 2;
+        ms = wml[i];
+        ls = wml[i + 1];
+    }
+    // ---- then this thread's partial columns of its splits (addresses
+    // clamped to the buffer; splits past the row's count get weight 0 and
+    // are skipped)
     const int nc4 = d / 4 > 0 ? d / 4 : 1;
     const int G = (int)blockDim.x / nc4;                        // split groups
     const int c = tid % nc4, g = tid / nc4;
@@ -296,14 +305,6 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
             if (q < nq) x[q] = wo4[(size_t)min(g + q * G, NS - 1) * sstride];
         }
     }
-    const int64_t t = a.q_pos[row];
-    const int lane = tid & (kWave - 1);
-    float ms = -INFINITY, ls = 0.0f;
-    if (tid < kWave) {
-        const size_t i = (mbase + (size_t)min(lane, NS - 1) * a.H) * 2;
-        ms = wml[i];
-        ls = wml[i + 1];
-    }
     stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
     const int64_t nc = comp_slots(a, t);
     const int nsplit = (int)attn_nsplit<int64_t>(nc + a.W, a.split_tq);
@@ -320,6 +321,17 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
         if (M != -INFINITY) den += expf(sk - M);
         wsc[lane] = w;
         if (lane == 0) den_s = den;
+    }
+    // the -t rotation of this thread's RoPE pairs (vector path: thread c <
+    // d / 4 owns dims 4c .. 4c + 3; pairs start at even dims and d - dr is
+    // even, so a pair never straddles two threads), from the argument block
+    float rsn[2] = {0.0f, 0.0f}, rcs[2] = {1.0f, 1.0f};
+    if (vec && tid < nc4) {
+        const double* rfa = (const double*)((const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(AttnArgs, rope));
+        const int k0 = 4 * tid, off = d - a.dr;
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+            if (k0 + 2 * u >= off) rope_sincos(-(double)t, rfa[(k0 + 2 * u - off) / 2], rsn[u], rcs[u]);
     }
     __syncthreads();
     if (!vec) {
@@ -360,8 +372,7 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     part[tid] = acc;
     __syncthreads();
     // ---- thread c < d / 4 adds the groups in order, normalises its four
-    // dims, rotates the RoPE pairs among them (pairs start at even dims and
-    // d - dr is even, so a pair never straddles two threads) and stores them
+    // dims, rotates the RoPE pairs among them and stores them as one vector
     if (tid < nc4) {
         const float den = den_s;
         float4 r = part[tid];
@@ -376,16 +387,22 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             if (k0 + 2 * u >= off) {
-                float sn, cs;
-                rope_sincos(-(double)t, rf[(k0 + 2 * u - off) / 2], sn, cs);
                 const float x0 = o[2 * u], x1 = o[2 * u + 1];
-                o[2 * u] = x0 * cs - x1 * sn;
-                o[2 * u + 1] = x0 * sn + x1 * cs;
+                o[2 * u] = x0 * rcs[u] - x1 * rsn[u];
+                o[2 * u + 1] = x0 * rsn[u] + x1 * rcs[u];
             }
         }
-        OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d;
+        OT* out = reinterpret_cast<OT*>(a.out) + (row * a.H + h) * d + k0;
+        if ((reinterpret_cast<uintptr_t>(out) & (4 * sizeof(OT) - 1)) != 0) {   // an unaligned output
 #pragma unroll
-        for (int u = 0; u < 4; u++) st_scalar<OT>(out, k0 + u, o[u]);
+            for (int u = 0; u < 4; u++) st_scalar<OT>(out, u, o[u]);
+        } else if constexpr (sizeof(OT) == 2) {
+            *reinterpret_cast<uint2*>(out) = make_uint2(
+                (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16),
+                (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16));
+        } else {
+            *reinterpret_cast<float4*>(out) = make_float4(o[0], o[1], o[2], o[3]);
+        }
     }
 }
 
