@@ -1720,7 +1720,7 @@ constexpr int kDfWaves = kDfThreads / kWave;
 constexpr int kDfTiles = 16;                                         // 32-key tiles per wave
 constexpr int kDfChunk = kDfWaves * kDfTiles * 32;                   // keys per filter workgroup
 constexpr int kDfSegCands = 1024;                                    // above-threshold slots per workgroup
-constexpr int kDsSampTiles = 64;                                     // sample tiles per row
+constexpr int kDsSampTiles = 32;                                     // sample tiles per row
 constexpr int kDsSampPerWave = kDsSampTiles / kDfWaves;
 constexpr int kDecMaxSeg = (int)(kIdxDecMaxCap / kDfChunk);          // workgroups per row at most
 constexpr int kDecHdr = 1024;                                        // T, counts per segment

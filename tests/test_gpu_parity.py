@@ -410,7 +410,7 @@ def test_indexer_decode_fallback_rows_exact():
     qs[1, 2] = 127
     w[1, 2] = 1.0
     ntile = -(-cap // 32)                                    # query (1, 2) sees every block
-    stride = -(-ntile // 64)
+    stride = -(-ntile // 32)                                 # the decode filter samples 32 tiles per row
     for i in range(-(-ntile // stride)):
         t0 = 32 * (i * stride + (((i * 37 + 11) & 63) * stride >> 6))
         kc[1, t0:t0 + 4] = 0x77
