@@ -19,6 +19,8 @@
 //
 // This file holds the generic kernel (fp32 VALU, any cache format); the MFMA
 // kernel for bf16 queries lives in attn_mfma.hip.
+#include <map>
+#include <mutex>
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,6 +34,7 @@ constexpr int kAttnMaxD = 1024;
 constexpr int kCombThreads = 1024;
 constexpr int kCombMaxSplits = 64;
 constexpr int kCombLoads = kCombMaxSplits / (kCombThreads / (kAttnMaxD / 4));
+constexpr int kComb256Loads = 8;           // loads per split group in the 256-thread combine
 constexpr int kAttnQFloats = 4096;
 
 __device__ __forceinline__ int64_t comp_slots(const AttnArgs& a, int64_t t) {
@@ -250,8 +253,18 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_valu(AttnArgs a, int HG) 
 // added in group order.  Loads return in order: the position and the split
 // maxima and sums go out first, then every partial, so the split weights and
 // the output's RoPE factors are formed while the partials are in flight.
-template <typename OT>
-__global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
+//
+// The split groups are those of a 1,024-thread workgroup (Gc = 1,024 / (d/4)
+// groups, whatever the launch) and every group is summed in the same order,
+// so the result bits do not depend on NT.  NT = 256 (bf16 partials, d/4
+// dividing 256, at most kComb256Loads loads per group): each thread runs R =
+// 4 of those groups, so four workgroups fit on a CU where one of 1,024
+// threads does (the launcher takes it when (head, row) pairs outnumber the
+// CUs).
+template <typename OT, int NT, bool PB>
+__global__ __launch_bounds__(NT) void k_attn_combine(AttnArgs a) {
+    constexpr int R = kCombThreads / NT;                        // canonical split groups per thread
+    constexpr int LQ = R == 1 ? kCombLoads : kComb256Loads;     // loads per group at most
     warm_kernargs(offsetof(AttnArgs, rope));
     __shared__ float v[kAttnMaxD];
     __shared__ float wsc[kCombMaxSplits];
@@ -278,31 +291,32 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
     // clamped to the buffer; splits past the row's count get weight 0 and
     // are skipped)
     const int nc4 = d / 4 > 0 ? d / 4 : 1;
-    const int G = (int)blockDim.x / nc4;                        // split groups
-    const int c = tid % nc4, g = tid / nc4;
+    const int G = kCombThreads / nc4;                           // split groups (canonical)
+    const int c = tid % nc4, g0 = R * (tid / nc4);              // this thread's column and first group
     const float4* wo4 = reinterpret_cast<const float4*>(wo + mbase * d) + c;
     const uint2* wb4 = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(a.ws) + mbase * d) + c;
     const size_t sstride = (size_t)a.H * d / 4;                 // 4-value groups between splits
     const bool vec = d % 4 == 0;
-    const bool pb = a.part_bf16 != 0;                           // partials in bf16
+    constexpr bool pb = PB;                                     // partials in bf16 (a.part_bf16)
     const int nq = vec ? (NS + G - 1) / G : 0;
-    float4 x[kCombLoads];
-    if (pb) {
-        uint2 xb[kCombLoads];
+    // group g0 + r, load q: split g0 + r + q G (bf16 partials stay packed
+    // until the weights are known)
+    uint2 xb[PB ? R : 1][PB ? LQ : 1];
+    float4 xf[PB ? 1 : LQ];
+    static_assert(PB || R == 1, "fp32 partials: the 1,024-thread combine");
+    if constexpr (PB) {
 #pragma unroll
-        for (int q = 0; q < kCombLoads; q++) {
-            xb[q] = make_uint2(0u, 0u);
-            if (q < nq) xb[q] = wb4[(size_t)min(g + q * G, NS - 1) * sstride];
-        }
+        for (int r = 0; r < R; r++)
 #pragma unroll
-        for (int q = 0; q < kCombLoads; q++)
-            x[q] = make_float4(__uint_as_float(xb[q].x << 16), __uint_as_float(xb[q].x & 0xFFFF0000u),
-                               __uint_as_float(xb[q].y << 16), __uint_as_float(xb[q].y & 0xFFFF0000u));
+            for (int q = 0; q < LQ; q++) {
+                xb[r][q] = make_uint2(0u, 0u);
+                if (q < nq) xb[r][q] = wb4[(size_t)min(g0 + r + q * G, NS - 1) * sstride];
+            }
     } else {
 #pragma unroll
-        for (int q = 0; q < kCombLoads; q++) {
-            x[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (q < nq) x[q] = wo4[(size_t)min(g + q * G, NS - 1) * sstride];
+        for (int q = 0; q < LQ; q++) {
+            xf[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (q < nq) xf[q] = wo4[(size_t)min(g0 + q * G, NS - 1) * sstride];
         }
     }
     stage_rope_arg(offsetof(AttnArgs, rope), rf, a.dr / 2);
@@ -354,22 +368,34 @@ __global__ __launch_bounds__(kCombThreads) void k_attn_combine(AttnArgs a) {
         for (int k = tid; k < d; k += blockDim.x) st_scalar<OT>(out, k, v[k]);
         return;
     }
-    // ---- this thread's splits in order, then the groups in order
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    if (g < G) {
+    // ---- each group's splits in order, then the groups in order
 #pragma unroll
-        for (int q = 0; q < kCombLoads; q++) {
-            const int s = g + q * G;
-            if (q < nq && s < nsplit) {
-                const float w = wsc[s];
-                acc.x = fmaf(w, x[q].x, acc.x);
-                acc.y = fmaf(w, x[q].y, acc.y);
-                acc.z = fmaf(w, x[q].z, acc.z);
-                acc.w = fmaf(w, x[q].w, acc.w);
+    for (int r = 0; r < R; r++) {
+        const int g = g0 + r;
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (g < G) {
+#pragma unroll
+            for (int q = 0; q < LQ; q++) {
+                const int s = g + q * G;
+                if (q < nq && s < nsplit) {
+                    const float w = wsc[s];
+                    float4 x;
+                    if constexpr (PB) {
+                        const uint2 u = xb[r][q];
+                        x = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+                    } else {
+                        x = xf[q];
+                    }
+                    acc.x = fmaf(w, x.x, acc.x);
+                    acc.y = fmaf(w, x.y, acc.y);
+                    acc.z = fmaf(w, x.z, acc.z);
+                    acc.w = fmaf(w, x.w, acc.w);
+                }
             }
+            part[g * nc4 + c] = acc;
         }
     }
-    part[tid] = acc;
     __syncthreads();
     // ---- thread c < d / 4 adds the groups in order, normalises its four
     // dims, rotates the RoPE pairs among them and stores them as one vector
@@ -412,6 +438,22 @@ int64_t attn_ws_bytes(int64_t rows, int32_t split_tq, int32_t H, int32_t d, int6
     return rows * nb * H * ((int64_t)d + 2) * 4;
 }
 
+// compute units of the current device, cached per device (a large number
+// when the runtime cannot say, which keeps the default combine)
+static int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 1 << 30;
+    std::lock_guard<std::mutex> lk(mu);
+    const auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 1 << 30;
+    cache[dev] = n;
+    return n;
+}
+
 hipError_t launch_attention(const AttnArgs& a0, int64_t max_entries, hipStream_t st) {
     if (a0.rows == 0) return hipSuccess;
     const int64_t nb = attn_nsplit_bound(max_entries, a0.split_tq);
@@ -436,8 +478,16 @@ hipError_t launch_attention(const AttnArgs& a0, int64_t max_entries, hipStream_t
     }
     if (nb > 1) {
         dim3 g2((unsigned)a.H, (unsigned)a.rows);
-        if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t>), g2, dim3(kCombThreads), 0, st, a);
-        else hipLaunchKernelGGL((k_attn_combine<float>), g2, dim3(kCombThreads), 0, st, a);
+        // more (head, row) pairs than CUs: the 256-thread combine (same bits,
+        // four workgroups per CU) where it applies
+        const int nc4 = a.d / 4;
+        const int Gc = nc4 > 0 ? kCombThreads / nc4 : 0;
+        const bool small = a.part_bf16 && a.d % 4 == 0 && nc4 > 0 && 256 % nc4 == 0 &&
+                           (nb + Gc - 1) / Gc <= kComb256Loads && (int64_t)a.H * a.rows > device_cus();
+        if (small) hipLaunchKernelGGL((k_attn_combine<uint16_t, 256, true>), g2, dim3(256), 0, st, a);
+        else if (a.part_bf16) hipLaunchKernelGGL((k_attn_combine<uint16_t, kCombThreads, true>), g2, dim3(kCombThreads), 0, st, a);
+        else if (a.out_fmt == CSA_BF16) hipLaunchKernelGGL((k_attn_combine<uint16_t, kCombThreads, false>), g2, dim3(kCombThreads), 0, st, a);
+        else hipLaunchKernelGGL((k_attn_combine<float, kCombThreads, false>), g2, dim3(kCombThreads), 0, st, a);
     }
     return hipGetLastError();
 }
