@@ -1006,7 +1006,7 @@ static void launch_d(const AttnArgs& a0, int nsplit, hipStream_t st) {
     int gx = nsplit;
     const int64_t per_slot = (int64_t)a.rows * groups;
     const int slots = a.d == 512 ? resident_wgs(reinterpret_cast<const void*>(k)) : 0;
-    if (slots > 0 && per_slot * nsplit > slots) {
+    if (slots > 0 && nsplit > 1 && per_slot * nsplit > slots) {
         gx = (int)std::max<int64_t>(1, slots / per_slot);
         k = a.H <= 32 ? k_attn_mfma<512, 64, F8, OT, 1, true> : k_attn_mfma<512, 64, F8, OT, 2, true>;
     }
