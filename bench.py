@@ -82,6 +82,8 @@ def parse():
     ap.add_argument("--summarize-pmc", metavar="DIR", nargs="+")
     ap.add_argument("--summarize-prefill", metavar="DIR")
     ap.add_argument("--summarize-pmc-kernels", metavar="DIR", nargs="+")
+    ap.add_argument("--summarize-pmc-dispatches", metavar="DIR", nargs="+",
+                    help="per-dispatch counter sums of k_attn_mfma in launch order (one counter per run)")
     ap.add_argument("--summarize-launches", metavar="DIR", nargs="+",
                     help="per kernel and grid: trace durations and counter means of trace / --pmc runs")
     return ap.parse_args()
@@ -911,6 +913,33 @@ def summarize_pmc(dirs):
     print(json.dumps(res, indent=1))
 
 
+def summarize_pmc_dispatches(dirs, match="k_attn_mfma"):
+    """Per-dispatch counter sums (over the counter's instances) in dispatch
+    order, for kernels whose name holds `match`, from rocprofv3 --pmc runs of
+    this benchmark (one counter per run); tells apart launches of one kernel
+    over the same grid (the prefill section's CSA launches come before its
+    HCA launches)."""
+    import sqlite3
+    cols = {}
+    for d in dirs:
+        db = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))[0]
+        c = sqlite3.connect(db)
+        acc = {}
+        for name, cn, v, did in c.execute("select name, counter_name, counter_value, dispatch_id from pmc_events"):
+            if match not in _short(name):
+                continue
+            acc[(did, cn)] = acc.get((did, cn), 0.0) + v
+        for (did, cn), v in acc.items():
+            cols.setdefault(cn, {})[did] = v
+        c.close()
+    names = sorted(cols)
+    print("| launch | " + " | ".join(names) + " |")
+    print("|---|" + "---|" * len(names))
+    per = [sorted(cols[n].items()) for n in names]
+    for i in range(min(len(p) for p in per) if per else 0):
+        print(f"| {i} | " + " | ".join(f"{p[i][1]:.1f}" for p in per) + " |")
+
+
 def summarize_pmc_kernels(dirs, match=("k_idxp_", "k_attn_mfma", "k_proj_mfma")):
     """Per-kernel counter means (per dispatch) from rocprofv3 --pmc runs of
     this benchmark (any counters, several runs), for kernels whose name holds
@@ -1015,6 +1044,8 @@ def main():
         return summarize_prefill(args.summarize_prefill)
     if args.summarize_pmc_kernels:
         return summarize_pmc_kernels(args.summarize_pmc_kernels)
+    if args.summarize_pmc_dispatches:
+        return summarize_pmc_dispatches(args.summarize_pmc_dispatches)
     if args.summarize_launches:
         return summarize_launches(args.summarize_launches)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

@@ -129,3 +129,24 @@ def test_launch_summary_by_grid(tmp_path, capsys):
     assert len(rows) == 2                                  # framework kernels are left out
     assert rows["448x1x1 wg of 256"] == ["3", "56.00", "55.00", "897", "200"]
     assert rows["112x1x1 wg of 256"] == ["3", "12.00", "12.00", "225", "200"]
+
+
+def test_pmc_dispatch_summary(tmp_path, capsys):
+    """Per-dispatch counter sums of one kernel, in dispatch order, one column
+    per counter run (instances of a dispatch summed, other kernels ignored)."""
+    import sqlite3
+    for sub, cn, base in (("f", "FETCH_SIZE", 100.0), ("w", "WRITE_SIZE", 10.0)):
+        (tmp_path / sub).mkdir()
+        c = sqlite3.connect(tmp_path / sub / "run_results.db")
+        c.execute("create table pmc_events (name text, counter_name text, counter_value real, dispatch_id integer)")
+        for did in (3, 1, 2):
+            for _ in range(2):
+                c.execute("insert into pmc_events values (?, ?, ?, ?)",
+                          ("void csa::k_attn_mfma<512, 64, true, unsigned short, 2, false>(csa::AttnArgs)", cn,
+                           base * did, did))
+            c.execute("insert into pmc_events values (?, ?, ?, ?)", ("csa::k_idxp_filter(csa::IndexerArgs)", cn, 1.0, 9))
+        c.commit()
+        c.close()
+    bench.summarize_pmc_dispatches([str(tmp_path / "f"), str(tmp_path / "w")])
+    rows = [ln for ln in capsys.readouterr().out.splitlines() if ln.startswith("| ") and not ln.startswith("| launch")]
+    assert rows == ["| 0 | 200.0 | 20.0 |", "| 1 | 400.0 | 40.0 |", "| 2 | 600.0 | 60.0 |"]
